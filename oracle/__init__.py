@@ -1,0 +1,209 @@
+"""Plain CPU oracle for split-KV PagedAttention decode (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the GPU library
+(``paged_attention_decode_tables_amd``) and never imports it; the GPU library
+never imports this.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64 accumulation); this module
+only builds it with gcc, loads it with ctypes and converts numpy arrays.
+Each function names the page passage it follows; see the header of
+``oracle.c`` for the list of pages and the readings taken where they are
+silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+
+
+def lib_path(mutant: int = 0) -> str:
+    name = "liboracle.so" if mutant == 0 else f"liboracle_mutant{mutant}.so"
+    return os.path.join(_HERE, name)
+
+
+def build(mutant: int = 0, openmp: bool = True) -> str:
+    """Compile oracle.c with gcc (mutant > 0 builds a planted-mistake variant)."""
+    out = lib_path(mutant)
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", _SRC, "-o", out + ".tmp", "-lm"]
+    if openmp:
+        cmd.insert(1, "-fopenmp")
+    if mutant:
+        cmd.insert(1, f"-DORACLE_MUTANT={mutant}")
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_F32P = ctypes.POINTER(ctypes.c_float)
+_F64P = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def _ptr(a: Optional[np.ndarray], ctype):
+    if a is None:
+        return ctypes.cast(None, ctype)
+    return a.ctypes.data_as(ctype)
+
+
+def _estrides(a: np.ndarray):
+    return tuple(s // a.itemsize for s in a.strides)
+
+
+class Oracle:
+    """ctypes wrapper around one build of oracle.c."""
+
+    def __init__(self, path: Optional[str] = None, mutant: int = 0):
+        path = path or lib_path(mutant)
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(mutant)
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        L.orc_token_offsets.argtypes = [_I64P, _I64, _I32P, _I64, _I64, _I32P, _I32P, _I32, _I32, _I64, _I64]
+        L.orc_page_indices.argtypes = [_I32P, _I32P, _I64, _I64, _I32P, _I32]
+        L.orc_num_kv_splits.argtypes = [_I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32]
+        common = [_F32P, _I64, _I64, _F32P, _I64, _I64, _F32P, _I64, _I64,
+                  _I32P, _I64, _I64, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                  ctypes.c_double]
+        L.orc_attention.argtypes = [_F64P] + common
+        L.orc_partials.argtypes = [_F64P, _F64P, _F64P] + common + [_I32P, _I32, _I32]
+        L.orc_reduce.argtypes = [_F64P, _F64P, _F64P, _F64P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32]
+        self.mutant = L.orc_mutant_id()
+
+    # -- integer helpers ----------------------------------------------------
+    def token_offsets(self, pages, seq_lens, block_size, block_stride=1, slot_stride=1,
+                      indptr=None, fill=-1):
+        """[S, max_len] int64: offset of token t of sequence s (Triton issue
+        2522, block-table example), -1 where t >= seq_len."""
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        S = seq_lens.shape[0]
+        max_len = int(max(1, seq_lens.max(initial=0)))
+        out = np.full((S, max_len), fill, dtype=np.int64)
+        pages = np.asarray(pages, dtype=np.int32)
+        if pages.ndim == 1:
+            ps, pb = 0, _estrides(pages)[0]
+        else:
+            ps, pb = _estrides(pages)
+        ip = None if indptr is None else np.ascontiguousarray(indptr, dtype=np.int32)
+        rc = self.lib.orc_token_offsets(_ptr(out, _I64P), max_len, _ptr(pages, _I32P), ps, pb,
+                                        _ptr(ip, _I32P), _ptr(seq_lens, _I32P), S, block_size,
+                                        block_stride, slot_stride)
+        assert rc == 0, rc
+        return out
+
+    def page_indices(self, block_table, cu_num_blocks, fill=-1):
+        """Flat page list (vLLM PR 35765, _copy_page_indices_kernel)."""
+        block_table = np.asarray(block_table, dtype=np.int32)
+        cu = np.ascontiguousarray(cu_num_blocks, dtype=np.int32)
+        nreq = cu.shape[0] - 1
+        out = np.full((max(int(cu[-1]), 0) if nreq >= 0 else 0,), fill, dtype=np.int32)
+        s0, s1 = _estrides(block_table) if block_table.ndim == 2 else (0, 1)
+        rc = self.lib.orc_page_indices(_ptr(out, _I32P), _ptr(block_table, _I32P), s0, s1,
+                                       _ptr(cu, _I32P), max(nreq, 0))
+        assert rc == 0, rc
+        return out
+
+    def num_kv_splits(self, seq_lens, num_group, num_head, num_kv_head, max_kv_splits,
+                      device_core_count):
+        """Per-(seq, group) split counts (sglang metadata.py,
+        get_num_kv_splits_triton)."""
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        out = np.zeros(seq_lens.shape[0] * num_group, dtype=np.int32)
+        rc = self.lib.orc_num_kv_splits(_ptr(out, _I32P), _ptr(seq_lens, _I32P), seq_lens.shape[0],
+                                        num_group, num_head, num_kv_head, max_kv_splits,
+                                        device_core_count)
+        if rc != 0:
+            raise ValueError(f"orc_num_kv_splits: invalid arguments (rc={rc})")
+        return out
+
+    # -- attention ----------------------------------------------------------
+    def _problem(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr):
+        q = np.asarray(query, dtype=np.float32)
+        kc = np.asarray(key_cache, dtype=np.float32)
+        vc = np.asarray(value_cache, dtype=np.float32)
+        assert q.ndim == 3 and kc.ndim == 5 and vc.ndim == 4
+        qs = _estrides(q)
+        ks = _estrides(kc)
+        vs = _estrides(vc)
+        S, H, D = q.shape
+        NB, Hkv, Dx, bs, x = kc.shape
+        Dv = vc.shape[2]
+        assert Dx * x == D and vc.shape[3] == bs
+        # inner dims must be packed (the C code walks them directly)
+        assert qs[2] == 1 and ks[2:] == (bs * x, x, 1) and vs[2:] == (bs, 1), (qs, ks, vs)
+        pages = np.asarray(pages, dtype=np.int32)
+        if indptr is not None:
+            ip = np.ascontiguousarray(indptr, dtype=np.int32)
+            ps, pb = 0, _estrides(pages)[0]
+        else:
+            ip = None
+            ps, pb = _estrides(pages)
+        seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        args = [_ptr(q, _F32P), qs[0], qs[1], _ptr(kc, _F32P), ks[0], ks[1], _ptr(vc, _F32P),
+                vs[0], vs[1], _ptr(pages, _I32P), ps, pb, _ptr(ip, _I32P), _ptr(seq, _I32P),
+                S, H, Hkv, D, Dv, bs, x, float(scale)]
+        keep = (q, kc, vc, pages, ip, seq)
+        return args, keep, (S, H, Dv)
+
+    def attention(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr=None):
+        """[S, H, Dv] float64 softmax attention of each query over its paged
+        K/V rows (paged_attention_v2_triton.py, phase-1 docstring steps 1-4
+        applied to the whole sequence)."""
+        args, keep, (S, H, Dv) = self._problem(query, key_cache, value_cache, pages, seq_lens,
+                                               scale, indptr)
+        out = np.empty((S, H, Dv), dtype=np.float64)
+        rc = self.lib.orc_attention(_ptr(out, _F64P), *args)
+        assert rc == 0, rc
+        return out
+
+    def partials(self, query, key_cache, value_cache, pages, seq_lens, scale, max_num_parts,
+                 partition_size=512, num_splits=None, indptr=None):
+        """Phase-1 intermediates (tmp [S,H,P,Dv], max_logits, exp_sums
+        [S,H,P]) in float64; tmp of empty partitions is NaN."""
+        args, keep, (S, H, Dv) = self._problem(query, key_cache, value_cache, pages, seq_lens,
+                                               scale, indptr)
+        tmp = np.full((S, H, max_num_parts, Dv), np.nan, dtype=np.float64)
+        ml = np.empty((S, H, max_num_parts), dtype=np.float64)
+        es = np.empty((S, H, max_num_parts), dtype=np.float64)
+        ns = None if num_splits is None else np.ascontiguousarray(num_splits, dtype=np.int32)
+        rc = self.lib.orc_partials(_ptr(tmp, _F64P), _ptr(ml, _F64P), _ptr(es, _F64P), *args,
+                                   _ptr(ns, _I32P), partition_size, max_num_parts)
+        assert rc == 0, rc
+        return tmp, ml, es
+
+    def reduce(self, tmp, max_logits, exp_sums, seq_lens, partition_size=512, num_splits=None):
+        """Phase-2 log-sum-exp merge (paged_attention_v2_triton.py,
+        _paged_attn_v2_reduce_kernel) -> [S, H, Dv] float64."""
+        tmp = np.ascontiguousarray(tmp, dtype=np.float64)
+        ml = np.ascontiguousarray(max_logits, dtype=np.float64)
+        es = np.ascontiguousarray(exp_sums, dtype=np.float64)
+        S, H, P, Dv = tmp.shape
+        seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        ns = None if num_splits is None else np.ascontiguousarray(num_splits, dtype=np.int32)
+        out = np.empty((S, H, Dv), dtype=np.float64)
+        rc = self.lib.orc_reduce(_ptr(out, _F64P), _ptr(tmp, _F64P), _ptr(ml, _F64P),
+                                 _ptr(es, _F64P), _ptr(seq, _I32P), _ptr(ns, _I32P),
+                                 partition_size, S, H, Dv, P)
+        assert rc == 0, rc
+        return out
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The real (unmutated) oracle, built on first use."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

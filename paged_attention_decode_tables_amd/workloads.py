@@ -1,0 +1,311 @@
+"""Seeded synthetic inputs for split-KV PagedAttention decode.
+
+This module draws inputs only: sequence lengths, block permutations, block
+tables and N(0, 1) query/key/value tensors in the paged layouts. It contains
+none of the method's arithmetic, and it is the one module that both the GPU
+path (tests, benchmark) and the CPU oracle's callers share.
+
+Draw order for every workload, from ``torch.Generator().manual_seed(seed)``:
+lengths, then the physical-block permutation (consumed in order by sequence,
+then logical block), then Q, then the key cache, then the value cache. Each
+is drawn as fp32 N(0, 1) and cast to the workload dtype, so the bits are the
+same wherever the same seed is used.
+
+Layouts (from the kernel signatures of paged_attention_v2_triton.py):
+  query        [S, H, D]
+  key_cache    [NB, Hkv, D/x, block_size, x]   x = 16 // element_size
+  value_cache  [NB, Hkv, Dv, block_size]
+  block_tables [S, max_blocks] int32
+The MLA-style workload stores one latent row of 576 values per page (page
+size 1); its key cache is that row viewed as [NB, 1, 72, 1, 8] and its value
+cache the first 512 values of the same row ([NB, 1, 512, 1], strides
+(576, 576, 1, 1)).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Workload:
+    name: str
+    description: str
+    dtype: torch.dtype
+    seq_lens: torch.Tensor            # [S] int32
+    block_tables: torch.Tensor        # [S, max_blocks] int32
+    query: torch.Tensor               # [S, H, D]
+    key_cache: torch.Tensor           # [NB, Hkv, D/x, bs, x]
+    value_cache: torch.Tensor         # [NB, Hkv, Dv, bs] (may alias key_cache storage)
+    scale: float
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    v_head_size: int
+    block_size: int
+    x: int
+    num_blocks: int
+    partition_size: int = 512
+    # Split-count heuristic inputs (None: fixed partition_size splits).
+    max_kv_splits: Optional[int] = None
+    device_core_count: Optional[int] = None
+    # CSR page list inputs (MLA-style workload): indptr over block_tables rows.
+    cu_num_blocks: Optional[torch.Tensor] = None
+    latent: Optional[torch.Tensor] = None
+    poison_block: Optional[int] = None
+    notes: List[str] = field(default_factory=list)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def elem_size(self) -> int:
+        return torch.tensor([], dtype=self.dtype).element_size()
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.seq_lens.clamp(min=0).sum())
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.num_seqs else 0
+
+    @property
+    def kv_aliased(self) -> bool:
+        return self.latent is not None
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes of one decode step: every live token's K and V
+        read once per kv head ((D + Dv) * elem), or D * elem when V aliases K."""
+        per_tok = self.head_size if self.kv_aliased else self.head_size + self.v_head_size
+        return self.total_tokens * self.num_kv_heads * per_tok * self.elem_size
+
+    def to(self, device) -> "Workload":
+        kw = {k: getattr(self, k) for k in self.__dataclass_fields__}
+        for k in ("seq_lens", "block_tables", "query", "cu_num_blocks"):
+            if kw[k] is not None:
+                kw[k] = kw[k].to(device)
+        if self.latent is not None:
+            lat = self.latent.to(device)
+            kw["latent"] = lat
+            kw["key_cache"], kw["value_cache"] = _mla_views(lat, self.v_head_size)
+        else:
+            kw["key_cache"] = self.key_cache.to(device)
+            kw["value_cache"] = self.value_cache.to(device)
+        kw["notes"] = list(self.notes)
+        return Workload(**kw)
+
+
+def _mla_views(latent: torch.Tensor, dv: int):
+    nb, d = latent.shape
+    x = 16 // latent.element_size()
+    k = latent.view(nb, 1, d // x, 1, x)
+    v = torch.as_strided(latent, (nb, 1, dv, 1), (d, d, 1, 1))
+    return k, v
+
+
+def _randn(gen, shape, dtype):
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(dtype)
+
+
+def _assign_blocks(perm: torch.Tensor, nblocks: List[int], max_blocks: int, pad: int) -> torch.Tensor:
+    """Block table rows filled from perm in order (seq, then logical block)."""
+    bt = torch.full((len(nblocks), max(max_blocks, 1)), pad, dtype=torch.int32)
+    pos = 0
+    for s, n in enumerate(nblocks):
+        bt[s, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+    return bt
+
+
+def _blocks_needed(lens, bs):
+    return [max(0, (int(L) + bs - 1) // bs) for L in lens]
+
+
+def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size: int,
+           v_head_size: Optional[int] = None, block_size: int, dtype="f32",
+           num_blocks: Optional[int] = None, partition_size: int = 512,
+           max_blocks: Optional[int] = None, poison: bool = False, name="custom") -> Workload:
+    """Standard layout workload with the given lengths (drawn in the standard order)."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    esz = torch.tensor([], dtype=dt).element_size()
+    x = 16 // esz
+    dv = v_head_size or head_size
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(seq_lens, dtype=torch.int32).clone()
+    need = _blocks_needed(lens.tolist(), block_size)
+    total = sum(need)
+    nb = num_blocks if num_blocks is not None else total + (1 if poison else 0)
+    if nb < total + (1 if poison else 0):
+        raise ValueError("not enough physical blocks")
+    perm = torch.randperm(nb, generator=gen)
+    S = lens.shape[0]
+    q = _randn(gen, (S, num_heads, head_size), dt)
+    kc = _randn(gen, (nb, num_kv_heads, head_size // x, block_size, x), dt)
+    vc = _randn(gen, (nb, num_kv_heads, dv, block_size), dt)
+    poison_block = int(perm[total]) if poison else None
+    mb = max_blocks if max_blocks is not None else max(need + [1])
+    bt = _assign_blocks(perm, need, mb, poison_block if poison else 0)
+    w = Workload(name=name, description=name, dtype=dt, seq_lens=lens, block_tables=bt, query=q,
+                 key_cache=kc, value_cache=vc, scale=1.0 / math.sqrt(head_size),
+                 num_heads=num_heads, num_kv_heads=num_kv_heads, head_size=head_size,
+                 v_head_size=dv, block_size=block_size, x=x, num_blocks=nb,
+                 partition_size=partition_size, poison_block=poison_block)
+    if poison:
+        _poison(w, need)
+    return w
+
+
+def _poison(w: Workload, need: List[int]):
+    """NaN in every unreferenced block and in the unused slots of each
+    sequence's last block; block-table padding points at a NaN block."""
+    used = torch.zeros(w.num_blocks, dtype=torch.bool)
+    for s, n in enumerate(need):
+        used[w.block_tables[s, :n].long()] = True
+    nan = float("nan")
+    w.key_cache[~used] = nan
+    w.value_cache[~used] = nan
+    bs = w.block_size
+    for s, n in enumerate(need):
+        L = int(w.seq_lens[s])
+        if n == 0 or L % bs == 0:
+            continue
+        last = int(w.block_tables[s, n - 1])
+        w.key_cache[last, :, :, L % bs:, :] = nan
+        w.value_cache[last, :, :, L % bs:] = nan
+
+
+CONFIG_NAMES = {
+    1: "tiny_f32",
+    2: "mha_f16",
+    3: "gqa_long_bf16",
+    4: "gqa_skewed_bf16",
+    5: "mla_bf16",
+}
+
+
+def config(cfg: int, *, poison: bool = False) -> Workload:
+    """The five reference workloads (seed = config number)."""
+    gen = torch.Generator().manual_seed(cfg)
+    if cfg == 1:
+        # 2 seqs, lengths 16 and 13, block size 8, 64 physical blocks; seq 0
+        # uses the block table [40, 30] of the Triton issue 2522 example, seq 1
+        # two distinct random blocks from the other 62.
+        lens = torch.tensor([16, 13], dtype=torch.int32)
+        others = torch.tensor([b for b in range(64) if b not in (40, 30)], dtype=torch.int64)
+        pick = others[torch.randperm(62, generator=gen)[:2]]
+        bt = torch.tensor([[40, 30], [int(pick[0]), int(pick[1])]], dtype=torch.int32)
+        dt, H, Hkv, D, bs, nb = torch.float32, 2, 2, 64, 8, 64
+        x = 4
+        q = _randn(gen, (2, H, D), dt)
+        kc = _randn(gen, (nb, Hkv, D // x, bs, x), dt)
+        vc = _randn(gen, (nb, Hkv, D, bs), dt)
+        w = Workload(name=CONFIG_NAMES[1], description="tiny paged decode fp32", dtype=dt,
+                     seq_lens=lens, block_tables=bt, query=q, key_cache=kc, value_cache=vc,
+                     scale=1.0 / math.sqrt(D), num_heads=H, num_kv_heads=Hkv, head_size=D,
+                     v_head_size=D, block_size=bs, x=x, num_blocks=nb)
+        if poison:
+            used = set(bt.flatten().tolist())
+            w.poison_block = next(b for b in range(nb) if b not in used)
+            _poison(w, [2, 2])
+        return w
+    if cfg == 2:
+        lens = torch.randint(1, 2049, (32,), generator=gen, dtype=torch.int64).to(torch.int32)
+        return _standard(gen, CONFIG_NAMES[2], "MHA decode fp16", lens, H=32, Hkv=32, D=128,
+                         bs=16, dt=torch.float16, nb=8192, poison=poison)
+    if cfg == 3:
+        lens = torch.full((8,), 32768, dtype=torch.int32)
+        return _standard(gen, CONFIG_NAMES[3], "long-context GQA decode bf16", lens, H=64, Hkv=8,
+                         D=128, bs=16, dt=torch.bfloat16, nb=20000, poison=poison)
+    if cfg == 4:
+        z = torch.randn((256,), generator=gen, dtype=torch.float64)
+        lens = torch.exp(math.log(1024.0) + 1.0 * z).round().clamp(1, 16384).to(torch.int32)
+        w = _standard(gen, CONFIG_NAMES[4], "skewed-batch GQA decode bf16", lens, H=32, Hkv=8,
+                      D=128, bs=32, dt=torch.bfloat16, nb=None, poison=poison)
+        w.max_kv_splits = 32
+        w.device_core_count = 256
+        return w
+    if cfg == 5:
+        return _mla(gen, poison=poison)
+    raise ValueError(f"unknown config {cfg}")
+
+
+def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison):
+    need = _blocks_needed(lens.tolist(), bs)
+    total = sum(need)
+    if nb is None:
+        nb = total + (1 if poison else 0)
+    perm = torch.randperm(nb, generator=gen)
+    x = 16 // torch.tensor([], dtype=dt).element_size()
+    S = lens.shape[0]
+    q = _randn(gen, (S, H, D), dt)
+    kc = _randn(gen, (nb, Hkv, D // x, bs, x), dt)
+    vc = _randn(gen, (nb, Hkv, D, bs), dt)
+    poison_block = int(perm[total]) if poison else None
+    bt = _assign_blocks(perm, need, max(need), poison_block if poison else 0)
+    w = Workload(name=name, description=desc, dtype=dt, seq_lens=lens, block_tables=bt, query=q,
+                 key_cache=kc, value_cache=vc, scale=1.0 / math.sqrt(D), num_heads=H,
+                 num_kv_heads=Hkv, head_size=D, v_head_size=D, block_size=bs, x=x, num_blocks=nb,
+                 poison_block=poison_block)
+    if poison:
+        _poison(w, need)
+    return w
+
+
+def _mla(gen, *, poison):
+    S, H, D, Dv = 64, 128, 576, 512
+    lens = torch.randint(1024, 8193, (S,), generator=gen, dtype=torch.int64).to(torch.int32)
+    total = int(lens.sum())
+    nb = total + (1 if poison else 0)
+    perm = torch.randperm(nb, generator=gen)
+    dt = torch.bfloat16
+    q = _randn(gen, (S, H, D), dt)
+    latent = _randn(gen, (nb, D), dt)
+    poison_block = int(perm[total]) if poison else None
+    bt = _assign_blocks(perm, lens.tolist(), 8192, poison_block if poison else 0)
+    cu = torch.zeros(S + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    if poison:
+        latent[poison_block] = float("nan")
+        used = torch.zeros(nb, dtype=torch.bool)
+        used[perm[:total]] = True
+        latent[~used] = float("nan")
+    k, v = _mla_views(latent, Dv)
+    return Workload(name=CONFIG_NAMES[5], description="MLA-style decode bf16", dtype=dt,
+                    seq_lens=lens, block_tables=bt, query=q, key_cache=k, value_cache=v,
+                    scale=1.0 / math.sqrt(192.0), num_heads=H, num_kv_heads=1, head_size=D,
+                    v_head_size=Dv, block_size=1, x=8, num_blocks=nb, cu_num_blocks=cu,
+                    latent=latent, poison_block=poison_block)
+
+
+def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512, max_blocks=None,
+               poison=False) -> Workload:
+    """Smaller MLA-style workload (page size 1, V aliasing the first Dv values of K)."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(seq_lens, dtype=torch.int32).clone()
+    S = lens.shape[0]
+    total = int(lens.clamp(min=0).sum())
+    nb = total + (1 if poison else 0)
+    perm = torch.randperm(nb, generator=gen)
+    dt = torch.bfloat16
+    q = _randn(gen, (S, num_heads, head_size), dt)
+    latent = _randn(gen, (nb, head_size), dt)
+    poison_block = int(perm[total]) if poison else None
+    mb = max_blocks or max(1, int(lens.max()))
+    bt = _assign_blocks(perm, [max(0, int(L)) for L in lens], mb, poison_block if poison else 0)
+    cu = torch.zeros(S + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens.clamp(min=0), 0).to(torch.int32)
+    if poison:
+        latent[poison_block] = float("nan")
+    k, v = _mla_views(latent, v_head_size)
+    return Workload(name="mla_custom", description="MLA-style custom", dtype=dt, seq_lens=lens,
+                    block_tables=bt, query=q, key_cache=k, value_cache=v,
+                    scale=1.0 / math.sqrt(192.0), num_heads=num_heads, num_kv_heads=1,
+                    head_size=head_size, v_head_size=v_head_size, block_size=1, x=8,
+                    num_blocks=nb, cu_num_blocks=cu, latent=latent, poison_block=poison_block)
