@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark: split-KV PagedAttention decode on one MI355X.
+
+One step = one decode step of the whole hot path for a batch: phase 1
+(paged_attn_decode) and phase 2 (paged_attn_reduce), plus num_kv_splits /
+build_page_indices for the workloads that use them. Inputs are synthetic and
+seeded (the workloads module) and already resident in HBM when timing starts.
+
+Default workload: long-context GQA decode, bf16 -- 8 sequences x 32768
+tokens, 64 query heads over 8 kv heads, head_dim 128, block size 16, 20000
+physical blocks in random order, 512-token partitions (64 per sequence).
+
+Prints one JSON line: KV read GB/s (value), microseconds per step, the
+roofline of the dominant kernel (phase 1) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_attention_decode_tables_amd as pad  # noqa: E402
+from paged_attention_decode_tables_amd import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+METRIC = "paged-decode KV read GB/s (% of MI355X HBM peak) + µs/decode step"
+KERNEL_SOURCES = {"mfma": "decode_mfma.hip", "valu": "decode_valu.hip"}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kind: str) -> str:
+    path = os.path.join(ROOT, "paged_attention_decode_tables_amd", "csrc", KERNEL_SOURCES[kind])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(os.path.dirname(path), "common.h")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Step:
+    """Device buffers and the launches of one decode step."""
+
+    def __init__(self, w: workloads.Workload, out_dtype=torch.bfloat16):
+        self.w = w
+        self.g = g = w.to("cuda")
+        self.ns = None
+        self.indptr = None
+        if w.max_kv_splits is not None:
+            self.max_parts = w.max_kv_splits
+            self.ns = torch.empty(w.num_seqs, dtype=torch.int32, device="cuda")
+        else:
+            self.max_parts = -(-w.max_seq_len // w.partition_size)
+        if w.cu_num_blocks is not None:
+            self.indptr = w.cu_num_blocks.to("cuda")
+            self.flat = torch.empty(int(w.cu_num_blocks[-1]), dtype=torch.int32, device="cuda")
+        S, H, Dv = w.num_seqs, w.num_heads, w.v_head_size
+        self.tmp = torch.empty((S, H, self.max_parts, Dv), dtype=torch.float32, device="cuda")
+        self.ml = torch.empty((S, H, self.max_parts), dtype=torch.float32, device="cuda")
+        self.es = torch.empty((S, H, self.max_parts), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((S, H, Dv), dtype=out_dtype, device="cuda")
+
+    def pre(self):
+        w, g = self.w, self.g
+        if self.ns is not None:
+            pad.num_kv_splits(self.ns, g.seq_lens, 1, w.num_heads, w.num_kv_heads, w.max_kv_splits,
+                              w.device_core_count)
+        if self.indptr is not None:
+            pad.build_page_indices(self.flat, g.block_tables, self.indptr)
+
+    def decode(self):
+        w, g = self.w, self.g
+        bt = self.flat if self.indptr is not None else g.block_tables
+        pad.paged_attn_decode(self.tmp, self.es, self.ml, g.query, g.key_cache, g.value_cache, bt,
+                              g.seq_lens, w.scale, w.max_seq_len, partition_size=w.partition_size,
+                              num_splits=self.ns, kv_indptr=self.indptr)
+
+    def reduce(self):
+        w, g = self.w, self.g
+        pad.paged_attn_reduce(self.out, self.tmp, self.es, self.ml, g.seq_lens,
+                              partition_size=w.partition_size, num_splits=self.ns)
+
+    def run(self):
+        self.pre()
+        self.decode()
+        self.reduce()
+
+
+def recorded_traffic(workload: str, kind: str, launches_kv_bytes: int):
+    """HBM traffic per phase-1 launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"paged_attn_decode_{kind}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_hash(kind):
+        return None
+    m = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int):
+    """The oracle, as it stands, timed on the first `sample_seqs` sequences."""
+    import ctypes
+
+    import oracle
+
+    orc = oracle.get()
+    sub = w.subset(range(sample_seqs))
+    args = (sub.query.float().numpy(), sub.key_cache.float().numpy(),
+            sub.value_cache.float().numpy(), sub.block_tables.numpy(), sub.seq_lens.numpy(),
+            sub.scale)
+    t0 = time.perf_counter()
+    ref = orc.attention(*args)
+    dt = time.perf_counter() - t0
+    try:
+        threads = int(ctypes.CDLL(orc.lib._name).omp_get_max_threads())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    threads = min(threads, sample_seqs * w.num_kv_heads)
+    kv = sub.kv_bytes()
+    err = float(np.abs(out[:sample_seqs].float().cpu().numpy() - ref).max())
+    return ({"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+             "sample": f"{sample_seqs} of {w.num_seqs} sequences (all heads), "
+                       f"{kv} KV bytes, {dt:.2f} s", "seconds": dt},
+            {"sample_seqs": sample_seqs, "max_abs_err": err})
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload number (3 = long-context GQA)")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not "
+                                   "part of this build (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    log(f"bench: generating workload {args.config}")
+    w = workloads.config(args.config)
+    step = Step(w)
+    kind = "mfma" if (w.num_heads // w.num_kv_heads) > 1 and w.dtype != torch.float32 \
+        and w.block_size >= 8 and w.head_size in (64, 128) else "valu"
+    torch.cuda.synchronize()
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"bench: timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(K):
+        step.pre()
+        ev[k][0].record()
+        step.decode()
+        ev[k][1].record()
+        step.reduce()
+        ev[k][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = start.elapsed_time(stop) / K
+    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    red_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    kv = w.kv_bytes()
+    value = kv / (ms_step * 1e-3) / 1e9
+    achieved = kv / (dec_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(w.name, kind, kv)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "seqs": w.num_seqs, "seq_len_max": w.max_seq_len,
+                   "tokens": w.total_tokens, "heads": w.num_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_size, "v_head_dim": w.v_head_size,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "partition": w.partition_size if w.max_kv_splits is None else "num_kv_splits",
+                   "kv_bytes_per_step": kv},
+        "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(dec_ms * 1e3, 2)},
+        "phase2_us": round(red_ms * 1e3, 2),
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        cb, parity = cpu_baseline(w, step.out, args.cpu_sample_seqs)
+        res["cpu_baseline"] = cb
+        res["parity_sample"] = parity
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

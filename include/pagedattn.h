@@ -1,0 +1,213 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: split-KV PagedAttention decode on
+ * AMD MI355X (gfx950).
+ *
+ * Pages the operations come from:
+ *   [T2522]   triton-lang/triton issue 2522, "Needs help on performance
+ *             optimization" (block-table example, index fragment).
+ *   [PAv2]    paged_attention_v2_triton.py (modelhub project_6): tensor
+ *             definitions in the partition- and reduce-kernel signatures,
+ *             the phase-1 algorithm in the module docstring, the phase-2
+ *             reduce kernel, the wrapper paged_attention_v2_triton.
+ *   [PR35765] vLLM PR 35765, "AITER MLA backend: Avoid CPU sync in
+ *             _build_decode" (_copy_page_indices_kernel, stride-robust form).
+ *   [SGMETA]  sglang kernels/ops/attention/metadata.py
+ *             (get_num_kv_splits_triton).
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers (HBM of the current HIP device) unless
+ *     said otherwise. The caller owns and allocates every buffer; the library
+ *     allocates nothing and never synchronises with the host ([PR35765]: the
+ *     point of the page-indices kernel is to avoid a host sync).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and completes asynchronously.
+ *   - Strides are in ELEMENTS. Index tensors honour every stride ([PR35765]
+ *     review); for the caches and activations the innermost dimensions must
+ *     be packed as stated, anything else returns PA_ENOTSUP.
+ *   - Return value: PA_OK (0) or a negative code. Arguments are validated on
+ *     the host before any launch; an error leaves every output untouched.
+ *     Values stored in device memory (lengths, block ids) cannot be checked
+ *     without a host sync; the rules they must follow are stated per call.
+ *     pa_last_error() returns a message for the last failure on this thread.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_EINVAL (-1)   /* bad scalar, shape, stride or null pointer */
+#define PA_ENOTSUP (-2)  /* valid, but this dtype/size/layout combination is not built */
+#define PA_ELAUNCH (-3)  /* the HIP launch itself failed */
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/*
+ * Phase 1 of split-KV decode ([PAv2] _paged_attn_v2_partition_kernel and the
+ * module docstring): for every sequence s, query head h and split p, over
+ * the tokens t of split p:
+ *     z_t = scale * q[s,h,:] . K_t,   m = max_t z_t,   l = sum_t exp(z_t - m),
+ *     tmp = sum_t exp(z_t - m) V_t / l
+ * and stores max_logits[s,h,p] = m, exp_sums[s,h,p] = l, tmp_output[s,h,p,:]
+ * = tmp (the normalised split output; phase 2 weights it by exp(m - M) * l).
+ * Query head h reads kv head h / (num_heads / num_kv_heads).
+ *
+ * Token t of sequence s is gathered in two steps ([PAv2] docstring; [T2522]):
+ * block = pages[t / block_size], slot = t % block_size, then
+ *     K_t[d] = key_cache[block, kvh, d / x, slot, d % x]
+ *     V_t[d] = value_cache[block, kvh, d, slot].
+ *
+ * Splits: with num_splits == NULL, split p covers [p*P, min((p+1)*P, L))
+ * with P = partition_size ([PAv2]: PARTITION_SIZE = 512). With a num_splits
+ * array (e.g. from num_kv_splits()), n_s = clamp(num_splits[s], 1,
+ * max_num_parts), the split length is cdiv(L, n_s) rounded up to a multiple
+ * of 64 tokens, and split p covers [p*len, min((p+1)*len, L)). A split with
+ * no tokens (p*len >= L) stores m = -inf, l = 0 and leaves tmp_output
+ * untouched, as the page's early exit does.
+ */
+typedef struct pa_decode_args {
+    /* outputs: fp32 workspaces */
+    float* tmp_output;           /* [num_seqs, num_heads, max_num_parts, v_head_size] */
+    int64_t tmp_stride_s, tmp_stride_h, tmp_stride_p, tmp_stride_d; /* stride_d must be 1 */
+    float* exp_sums;             /* [num_seqs, num_heads, max_num_parts] */
+    float* max_logits;           /* same shape and strides as exp_sums */
+    int64_t ml_stride_s, ml_stride_h, ml_stride_p;                  /* stride_p must be 1 */
+
+    /* inputs, all of element type `dtype` */
+    const void* query;           /* [num_seqs, num_heads, head_size] */
+    int64_t q_stride_s, q_stride_h, q_stride_d;                     /* stride_d must be 1 */
+    const void* key_cache;       /* [num_blocks, num_kv_heads, head_size/x, block_size, x] */
+    int64_t k_stride_b, k_stride_h, k_stride_dx, k_stride_bs, k_stride_x;
+                                 /* dx, bs, x must be block_size*x, x, 1 */
+    const void* value_cache;     /* [num_blocks, num_kv_heads, v_head_size, block_size] */
+    int64_t v_stride_b, v_stride_h, v_stride_d, v_stride_bs;
+                                 /* d, bs must be block_size, 1. value_cache may alias
+                                    key_cache (MLA-style latent rows with block_size 1,
+                                    V = the first v_head_size values of each row). */
+
+    /* page lists (int32 physical block ids):
+       kv_indptr == NULL: pages = block_tables[num_seqs, max_blocks] with strides
+         (bt_stride_s, bt_stride_b);
+       kv_indptr != NULL: CSR form ([PR35765] paged_kv_indptr/paged_kv_indices):
+         the pages of sequence s are block_tables[(kv_indptr[s] + i) * bt_stride_b].
+       Sequence s must list at least cdiv(seq_lens[s], block_size) valid block
+       ids in [0, num_blocks); entries past that are never read. */
+    const int32_t* block_tables;
+    int64_t bt_stride_s, bt_stride_b;
+    const int32_t* kv_indptr;    /* optional, [num_seqs + 1] */
+    const int32_t* seq_lens;     /* [num_seqs]; each must be <= max_seq_len. L <= 0 gives
+                                    only empty splits. */
+    const int32_t* num_splits;   /* optional, [num_seqs] (see "Splits" above) */
+
+    float scale;                 /* multiplies q . k before the softmax */
+    int32_t num_seqs, num_heads, num_kv_heads;
+    int32_t head_size;           /* D  */
+    int32_t v_head_size;         /* Dv */
+    int32_t block_size;          /* power of two, 1..1024 */
+    int32_t x;                   /* key packing: 16 / element size ([PAv2] X_PACK) */
+    int32_t partition_size;      /* > 0 and a multiple of 64 when num_splits == NULL */
+    int32_t max_num_parts;       /* partition dimension of the workspaces; must be
+                                    >= cdiv(max_seq_len, partition_size) without num_splits */
+    int32_t max_seq_len;         /* host-side bound on seq_lens (sizes the grid) */
+    int32_t dtype;               /* pa_dtype of query, key_cache and value_cache */
+    int32_t kernel_hint;         /* PA_KERNEL_AUTO (0): pick the kernel; PA_KERNEL_VALU: the
+                                    vector-ALU kernel; PA_KERNEL_MFMA: the matrix-core kernel
+                                    (PA_ENOTSUP where it does not apply). Results agree
+                                    within the documented tolerance either way. */
+} pa_decode_args;
+
+#define PA_KERNEL_AUTO 0
+#define PA_KERNEL_VALU 1
+#define PA_KERNEL_MFMA 2
+
+/*
+ * Supported combinations (others return PA_ENOTSUP):
+ *   dtype f32, f16, bf16 with x = 16 / element size;
+ *   (head_size, v_head_size) in {(64,64), (128,128), (256,256), (576,512)};
+ *   any group size num_heads / num_kv_heads (grouped heads of f16/bf16 caches
+ *   run on MFMA when block_size >= 8 and the group is at most 16).
+ */
+int paged_attn_decode(const pa_decode_args* args, void* stream);
+
+/*
+ * Phase 2 ([PAv2] _paged_attn_v2_reduce_kernel): for each (s, h), over the n
+ * nonempty splits of sequence s (the split rule of paged_attn_decode),
+ *     M = max_p m_p,  w_p = exp(m_p - M) * l_p,
+ *     output[s,h,:] = sum_p w_p * tmp_output[s,h,p,:] / sum_p w_p.
+ * Every split is merged (no cap on the number of partitions). Splits past n
+ * are never read, so their workspace contents do not matter. A sequence with
+ * L <= 0 gets a zero output row.
+ */
+typedef struct pa_reduce_args {
+    void* output;                /* [num_seqs, num_heads, v_head_size] of out_dtype */
+    int64_t out_stride_s, out_stride_h, out_stride_d;               /* stride_d must be 1 */
+    int32_t out_dtype;           /* pa_dtype */
+    const float* tmp_output;
+    int64_t tmp_stride_s, tmp_stride_h, tmp_stride_p, tmp_stride_d; /* stride_d must be 1 */
+    const float* exp_sums;
+    const float* max_logits;
+    int64_t ml_stride_s, ml_stride_h, ml_stride_p;                  /* stride_p must be 1 */
+    const int32_t* seq_lens;     /* [num_seqs] */
+    const int32_t* num_splits;   /* optional, as given to paged_attn_decode */
+    int32_t num_seqs, num_heads, v_head_size;
+    int32_t partition_size;      /* as given to paged_attn_decode */
+    int32_t max_num_parts;
+} pa_reduce_args;
+
+int paged_attn_reduce(const pa_reduce_args* args, void* stream);
+
+/*
+ * Flat page list from a block table ([PR35765] _copy_page_indices_kernel,
+ * stride-robust form from its review): for each request r,
+ *     page_indices[cu_num_blocks[r] + i] = block_table[r*bt_stride0 + i*bt_stride1]
+ * for 0 <= i < cu_num_blocks[r+1] - cu_num_blocks[r]. cu_num_blocks is an
+ * int32 indptr of num_reqs + 1 entries, non-decreasing, with row r holding at
+ * least cu[r+1] - cu[r] entries; page_indices holds cu[num_reqs] entries.
+ * num_reqs == 0 is a no-op.
+ */
+int build_page_indices(int32_t* page_indices, const int32_t* block_table, int64_t bt_stride0,
+                       int64_t bt_stride1, const int32_t* cu_num_blocks, int32_t num_reqs,
+                       void* stream);
+
+/*
+ * Split-count heuristic ([SGMETA] get_num_kv_splits_triton), one workgroup,
+ * no host sync. With max and min of the lengths (a length <= 0 counts as 1):
+ * if max*8 < min*10 then min = max; chunk_1 = cdiv(max, min(cdiv(max, min),
+ * max_kv_splits)); cores_ext = int32(fp32(cores) * max(log2(fp32(max)/64), 1))
+ * in fp32 with log2 correctly rounded to fp32; with group = num_head /
+ * num_kv_head the token grid is num_seq*num_group*num_head (group 1) or
+ * num_seq*num_group*cdiv(num_head, min(16, group)); chunk_2 = cdiv(max,
+ * min(cdiv(cores_ext, grid), max_kv_splits)); and
+ *     out[s*num_group + g] = max(cdiv(L_s, chunk_1), cdiv(L_s, chunk_2)).
+ * out holds num_seq * num_group int32 entries. num_seq == 0 is a no-op.
+ */
+int num_kv_splits(int32_t* out, const int32_t* seq_lens, int32_t num_seq, int32_t num_group,
+                  int32_t num_head, int32_t num_kv_head, int32_t max_kv_splits,
+                  int32_t device_core_count, void* stream);
+
+/*
+ * Test hook for the address arithmetic shared by the decode kernels
+ * ([T2522] block-table example): for t < seq_lens[s],
+ *     out[s*out_stride_s + t] = pages[t / block_size] * block_stride
+ *                              + (t % block_size) * slot_stride
+ * with the page list as in pa_decode_args (kv_indptr may be NULL). Entries
+ * t >= seq_lens[s] are not written; out rows must hold max_seq_len entries.
+ */
+int paged_token_offsets(int64_t* out, int64_t out_stride_s, const int32_t* block_tables,
+                        int64_t bt_stride_s, int64_t bt_stride_b, const int32_t* kv_indptr,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                        int32_t block_size, int64_t block_stride, int64_t slot_stride,
+                        void* stream);
+
+/* Message describing the last non-OK return on the calling thread. */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

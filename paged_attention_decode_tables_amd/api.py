@@ -1,0 +1,232 @@
+"""ctypes binding of libpagedattn.so (C ABI in include/pagedattn.h).
+
+Argument marshalling only: each function reads shapes, strides, dtypes and
+data pointers from torch tensors, fills the C argument block and calls the
+library on the current (or given) HIP stream. All computation happens in the
+library's HIP kernels. There is no fallback: if the library is missing the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libpagedattn.so"
+
+PA_OK, PA_EINVAL, PA_ENOTSUP, PA_ELAUNCH = 0, -1, -2, -3
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_KERNEL = {"auto": 0, "valu": 1, "mfma": 2}
+_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_CODE_NAMES = {PA_EINVAL: "PA_EINVAL", PA_ENOTSUP: "PA_ENOTSUP", PA_ELAUNCH: "PA_ELAUNCH"}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODE_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("tmp_output", _vp), ("tmp_stride_s", _i64), ("tmp_stride_h", _i64),
+        ("tmp_stride_p", _i64), ("tmp_stride_d", _i64),
+        ("exp_sums", _vp), ("max_logits", _vp),
+        ("ml_stride_s", _i64), ("ml_stride_h", _i64), ("ml_stride_p", _i64),
+        ("query", _vp), ("q_stride_s", _i64), ("q_stride_h", _i64), ("q_stride_d", _i64),
+        ("key_cache", _vp), ("k_stride_b", _i64), ("k_stride_h", _i64), ("k_stride_dx", _i64),
+        ("k_stride_bs", _i64), ("k_stride_x", _i64),
+        ("value_cache", _vp), ("v_stride_b", _i64), ("v_stride_h", _i64), ("v_stride_d", _i64),
+        ("v_stride_bs", _i64),
+        ("block_tables", _vp), ("bt_stride_s", _i64), ("bt_stride_b", _i64),
+        ("kv_indptr", _vp), ("seq_lens", _vp), ("num_splits", _vp),
+        ("scale", ctypes.c_float),
+        ("num_seqs", _i32), ("num_heads", _i32), ("num_kv_heads", _i32),
+        ("head_size", _i32), ("v_head_size", _i32), ("block_size", _i32), ("x", _i32),
+        ("partition_size", _i32), ("max_num_parts", _i32), ("max_seq_len", _i32),
+        ("dtype", _i32), ("kernel_hint", _i32),
+    ]
+
+
+class ReduceArgs(ctypes.Structure):
+    _fields_ = [
+        ("output", _vp), ("out_stride_s", _i64), ("out_stride_h", _i64), ("out_stride_d", _i64),
+        ("out_dtype", _i32),
+        ("tmp_output", _vp), ("tmp_stride_s", _i64), ("tmp_stride_h", _i64),
+        ("tmp_stride_p", _i64), ("tmp_stride_d", _i64),
+        ("exp_sums", _vp), ("max_logits", _vp),
+        ("ml_stride_s", _i64), ("ml_stride_h", _i64), ("ml_stride_p", _i64),
+        ("seq_lens", _vp), ("num_splits", _vp),
+        ("num_seqs", _i32), ("num_heads", _i32), ("v_head_size", _i32),
+        ("partition_size", _i32), ("max_num_parts", _i32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.environ.get("PAGEDATTN_LIB", os.path.join(_PKG, LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpagedattn.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m paged_attention_decode_tables_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.paged_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+    lib.paged_attn_reduce.argtypes = [ctypes.POINTER(ReduceArgs), _vp]
+    lib.build_page_indices.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp]
+    lib.num_kv_splits.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.paged_token_offsets.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32,
+                                        _i64, _i64, _vp]
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != PA_OK:
+        raise PagedAttnError(rc, load_library().pa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+def _page_strides(block_tables: torch.Tensor, kv_indptr):
+    if kv_indptr is not None or block_tables.dim() == 1:
+        return 0, block_tables.stride(-1)
+    return block_tables.stride(0), block_tables.stride(1)
+
+
+def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
+                      query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                      max_seq_len: int, *, partition_size: int = 512,
+                      num_splits: Optional[torch.Tensor] = None,
+                      kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
+                      stream=None) -> None:
+    """Phase 1: per-split max logits, exp sums and normalised outputs.
+
+    Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
+    fp32; query [S, H, D]; key_cache [NB, Hkv, D/x, bs, x]; value_cache
+    [NB, Hkv, Dv, bs]; block_tables [S, max_blocks] int32 (or the flat page
+    list when kv_indptr is given); seq_lens [S] int32.
+    """
+    lib = load_library()
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise TypeError("query, key_cache and value_cache must share one dtype")
+    S, H, D = query.shape
+    NB, Hkv, Dx, bs, x = key_cache.shape
+    Dv = value_cache.shape[2]
+    a = DecodeArgs()
+    a.tmp_output = _ptr(tmp_output)
+    a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
+    a.exp_sums = _ptr(exp_sums)
+    a.max_logits = _ptr(max_logits)
+    if exp_sums.stride() != max_logits.stride():
+        raise ValueError("exp_sums and max_logits must share strides")
+    a.ml_stride_s, a.ml_stride_h, a.ml_stride_p = exp_sums.stride()
+    a.query = _ptr(query)
+    a.q_stride_s, a.q_stride_h, a.q_stride_d = query.stride()
+    a.key_cache = _ptr(key_cache)
+    (a.k_stride_b, a.k_stride_h, a.k_stride_dx, a.k_stride_bs, a.k_stride_x) = key_cache.stride()
+    a.value_cache = _ptr(value_cache)
+    a.v_stride_b, a.v_stride_h, a.v_stride_d, a.v_stride_bs = value_cache.stride()
+    a.block_tables = _ptr(block_tables)
+    a.bt_stride_s, a.bt_stride_b = _page_strides(block_tables, kv_indptr)
+    a.kv_indptr = _ptr(kv_indptr)
+    a.seq_lens = _ptr(seq_lens)
+    a.num_splits = _ptr(num_splits)
+    a.scale = float(scale)
+    a.num_seqs, a.num_heads, a.num_kv_heads = S, H, Hkv
+    a.head_size, a.v_head_size, a.block_size, a.x = D, Dv, bs, x
+    a.partition_size = partition_size
+    a.max_num_parts = tmp_output.shape[2]
+    a.max_seq_len = int(max_seq_len)
+    a.dtype = _dtype(query)
+    a.kernel_hint = PA_KERNEL[kernel]
+    _check(lib.paged_attn_decode(ctypes.byref(a), _stream(stream)))
+
+
+def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: torch.Tensor,
+                      max_logits: torch.Tensor, seq_lens: torch.Tensor, *,
+                      partition_size: int = 512, num_splits: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Phase 2: log-sum-exp merge of the splits into output [S, H, Dv]."""
+    lib = load_library()
+    S, H, P, Dv = tmp_output.shape
+    a = ReduceArgs()
+    a.output = _ptr(output)
+    a.out_stride_s, a.out_stride_h, a.out_stride_d = output.stride()
+    a.out_dtype = _dtype(output)
+    a.tmp_output = _ptr(tmp_output)
+    a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
+    a.exp_sums = _ptr(exp_sums)
+    a.max_logits = _ptr(max_logits)
+    if exp_sums.stride() != max_logits.stride():
+        raise ValueError("exp_sums and max_logits must share strides")
+    a.ml_stride_s, a.ml_stride_h, a.ml_stride_p = exp_sums.stride()
+    a.seq_lens = _ptr(seq_lens)
+    a.num_splits = _ptr(num_splits)
+    a.num_seqs, a.num_heads, a.v_head_size = S, H, Dv
+    a.partition_size = partition_size
+    a.max_num_parts = P
+    _check(lib.paged_attn_reduce(ctypes.byref(a), _stream(stream)))
+
+
+def build_page_indices(page_indices: torch.Tensor, block_table: torch.Tensor,
+                       cu_num_blocks: torch.Tensor, stream=None) -> None:
+    """page_indices[cu[r] + i] = block_table[r, i] for i < cu[r+1] - cu[r]."""
+    lib = load_library()
+    num_reqs = cu_num_blocks.shape[0] - 1
+    s0, s1 = block_table.stride()
+    _check(lib.build_page_indices(_ptr(page_indices), _ptr(block_table), s0, s1,
+                                  _ptr(cu_num_blocks), num_reqs, _stream(stream)))
+
+
+def num_kv_splits(out: torch.Tensor, seq_lens: torch.Tensor, num_group: int, num_head: int,
+                  num_kv_head: int, max_kv_splits: int, device_core_count: int,
+                  stream=None) -> None:
+    """Per-(seq, group) split counts from the sglang heuristic, on the device."""
+    lib = load_library()
+    _check(lib.num_kv_splits(_ptr(out), _ptr(seq_lens), seq_lens.shape[0], num_group, num_head,
+                             num_kv_head, max_kv_splits, device_core_count, _stream(stream)))
+
+
+def paged_token_offsets(out: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                        block_size: int, block_stride: int, slot_stride: int,
+                        kv_indptr: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Test hook: out[s, t] = pages[t // bs] * block_stride + (t % bs) * slot_stride."""
+    lib = load_library()
+    S, max_len = out.shape
+    bs_s, bs_b = _page_strides(block_tables, kv_indptr)
+    _check(lib.paged_token_offsets(_ptr(out), out.stride(0), _ptr(block_tables), bs_s, bs_b,
+                                   _ptr(kv_indptr), _ptr(seq_lens), S, max_len, block_size,
+                                   block_stride, slot_stride, _stream(stream)))

@@ -1,0 +1,243 @@
+// api.hip -- the exported C ABI of libpagedattn.so (declared in pagedattn.h).
+// Every entry point validates its arguments on the host, then enqueues its
+// kernels on the caller's stream. Nothing here allocates or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kernels.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int launched(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(PA_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return PA_OK;
+}
+
+int elem_size(int dtype)
+{
+    switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    default: return 0;
+    }
+}
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(int64_t v)
+{
+    int s = 0;
+    while ((int64_t(1) << s) < v) ++s;
+    return s;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kMaxGridYZ = 65535;
+
+}  // namespace
+
+PA_EXPORT const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
+{
+    if (!a) return fail(PA_EINVAL, "paged_attn_decode: args is NULL");
+    const int esz = elem_size(a->dtype);
+    if (!esz) return fail(PA_EINVAL, "paged_attn_decode: unknown dtype %d", a->dtype);
+    if (a->num_seqs < 0) return fail(PA_EINVAL, "paged_attn_decode: num_seqs < 0");
+    if (a->num_heads < 1 || a->num_kv_heads < 1 || a->num_heads % a->num_kv_heads)
+        return fail(PA_EINVAL, "paged_attn_decode: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    a->num_heads, a->num_kv_heads);
+    if (a->head_size < 1 || a->v_head_size < 1)
+        return fail(PA_EINVAL, "paged_attn_decode: head sizes must be positive");
+    if (!pow2(a->block_size) || a->block_size > 1024)
+        return fail(PA_EINVAL, "paged_attn_decode: block_size %d is not a power of two in [1, 1024]", a->block_size);
+    if (a->x < 1 || a->head_size % a->x)
+        return fail(PA_EINVAL, "paged_attn_decode: x = %d must divide head_size %d", a->x, a->head_size);
+    if (a->x * esz != 16)
+        return fail(PA_ENOTSUP, "paged_attn_decode: key packing x = %d, only 16 / element size (%d) is built", a->x, 16 / esz);
+    if (a->max_num_parts < 1) return fail(PA_EINVAL, "paged_attn_decode: max_num_parts < 1");
+    if (a->max_seq_len < 0) return fail(PA_EINVAL, "paged_attn_decode: max_seq_len < 0");
+    int64_t parts;
+    if (!a->num_splits) {
+        if (a->partition_size < 64 || a->partition_size % 64)
+            return fail(PA_EINVAL, "paged_attn_decode: partition_size %d is not a positive multiple of 64", a->partition_size);
+        parts = cdiv(a->max_seq_len, a->partition_size);
+        if (parts > a->max_num_parts)
+            return fail(PA_EINVAL, "paged_attn_decode: max_num_parts %d < cdiv(max_seq_len %d, partition_size %d) = %lld",
+                        a->max_num_parts, a->max_seq_len, a->partition_size, (long long)parts);
+    } else {
+        parts = a->max_num_parts;
+    }
+    if (a->num_seqs == 0 || parts == 0) return PA_OK;
+    if (!a->tmp_output || !a->exp_sums || !a->max_logits || !a->query || !a->key_cache ||
+        !a->value_cache || !a->block_tables || !a->seq_lens)
+        return fail(PA_EINVAL, "paged_attn_decode: a required pointer is NULL");
+    if (a->tmp_stride_d != 1 || a->ml_stride_p != 1 || a->q_stride_d != 1)
+        return fail(PA_ENOTSUP, "paged_attn_decode: innermost strides of tmp_output, max_logits/exp_sums and query must be 1");
+    const int64_t bs = a->block_size, x = a->x;
+    if (a->k_stride_x != 1 || a->k_stride_bs != x || a->k_stride_dx != bs * x)
+        return fail(PA_ENOTSUP, "paged_attn_decode: key_cache inner dims must be packed [head_size/x, block_size, x]");
+    if (a->v_stride_bs != 1 || a->v_stride_d != bs)
+        return fail(PA_ENOTSUP, "paged_attn_decode: value_cache inner dims must be packed [v_head_size, block_size]");
+    // 16-byte vector accesses
+    if (!aligned16(a->query) || !aligned16(a->key_cache) || !aligned16(a->value_cache) ||
+        !aligned16(a->tmp_output))
+        return fail(PA_ENOTSUP, "paged_attn_decode: query, caches and tmp_output must be 16-byte aligned");
+    if ((a->q_stride_s * esz) % 16 || (a->q_stride_h * esz) % 16 || (a->k_stride_b * esz) % 16 ||
+        (a->k_stride_h * esz) % 16 || (a->v_stride_b * esz) % 16 || (a->v_stride_h * esz) % 16 ||
+        a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
+        return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
+    if (a->num_seqs > kMaxGridYZ || a->num_heads > kMaxGridYZ)
+        return fail(PA_ENOTSUP, "paged_attn_decode: num_seqs and num_heads must be <= %d", kMaxGridYZ);
+    const int D = a->head_size, Dv = a->v_head_size, group = a->num_heads / a->num_kv_heads;
+    if (!pa::decode_valu_supported(a->dtype, D, Dv))
+        return fail(PA_ENOTSUP, "paged_attn_decode: (head_size, v_head_size) = (%d, %d) is not built", D, Dv);
+
+    pa::DecodeParams p{};
+    p.tmp = a->tmp_output;
+    p.tmp_ss = a->tmp_stride_s;
+    p.tmp_sh = a->tmp_stride_h;
+    p.tmp_sp = a->tmp_stride_p;
+    p.exp_sums = a->exp_sums;
+    p.max_logits = a->max_logits;
+    p.ml_ss = a->ml_stride_s;
+    p.ml_sh = a->ml_stride_h;
+    p.q = a->query;
+    p.q_ss = a->q_stride_s;
+    p.q_sh = a->q_stride_h;
+    p.kc = a->key_cache;
+    p.k_sb = a->k_stride_b;
+    p.k_sh = a->k_stride_h;
+    p.vc = a->value_cache;
+    p.v_sb = a->v_stride_b;
+    p.v_sh = a->v_stride_h;
+    p.pl = pa::PageList{a->block_tables, a->bt_stride_s, a->bt_stride_b, a->kv_indptr};
+    p.seq_lens = a->seq_lens;
+    p.num_splits = a->num_splits;
+    p.scale_log2 = a->scale * pa::kLog2e;
+    p.num_heads = a->num_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.group = group;
+    p.bs_shift = log2i(bs);
+    p.partition_size = a->partition_size;
+    p.max_num_parts = a->max_num_parts;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size);
+    if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok)
+        return fail(PA_ENOTSUP, "paged_attn_decode: the MFMA kernel does not serve this problem");
+    const bool use_mfma = a->kernel_hint == PA_KERNEL_VALU ? false : mfma_ok;
+    if (use_mfma)
+        return launched(pa::launch_decode_mfma(p, a->dtype, D, Dv, a->num_seqs, (int)parts, st),
+                        "paged_attn_decode (mfma)");
+    return launched(pa::launch_decode_valu(p, a->dtype, D, Dv, a->num_seqs, (int)parts, st),
+                    "paged_attn_decode (valu)");
+}
+
+PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
+{
+    if (!a) return fail(PA_EINVAL, "paged_attn_reduce: args is NULL");
+    if (!elem_size(a->out_dtype)) return fail(PA_EINVAL, "paged_attn_reduce: unknown out_dtype %d", a->out_dtype);
+    if (a->num_seqs < 0 || a->num_heads < 1 || a->v_head_size < 1 || a->max_num_parts < 1)
+        return fail(PA_EINVAL, "paged_attn_reduce: num_seqs >= 0, num_heads, v_head_size, max_num_parts >= 1 required");
+    if (!a->num_splits && (a->partition_size < 64 || a->partition_size % 64))
+        return fail(PA_EINVAL, "paged_attn_reduce: partition_size %d is not a positive multiple of 64", a->partition_size);
+    if (a->num_seqs == 0) return PA_OK;
+    if (!a->output || !a->tmp_output || !a->exp_sums || !a->max_logits || !a->seq_lens)
+        return fail(PA_EINVAL, "paged_attn_reduce: a required pointer is NULL");
+    if (a->out_stride_d != 1 || a->tmp_stride_d != 1 || a->ml_stride_p != 1)
+        return fail(PA_ENOTSUP, "paged_attn_reduce: innermost strides must be 1");
+    if (!pa::reduce_supported(a->v_head_size))
+        return fail(PA_ENOTSUP, "paged_attn_reduce: v_head_size %d is not built", a->v_head_size);
+    if (!aligned16(a->tmp_output) || a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
+        return fail(PA_ENOTSUP, "paged_attn_reduce: tmp_output rows must be 16-byte aligned");
+    const int64_t pairs = (int64_t)a->num_seqs * a->num_heads;
+    if ((pairs + 3) / 4 > 0x7fffffff) return fail(PA_ENOTSUP, "paged_attn_reduce: too many (seq, head) pairs");
+
+    pa::ReduceParams p{};
+    p.out = a->output;
+    p.out_ss = a->out_stride_s;
+    p.out_sh = a->out_stride_h;
+    p.tmp = a->tmp_output;
+    p.tmp_ss = a->tmp_stride_s;
+    p.tmp_sh = a->tmp_stride_h;
+    p.tmp_sp = a->tmp_stride_p;
+    p.exp_sums = a->exp_sums;
+    p.max_logits = a->max_logits;
+    p.ml_ss = a->ml_stride_s;
+    p.ml_sh = a->ml_stride_h;
+    p.seq_lens = a->seq_lens;
+    p.num_splits = a->num_splits;
+    p.num_seqs = a->num_seqs;
+    p.num_heads = a->num_heads;
+    p.partition_size = a->partition_size;
+    p.max_num_parts = a->max_num_parts;
+    return launched(pa::launch_reduce(p, a->out_dtype, a->v_head_size, reinterpret_cast<hipStream_t>(stream)),
+                    "paged_attn_reduce");
+}
+
+PA_EXPORT int build_page_indices(int32_t* page_indices, const int32_t* block_table, int64_t bt_stride0,
+                                 int64_t bt_stride1, const int32_t* cu_num_blocks, int32_t num_reqs,
+                                 void* stream)
+{
+    if (num_reqs < 0) return fail(PA_EINVAL, "build_page_indices: num_reqs < 0");
+    if (num_reqs == 0) return PA_OK;
+    if (!page_indices || !block_table || !cu_num_blocks)
+        return fail(PA_EINVAL, "build_page_indices: a required pointer is NULL");
+    return launched(pa::launch_page_indices(page_indices, block_table, bt_stride0, bt_stride1, cu_num_blocks,
+                                            num_reqs, reinterpret_cast<hipStream_t>(stream)),
+                    "build_page_indices");
+}
+
+PA_EXPORT int num_kv_splits(int32_t* out, const int32_t* seq_lens, int32_t num_seq, int32_t num_group,
+                            int32_t num_head, int32_t num_kv_head, int32_t max_kv_splits,
+                            int32_t device_core_count, void* stream)
+{
+    if (num_seq < 0 || num_group < 1 || num_head < 1 || num_kv_head < 1 || max_kv_splits < 1 ||
+        device_core_count < 1)
+        return fail(PA_EINVAL, "num_kv_splits: num_seq >= 0 and positive group/head/split/core counts required");
+    if (num_seq == 0) return PA_OK;
+    if (!out || !seq_lens) return fail(PA_EINVAL, "num_kv_splits: a required pointer is NULL");
+    return launched(pa::launch_num_kv_splits(out, seq_lens, num_seq, num_group, num_head, num_kv_head,
+                                             max_kv_splits, device_core_count,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "num_kv_splits");
+}
+
+PA_EXPORT int paged_token_offsets(int64_t* out, int64_t out_stride_s, const int32_t* block_tables,
+                                  int64_t bt_stride_s, int64_t bt_stride_b, const int32_t* kv_indptr,
+                                  const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                  int32_t block_size, int64_t block_stride, int64_t slot_stride,
+                                  void* stream)
+{
+    if (num_seqs < 0 || max_seq_len < 0) return fail(PA_EINVAL, "paged_token_offsets: negative size");
+    if (!pow2(block_size) || block_size > 1024)
+        return fail(PA_EINVAL, "paged_token_offsets: block_size %d is not a power of two in [1, 1024]", block_size);
+    if (num_seqs == 0 || max_seq_len == 0) return PA_OK;
+    if (!out || !block_tables || !seq_lens) return fail(PA_EINVAL, "paged_token_offsets: a required pointer is NULL");
+    if (num_seqs > kMaxGridYZ) return fail(PA_ENOTSUP, "paged_token_offsets: num_seqs > %d", kMaxGridYZ);
+    pa::PageList pl{block_tables, bt_stride_s, bt_stride_b, kv_indptr};
+    return launched(pa::launch_token_offsets(out, out_stride_s, pl, seq_lens, num_seqs, max_seq_len,
+                                             log2i(block_size), block_stride, slot_stride,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "paged_token_offsets");
+}

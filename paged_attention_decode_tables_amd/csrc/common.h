@@ -1,0 +1,160 @@
+// common.h -- device helpers shared by the libpagedattn kernels (gfx950,
+// 64-lane wavefronts). Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element types. Storage is read as raw bits and widened to fp32.
+// ---------------------------------------------------------------------------
+struct F32 {
+    using storage = float;
+    static constexpr int size = 4;
+    static constexpr int dtype = PA_F32;
+};
+struct F16 {
+    using storage = _Float16;
+    static constexpr int size = 2;
+    static constexpr int dtype = PA_F16;
+};
+struct BF16 {
+    using storage = __bf16;
+    static constexpr int size = 2;
+    static constexpr int dtype = PA_BF16;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(__bf16 v)
+{
+    return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, v) << 16);
+}
+
+// Low / high 16-bit halves of a packed dword, widened.
+template <class E> __device__ __forceinline__ float lo16(uint32_t w);
+template <class E> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<BF16>(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+template <> __device__ __forceinline__ float hi16<BF16>(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+template <> __device__ __forceinline__ float lo16<F16>(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <> __device__ __forceinline__ float hi16<F16>(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Element i (0-based) of a 16-byte vector holding 16/size elements.
+template <class E> __device__ __forceinline__ float elem16(const u32x4& v, int i)
+{
+    if constexpr (E::size == 4) {
+        // copy the element out first: bit-casting the vector-element lvalue
+        // directly reads element 0 with this compiler
+        const uint32_t w = v[i];
+        return __uint_as_float(w);
+    } else {
+        return (i & 1) ? hi16<E>(v[i >> 1]) : lo16<E>(v[i >> 1]);
+    }
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <class E> __device__ __forceinline__ void store_out(void* base, int64_t idx, float v);
+template <> __device__ __forceinline__ void store_out<F32>(void* base, int64_t idx, float v)
+{
+    reinterpret_cast<float*>(base)[idx] = v;
+}
+template <> __device__ __forceinline__ void store_out<F16>(void* base, int64_t idx, float v)
+{
+    reinterpret_cast<_Float16*>(base)[idx] = (_Float16)v;
+}
+template <> __device__ __forceinline__ void store_out<BF16>(void* base, int64_t idx, float v)
+{
+    reinterpret_cast<__bf16*>(base)[idx] = (__bf16)v;
+}
+
+// ---------------------------------------------------------------------------
+// Page lists and the token -> (block, slot) map (block-table example of
+// triton issue 2522; two-step gather of paged_attention_v2_triton.py).
+// ---------------------------------------------------------------------------
+struct PageList {
+    const int32_t* pages;
+    int64_t stride_s;  // row stride of a 2-D block table
+    int64_t stride_b;  // element stride within a row (and CSR element stride)
+    const int32_t* indptr;  // CSR row starts, or nullptr for a 2-D table
+};
+
+// First element of sequence s's page list.
+__device__ __forceinline__ const int32_t* page_row(const PageList& pl, int s)
+{
+    int64_t off = pl.indptr ? (int64_t)pl.indptr[s] * pl.stride_b : (int64_t)s * pl.stride_s;
+    return pl.pages + off;
+}
+
+// Physical block holding token t (block_size = 1 << bs_shift).
+__device__ __forceinline__ int64_t token_block(const int32_t* row, int64_t stride_b, int64_t t,
+                                               int bs_shift)
+{
+    return (int64_t)row[(t >> bs_shift) * stride_b];
+}
+
+// Offset of token t: block * block_stride + slot * slot_stride.
+__device__ __forceinline__ int64_t token_offset(const int32_t* row, int64_t stride_b, int64_t t,
+                                                int bs_shift, int64_t block_stride,
+                                                int64_t slot_stride)
+{
+    int64_t slot = t & ((int64_t(1) << bs_shift) - 1);
+    return token_block(row, stride_b, t, bs_shift) * block_stride + slot * slot_stride;
+}
+
+// Split rule shared by phase 1 and phase 2: fixed partition size, or the
+// per-sequence split count clamped to [1, max_parts] with the split length
+// cdiv(L, n) rounded up to 64 tokens.
+__device__ __forceinline__ int64_t split_length(int L, const int32_t* num_splits, int s,
+                                                int partition_size, int max_parts)
+{
+    if (!num_splits) return partition_size;
+    int n = num_splits[s];
+    n = n < 1 ? 1 : (n > max_parts ? max_parts : n);
+    int64_t Lc = L < 1 ? 1 : L;
+    int64_t c = (Lc + n - 1) / n;
+    return (c + 63) & ~int64_t(63);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,196 @@
+// decode_valu.hip -- phase 1 of split-KV decode on the vector ALUs
+// (paged_attention_v2_triton.py, partition kernel and module docstring:
+// per (seq, head, split) load q, gather the split's K/V rows through the
+// block table, scores, online softmax, weighted V, store m, l and the
+// normalised split output).
+//
+// One 64-lane wavefront per (split, head, seq). The split is walked in
+// 64-token chunks:
+//   QK     lane <-> token. Each lane reads its token's key row as D/x
+//          16-byte pieces (x = 16 / element size values of one token are
+//          contiguous in the x-packed cache) and dots it with q from LDS.
+//   softmax  wave max over the chunk, running max m and per-lane partial
+//          sums in base 2 (log2(e) folded into the scale).
+//   PV     lane <-> value row. With block_size * element size >= 16 a lane
+//          reads 16 bytes = 16/size consecutive tokens of its row; with page
+//          size 1 (latent rows) a lane owns Dv/64 consecutive values of every
+//          row. The chunk's probabilities are broadcast from LDS.
+// Tokens past the split end are masked: their scores are -inf and their
+// values are replaced by 0 before use, so NaN padding never propagates.
+#include "kernels.h"
+
+namespace pa {
+
+template <class E, int D, int DV, bool ROWV>
+__global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
+{
+    using T = typename E::storage;
+    constexpr int X = 16 / E::size;       // key packing
+    constexpr int DVR = DV / kWave;       // value rows (or values) per lane
+    __shared__ float q_lds[D];
+    __shared__ float p_lds[kWave];
+
+    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int L = p.seq_lens[s];
+    const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+    const int64_t start = (int64_t)part * len;
+    const int64_t end = (int64_t)L < start + len ? (int64_t)L : start + len;
+    float* mlp = p.max_logits + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
+    float* esp = p.exp_sums + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
+    if (start >= end) {
+        if (lane == 0) {
+            *mlp = -INFINITY;
+            *esp = 0.0f;
+        }
+        return;
+    }
+    const int kvh = h / p.group;
+    const int bs_shift = p.bs_shift;
+    const int64_t bs = int64_t(1) << bs_shift;
+
+    const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
+    for (int i = lane; i < D; i += kWave) q_lds[i] = to_f32(q[i]);
+    __syncthreads();
+
+    const int32_t* row = page_row(p.pl, s);
+    const int64_t sb = p.pl.stride_b;
+    const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
+    const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)kvh * p.v_sh;
+
+    float m = -INFINITY;  // running max (base 2)
+    float l = 0.0f;       // per-lane partial sum
+    float acc[DVR];
+#pragma unroll
+    for (int r = 0; r < DVR; ++r) acc[r] = 0.0f;
+
+    for (int64_t c0 = start; c0 < end; c0 += kWave) {
+        const int n = (int)((end - c0) < kWave ? (end - c0) : kWave);
+        // ---- scores: lane <-> token (clamped to a valid token for the load)
+        const int64_t t = c0 + (lane < n ? lane : n - 1);
+        const T* kp = kc + token_block(row, sb, t, bs_shift) * p.k_sb + (t & (bs - 1)) * X;
+        float dot = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < D / X; ++c) {
+            const u32x4 kv = load16(kp + (int64_t)c * bs * X);
+#pragma unroll
+            for (int j = 0; j < X; ++j) dot += q_lds[c * X + j] * elem16<E>(kv, j);
+        }
+        const float sc = lane < n ? dot * p.scale_log2 : -INFINITY;
+        const float mn = fmaxf(m, wave_max(sc));
+        const float alpha = fast_exp2(m - mn);
+        const float pl = lane < n ? fast_exp2(sc - mn) : 0.0f;
+        l = l * alpha + pl;
+        m = mn;
+        p_lds[lane] = pl;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < DVR; ++r) acc[r] *= alpha;
+
+        // ---- weighted values
+        if constexpr (!ROWV) {
+            // lane <-> row dv = lane + 64*r; VT consecutive tokens per load
+            constexpr int VT = X;
+            if (bs >= VT) {
+                const int nv = (n + VT - 1) / VT;
+                for (int v = 0; v < nv; ++v) {
+                    const int64_t tv = c0 + v * VT;
+                    const T* vp = vc + token_block(row, sb, tv, bs_shift) * p.v_sb + (tv & (bs - 1));
+                    float pv[VT];
+#pragma unroll
+                    for (int j = 0; j < VT; ++j) pv[j] = p_lds[v * VT + j];
+                    const bool full = (v + 1) * VT <= n;
+#pragma unroll
+                    for (int r = 0; r < DVR; ++r) {
+                        const u32x4 vv = load16(vp + (int64_t)(lane + kWave * r) * bs);
+#pragma unroll
+                        for (int j = 0; j < VT; ++j) {
+                            float x = elem16<E>(vv, j);
+                            if (!full) x = (v * VT + j < n) ? x : 0.0f;
+                            acc[r] += pv[j] * x;
+                        }
+                    }
+                }
+            } else {
+                // small blocks: one token at a time, one element per row
+                for (int j = 0; j < n; ++j) {
+                    const int64_t tj = c0 + j;
+                    const T* vp = vc + token_block(row, sb, tj, bs_shift) * p.v_sb + (tj & (bs - 1));
+                    const float pj = p_lds[j];
+#pragma unroll
+                    for (int r = 0; r < DVR; ++r) acc[r] += pj * to_f32(vp[(int64_t)(lane + kWave * r) * bs]);
+                }
+            }
+        } else {
+            // page size 1: lane <-> values [lane*DVR, lane*DVR + DVR) of each row
+            for (int j = 0; j < n; ++j) {
+                const int64_t tj = c0 + j;
+                const T* vp = vc + token_block(row, sb, tj, 0) * p.v_sb + lane * DVR;
+                const float pj = p_lds[j];
+                if constexpr (DVR * E::size == 16) {
+                    const u32x4 vv = load16(vp);
+#pragma unroll
+                    for (int r = 0; r < DVR; ++r) acc[r] += pj * elem16<E>(vv, r);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < DVR; ++r) acc[r] += pj * to_f32(vp[r]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    const float lsum = wave_sum(l);
+    if (lane == 0) {
+        *mlp = m * kLn2;
+        *esp = lsum;
+    }
+    const float inv = 1.0f / lsum;
+    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp;
+#pragma unroll
+    for (int r = 0; r < DVR; ++r) {
+        const int dv = ROWV ? lane * DVR + r : lane + kWave * r;
+        out[dv] = acc[r] * inv;
+    }
+}
+
+bool decode_valu_supported(int dtype, int D, int Dv)
+{
+    (void)dtype;
+    return (D == Dv && (D == 64 || D == 128 || D == 256)) || (D == 576 && Dv == 512);
+}
+
+template <class E, int D, int DV>
+static hipError_t launch_valu_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
+{
+    dim3 grid(parts, p.num_heads, num_seqs), block(kWave);
+    if (p.bs_shift == 0)
+        hipLaunchKernelGGL((k_decode_valu<E, D, DV, true>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((k_decode_valu<E, D, DV, false>), grid, block, 0, st, p);
+    return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_valu_e(const DecodeParams& p, int D, int Dv, int num_seqs, int parts,
+                                hipStream_t st)
+{
+    if (D == 64 && Dv == 64) return launch_valu_t<E, 64, 64>(p, num_seqs, parts, st);
+    if (D == 128 && Dv == 128) return launch_valu_t<E, 128, 128>(p, num_seqs, parts, st);
+    if (D == 256 && Dv == 256) return launch_valu_t<E, 256, 256>(p, num_seqs, parts, st);
+    if (D == 576 && Dv == 512) return launch_valu_t<E, 576, 512>(p, num_seqs, parts, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, int Dv, int num_seqs,
+                              int parts, hipStream_t st)
+{
+    switch (dtype) {
+    case PA_F32: return launch_valu_e<F32>(p, D, Dv, num_seqs, parts, st);
+    case PA_F16: return launch_valu_e<F16>(p, D, Dv, num_seqs, parts, st);
+    case PA_BF16: return launch_valu_e<BF16>(p, D, Dv, num_seqs, parts, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,144 @@
+// index_kernels.hip -- integer helpers of the decode step: the flat page list,
+// the split-count heuristic and the token-offset test hook.
+#include <limits.h>
+
+#include "kernels.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// Flat page list (vLLM PR 35765, _copy_page_indices_kernel in its
+// stride-robust form): one workgroup per request copies its
+// cu[r+1] - cu[r] table entries to page_indices[cu[r] ...], reading the row
+// with both strides. 1024 lanes per row keep a long row to a few passes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_page_indices(int32_t* __restrict__ out,
+                                                       const int32_t* __restrict__ bt, int64_t s0,
+                                                       int64_t s1,
+                                                       const int32_t* __restrict__ cu)
+{
+    const int r = blockIdx.x;
+    const int64_t start = cu[r];
+    const int64_t n = (int64_t)cu[r + 1] - start;
+    const int32_t* row = bt + (int64_t)r * s0;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) out[start + i] = row[i * s1];
+}
+
+hipError_t launch_page_indices(int32_t* out, const int32_t* bt, int64_t s0, int64_t s1,
+                               const int32_t* cu, int num_reqs, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_page_indices, dim3(num_reqs), dim3(1024), 0, st, out, bt, s0, s1, cu);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-count heuristic (sglang metadata.py, get_num_kv_splits_triton), one
+// workgroup: block-wide max/min of the lengths, then each lane evaluates the
+// formula for its sequences. The float steps follow the page's fp32
+// arithmetic: fp32(max)/64, log2 (the double log2 rounded to fp32), one
+// fp32 multiply by the core count, truncation to int32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__global__ __launch_bounds__(1024) void k_num_kv_splits(int32_t* __restrict__ out,
+                                                        const int32_t* __restrict__ seq_lens,
+                                                        int num_seq, int num_group, int num_head,
+                                                        int num_kv_head, int max_kv_splits,
+                                                        int cores)
+{
+    __shared__ int s_max[16], s_min[16];
+    const int tid = threadIdx.x;
+    int mx = 1, mn = INT_MAX;
+    for (int i = tid; i < num_seq; i += blockDim.x) {
+        int L = seq_lens[i];
+        L = L < 1 ? 1 : L;
+        mx = L > mx ? L : mx;
+        mn = L < mn ? L : mn;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        int a = __shfl_xor(mx, o, kWave), b = __shfl_xor(mn, o, kWave);
+        mx = a > mx ? a : mx;
+        mn = b < mn ? b : mn;
+    }
+    const int wave = tid / kWave, nwaves = blockDim.x / kWave;
+    if ((tid & (kWave - 1)) == 0) {
+        s_max[wave] = mx;
+        s_min[wave] = mn;
+    }
+    __syncthreads();
+    int64_t max_len = s_max[0], min_len = s_min[0];
+    for (int w = 1; w < nwaves; ++w) {
+        max_len = s_max[w] > max_len ? s_max[w] : max_len;
+        min_len = s_min[w] < min_len ? s_min[w] : min_len;
+    }
+    if (max_len * 8 < min_len * 10) min_len = max_len;
+    int64_t splits1 = cdiv(max_len, min_len);
+    splits1 = splits1 < max_kv_splits ? splits1 : max_kv_splits;
+    const int64_t chunk1 = cdiv(max_len, splits1);
+
+    const float ext = (float)max_len / 64.0f;
+    const float lg = (float)log2((double)ext);
+    const float prod = __fmul_rn((float)cores, fmaxf(lg, 1.0f));
+    const int64_t cores_ext = (int32_t)prod;
+
+    const int64_t group = num_head / num_kv_head;
+    int64_t grid;
+    if (group == 1) {
+        grid = (int64_t)num_seq * num_group * num_head;
+    } else {
+        const int64_t bh = group < 16 ? group : 16;
+        grid = (int64_t)num_seq * num_group * cdiv(num_head, bh);
+    }
+    int64_t splits2 = cdiv(cores_ext, grid);
+    splits2 = splits2 < max_kv_splits ? splits2 : max_kv_splits;
+    const int64_t chunk2 = cdiv(max_len, splits2);
+
+    for (int i = tid; i < num_seq; i += blockDim.x) {
+        int64_t L = seq_lens[i];
+        L = L < 1 ? 1 : L;
+        const int64_t a = cdiv(L, chunk1), b = cdiv(L, chunk2);
+        const int32_t n = (int32_t)(a > b ? a : b);
+        for (int g = 0; g < num_group; ++g) out[(int64_t)i * num_group + g] = n;
+    }
+}
+
+hipError_t launch_num_kv_splits(int32_t* out, const int32_t* seq_lens, int num_seq, int num_group,
+                                int num_head, int num_kv_head, int max_kv_splits, int cores,
+                                hipStream_t st)
+{
+    hipLaunchKernelGGL(k_num_kv_splits, dim3(1), dim3(1024), 0, st, out, seq_lens, num_seq,
+                       num_group, num_head, num_kv_head, max_kv_splits, cores);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token offsets through the same address helper the decode kernels use.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_token_offsets(int64_t* __restrict__ out, int64_t out_ss,
+                                                       PageList pl,
+                                                       const int32_t* __restrict__ seq_lens,
+                                                       int max_seq_len, int bs_shift,
+                                                       int64_t block_stride, int64_t slot_stride)
+{
+    const int s = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t L = seq_lens[s];
+    L = L < max_seq_len ? L : max_seq_len;
+    if (t >= L) return;
+    const int32_t* row = page_row(pl, s);
+    out[(int64_t)s * out_ss + t] = token_offset(row, pl.stride_b, t, bs_shift, block_stride, slot_stride);
+}
+
+hipError_t launch_token_offsets(int64_t* out, int64_t out_ss, const PageList& pl,
+                                const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                                int bs_shift, int64_t block_stride, int64_t slot_stride,
+                                hipStream_t st)
+{
+    dim3 grid((max_seq_len + 255) / 256, num_seqs);
+    hipLaunchKernelGGL(k_token_offsets, grid, dim3(256), 0, st, out, out_ss, pl, seq_lens,
+                       max_seq_len, bs_shift, block_stride, slot_stride);
+    return hipGetLastError();
+}
+
+}  // namespace pa

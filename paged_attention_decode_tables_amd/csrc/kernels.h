@@ -1,0 +1,72 @@
+// kernels.h -- kernel parameter blocks and host launchers inside libpagedattn.
+// Validation happens in api.hip before any launcher is called; launchers
+// assume valid arguments and return the hipError_t of their launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace pa {
+
+// Phase-1 parameters (validated copy of pa_decode_args).
+struct DecodeParams {
+    float* tmp;
+    int64_t tmp_ss, tmp_sh, tmp_sp;
+    float* exp_sums;
+    float* max_logits;
+    int64_t ml_ss, ml_sh;
+    const void* q;
+    int64_t q_ss, q_sh;
+    const void* kc;
+    int64_t k_sb, k_sh;
+    const void* vc;
+    int64_t v_sb, v_sh;
+    PageList pl;
+    const int32_t* seq_lens;
+    const int32_t* num_splits;
+    float scale_log2;  // scale * log2(e): logits are kept in base 2
+    int num_heads, num_kv_heads, group;
+    int bs_shift;
+    int partition_size, max_num_parts;
+};
+
+struct ReduceParams {
+    void* out;
+    int64_t out_ss, out_sh;
+    const float* tmp;
+    int64_t tmp_ss, tmp_sh, tmp_sp;
+    const float* exp_sums;
+    const float* max_logits;
+    int64_t ml_ss, ml_sh;
+    const int32_t* seq_lens;
+    const int32_t* num_splits;
+    int num_seqs, num_heads, partition_size, max_num_parts;
+};
+
+// Which phase-1 kernel family serves a problem.
+enum class DecodeKernel { VALU, MFMA };
+
+// Launchers. `parts` is the grid's split dimension.
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, int Dv, int num_seqs,
+                              int parts, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int D, int Dv, int num_seqs,
+                              int parts, hipStream_t st);
+bool decode_valu_supported(int dtype, int D, int Dv);
+bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size);
+
+hipError_t launch_reduce(const ReduceParams& p, int out_dtype, int Dv, hipStream_t st);
+bool reduce_supported(int Dv);
+
+hipError_t launch_page_indices(int32_t* out, const int32_t* bt, int64_t s0, int64_t s1,
+                               const int32_t* cu, int num_reqs, hipStream_t st);
+hipError_t launch_num_kv_splits(int32_t* out, const int32_t* seq_lens, int num_seq, int num_group,
+                                int num_head, int num_kv_head, int max_kv_splits, int cores,
+                                hipStream_t st);
+hipError_t launch_token_offsets(int64_t* out, int64_t out_ss, const PageList& pl,
+                                const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                                int bs_shift, int64_t block_stride, int64_t slot_stride,
+                                hipStream_t st);
+
+}  // namespace pa

@@ -86,6 +86,17 @@ class Workload:
         per_tok = self.head_size if self.kv_aliased else self.head_size + self.v_head_size
         return self.total_tokens * self.num_kv_heads * per_tok * self.elem_size
 
+    def subset(self, seqs) -> "Workload":
+        """The same workload restricted to some sequences (shares the caches)."""
+        idx = torch.as_tensor(list(seqs), dtype=torch.long)
+        kw = {k: getattr(self, k) for k in self.__dataclass_fields__}
+        kw["seq_lens"] = self.seq_lens[idx].clone()
+        kw["block_tables"] = self.block_tables[idx].clone()
+        kw["query"] = self.query[idx].clone()
+        kw["cu_num_blocks"] = None
+        kw["notes"] = list(self.notes)
+        return Workload(**kw)
+
     def to(self, device) -> "Workload":
         kw = {k: getattr(self, k) for k in self.__dataclass_fields__}
         for k in ("seq_lens", "block_tables", "query", "cu_num_blocks"):

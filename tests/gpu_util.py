@@ -1,0 +1,142 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+the oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import paged_attention_decode_tables_amd as pad
+from paged_attention_decode_tables_amd import workloads
+
+DEV = "cuda:0"
+
+# Tolerances on fp32 outputs against the float64 oracle (max abs error):
+# 2e-3 for fp32 caches, 1e-2 for fp16/bf16 caches.
+ATOL = {torch.float32: 2e-3, torch.float16: 1e-2, torch.bfloat16: 1e-2}
+# exp_sums relative tolerance: the matrix-core path rounds each probability
+# to the cache type before the P.V product and sums the rounded values
+# (relative rounding <= 2^-9 for bf16, 2^-11 for f16); the vector path sums
+# fp32 values.
+LTOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 4e-3}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def oracle_args(w: workloads.Workload):
+    return (np64(w.query), np64(w.key_cache), np64(w.value_cache), w.block_tables.numpy(),
+            w.seq_lens.numpy(), w.scale)
+
+
+def workspace(w: workloads.Workload, max_parts: int, device=DEV):
+    S, H, Dv = w.num_seqs, w.num_heads, w.v_head_size
+    nan = float("nan")
+    tmp = torch.full((S, H, max_parts, Dv), nan, dtype=torch.float32, device=device)
+    ml = torch.full((S, H, max_parts), nan, dtype=torch.float32, device=device)
+    es = torch.full((S, H, max_parts), nan, dtype=torch.float32, device=device)
+    return tmp, ml, es
+
+
+def max_parts_for(w: workloads.Workload, partition_size: int) -> int:
+    return max(1, math.ceil(max(w.max_seq_len, 1) / partition_size))
+
+
+def run_gpu(w: workloads.Workload, *, partition_size=512, num_splits=None, max_parts=None,
+            kernel="auto", out_dtype=torch.float32, csr=False, block_tables=None):
+    """Phase 1 + phase 2 on the GPU. Returns (out, tmp, ml, es) on the CPU."""
+    g = w.to(DEV)
+    if max_parts is None:
+        max_parts = max_parts_for(w, partition_size) if num_splits is None else 32
+    tmp, ml, es = workspace(w, max_parts)
+    ns = None if num_splits is None else torch.as_tensor(num_splits, dtype=torch.int32, device=DEV)
+    bt = g.block_tables if block_tables is None else block_tables.to(DEV)
+    indptr = None
+    if csr:
+        cu = torch.zeros(w.num_seqs + 1, dtype=torch.int32)
+        nblk = [(max(int(L), 0) + w.block_size - 1) // w.block_size for L in w.seq_lens]
+        cu[1:] = torch.cumsum(torch.tensor(nblk, dtype=torch.int32), 0)
+        indptr = cu.to(DEV)
+        flat = torch.full((max(int(cu[-1]), 1),), -1, dtype=torch.int32, device=DEV)
+        pad.build_page_indices(flat, bt, indptr)
+        bt = flat
+    pad.paged_attn_decode(tmp, es, ml, g.query, g.key_cache, g.value_cache, bt, g.seq_lens,
+                          w.scale, w.max_seq_len, partition_size=partition_size,
+                          num_splits=ns, kv_indptr=indptr, kernel=kernel)
+    out = torch.full((w.num_seqs, w.num_heads, w.v_head_size), float("nan"), dtype=out_dtype,
+                     device=DEV)
+    pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens, partition_size=partition_size,
+                          num_splits=ns)
+    torch.cuda.synchronize()
+    return out.cpu(), tmp.cpu(), ml.cpu(), es.cpu()
+
+
+def split_lengths(w, partition_size, num_splits, max_parts):
+    """Per-sequence split length under the documented split rule."""
+    out = []
+    for s in range(w.num_seqs):
+        if num_splits is None:
+            out.append(partition_size)
+        else:
+            n = min(max(int(num_splits[s]), 1), max_parts)
+            L = max(int(w.seq_lens[s]), 1)
+            out.append(math.ceil(math.ceil(L / n) / 64) * 64)
+    return out
+
+
+def check_partials(w, orc, tmp, ml, es, *, partition_size=512, num_splits=None, seqs=None):
+    """Compare the GPU phase-1 outputs with the oracle's per-split statistics."""
+    P = tmp.shape[2]
+    sub = w if seqs is None else subset(w, seqs)
+    otmp, oml, oes = orc.partials(*oracle_args(sub), max_num_parts=P, partition_size=partition_size,
+                                  num_splits=None if num_splits is None else
+                                  np.asarray(num_splits)[seqs if seqs is not None else slice(None)])
+    idx = list(range(w.num_seqs)) if seqs is None else list(seqs)
+    lens = split_lengths(sub, partition_size, None if num_splits is None else
+                         np.asarray(num_splits)[idx], P)
+    atol, ltol = ATOL[w.dtype], LTOL[w.dtype]
+    for i, s in enumerate(idx):
+        L = int(w.seq_lens[s])
+        n = 0 if L <= 0 else min(math.ceil(L / lens[i]), P)
+        gm, ge, gt = ml[s].double().numpy(), es[s].double().numpy(), tmp[s].double().numpy()
+        # empty splits: -inf / 0, tmp untouched (still NaN)
+        assert np.all(gm[:, n:] == -np.inf) and np.all(ge[:, n:] == 0), (s, n)
+        assert np.all(np.isnan(gt[:, n:])), s
+        if n == 0:
+            continue
+        em = np.abs(gm[:, :n] - oml[i, :, :n])
+        assert em.max() <= 2e-4 + 1e-5 * np.abs(oml[i, :, :n]).max(), (s, em.max())
+        el = np.abs(ge[:, :n] / oes[i, :, :n] - 1.0)
+        assert el.max() <= ltol, (s, el.max())
+        et = np.abs(gt[:, :n] - otmp[i, :, :n])
+        assert et.max() <= atol, (s, et.max())
+
+
+def subset(w: workloads.Workload, seqs) -> workloads.Workload:
+    return w.subset(seqs)
+
+
+def check_output(w, orc, out, seqs=None):
+    """Compare final outputs (any dtype) with the oracle's attention."""
+    idx = list(range(w.num_seqs)) if seqs is None else list(seqs)
+    sub = w if seqs is None else subset(w, idx)
+    ref = orc.attention(*oracle_args(sub))
+    got = out[idx].double().numpy()
+    tol = ATOL[w.dtype]
+    if out.dtype == torch.float32:
+        err = np.abs(got - ref)
+        assert err.max() <= tol, err.max()
+    else:
+        # output rounded to a 16-bit type: allow its half ulp on top
+        half_ulp = 2.0 ** (-8 if out.dtype == torch.bfloat16 else -10)
+        err = np.abs(got - ref) - half_ulp * np.abs(ref)
+        assert err.max() <= tol, err.max()
+    return float(np.abs(got - ref).max())

@@ -1,0 +1,205 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/pagedattn.h declares, its argument blocks have the header's layout,
+and invalid arguments are rejected on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime first, as the product does)
+
+from paged_attention_decode_tables_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return api.load_library()
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("paged_attn_decode", "paged_attn_reduce", "build_page_indices", "num_kv_splits"):
+        assert n in names
+    assert len(names) >= 6, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def _c_layout(struct: str, fields):
+    src = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){",
+           f'printf("%zu\\n", sizeof({struct}));']
+    src += [f'printf("%zu\\n", offsetof({struct}, {f}));' for f in fields]
+    src += ["return 0;}"]
+    d = os.path.join(ROOT, "_build")
+    os.makedirs(d, exist_ok=True)
+    c = os.path.join(d, f"layout_{struct}.c")
+    exe = c[:-2]
+    open(c, "w").write("\n".join(src))
+    subprocess.run(["gcc", "-std=c99", c, "-o", exe], check=True)
+    vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("cls,cname", [(api.DecodeArgs, "pa_decode_args"), (api.ReduceArgs, "pa_reduce_args")])
+def test_argument_block_layout_matches_header(cls, cname):
+    fields = [f for f, _ in cls._fields_]
+    size, offs = _c_layout(cname, fields)
+    assert ctypes.sizeof(cls) == size
+    assert [getattr(cls, f).offset for f in fields] == offs
+
+
+# ---------------------------------------------------------------------------
+# host-side validation (dummy device addresses are never dereferenced: every
+# case below must be rejected before a launch)
+# ---------------------------------------------------------------------------
+FAKE = 1 << 20  # 16-byte aligned stand-in address
+
+
+def good_decode(dtype=api.PA_BF16, D=128, Dv=128, H=8, Hkv=2, bs=16, P=512):
+    a = api.DecodeArgs()
+    esz = 4 if dtype == api.PA_F32 else 2
+    x = 16 // esz
+    S, maxp = 2, 4
+    a.tmp_output = FAKE
+    a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = H * maxp * Dv, maxp * Dv, Dv, 1
+    a.exp_sums = a.max_logits = FAKE
+    a.ml_stride_s, a.ml_stride_h, a.ml_stride_p = H * maxp, maxp, 1
+    a.query = FAKE
+    a.q_stride_s, a.q_stride_h, a.q_stride_d = H * D, D, 1
+    a.key_cache = FAKE
+    a.k_stride_b, a.k_stride_h, a.k_stride_dx, a.k_stride_bs, a.k_stride_x = Hkv * D * bs, D * bs, bs * x, x, 1
+    a.value_cache = FAKE
+    a.v_stride_b, a.v_stride_h, a.v_stride_d, a.v_stride_bs = Hkv * Dv * bs, Dv * bs, bs, 1
+    a.block_tables = a.seq_lens = FAKE
+    a.bt_stride_s, a.bt_stride_b = 128, 1
+    a.scale = 0.1
+    a.num_seqs, a.num_heads, a.num_kv_heads = S, H, Hkv
+    a.head_size, a.v_head_size, a.block_size, a.x = D, Dv, bs, x
+    a.partition_size, a.max_num_parts, a.max_seq_len = P, maxp, 2048
+    a.dtype = dtype
+    return a
+
+
+def _mut(a, **kw):
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+DECODE_BAD = [
+    ("dtype", dict(dtype=7), api.PA_EINVAL),
+    ("heads", dict(num_heads=7), api.PA_EINVAL),
+    ("kvheads0", dict(num_kv_heads=0), api.PA_EINVAL),
+    ("bs_not_pow2", dict(block_size=12), api.PA_EINVAL),
+    ("bs_too_big", dict(block_size=2048), api.PA_EINVAL),
+    ("x_mismatch", dict(x=4, k_stride_bs=4, k_stride_dx=64), api.PA_ENOTSUP),
+    ("partition_not_64", dict(partition_size=100), api.PA_EINVAL),
+    ("too_few_parts", dict(max_seq_len=4096), api.PA_EINVAL),
+    ("null_query", dict(query=None), api.PA_EINVAL),
+    ("null_seq_lens", dict(seq_lens=None), api.PA_EINVAL),
+    ("q_inner_stride", dict(q_stride_d=2), api.PA_ENOTSUP),
+    ("k_inner_stride", dict(k_stride_bs=16), api.PA_ENOTSUP),
+    ("v_inner_stride", dict(v_stride_d=128, v_stride_bs=16), api.PA_ENOTSUP),
+    ("tmp_inner_stride", dict(tmp_stride_d=2), api.PA_ENOTSUP),
+    ("head_size", dict(head_size=96, v_head_size=96), api.PA_ENOTSUP),
+    ("misaligned_key", dict(key_cache=FAKE + 2), api.PA_ENOTSUP),
+    ("misaligned_row", dict(k_stride_b=16 * 128 * 2 + 1), api.PA_ENOTSUP),
+    ("max_parts0", dict(max_num_parts=0), api.PA_EINVAL),
+    ("neg_seqs", dict(num_seqs=-1), api.PA_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,change,code", DECODE_BAD, ids=[c[0] for c in DECODE_BAD])
+def test_decode_rejects(lib, name, change, code):
+    a = _mut(good_decode(), **change)
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == code
+    assert lib.pa_last_error()
+
+
+def test_decode_mfma_hint_rejected_where_it_does_not_apply(lib):
+    a = _mut(good_decode(dtype=api.PA_F32, D=64, Dv=64), kernel_hint=api.PA_KERNEL["mfma"])
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
+    a = _mut(good_decode(H=2, Hkv=2), kernel_hint=api.PA_KERNEL["mfma"])  # group 1
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
+
+
+def test_decode_empty_batch_is_a_noop(lib):
+    a = _mut(good_decode(), num_seqs=0, query=None)
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_OK
+    a = _mut(good_decode(), max_seq_len=0)
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_OK
+
+
+def good_reduce():
+    a = api.ReduceArgs()
+    S, H, P, Dv = 2, 8, 4, 128
+    a.output = FAKE
+    a.out_stride_s, a.out_stride_h, a.out_stride_d = H * Dv, Dv, 1
+    a.out_dtype = api.PA_BF16
+    a.tmp_output = FAKE
+    a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = H * P * Dv, P * Dv, Dv, 1
+    a.exp_sums = a.max_logits = FAKE
+    a.ml_stride_s, a.ml_stride_h, a.ml_stride_p = H * P, P, 1
+    a.seq_lens = FAKE
+    a.num_seqs, a.num_heads, a.v_head_size = S, H, Dv
+    a.partition_size, a.max_num_parts = 512, P
+    return a
+
+
+REDUCE_BAD = [
+    ("out_dtype", dict(out_dtype=9), api.PA_EINVAL),
+    ("heads0", dict(num_heads=0), api.PA_EINVAL),
+    ("partition", dict(partition_size=32), api.PA_EINVAL),
+    ("null_tmp", dict(tmp_output=None), api.PA_EINVAL),
+    ("dv", dict(v_head_size=96), api.PA_ENOTSUP),
+    ("inner", dict(out_stride_d=2), api.PA_ENOTSUP),
+    ("tmp_align", dict(tmp_stride_p=130), api.PA_ENOTSUP),
+]
+
+
+@pytest.mark.parametrize("name,change,code", REDUCE_BAD, ids=[c[0] for c in REDUCE_BAD])
+def test_reduce_rejects(lib, name, change, code):
+    a = _mut(good_reduce(), **change)
+    assert lib.paged_attn_reduce(ctypes.byref(a), None) == code
+
+
+def test_reduce_empty_batch_is_a_noop(lib):
+    a = _mut(good_reduce(), num_seqs=0, output=None)
+    assert lib.paged_attn_reduce(ctypes.byref(a), None) == api.PA_OK
+
+
+def test_index_helpers_reject(lib):
+    assert lib.build_page_indices(FAKE, FAKE, 8, 1, FAKE, -1, None) == api.PA_EINVAL
+    assert lib.build_page_indices(None, FAKE, 8, 1, FAKE, 3, None) == api.PA_EINVAL
+    assert lib.build_page_indices(None, None, 8, 1, None, 0, None) == api.PA_OK
+    assert lib.num_kv_splits(FAKE, FAKE, 4, 1, 8, 1, 0, 256, None) == api.PA_EINVAL
+    assert lib.num_kv_splits(FAKE, FAKE, 4, 0, 8, 1, 16, 256, None) == api.PA_EINVAL
+    assert lib.num_kv_splits(FAKE, FAKE, 4, 1, 8, 1, 16, 0, None) == api.PA_EINVAL
+    assert lib.num_kv_splits(None, None, 0, 1, 8, 1, 16, 256, None) == api.PA_OK
+    assert lib.paged_token_offsets(FAKE, 8, FAKE, 8, 1, None, FAKE, 2, 8, 3, 1, 1, None) == api.PA_EINVAL
+    assert lib.paged_token_offsets(None, 8, FAKE, 8, 1, None, FAKE, 2, 8, 4, 1, 1, None) == api.PA_EINVAL
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(api.PagedAttnError) as e:
+        api._check(api.PA_EINVAL)
+    assert e.value.code == api.PA_EINVAL

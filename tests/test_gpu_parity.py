@@ -1,0 +1,349 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer work (token offsets, page_indices, num_kv_splits) must match bit for
+bit; attention outputs within max abs error 2e-3 (fp32 caches) or 1e-2
+(fp16/bf16 caches) on fp32 outputs. Unused cache slots, unreferenced blocks,
+block-table padding and the workspaces are poisoned with NaN (padding points
+at a NaN-filled block), so any read of data the method must not read shows.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_decode_tables_amd as pad
+from paged_attention_decode_tables_amd import workloads
+from gpu_util import (DEV, check_output, check_partials, max_parts_for, np64, oracle_args,
+                      run_gpu, say, subset)
+import pins
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pad.load_library()
+
+
+# ---------------------------------------------------------------------------
+# integer helpers: bit-exact
+# ---------------------------------------------------------------------------
+def test_token_offsets_worked_example():
+    say("token offsets: worked example")
+    bt = torch.tensor([[40, 30]], dtype=torch.int32, device=DEV)
+    out = torch.full((1, 16), -1, dtype=torch.int64, device=DEV)
+    pad.paged_token_offsets(out, bt, torch.tensor([16], dtype=torch.int32, device=DEV), 8, 1, 1)
+    rows = [ln.split() for ln in open(pins.GOLDEN + "/worked_example_offsets.txt")
+            if ln.strip() and not ln.startswith("#")]
+    assert out.cpu()[0].tolist() == [int(r[1]) for r in rows]
+
+
+@pytest.mark.parametrize("bs", [1, 2, 8, 16, 32, 128])
+def test_token_offsets_match_oracle(orc, bs):
+    say(f"token offsets bs={bs}")
+    rng = np.random.default_rng(bs)
+    S = 5
+    lens = rng.integers(0, 700, S).astype(np.int32)
+    lens[1] = 0
+    need = [-(-int(L) // bs) for L in lens]
+    nb = sum(need) + 1
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((S, max(need) + 3), nb - 1, dtype=np.int32)
+    pos = 0
+    for s, n in enumerate(need):
+        bt[s, :n] = perm[pos:pos + n]
+        pos += n
+    block_stride, slot_stride = 8 * 16 * bs * 8, 8
+    want = orc.token_offsets(bt, lens, bs, block_stride, slot_stride)
+    out = torch.full(want.shape, -1, dtype=torch.int64, device=DEV)
+    pad.paged_token_offsets(out, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV), bs,
+                            block_stride, slot_stride)
+    assert np.array_equal(out.cpu().numpy(), want)
+    # non-unit element stride (every other column of a wider table)
+    wide = np.repeat(bt, 2, axis=1)
+    view = torch.from_numpy(wide).to(DEV)[:, ::2]
+    out2 = torch.full(want.shape, -1, dtype=torch.int64, device=DEV)
+    pad.paged_token_offsets(out2, view, torch.from_numpy(lens).to(DEV), bs, block_stride, slot_stride)
+    assert np.array_equal(out2.cpu().numpy(), want)
+
+
+def test_page_indices_match_oracle(orc):
+    say("page indices")
+    rng = np.random.default_rng(3)
+    R, maxB = 37, 3000
+    big = rng.integers(0, 1 << 30, (maxB, R)).astype(np.int32)
+    big_d = torch.from_numpy(big).to(DEV)
+    for contiguous in (True, False):
+        # a contiguous [R, maxB] table, then the transposed view of [maxB, R] (stride1 = R)
+        bt_np = np.ascontiguousarray(big.T) if contiguous else big.T
+        bt_d = big_d.t().contiguous() if contiguous else big_d.t()
+        n = rng.integers(0, maxB + 1, R)
+        n[[0, 5]] = 0
+        n[7] = maxB
+        cu = np.zeros(R + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(n)
+        want = orc.page_indices(bt_np, cu)
+        out = torch.full((int(cu[-1]),), -1, dtype=torch.int32, device=DEV)
+        pad.build_page_indices(out, bt_d, torch.from_numpy(cu).to(DEV))
+        assert np.array_equal(out.cpu().numpy(), want), contiguous
+
+
+def test_page_indices_mla_config(orc):
+    say("page indices: MLA config")
+    w = workloads.config(5)
+    want = orc.page_indices(w.block_tables.numpy(), w.cu_num_blocks.numpy())
+    out = torch.full((int(w.cu_num_blocks[-1]),), -1, dtype=torch.int32, device=DEV)
+    pad.build_page_indices(out, w.block_tables.to(DEV), w.cu_num_blocks.to(DEV))
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def _splits_gpu(lens, g, hq, hk, mx, cores):
+    t = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+    out = torch.full((len(lens) * g,), -1, dtype=torch.int32, device=DEV)
+    pad.num_kv_splits(out, t, g, hq, hk, mx, cores)
+    return out.cpu().numpy()
+
+
+def test_num_kv_splits_golden():
+    say("num_kv_splits golden")
+    for ln in open(pins.GOLDEN + "/num_kv_splits_pins.txt"):
+        if not ln.strip() or ln.startswith("#"):
+            continue
+        f = [c.strip() for c in ln.split("|")]
+        lens = [int(v) for v in f[1].split(",")]
+        g, hq, hk, mx, cores = (int(v) for v in f[2:7])
+        want = [int(v) for v in f[7].split(",")]
+        assert _splits_gpu(lens, g, hq, hk, mx, cores).tolist() == want, f[0]
+
+
+def test_num_kv_splits_random(orc):
+    say("num_kv_splits random")
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        S = int(rng.integers(1, 3000))
+        lens = np.exp(rng.normal(math.log(rng.integers(1, 20000)), rng.uniform(0, 2), S))
+        lens = np.clip(np.rint(lens), -3, 200000).astype(np.int32)
+        g = int(rng.integers(1, 4))
+        hk = int(rng.integers(1, 9))
+        hq = hk * int(rng.choice([1, 2, 4, 8, 16, 32]))
+        mx = int(rng.integers(1, 65))
+        cores = int(rng.choice([1, 80, 256, 304]))
+        want = orc.num_kv_splits(lens, g, hq, hk, mx, cores)
+        got = _splits_gpu(lens, g, hq, hk, mx, cores)
+        assert np.array_equal(got, want), trial
+
+
+def test_num_kv_splits_skewed_config(orc):
+    say("num_kv_splits: skewed config")
+    w = workloads.config(4)
+    want = orc.num_kv_splits(w.seq_lens.numpy(), 1, w.num_heads, w.num_kv_heads, w.max_kv_splits,
+                             w.device_core_count)
+    got = _splits_gpu(w.seq_lens.tolist(), 1, w.num_heads, w.num_kv_heads, w.max_kv_splits,
+                      w.device_core_count)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# attention: small cases spanning several chunks / partitions, ragged tails
+# ---------------------------------------------------------------------------
+SMALL = [
+    # name, dtype, lens, H, Hkv, D, bs, partition
+    ("f32_mha_bs8", "f32", [16, 13, 300, 1, 0, 129], 2, 2, 64, 8, 64),
+    ("f32_gqa_bs4", "f32", [200, 77, 64], 8, 2, 64, 4, 128),
+    ("f32_d128_bs1", "f32", [70, 3], 4, 4, 128, 1, 64),
+    ("f16_mha_bs16", "f16", [1, 17, 511, 512, 513, 1300], 4, 4, 128, 16, 512),
+    ("f16_mha_bs2", "f16", [33, 140], 2, 2, 64, 2, 64),
+    ("bf16_mha_bs128", "bf16", [1000, 129, 255], 2, 2, 128, 128, 256),
+    ("bf16_gqa8_bs16", "bf16", [1, 31, 32, 33, 700, 1500, 64], 16, 2, 128, 16, 512),
+    ("bf16_gqa8_p64", "bf16", [333, 65], 8, 1, 128, 16, 64),
+    ("bf16_gqa4_bs32", "bf16", [2047, 96, 5], 8, 2, 128, 32, 512),
+    ("bf16_gqa16_bs8", "bf16", [190, 9], 32, 2, 64, 8, 128),
+    ("bf16_gqa2_bs64", "bf16", [450, 700], 4, 2, 128, 64, 192),
+    ("f16_gqa8_bs16", "f16", [900, 37], 16, 2, 128, 16, 256),
+    ("f16_gqa3_d64", "f16", [129, 400], 6, 2, 64, 16, 128),
+    ("bf16_d256_gqa4", "bf16", [300, 41], 8, 2, 256, 16, 128),
+    ("f32_gqa4_d256", "f32", [150], 4, 1, 256, 16, 64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_decode_small(orc, case):
+    name, dt, lens, H, Hkv, D, bs, P = case
+    say(f"decode small {name}")
+    w = workloads.custom(seed=zlib.crc32(name.encode()) % 10007, seq_lens=lens, num_heads=H, num_kv_heads=Hkv,
+                         head_size=D, block_size=bs, dtype=dt, partition_size=P, poison=True)
+    kernels = ["auto", "valu"]
+    for kernel in kernels:
+        out, tmp, ml, es = run_gpu(w, partition_size=P, kernel=kernel)
+        check_partials(w, orc, tmp, ml, es, partition_size=P)
+        check_output(w, orc, out)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_decode_output_dtypes(orc, out_dtype):
+    say(f"decode output dtype {out_dtype}")
+    w = workloads.custom(seed=5, seq_lens=[900, 3, 64], num_heads=16, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="bf16", poison=True)
+    out, *_ = run_gpu(w, out_dtype=out_dtype)
+    check_output(w, orc, out)
+
+
+def test_decode_csr_page_list(orc):
+    say("decode CSR page list")
+    w = workloads.custom(seed=6, seq_lens=[515, 1, 250], num_heads=8, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="bf16", poison=True)
+    out, tmp, ml, es = run_gpu(w, csr=True)
+    check_partials(w, orc, tmp, ml, es)
+    check_output(w, orc, out)
+
+
+def test_decode_strided_caches_and_table(orc):
+    """K and V interleaved in one allocation (outer strides larger than packed)
+    and a block table read with element stride 2."""
+    say("decode strided caches")
+    w = workloads.custom(seed=8, seq_lens=[300, 45], num_heads=8, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="f16", poison=True)
+    NB = w.num_blocks
+    kv = torch.stack([w.key_cache.reshape(NB, -1), w.value_cache.reshape(NB, -1)], dim=1).to(DEV)
+    kd = kv[:, 0].view(w.key_cache.shape)    # block stride 2 * Hkv * D * bs
+    vd = kv[:, 1].view(w.value_cache.shape)
+    assert kd.stride(0) == 2 * 2 * 128 * 16 and vd.stride(0) == kd.stride(0)
+    g = w.to(DEV)
+    wide = torch.repeat_interleave(w.block_tables, 2, dim=1).to(DEV)[:, ::2]
+    P = 512
+    mp = max_parts_for(w, P)
+    tmp = torch.full((2, 8, mp, 128), float("nan"), device=DEV)
+    ml = torch.full((2, 8, mp), float("nan"), device=DEV)
+    es = torch.full((2, 8, mp), float("nan"), device=DEV)
+    pad.paged_attn_decode(tmp, es, ml, g.query, kd, vd, wide, g.seq_lens, w.scale, w.max_seq_len)
+    out = torch.empty((2, 8, 128), device=DEV)
+    pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens)
+    check_output(w, orc, out.cpu())
+
+
+def test_decode_num_splits(orc):
+    """Split counts from the heuristic on the device, consumed by both phases."""
+    say("decode num_splits")
+    w = workloads.custom(seed=9, seq_lens=[3000, 17, 400, 1, 1024, 2500], num_heads=16,
+                         num_kv_heads=4, head_size=128, block_size=32, dtype="bf16", poison=True)
+    g = w.to(DEV)
+    ns = torch.empty(w.num_seqs, dtype=torch.int32, device=DEV)
+    pad.num_kv_splits(ns, g.seq_lens, 1, w.num_heads, w.num_kv_heads, 16, 256)
+    nsc = ns.cpu().numpy()
+    assert np.array_equal(nsc, orc.num_kv_splits(w.seq_lens.numpy(), 1, 16, 4, 16, 256))
+    for kernel in ("auto", "valu"):
+        out, tmp, ml, es = run_gpu(w, num_splits=nsc, max_parts=16, kernel=kernel)
+        check_partials(w, orc, tmp, ml, es, num_splits=nsc)
+        check_output(w, orc, out)
+    # clamped to max_num_parts
+    out, tmp, ml, es = run_gpu(w, num_splits=[40] * 6, max_parts=4)
+    check_partials(w, orc, tmp, ml, es, num_splits=[40] * 6)
+    check_output(w, orc, out)
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+def test_block_permutation_is_bit_identical(kernel):
+    say(f"block permutation {kernel}")
+    w = workloads.custom(seed=12, seq_lens=[700, 90], num_heads=8, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="bf16", num_blocks=80)
+    out1, *_ = run_gpu(w, kernel=kernel)
+    perm = torch.randperm(80, generator=torch.Generator().manual_seed(1))
+    w2 = subset(w, [0, 1])
+    w2.key_cache = torch.empty_like(w.key_cache)
+    w2.value_cache = torch.empty_like(w.value_cache)
+    w2.key_cache[perm] = w.key_cache
+    w2.value_cache[perm] = w.value_cache
+    w2.block_tables = perm[w.block_tables.long()].to(torch.int32)
+    out2, *_ = run_gpu(w2, kernel=kernel)
+    assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+def test_length_one_returns_the_value_row(kernel):
+    say(f"length one {kernel}")
+    w = workloads.custom(seed=13, seq_lens=[1, 1, 1], num_heads=8, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="bf16", poison=True)
+    out, *_ = run_gpu(w, kernel=kernel)
+    for s in range(3):
+        blk = int(w.block_tables[s, 0])
+        for h in range(8):
+            assert torch.equal(out[s, h], w.value_cache[blk, h // 4, :, 0].float())
+
+
+def test_partition_size_invariance():
+    say("partition invariance")
+    w = workloads.custom(seed=14, seq_lens=[1500, 600], num_heads=8, num_kv_heads=2, head_size=128,
+                         block_size=16, dtype="bf16")
+    ref, *_ = run_gpu(w, partition_size=2048)
+    for P in (64, 192, 512):
+        out, *_ = run_gpu(w, partition_size=P)
+        assert (out - ref).abs().max().item() < 1e-2
+
+
+def test_constant_values():
+    say("constant values")
+    w = workloads.custom(seed=15, seq_lens=[777, 40], num_heads=16, num_kv_heads=2, head_size=64,
+                         block_size=16, dtype="bf16")
+    w.value_cache[:] = 1.5
+    for kernel in ("auto", "valu"):
+        out, *_ = run_gpu(w, kernel=kernel)
+        assert (out - 1.5).abs().max().item() < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# reduce alone, fed oracle partials
+# ---------------------------------------------------------------------------
+def test_reduce_with_oracle_partials(orc):
+    say("reduce with oracle partials")
+    w = workloads.custom(seed=16, seq_lens=[2000, 5, 0, 513], num_heads=4, num_kv_heads=1,
+                         head_size=64, v_head_size=64, block_size=16, dtype="f32", poison=True)
+    P = 64
+    mp = max_parts_for(w, P) + 2
+    otmp, oml, oes = orc.partials(*oracle_args(w), max_num_parts=mp, partition_size=P)
+    want = orc.reduce(np.nan_to_num(otmp, nan=0.0), oml, oes, w.seq_lens.numpy(), partition_size=P)
+    tmp = torch.from_numpy(otmp).float().to(DEV)  # NaN stays in the empty splits
+    ml = torch.from_numpy(oml).float().to(DEV)
+    es = torch.from_numpy(oes).float().to(DEV)
+    out = torch.empty((4, 4, 64), device=DEV)
+    pad.paged_attn_reduce(out, tmp, es, ml, w.seq_lens.to(DEV), partition_size=P)
+    got = out.cpu().double().numpy()
+    assert np.abs(got - want).max() < 1e-5
+    assert np.all(got[2] == 0)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times;
+# the oracle checks sampled sequences
+# ---------------------------------------------------------------------------
+FULL = [(1, None), (2, [0, 7, 31]), (3, [2, 5]), (4, "sample"), (5, [0, 33])]
+
+
+@pytest.mark.parametrize("cfg,seqs", FULL, ids=[f"config{c}" for c, _ in FULL])
+def test_full_config(orc, cfg, seqs):
+    say(f"full config {cfg}")
+    w = workloads.config(cfg, poison=True)
+    ns = None
+    mp = None
+    if cfg == 4:
+        g = w.to(DEV)
+        t = torch.empty(w.num_seqs, dtype=torch.int32, device=DEV)
+        pad.num_kv_splits(t, g.seq_lens, 1, w.num_heads, w.num_kv_heads, w.max_kv_splits,
+                          w.device_core_count)
+        ns = t.cpu().numpy()
+        assert np.array_equal(ns, orc.num_kv_splits(w.seq_lens.numpy(), 1, w.num_heads,
+                                                    w.num_kv_heads, w.max_kv_splits,
+                                                    w.device_core_count))
+        mp = w.max_kv_splits
+        order = np.argsort(w.seq_lens.numpy())
+        seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    out, tmp, ml, es = run_gpu(w, num_splits=ns, max_parts=mp, csr=(cfg == 5))
+    check_output(w, orc, out, seqs=seqs)
+    check_partials(w, orc, tmp, ml, es, num_splits=ns, seqs=seqs if seqs is not None else None)
+    assert torch.isfinite(out).all()
