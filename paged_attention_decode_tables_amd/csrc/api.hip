@@ -106,8 +106,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
         (a->k_stride_h * esz) % 16 || (a->v_stride_b * esz) % 16 || (a->v_stride_h * esz) % 16 ||
         a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
         return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
-    if (a->num_seqs > kMaxGridYZ || a->num_heads > kMaxGridYZ)
-        return fail(PA_ENOTSUP, "paged_attn_decode: num_seqs and num_heads must be <= %d", kMaxGridYZ);
+    if (parts > kMaxGridYZ || a->num_heads > kMaxGridYZ)
+        return fail(PA_ENOTSUP, "paged_attn_decode: partitions and num_heads must be <= %d", kMaxGridYZ);
     const int D = a->head_size, Dv = a->v_head_size, group = a->num_heads / a->num_kv_heads;
     if (!pa::decode_valu_supported(a->dtype, D, Dv))
         return fail(PA_ENOTSUP, "paged_attn_decode: (head_size, v_head_size) = (%d, %d) is not built", D, Dv);
@@ -171,7 +171,7 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
     if (!aligned16(a->tmp_output) || a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
         return fail(PA_ENOTSUP, "paged_attn_reduce: tmp_output rows must be 16-byte aligned");
     const int64_t pairs = (int64_t)a->num_seqs * a->num_heads;
-    if ((pairs + 3) / 4 > 0x7fffffff) return fail(PA_ENOTSUP, "paged_attn_reduce: too many (seq, head) pairs");
+    if (pairs > 0x7fffffff) return fail(PA_ENOTSUP, "paged_attn_reduce: too many (seq, head) pairs");
 
     pa::ReduceParams p{};
     p.out = a->output;

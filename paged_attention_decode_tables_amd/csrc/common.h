@@ -77,6 +77,14 @@ __device__ __forceinline__ u32x4 load16(const void* p)
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Streaming load for cache data read once per step: the nontemporal hint
+// keeps the lines from being allocated in L2 / the Infinity Cache, which
+// measurably raises the HBM read rate of the paged gather on gfx950.
+__device__ __forceinline__ u32x4 load16_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <class E> __device__ __forceinline__ void store_out(void* base, int64_t idx, float v);
 template <> __device__ __forceinline__ void store_out<F32>(void* base, int64_t idx, float v)
 {

@@ -7,10 +7,13 @@
 // heads that share one kv head at once, so each K/V byte is read from HBM
 // once per (seq, kv head) instead of G times.
 //
-// One 64-lane wavefront per (split, kv head, seq); lane = 16*g + r
-// (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
+// One workgroup per (seq, kv head, split); its waves take contiguous runs of
+// the split's chunks and merge their softmax states at the end. In a wave,
+// lane = 16*g + r (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
 // unused columns get q = 0 and are never stored). The split is walked in
-// 32-token chunks, all in registers:
+// 32-token chunks, all in registers, software-pipelined at half-chunk
+// granularity (see the main loop), with the split's block ids held in a
+// register and fetched by lane shuffles:
 //
 //   QK:  S^T[t][h] = sum_d K[t][d] Q[h][d] as two 16x16x32 products per
 //        32 d (tile 0 and tile 1 of the chunk). Lane (g, r) feeds A with 8
@@ -51,33 +54,59 @@ template <> struct MfmaOps<F16> {
     }
 };
 
-template <class E, int D, int DV>
-__global__ __launch_bounds__(64) void k_decode_mfma(DecodeParams p)
+// Waves per workgroup. The chunks of a split are shared out in contiguous
+// runs, one run per wave, and the waves' softmax states are merged through
+// LDS at the end; several short runs per split keep the tail of the grid
+// short when the splits outnumber the wave slots.
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 1
+#endif
+constexpr int kMfmaWaves = PA_MFMA_WAVES;
+// Waves per SIMD the register budget is sized for.
+#ifndef PA_MFMA_OCCUPANCY
+#define PA_MFMA_OCCUPANCY 3
+#endif
+
+// BS > 0 fixes the block size at compile time (every load of a chunk is then
+// an immediate offset from two base addresses); BS == 0 reads it at run time.
+template <class E, int D, int DV, int BS>
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCUPANCY))) void k_decode_mfma(DecodeParams p)
 {
     using T = typename E::storage;
     using Ops = MfmaOps<E>;
     using vec = typename Ops::vec;
     constexpr int KS = D / 32;   // QK k-steps
     constexpr int MT = DV / 16;  // PV value-row tiles
+    constexpr int W = kMfmaWaves;
 
-    const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    // grid (seq, kv head, split): workgroups are dealt to the XCDs round-robin
+    // by linear id, so putting the sequence first spreads the work of every
+    // split index (split 0 is never empty, high splits often are) over all
+    // XCDs instead of piling the non-empty splits onto a few of them.
+    const int s = blockIdx.x, kvh = blockIdx.y, part = blockIdx.z;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int G = p.group;
     const int h = kvh * G + r;
     const bool head_ok = r < G;
 
+    // token positions fit in 32 bits (lengths are int32)
     const int L = p.seq_lens[s];
-    const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
-    const int64_t start = (int64_t)part * len;
-    const int64_t end = (int64_t)L < start + len ? (int64_t)L : start + len;
-    const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
-    if (start >= end) {
-        if (head_ok && g == 0) {
+    const int64_t len64 = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+    const int64_t start64 = (int64_t)part * len64;
+    if (start64 >= (int64_t)L) {
+        if (wave == 0 && head_ok && g == 0) {
+            const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
             p.max_logits[mloff] = -INFINITY;
             p.exp_sums[mloff] = 0.0f;
         }
         return;
     }
+    const int start = (int)start64;
+    const int end = (int)((int64_t)L < start64 + len64 ? (int64_t)L : start64 + len64);
+    // this wave's run of 32-token chunks: [ca, cb)
+    const int nc = (end - start + 31) >> 5;
+    const int ca = wave * nc / W, cb = (wave + 1) * nc / W;
 
     // B operand of QK: lane (g, r) holds q[h][32*ks + 8g .. +8]
     vec qv[KS];
@@ -90,13 +119,60 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeParams p)
         }
     }
 
-    const int bs_shift = p.bs_shift;
-    const int64_t bs = int64_t(1) << bs_shift;
+    const int bs_shift = BS > 0 ? __builtin_ctz(BS) : p.bs_shift;
+    const int bs = 1 << bs_shift;
     const int32_t* row = page_row(p.pl, s);
     const int64_t sb = p.pl.stride_b;
     const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
     const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)kvh * p.v_sh;
-    const int64_t last_group = (end - 1) & ~int64_t(7);
+    const int last_group = (end - 1) & ~7;
+
+    // Block-table window held in a register: lane i has the id of block
+    // blk0 + wb + i of this wave's run; the next 64 ids are fetched one window
+    // ahead. Chunks never straddle a window (runs start on 32-token
+    // boundaries, so a window of 64 whole blocks ends on a chunk boundary).
+    const int wstart = start + 32 * ca;
+    const int wend = min(end, start + 32 * cb);
+    const int blk0 = wstart >> bs_shift;
+    const int nblk = ca < cb ? ((wend - 1) >> bs_shift) - blk0 + 1 : 0;
+    auto fetch_window = [&](int base) -> int32_t {
+        const int b = base + lane;
+        return b < nblk ? row[(int64_t)(blk0 + b) * sb] : 0;
+    };
+    int wb = 0;
+    int32_t win = fetch_window(0);
+    int32_t win_next = nblk > 64 ? fetch_window(64) : 0;
+
+    auto advance_window = [&](int c0) {
+        if ((c0 >> bs_shift) - blk0 >= wb + 64) {
+            wb += 64;
+            win = win_next;
+            if (nblk > wb + 64) win_next = fetch_window(wb + 64);
+        }
+    };
+    auto block_of = [&](int t) -> int64_t { return __shfl(win, (t >> bs_shift) - blk0 - wb, kWave); };
+
+    // Chunk loads. tk: this lane's 8-token key group (row r of the QK
+    // tiles), tv: its value group (column group g of the PV tile); both are
+    // clamped to the last valid group so every load stays inside a block
+    // that holds live tokens.
+    u32x4 kt[2 * KS];  // K of the chunk: tile 0 (tokens 8j..8j+3), tile 1 (+4)
+    u32x4 vt[MT];      // V of the chunk: 16 value rows per tile
+    auto issue_k = [&](int c0) {
+        const int tk = min(c0 + 8 * (r >> 2), last_group);
+        const T* kp = kc + block_of(tk) * p.k_sb + (((tk & (bs - 1)) + (r & 3)) * 8 + g * bs * 8);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kt[2 * ks] = load16_stream(kp + ks * 4 * bs * 8);
+            kt[2 * ks + 1] = load16_stream(kp + ks * 4 * bs * 8 + 32);
+        }
+    };
+    auto issue_v = [&](int c0) {
+        const int tv = min(c0 + 8 * g, last_group);
+        const T* vp = vc + block_of(tv) * p.v_sb + (r * bs + (tv & (bs - 1)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) vt[mt] = load16_stream(vp + mt * 16 * bs);
+    };
 
     float m = -INFINITY;  // running max of head r (base 2)
     float l = 0.0f;       // this lane's share of the running sum
@@ -104,33 +180,15 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeParams p)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t c0 = start; c0 < end; c0 += 32) {
-        const bool tail = end - c0 < 32;
-        // ---- addresses: K group of row r, V group of lane group g
-        int64_t tk = c0 + 8 * (r >> 2);
-        tk = tk <= last_group ? tk : last_group;
-        int64_t tv = c0 + 8 * g;
-        tv = tv <= last_group ? tv : last_group;
-        const T* kp = kc + token_block(row, sb, tk, bs_shift) * p.k_sb +
-                      ((tk & (bs - 1)) + (r & 3)) * 8 + (int64_t)g * bs * 8;
-        const T* vp = vc + token_block(row, sb, tv, bs_shift) * p.v_sb + (int64_t)r * bs + (tv & (bs - 1));
-
-        // ---- loads
-        u32x4 k0[KS], k1[KS], vv[MT];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            k0[ks] = load16(kp + (int64_t)ks * 4 * bs * 8);
-            k1[ks] = load16(kp + (int64_t)ks * 4 * bs * 8 + 32);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vv[mt] = load16(vp + (int64_t)mt * 16 * bs);
-
-        // ---- scores
+    // Scores and online-softmax update for the chunk at c0 (uses kt); returns
+    // the probabilities as the P.V operand and leaves alpha for the rescale.
+    float alpha = 1.0f;
+    auto scores = [&](int c0) -> vec {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            s0 = Ops::mma(__builtin_bit_cast(vec, k0[ks]), qv[ks], s0);
-            s1 = Ops::mma(__builtin_bit_cast(vec, k1[ks]), qv[ks], s1);
+            s0 = Ops::mma(__builtin_bit_cast(vec, kt[2 * ks]), qv[ks], s0);
+            s1 = Ops::mma(__builtin_bit_cast(vec, kt[2 * ks + 1]), qv[ks], s1);
         }
         float sc[8];
 #pragma unroll
@@ -138,20 +196,18 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeParams p)
             sc[i] = s0[i] * p.scale_log2;
             sc[4 + i] = s1[i] * p.scale_log2;
         }
-        const int64_t t0 = c0 + 8 * g;  // this lane's first token
-        if (tail) {
+        const int t0 = c0 + 8 * g;  // this lane's first token
+        if (end - c0 < 32) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) sc[j] = (t0 + j < end) ? sc[j] : -INFINITY;
         }
-
-        // ---- online softmax
         float mloc = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[j]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
         const float mn = fmaxf(m, mloc);
-        const float alpha = fast_exp2(m - mn);
+        alpha = fast_exp2(m - mn);
         m = mn;
         vec pv;
         float psum = 0.0f;
@@ -162,25 +218,87 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeParams p)
             psum += (float)e;
         }
         l = l * alpha + psum;
+        return pv;
+    };
+    // Rescale and P.V for the chunk at c0 (uses vt).
+    auto weigh = [&](int c0, vec pv) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-
-        // ---- weighted values
-        if (tail) {
+        if (end - c0 < 32) {
+            const int t0 = c0 + 8 * g;
             u32x4 keep;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
                 keep[w] = (t0 + 2 * w < end ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < end ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vv[mt] &= keep;
+            for (int mt = 0; mt < MT; ++mt) vt[mt] &= keep;
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = Ops::mma(__builtin_bit_cast(vec, vv[mt]), pv, acc[mt]);
-    }
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = Ops::mma(__builtin_bit_cast(vec, vt[mt]), pv, acc[mt]);
+    };
 
+    // Software pipeline at half-chunk granularity: once the scores of chunk
+    // i are formed its K registers receive chunk i+1's keys, and once its
+    // P.V is done its V registers receive chunk i+1's values, so one half of
+    // a chunk (8 KB) is always in flight while the other half is used. The
+    // last chunk is peeled so every wait in the loop is a fixed count; the
+    // scheduling fences keep the next loads from being hoisted above the
+    // math that frees their registers.
+    if (ca < cb) {
+        issue_k(wstart);
+        issue_v(wstart);
+        int c0 = wstart;
+        for (int i = ca; i + 1 < cb; ++i, c0 += 32) {
+            advance_window(c0 + 32);
+            vec pv = scores(c0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_k(c0 + 32);
+            __builtin_amdgcn_sched_barrier(0);
+            weigh(c0, pv);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_v(c0 + 32);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        vec pv = scores(c0);
+        weigh(c0, pv);
+    }
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
+
+    // Merge the waves' states (max, sum, accumulator of each head) in wave 0:
+    // M = max_w m_w, l = sum_w exp(m_w - M) l_w, acc = sum_w exp(m_w - M) acc_w.
+    // A wave without chunks holds m = -inf and contributes nothing.
+    if constexpr (W > 1) {
+        __shared__ f32x4 acc_lds[W > 1 ? W - 1 : 1][MT][kWave];
+        __shared__ float m_lds[W > 1 ? W - 1 : 1][16], l_lds[W > 1 ? W - 1 : 1][16];
+        if (wave > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc_lds[wave - 1][mt][lane] = acc[mt];
+            if (g == 0) {
+                m_lds[wave - 1][r] = m;
+                l_lds[wave - 1][r] = l;
+            }
+        }
+        __syncthreads();
+        if (wave > 0) return;
+        float M = m;
+#pragma unroll
+        for (int w = 0; w < W - 1; ++w) M = fmaxf(M, m_lds[w][r]);
+        const float f0 = fast_exp2(m - M);
+        l *= f0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] *= f0;
+        for (int w = 0; w < W - 1; ++w) {
+            const float f = fast_exp2(m_lds[w][r] - M);
+            l += f * l_lds[w][r];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] += f * acc_lds[w][mt][lane];
+        }
+        m = M;
+    }
+
     if (!head_ok) return;
+    const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
     if (g == 0) {
         p.max_logits[mloff] = m * kLn2;
         p.exp_sums[mloff] = l;
@@ -200,8 +318,12 @@ bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
 template <class E, int D>
 static hipError_t launch_mfma_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    dim3 grid(parts, p.num_kv_heads, num_seqs), block(kWave);
-    hipLaunchKernelGGL((k_decode_mfma<E, D, D>), grid, block, 0, st, p);
+    dim3 grid(num_seqs, p.num_kv_heads, parts), block(kWave * kMfmaWaves);
+    switch (p.bs_shift) {
+    case 4: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 16>), grid, block, 0, st, p); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 32>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 0>), grid, block, 0, st, p); break;
+    }
     return hipGetLastError();
 }
 

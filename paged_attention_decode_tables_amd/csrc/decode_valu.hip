@@ -4,7 +4,7 @@
 // block table, scores, online softmax, weighted V, store m, l and the
 // normalised split output).
 //
-// One 64-lane wavefront per (split, head, seq). The split is walked in
+// One 64-lane wavefront per (seq, head, split). The split is walked in
 // 64-token chunks:
 //   QK     lane <-> token. Each lane reads its token's key row as D/x
 //          16-byte pieces (x = 16 / element size values of one token are
@@ -21,7 +21,10 @@
 
 namespace pa {
 
-template <class E, int D, int DV, bool ROWV>
+// STREAM: every K/V byte is read by exactly one wave (group size 1), so the
+// loads carry the nontemporal hint; with grouped heads the G waves of a kv
+// head share the lines through the caches and use plain loads.
+template <class E, int D, int DV, bool ROWV, bool STREAM>
 __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
 {
     using T = typename E::storage;
@@ -30,7 +33,9 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
     __shared__ float q_lds[D];
     __shared__ float p_lds[kWave];
 
-    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    // grid (seq, head, split): sequence first so each split index's work is
+    // spread over all XCDs (workgroups are dealt to XCDs by linear id)
+    const int s = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
     const int lane = threadIdx.x;
     const int L = p.seq_lens[s];
     const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
         float dot = 0.0f;
 #pragma unroll 8
         for (int c = 0; c < D / X; ++c) {
-            const u32x4 kv = load16(kp + (int64_t)c * bs * X);
+            const u32x4 kv = STREAM ? load16_stream(kp + (int64_t)c * bs * X) : load16(kp + (int64_t)c * bs * X);
 #pragma unroll
             for (int j = 0; j < X; ++j) dot += q_lds[c * X + j] * elem16<E>(kv, j);
         }
@@ -102,7 +107,8 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
                     const bool full = (v + 1) * VT <= n;
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) {
-                        const u32x4 vv = load16(vp + (int64_t)(lane + kWave * r) * bs);
+                        const T* vr = vp + (int64_t)(lane + kWave * r) * bs;
+                        const u32x4 vv = STREAM ? load16_stream(vr) : load16(vr);
 #pragma unroll
                         for (int j = 0; j < VT; ++j) {
                             float x = elem16<E>(vv, j);
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
                 const T* vp = vc + token_block(row, sb, tj, 0) * p.v_sb + lane * DVR;
                 const float pj = p_lds[j];
                 if constexpr (DVR * E::size == 16) {
-                    const u32x4 vv = load16(vp);
+                    const u32x4 vv = STREAM ? load16_stream(vp) : load16(vp);
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) acc[r] += pj * elem16<E>(vv, r);
                 } else {
@@ -163,11 +169,15 @@ bool decode_valu_supported(int dtype, int D, int Dv)
 template <class E, int D, int DV>
 static hipError_t launch_valu_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    dim3 grid(parts, p.num_heads, num_seqs), block(kWave);
-    if (p.bs_shift == 0)
-        hipLaunchKernelGGL((k_decode_valu<E, D, DV, true>), grid, block, 0, st, p);
-    else
-        hipLaunchKernelGGL((k_decode_valu<E, D, DV, false>), grid, block, 0, st, p);
+    dim3 grid(num_seqs, p.num_heads, parts), block(kWave);
+    const bool stream = p.group == 1;
+    if (p.bs_shift == 0) {
+        if (stream) hipLaunchKernelGGL((k_decode_valu<E, D, DV, true, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_decode_valu<E, D, DV, true, false>), grid, block, 0, st, p);
+    } else {
+        if (stream) hipLaunchKernelGGL((k_decode_valu<E, D, DV, false, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_decode_valu<E, D, DV, false, false>), grid, block, 0, st, p);
+    }
     return hipGetLastError();
 }
 

@@ -2,53 +2,59 @@
 // outputs (paged_attention_v2_triton.py, _paged_attn_v2_reduce_kernel:
 // global max, rescale by exp(m_p - M) * l_p, normalise, weighted sum).
 //
-// One wavefront per (seq, head); four per workgroup. Lane l owns the VPL
-// consecutive output values [l*VPL, (l+1)*VPL), so each split row of
-// tmp_output is read as one contiguous 4*Dv-byte run. The split weights are
-// computed 64 at a time (lane <-> split) and broadcast with readlane.
+// One 256-thread workgroup per (seq, head). The Dv-wide rows are read as
+// float4 columns: C = Dv/4 threads cover a row and the 256/C thread groups
+// take every (256/C)-th split, so all of a (seq, head)'s split rows are
+// requested at once (up to 8 loads per thread in flight). The split weights
+// w_p = exp(m_p - M) * l_p are formed once per split in LDS, the column sums
+// of the groups are merged through LDS, and the result is scaled by
+// 1 / sum_p w_p. Splits past the sequence's count are never read.
 #include "kernels.h"
 
 namespace pa {
 
-template <int VPL>
-struct RowVec {
-    float v[VPL];
-};
+constexpr int kRedThreads = 256;
+constexpr int kRedChunk = 1024;  // splits whose weights sit in LDS at once
 
-template <int VPL>
-__device__ __forceinline__ RowVec<VPL> load_row(const float* p)
+__device__ __forceinline__ float block_max(float v, float* red)
 {
-    RowVec<VPL> r;
-    if constexpr (VPL % 4 == 0) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
 #pragma unroll
-        for (int i = 0; i < VPL; i += 4) {
-            f32x4 t = *reinterpret_cast<const f32x4*>(p + i);
-            r.v[i] = t[0];
-            r.v[i + 1] = t[1];
-            r.v[i + 2] = t[2];
-            r.v[i + 3] = t[3];
-        }
-    } else if constexpr (VPL == 2) {
-        float2 t = *reinterpret_cast<const float2*>(p);
-        r.v[0] = t.x;
-        r.v[1] = t.y;
-    } else {
+    for (int i = 1; i < kRedThreads / kWave; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) r.v[i] = p[i];
-    }
+    for (int i = 1; i < kRedThreads / kWave; ++i) r += red[i];
     return r;
 }
 
 template <class OutE, int DV>
-__global__ __launch_bounds__(256) void k_reduce(ReduceParams p)
+__global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
 {
-    constexpr int VPL = DV / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= (int64_t)p.num_seqs * p.num_heads) return;
-    const int s = (int)(pair / p.num_heads);
-    const int h = (int)(pair % p.num_heads);
-    const int64_t obase = (int64_t)s * p.out_ss + (int64_t)h * p.out_sh + lane * VPL;
+    constexpr int C = DV / 4;                 // threads per row (float4 columns)
+    constexpr int NG = kRedThreads / C;       // split groups
+    __shared__ float w_lds[kRedChunk];
+    __shared__ float red[kRedThreads / kWave];
+    __shared__ f32x4 part_lds[NG > 1 ? (NG - 1) * C : 1];
+
+    const int tid = threadIdx.x;
+    const int col = tid % C, grp = tid / C;
+    const int s = blockIdx.x / p.num_heads, h = blockIdx.x % p.num_heads;
+    const int64_t obase = (int64_t)s * p.out_ss + (int64_t)h * p.out_sh + 4 * col;
 
     const int L = p.seq_lens[s];
     int64_t n = 0;
@@ -58,52 +64,55 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceParams p)
         n = n < p.max_num_parts ? n : p.max_num_parts;
     }
     if (n == 0) {
+        if (grp == 0)
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) store_out<OutE>(p.out, obase + i, 0.0f);
+            for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, 0.0f);
         return;
     }
     const float* ml = p.max_logits + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh;
     const float* es = p.exp_sums + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh;
-    const float* tmp = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + lane * VPL;
+    const float* tmp = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
 
-    // global max over the nonempty splits
     float M = -INFINITY;
-    for (int64_t q = lane; q < n; q += kWave) M = fmaxf(M, ml[q]);
-    M = wave_max(M);
+    for (int64_t q = tid; q < n; q += kRedThreads) M = fmaxf(M, ml[q]);
+    M = block_max(M, red);
 
-    float acc[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) acc[i] = 0.0f;
-    float wsum = 0.0f;
-    for (int64_t q0 = 0; q0 < n; q0 += kWave) {
-        const int64_t q = q0 + lane;
-        float w = 0.0f;
-        if (q < n) w = fast_exp2((ml[q] - M) * kLog2e) * es[q];
-        wsum += w;
-        const int cnt = (int)((n - q0) < kWave ? (n - q0) : kWave);
-        const float* row = tmp + q0 * p.tmp_sp;
-        int j = 0;
-        for (; j + 4 <= cnt; j += 4) {
-            RowVec<VPL> r0 = load_row<VPL>(row + (int64_t)(j + 0) * p.tmp_sp);
-            RowVec<VPL> r1 = load_row<VPL>(row + (int64_t)(j + 1) * p.tmp_sp);
-            RowVec<VPL> r2 = load_row<VPL>(row + (int64_t)(j + 2) * p.tmp_sp);
-            RowVec<VPL> r3 = load_row<VPL>(row + (int64_t)(j + 3) * p.tmp_sp);
-            const float w0 = __shfl(w, j + 0, kWave), w1 = __shfl(w, j + 1, kWave);
-            const float w2 = __shfl(w, j + 2, kWave), w3 = __shfl(w, j + 3, kWave);
-#pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                acc[i] += w0 * r0.v[i] + w1 * r1.v[i] + w2 * r2.v[i] + w3 * r3.v[i];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wpart = 0.0f;
+    for (int64_t q0 = 0; q0 < n; q0 += kRedChunk) {
+        const int cnt = (int)((n - q0) < kRedChunk ? (n - q0) : kRedChunk);
+        __syncthreads();
+        for (int j = tid; j < cnt; j += kRedThreads) {
+            const float w = fast_exp2((ml[q0 + j] - M) * kLog2e) * es[q0 + j];
+            w_lds[j] = w;
+            wpart += w;
         }
-        for (; j < cnt; ++j) {
-            RowVec<VPL> r0 = load_row<VPL>(row + (int64_t)j * p.tmp_sp);
-            const float w0 = __shfl(w, j, kWave);
+        __syncthreads();
+        const float* rows = tmp + q0 * p.tmp_sp;
+        int j = grp;
+        for (; j + 3 * NG < cnt; j += 4 * NG) {
+            const f32x4 r0 = *reinterpret_cast<const f32x4*>(rows + (int64_t)j * p.tmp_sp);
+            const f32x4 r1 = *reinterpret_cast<const f32x4*>(rows + (int64_t)(j + NG) * p.tmp_sp);
+            const f32x4 r2 = *reinterpret_cast<const f32x4*>(rows + (int64_t)(j + 2 * NG) * p.tmp_sp);
+            const f32x4 r3 = *reinterpret_cast<const f32x4*>(rows + (int64_t)(j + 3 * NG) * p.tmp_sp);
+            acc += w_lds[j] * r0 + w_lds[j + NG] * r1 + w_lds[j + 2 * NG] * r2 + w_lds[j + 3 * NG] * r3;
+        }
+        for (; j < cnt; j += NG) acc += w_lds[j] * *reinterpret_cast<const f32x4*>(rows + (int64_t)j * p.tmp_sp);
+    }
+    const float inv = 1.0f / block_sum(wpart, red);
+
+    if constexpr (NG > 1) {
+        if (grp > 0) part_lds[(grp - 1) * C + col] = acc;
+        __syncthreads();
+        if (grp == 0) {
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) acc[i] += w0 * r0.v[i];
+            for (int g2 = 1; g2 < NG; ++g2) acc += part_lds[(g2 - 1) * C + col];
         }
     }
-    const float inv = 1.0f / wave_sum(wsum);
+    if (grp == 0) {
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) store_out<OutE>(p.out, obase + i, acc[i] * inv);
+        for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, acc[i] * inv);
+    }
 }
 
 bool reduce_supported(int Dv) { return Dv == 64 || Dv == 128 || Dv == 256 || Dv == 512; }
@@ -112,7 +121,7 @@ template <class OutE>
 static hipError_t launch_reduce_t(const ReduceParams& p, int Dv, hipStream_t st)
 {
     const int64_t pairs = (int64_t)p.num_seqs * p.num_heads;
-    dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
+    dim3 grid((unsigned)pairs), block(kRedThreads);
     switch (Dv) {
     case 64: hipLaunchKernelGGL((k_reduce<OutE, 64>), grid, block, 0, st, p); break;
     case 128: hipLaunchKernelGGL((k_reduce<OutE, 128>), grid, block, 0, st, p); break;
