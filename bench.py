@@ -148,6 +148,9 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = long-context GQA)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a kernel of known "
+                         "traffic for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -158,6 +161,16 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: calibration copy of {n} bytes done")
+        del src, dst
 
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config)
