@@ -11,9 +11,9 @@
 // the split's chunks and merge their softmax states at the end. In a wave,
 // lane = 16*g + r (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
 // unused columns get q = 0 and are never stored). The split is walked in
-// 32-token chunks, all in registers, software-pipelined at half-chunk
-// granularity (see the main loop), with the split's block ids held in a
-// register and fetched by lane shuffles:
+// 32-token chunks, all in registers, double-buffered (the next chunk's 16 KB
+// of K/V loads are in flight while the current chunk is used), with the
+// split's block ids held in a register and fetched by lane shuffles:
 //
 //   QK:  S^T[t][h] = sum_d K[t][d] Q[h][d] as two 16x16x32 products per
 //        32 d (tile 0 and tile 1 of the chunk). Lane (g, r) feeds A with 8
@@ -62,9 +62,14 @@ template <> struct MfmaOps<F16> {
 #define PA_MFMA_WAVES 1
 #endif
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
+// Pipeline depth: 1 = half-chunk pipeline (one 8 KB half in flight while
+// the other is used), 2 = double buffering (the next 16 KB chunk in flight).
+#ifndef PA_MFMA_PIPE
+#define PA_MFMA_PIPE 2
+#endif
 // Waves per SIMD the register budget is sized for.
 #ifndef PA_MFMA_OCCUPANCY
-#define PA_MFMA_OCCUPANCY 3
+#define PA_MFMA_OCCUPANCY (PA_MFMA_PIPE == 1 ? 3 : 2)
 #endif
 
 // BS > 0 fixes the block size at compile time (every load of a chunk is then
@@ -156,22 +161,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     // tiles), tv: its value group (column group g of the PV tile); both are
     // clamped to the last valid group so every load stays inside a block
     // that holds live tokens.
-    u32x4 kt[2 * KS];  // K of the chunk: tile 0 (tokens 8j..8j+3), tile 1 (+4)
-    u32x4 vt[MT];      // V of the chunk: 16 value rows per tile
-    auto issue_k = [&](int c0) {
+    struct Tile {
+        u32x4 k[2 * KS];  // K of the chunk: tile 0 (tokens 8j..8j+3), tile 1 (+4)
+        u32x4 v[MT];      // V of the chunk: 16 value rows per tile
+    };
+    auto issue_k = [&](Tile& t, int c0) {
         const int tk = min(c0 + 8 * (r >> 2), last_group);
         const T* kp = kc + block_of(tk) * p.k_sb + (((tk & (bs - 1)) + (r & 3)) * 8 + g * bs * 8);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            kt[2 * ks] = load16_stream(kp + ks * 4 * bs * 8);
-            kt[2 * ks + 1] = load16_stream(kp + ks * 4 * bs * 8 + 32);
+            t.k[2 * ks] = load16_stream(kp + ks * 4 * bs * 8);
+            t.k[2 * ks + 1] = load16_stream(kp + ks * 4 * bs * 8 + 32);
         }
     };
-    auto issue_v = [&](int c0) {
+    auto issue_v = [&](Tile& t, int c0) {
         const int tv = min(c0 + 8 * g, last_group);
         const T* vp = vc + block_of(tv) * p.v_sb + (r * bs + (tv & (bs - 1)));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vt[mt] = load16_stream(vp + mt * 16 * bs);
+        for (int mt = 0; mt < MT; ++mt) t.v[mt] = load16_stream(vp + mt * 16 * bs);
     };
 
     float m = -INFINITY;  // running max of head r (base 2)
@@ -183,12 +190,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     // Scores and online-softmax update for the chunk at c0 (uses kt); returns
     // the probabilities as the P.V operand and leaves alpha for the rescale.
     float alpha = 1.0f;
-    auto scores = [&](int c0) -> vec {
+    auto scores = [&](Tile& t, int c0) -> vec {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            s0 = Ops::mma(__builtin_bit_cast(vec, kt[2 * ks]), qv[ks], s0);
-            s1 = Ops::mma(__builtin_bit_cast(vec, kt[2 * ks + 1]), qv[ks], s1);
+            s0 = Ops::mma(__builtin_bit_cast(vec, t.k[2 * ks]), qv[ks], s0);
+            s1 = Ops::mma(__builtin_bit_cast(vec, t.k[2 * ks + 1]), qv[ks], s1);
         }
         float sc[8];
 #pragma unroll
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         return pv;
     };
     // Rescale and P.V for the chunk at c0 (uses vt).
-    auto weigh = [&](int c0, vec pv) {
+    auto weigh = [&](Tile& t, int c0, vec pv) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
         if (end - c0 < 32) {
@@ -231,12 +238,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             for (int w = 0; w < 4; ++w)
                 keep[w] = (t0 + 2 * w < end ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < end ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) vt[mt] &= keep;
+            for (int mt = 0; mt < MT; ++mt) t.v[mt] &= keep;
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = Ops::mma(__builtin_bit_cast(vec, vt[mt]), pv, acc[mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = Ops::mma(__builtin_bit_cast(vec, t.v[mt]), pv, acc[mt]);
     };
 
+#if PA_MFMA_PIPE == 1
     // Software pipeline at half-chunk granularity: once the scores of chunk
     // i are formed its K registers receive chunk i+1's keys, and once its
     // P.V is done its V registers receive chunk i+1's values, so one half of
@@ -245,23 +253,61 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     // scheduling fences keep the next loads from being hoisted above the
     // math that frees their registers.
     if (ca < cb) {
-        issue_k(wstart);
-        issue_v(wstart);
+        Tile t;
+        issue_k(t, wstart);
+        issue_v(t, wstart);
         int c0 = wstart;
         for (int i = ca; i + 1 < cb; ++i, c0 += 32) {
             advance_window(c0 + 32);
-            vec pv = scores(c0);
+            vec pv = scores(t, c0);
             __builtin_amdgcn_sched_barrier(0);
-            issue_k(c0 + 32);
+            issue_k(t, c0 + 32);
             __builtin_amdgcn_sched_barrier(0);
-            weigh(c0, pv);
+            weigh(t, c0, pv);
             __builtin_amdgcn_sched_barrier(0);
-            issue_v(c0 + 32);
+            issue_v(t, c0 + 32);
             __builtin_amdgcn_sched_barrier(0);
         }
-        vec pv = scores(c0);
-        weigh(c0, pv);
+        vec pv = scores(t, c0);
+        weigh(t, c0, pv);
     }
+#else
+    // Double buffering: the whole next chunk (16 KB) is requested before the
+    // current one is used. The loop is unrolled by two so the buffers have
+    // fixed registers and every wait is for exactly one tile.
+    if (ca < cb) {
+        Tile A, B;
+        issue_k(A, wstart);
+        issue_v(A, wstart);
+        int c0 = wstart;
+        int i = ca;
+        for (; i + 2 < cb; i += 2, c0 += 64) {
+            advance_window(c0 + 32);
+            issue_k(B, c0 + 32);
+            issue_v(B, c0 + 32);
+            __builtin_amdgcn_sched_barrier(0);
+            weigh(A, c0, scores(A, c0));
+            __builtin_amdgcn_sched_barrier(0);
+            advance_window(c0 + 64);
+            issue_k(A, c0 + 64);
+            issue_v(A, c0 + 64);
+            __builtin_amdgcn_sched_barrier(0);
+            weigh(B, c0 + 32, scores(B, c0 + 32));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i + 1 < cb) {
+            advance_window(c0 + 32);
+            issue_k(B, c0 + 32);
+            issue_v(B, c0 + 32);
+            __builtin_amdgcn_sched_barrier(0);
+            weigh(A, c0, scores(A, c0));
+            __builtin_amdgcn_sched_barrier(0);
+            weigh(B, c0 + 32, scores(B, c0 + 32));
+        } else {
+            weigh(A, c0, scores(A, c0));
+        }
+    }
+#endif
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
 
