@@ -3,53 +3,27 @@
 // global max, rescale by exp(m_p - M) * l_p, normalise, weighted sum).
 //
 // One 256-thread workgroup per (seq, head). The Dv-wide rows are read as
-// float4 columns: C = Dv/4 threads cover a row and the 256/C thread groups
-// take every (256/C)-th split, so all of a (seq, head)'s split rows are
-// requested at once (up to 8 loads per thread in flight). The split weights
-// w_p = exp(m_p - M) * l_p are formed once per split in LDS, the column sums
-// of the groups are merged through LDS, and the result is scaled by
-// 1 / sum_p w_p. Splits past the sequence's count are never read.
+// float4 columns: C = Dv/4 threads cover a row and the NG = 256/C thread
+// groups take every NG-th split. Each thread folds its splits into a local
+// (max, sum, row) state, R splits at a time with all their loads in flight,
+// and the groups' states are merged once through LDS with the same rule
+// (M = max m_g, weights exp(m_g - M)), so the whole merge costs one memory
+// round trip and one barrier. Splits past the sequence's count are never
+// read.
 #include "kernels.h"
 
 namespace pa {
 
 constexpr int kRedThreads = 256;
-constexpr int kRedChunk = 1024;  // splits whose weights sit in LDS at once
-
-__device__ __forceinline__ float block_max(float v, float* red)
-{
-    v = wave_max(v);
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < kRedThreads / kWave; ++i) r = fmaxf(r, red[i]);
-    return r;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red)
-{
-    v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < kRedThreads / kWave; ++i) r += red[i];
-    return r;
-}
+constexpr int kRedBatch = 8;  // splits per thread per round of loads
 
 template <class OutE, int DV>
 __global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
 {
-    constexpr int C = DV / 4;                 // threads per row (float4 columns)
-    constexpr int NG = kRedThreads / C;       // split groups
-    __shared__ float w_lds[kRedChunk];
-    __shared__ float red[kRedThreads / kWave];
-    __shared__ f32x4 part_lds[NG > 1 ? (NG - 1) * C : 1];
+    constexpr int C = DV / 4;             // threads per row (float4 columns)
+    constexpr int NG = kRedThreads / C;   // split groups
+    __shared__ f32x4 acc_lds[NG][C];
+    __shared__ float m_lds[NG], w_lds[NG];
 
     const int tid = threadIdx.x;
     const int col = tid % C, grp = tid / C;
@@ -73,46 +47,62 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
     const float* es = p.exp_sums + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh;
     const float* tmp = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
 
-    float M = -INFINITY;
-    for (int64_t q = tid; q < n; q += kRedThreads) M = fmaxf(M, ml[q]);
-    M = block_max(M, red);
-
+    // this thread's splits grp, grp + NG, ...: local max M (base e), sum W
+    // of exp(m_p - M) l_p, and acc = sum of exp(m_p - M) l_p tmp_p
+    float M = -INFINITY, W = 0.0f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wpart = 0.0f;
-    for (int64_t q0 = 0; q0 < n; q0 += kRedChunk) {
-        const int cnt = (int)((n - q0) < kRedChunk ? (n - q0) : kRedChunk);
-        __syncthreads();
-        for (int j = tid; j < cnt; j += kRedThreads) {
-            const float w = fast_exp2((ml[q0 + j] - M) * kLog2e) * es[q0 + j];
-            w_lds[j] = w;
-            wpart += w;
+    for (int64_t q0 = grp; q0 < n; q0 += (int64_t)NG * kRedBatch) {
+        f32x4 rows[kRedBatch];
+        float mv[kRedBatch], lv[kRedBatch];
+#pragma unroll
+        for (int r = 0; r < kRedBatch; ++r) {
+            const int64_t q = q0 + (int64_t)r * NG;
+            if (q < n) {
+                rows[r] = *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp);
+                mv[r] = ml[q];
+                lv[r] = es[q];
+            } else {
+                rows[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                mv[r] = -INFINITY;
+                lv[r] = 0.0f;
+            }
         }
-        __syncthreads();
-        const float* rows = tmp + q0 * p.tmp_sp;
-        int j = grp;
-        for (; j + 3 * NG < cnt; j += 4 * NG) {
-            const f32x4 r0 = *reinterpret_cast<const f32x4*>(rows + (int64_t)j * p.tmp_sp);
-            const f32x4 r1 = *reinterpret_cast<const f32x4*>(rows + (int64_t)(j + NG) * p.tmp_sp);
-            const f32x4 r2 = *reinterpret_cast<const f32x4*>(rows + (int64_t)(j + 2 * NG) * p.tmp_sp);
-            const f32x4 r3 = *reinterpret_cast<const f32x4*>(rows + (int64_t)(j + 3 * NG) * p.tmp_sp);
-            acc += w_lds[j] * r0 + w_lds[j + NG] * r1 + w_lds[j + 2 * NG] * r2 + w_lds[j + 3 * NG] * r3;
+        float mb = M;
+#pragma unroll
+        for (int r = 0; r < kRedBatch; ++r) mb = fmaxf(mb, mv[r]);
+        const float f = fast_exp2((M - mb) * kLog2e);
+        acc *= f;
+        W *= f;
+#pragma unroll
+        for (int r = 0; r < kRedBatch; ++r) {
+            const float w = fast_exp2((mv[r] - mb) * kLog2e) * lv[r];
+            acc += w * rows[r];
+            W += w;
         }
-        for (; j < cnt; j += NG) acc += w_lds[j] * *reinterpret_cast<const f32x4*>(rows + (int64_t)j * p.tmp_sp);
+        M = mb;
     }
-    const float inv = 1.0f / block_sum(wpart, red);
 
-    if constexpr (NG > 1) {
-        if (grp > 0) part_lds[(grp - 1) * C + col] = acc;
-        __syncthreads();
-        if (grp == 0) {
-#pragma unroll
-            for (int g2 = 1; g2 < NG; ++g2) acc += part_lds[(g2 - 1) * C + col];
-        }
+    acc_lds[grp][col] = acc;
+    if (col == 0) {
+        m_lds[grp] = M;
+        w_lds[grp] = W;
     }
-    if (grp == 0) {
+    __syncthreads();
+    if (grp != 0) return;
+    float Mt = m_lds[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, acc[i] * inv);
+    for (int g = 1; g < NG; ++g) Mt = fmaxf(Mt, m_lds[g]);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    float Wt = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const float f = fast_exp2((m_lds[g] - Mt) * kLog2e);  // empty groups: exp2(-inf) = 0
+        a += f * acc_lds[g][col];
+        Wt += f * w_lds[g];
     }
+    const float inv = 1.0f / Wt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, a[i] * inv);
 }
 
 bool reduce_supported(int Dv) { return Dv == 64 || Dv == 128 || Dv == 256 || Dv == 512; }
