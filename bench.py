@@ -35,12 +35,25 @@ from paged_attention_decode_tables_amd import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "paged-decode KV read GB/s (% of MI355X HBM peak) + µs/decode step"
-KERNEL_SOURCES = {"mfma": "decode_mfma.hip", "valu": "decode_valu.hip"}
+KERNEL_SOURCES = {"mfma": "decode_mfma.hip", "valu": "decode_valu.hip", "mla": "decode_mla.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_kind(w) -> str:
+    """Which phase-1 kernel the library dispatches for workload `w` (the
+    selection rule of paged_attn_decode with the automatic kernel hint)."""
+    group = w.num_heads // w.num_kv_heads
+    low = w.dtype in (torch.float16, torch.bfloat16)
+    if low and w.head_size == 576 and w.v_head_size == 512 and w.block_size == 1 \
+            and group in (64, 128) and w.latent is not None:
+        return "mla"
+    if low and group > 1 and w.block_size >= 8 and w.head_size in (64, 128):
+        return "mfma"
+    return "valu"
 
 
 def kernel_source_hash(kind: str) -> str:
@@ -175,8 +188,7 @@ def main():
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config)
     step = Step(w)
-    kind = "mfma" if (w.num_heads // w.num_kv_heads) > 1 and w.dtype != torch.float32 \
-        and w.block_size >= 8 and w.head_size in (64, 128) else "valu"
+    kind = kernel_kind(w)
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup}")

@@ -142,11 +142,17 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     p.max_num_parts = a->max_num_parts;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // latent rows: the value cache is the leading v_head_size columns of the key rows
+    const bool mla_ok = pa::decode_mla_supported(a->dtype, D, Dv, group, a->block_size) &&
+                        a->value_cache == a->key_cache && a->v_stride_b == a->k_stride_b &&
+                        a->v_stride_h == a->k_stride_h;
     const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size);
-    if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok)
-        return fail(PA_ENOTSUP, "paged_attn_decode: the MFMA kernel does not serve this problem");
-    const bool use_mfma = a->kernel_hint == PA_KERNEL_VALU ? false : mfma_ok;
-    if (use_mfma)
+    if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok && !mla_ok)
+        return fail(PA_ENOTSUP, "paged_attn_decode: no matrix-core kernel serves this problem");
+    if (a->kernel_hint != PA_KERNEL_VALU && mla_ok)
+        return launched(pa::launch_decode_mla(p, a->dtype, a->num_seqs, (int)parts, st),
+                        "paged_attn_decode (mla)");
+    if (a->kernel_hint != PA_KERNEL_VALU && mfma_ok)
         return launched(pa::launch_decode_mfma(p, a->dtype, D, Dv, a->num_seqs, (int)parts, st),
                         "paged_attn_decode (mfma)");
     return launched(pa::launch_decode_valu(p, a->dtype, D, Dv, a->num_seqs, (int)parts, st),

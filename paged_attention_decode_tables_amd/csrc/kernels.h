@@ -55,6 +55,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int D, int Dv, i
                               int parts, hipStream_t st);
 bool decode_valu_supported(int dtype, int D, int Dv);
 bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size);
+hipError_t launch_decode_mla(const DecodeParams& p, int dtype, int num_seqs, int parts, hipStream_t st);
+bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size);
 
 hipError_t launch_reduce(const ReduceParams& p, int out_dtype, int Dv, hipStream_t st);
 bool reduce_supported(int Dv);

@@ -246,6 +246,41 @@ def test_decode_num_splits(orc):
 
 
 # ---------------------------------------------------------------------------
+# MLA-style latent rows (page size 1, V = leading columns of K)
+# ---------------------------------------------------------------------------
+MLA_CASES = [
+    # name, heads, lens, partition
+    ("g128_ragged", 128, [1, 15, 16, 17, 100, 513, 1030], 512),
+    ("g64_p64", 64, [64, 65, 300, 7], 64),
+    ("g128_long", 128, [2500, 4097], 1024),
+]
+
+
+@pytest.mark.parametrize("case", MLA_CASES, ids=[c[0] for c in MLA_CASES])
+def test_decode_mla(orc, case):
+    name, H, lens, P = case
+    say(f"decode mla {name}")
+    w = workloads.mla_custom(seed=zlib.crc32(name.encode()) % 10007, seq_lens=lens, num_heads=H,
+                             poison=True)
+    for kernel in ("auto", "valu"):
+        out, tmp, ml, es = run_gpu(w, partition_size=P, kernel=kernel, csr=True)
+        check_partials(w, orc, tmp, ml, es, partition_size=P)
+        check_output(w, orc, out)
+
+
+def test_decode_mla_num_splits(orc):
+    say("decode mla num_splits")
+    w = workloads.mla_custom(seed=77, seq_lens=[3000, 129, 1, 900], num_heads=128, poison=True)
+    g = w.to(DEV)
+    ns = torch.empty(w.num_seqs, dtype=torch.int32, device=DEV)
+    pad.num_kv_splits(ns, g.seq_lens, 1, 128, 1, 8, 256)
+    nsc = ns.cpu().numpy()
+    out, tmp, ml, es = run_gpu(w, num_splits=nsc, max_parts=8, csr=True)
+    check_partials(w, orc, tmp, ml, es, num_splits=nsc)
+    check_output(w, orc, out)
+
+
+# ---------------------------------------------------------------------------
 # invariants on the GPU
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("kernel", ["auto", "valu"])
