@@ -78,6 +78,9 @@ class Oracle:
         L.orc_attention.argtypes = [_F64P] + common
         L.orc_partials.argtypes = [_F64P, _F64P, _F64P] + common + [_I32P, _I32, _I32]
         L.orc_reduce.argtypes = [_F64P, _F64P, _F64P, _F64P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32]
+        L.orc_decode_metadata.argtypes = [_I32P, _I64, _I32P, _I64, _I32P, _I64, _I64,
+                                          _I32P, _I64, _I64, _I64P, _I64, _I32P, _I64, _I64,
+                                          _I64P, _I64, _I32P, _I64, _I32, _I32, _I32, _I64]
         self.mutant = L.orc_mutant_id()
 
     # -- integer helpers ----------------------------------------------------
@@ -125,6 +128,40 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"orc_num_kv_splits: invalid arguments (rc={rc})")
         return out
+
+    def decode_metadata(self, seq_lens, req_to_token, req_pool_indices, max_seq_pages,
+                        page_size, seq_len_delta=0, full_to_swa=None):
+        """Decode metadata (sglang metadata.py, normal_decode_set_metadata):
+        returns (cache_seqlens [B] int32, cu_seqlens_k [B+1] int32,
+        page_table [B, max_seq_pages] int32, swa_page_table or None). Inputs
+        may be strided numpy views; seq_lens and req_pool_indices are int64,
+        req_to_token and full_to_swa int32."""
+        seq_lens = np.asarray(seq_lens)
+        assert seq_lens.dtype == np.int64 and seq_lens.ndim == 1
+        B = seq_lens.shape[0]
+        rt = np.asarray(req_to_token)
+        assert rt.dtype == np.int32 and rt.ndim == 2
+        rpi = np.asarray(req_pool_indices)
+        assert rpi.dtype == np.int64 and rpi.shape == (B,)
+        cs = np.zeros(B, dtype=np.int32)
+        cu = np.zeros(B + 1, dtype=np.int32)
+        pt = np.full((B, max_seq_pages), -7, dtype=np.int32)
+        swa = None
+        f2s_stride = 0
+        if full_to_swa is not None:
+            full_to_swa = np.asarray(full_to_swa)
+            assert full_to_swa.dtype == np.int32 and full_to_swa.ndim == 1
+            f2s_stride = _estrides(full_to_swa)[0]
+            swa = np.full((B, max_seq_pages), -7, dtype=np.int32)
+        rc = self.lib.orc_decode_metadata(
+            _ptr(cs, _I32P), 1, _ptr(cu, _I32P), 1, _ptr(pt, _I32P), max(max_seq_pages, 1), 1,
+            _ptr(swa, _I32P), max(max_seq_pages, 1), 1,
+            _ptr(seq_lens, _I64P), _estrides(seq_lens)[0],
+            _ptr(rt, _I32P), *_estrides(rt), _ptr(rpi, _I64P), _estrides(rpi)[0],
+            _ptr(full_to_swa, _I32P), f2s_stride, B, max_seq_pages, page_size, seq_len_delta)
+        if rc != 0:
+            raise ValueError(f"orc_decode_metadata: invalid arguments (rc={rc})")
+        return cs, cu, pt, swa
 
     # -- attention ----------------------------------------------------------
     def _problem(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr):

@@ -20,7 +20,9 @@
  *            _build_decode": _copy_page_indices_kernel and the review's
  *            stride-robust version of it.
  *   [SGMETA] sglang kernels/ops/attention/metadata.py:
- *            get_num_kv_splits_triton.
+ *            get_num_kv_splits_triton, and normal_decode_set_metadata with
+ *            its two fused metadata kernels (the docstring lists the five
+ *            steps; the kernels fix the index arithmetic).
  *
  * Precision: attention is accumulated in double. The split heuristic follows
  * the fp32 arithmetic its page prescribes (tl.float32 cast, fp32 log2 and
@@ -42,6 +44,22 @@
  *       length is P ([PAv2]: part_start = part_idx * PARTITION_SIZE).
  *   R5  the heuristic treats a length <= 0 as 1 (its page would divide by a
  *       zero minimum length).
+ *   R6  decode metadata: seq_lens and req_pool_indices are int64 (the
+ *       docstring casts seq_lens from int64; the pool indices are taken to
+ *       be the same index type); req_to_token, the SWA map and every output
+ *       are int32.
+ *   R7  int32 results wrap in two's complement: cache_seqlens is the low 32
+ *       bits of seq_len + delta and the prefix sum runs in int32.
+ *   R8  the page table is gathered for every column below max_seq_pages of
+ *       every row, whatever that row's length (the kernels mask on
+ *       max_seq_pages only).
+ *   R9  page = slot floor-divided by the page size (the docstring's floor
+ *       division; the kernels' arithmetic right shift by log2(page size) is
+ *       the same thing for a power-of-two size, negative slots included).
+ *   R10 with an empty batch, cu_seqlens_k[0] = 0 is still written (the
+ *       prefix sum of nothing).
+ *   R11 the SWA table is built only when both it and the full-to-SWA map are
+ *       given; it maps the raw slot (before the division) and then divides.
  */
 #include <math.h>
 #include <stdint.h>
@@ -464,6 +482,92 @@ int orc_reduce(double* out, const double* tmp, const double* max_logits, const d
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Decode metadata, [SGMETA] normal_decode_set_metadata, its docstring's steps
+ * in order:
+ *   1. cache_seqlens[b] = int32(seq_lens[b] + delta)
+ *   2. cu_seqlens_k = exclusive prefix sum of cache_seqlens, total at [B]
+ *   3. slot = req_to_token[req_pool_indices[b], col * page_size] for
+ *      0 <= col < max_seq_pages (the 2-D gather; every page_size-th token
+ *      slot of the request's row is the first slot of one page)
+ *   4. page_table[b, col] = floor(slot / page_size)
+ *   5. optional: swa_page_table[b, col] = floor(full_to_swa[slot] / page_size)
+ * All arrays are addressed through element strides. page_size must be a
+ * power of two (the page asserts it).
+ * ------------------------------------------------------------------------ */
+static int64_t floor_div64(int64_t a, int64_t b)
+{
+    int64_t q = a / b;
+    return (a % b != 0 && ((a < 0) != (b < 0))) ? q - 1 : q;
+}
+
+int orc_decode_metadata(int32_t* cache_seqlens, int64_t cs_stride,
+                        int32_t* cu_seqlens_k, int64_t cu_stride,
+                        int32_t* page_table, int64_t pt_s0, int64_t pt_s1,
+                        int32_t* swa_page_table, int64_t swa_s0, int64_t swa_s1,
+                        const int64_t* seq_lens, int64_t sl_stride,
+                        const int32_t* req_to_token, int64_t rt_s0, int64_t rt_s1,
+                        const int64_t* req_pool_indices, int64_t rpi_stride,
+                        const int32_t* full_to_swa, int64_t f2s_stride,
+                        int32_t batch, int32_t max_seq_pages, int32_t page_size,
+                        int64_t seq_len_delta)
+{
+    if (batch < 0 || max_seq_pages < 0 || page_size <= 0 || (page_size & (page_size - 1)))
+        return ORC_EINVAL;
+    if (!cu_seqlens_k || (batch > 0 && (!cache_seqlens || !seq_lens))) return ORC_EINVAL;
+    if (batch > 0 && max_seq_pages > 0 && (!page_table || !req_to_token || !req_pool_indices))
+        return ORC_EINVAL;
+    const int use_swa = swa_page_table != NULL && full_to_swa != NULL;
+
+    /* steps 1 and 2 (R7: int32 wrap, done through uint32) */
+    uint32_t total = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+#if ORACLE_MUTANT == 12
+        uint32_t v = (uint32_t)(uint64_t)seq_lens[(int64_t)b * sl_stride]; /* planted: delta dropped */
+#else
+        uint32_t v = (uint32_t)(uint64_t)(seq_lens[(int64_t)b * sl_stride] + seq_len_delta);
+#endif
+        cache_seqlens[(int64_t)b * cs_stride] = (int32_t)v;
+#if ORACLE_MUTANT == 11
+        total += v; /* planted: inclusive prefix sum */
+        cu_seqlens_k[(int64_t)b * cu_stride] = (int32_t)total;
+#else
+        cu_seqlens_k[(int64_t)b * cu_stride] = (int32_t)total;
+        total += v;
+#endif
+    }
+    cu_seqlens_k[(int64_t)batch * cu_stride] = (int32_t)total;
+
+    /* steps 3 to 5 */
+    for (int32_t b = 0; b < batch; ++b) {
+#if ORACLE_MUTANT == 15
+        int64_t row = b; /* planted: pool index ignored */
+#else
+        int64_t row = req_pool_indices[(int64_t)b * rpi_stride];
+#endif
+        for (int32_t col = 0; col < max_seq_pages; ++col) {
+#if ORACLE_MUTANT == 13
+            int64_t tok = col; /* planted: column not scaled to a token position */
+#else
+            int64_t tok = (int64_t)col * page_size;
+#endif
+            int64_t slot = req_to_token[row * rt_s0 + tok * rt_s1];
+            int64_t page = floor_div64(slot, page_size);
+            page_table[(int64_t)b * pt_s0 + (int64_t)col * pt_s1] = (int32_t)page;
+            if (use_swa) {
+#if ORACLE_MUTANT == 14
+                int64_t swa_slot = full_to_swa[page * f2s_stride]; /* planted: maps the page */
+#else
+                int64_t swa_slot = full_to_swa[slot * f2s_stride];
+#endif
+                swa_page_table[(int64_t)b * swa_s0 + (int64_t)col * swa_s1] =
+                    (int32_t)floor_div64(swa_slot, page_size);
+            }
+        }
+    }
+    return ORC_OK;
+}
+
 /* Number of planted-mistake variants this file defines (for the tests). */
-int orc_num_mutants(void) { return 10; }
+int orc_num_mutants(void) { return 15; }
 int orc_mutant_id(void) { return ORACLE_MUTANT; }

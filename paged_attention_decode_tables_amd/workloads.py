@@ -320,3 +320,70 @@ def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512,
                     scale=1.0 / math.sqrt(192.0), num_heads=num_heads, num_kv_heads=1,
                     head_size=head_size, v_head_size=v_head_size, block_size=1, x=8,
                     num_blocks=nb, cu_num_blocks=cu, latent=latent, poison_block=poison_block)
+
+
+# ---------------------------------------------------------------------------
+# Decode-metadata inputs (the step before the path): a request -> token-slot
+# table of a KV pool, as a serving engine keeps it.
+# ---------------------------------------------------------------------------
+@dataclass
+class MetadataCase:
+    """Inputs of one decode-metadata call plus the block table they encode.
+
+    ``req_to_token[req_pool_indices[b], t]`` is the pool slot of token t of
+    request b: ``block_tables[b, t // page_size] * page_size + t % page_size``
+    for t < seq_lens[b], and a stale slot (any earlier occupant's) beyond.
+    ``full_to_swa`` (optional) maps every full-pool slot to a sliding-window
+    pool slot, page by page: slot ``blk * page_size + o`` goes to
+    ``swa_block_of[blk] * page_size + o``.
+    """
+    seq_lens: torch.Tensor          # int64 [B]
+    req_to_token: torch.Tensor      # int32 [pool_rows, max_context]
+    req_pool_indices: torch.Tensor  # int64 [B]
+    block_tables: torch.Tensor      # int32 [B, max_pages]
+    page_size: int
+    max_seq_pages: int
+    seq_len_delta: int
+    full_to_swa: Optional[torch.Tensor] = None   # int32 [num_slots]
+    swa_block_of: Optional[torch.Tensor] = None  # int64 [num_blocks]
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+
+def metadata_case(*, seed: int, seq_lens, page_size: int, pool_rows: Optional[int] = None,
+                  max_context: Optional[int] = None, seq_len_delta: int = 0, swa: bool = False,
+                  max_seq_pages: Optional[int] = None) -> MetadataCase:
+    """Seeded decode-metadata inputs. Draw order: pool row permutation, block
+    permutation, stale slots, then the SWA block map."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(seq_lens, dtype=torch.int64).clone()
+    B = lens.shape[0]
+    ps = page_size
+    need = [(max(0, int(L)) + ps - 1) // ps for L in lens]
+    max_pages = max(need + [1])
+    pool_rows = pool_rows or 2 * B + 3
+    max_context = max_context or max_pages * ps
+    assert pool_rows >= B and max_context >= max_pages * ps
+    rows = torch.randperm(pool_rows, generator=gen)[:B].to(torch.int64)
+    nblocks = sum(need) + 8
+    perm = torch.randperm(nblocks, generator=gen)
+    bt = _assign_blocks(perm, need, max_pages, 0)
+    nslots = nblocks * ps
+    # stale slots everywhere, then each request's live tokens
+    rtt = torch.randint(0, nslots, (pool_rows, max_context), generator=gen, dtype=torch.int64)
+    for b in range(B):
+        L = max(0, int(lens[b]))
+        t = torch.arange(L)
+        rtt[int(rows[b]), :L] = bt[b, t // ps].to(torch.int64) * ps + t % ps
+    f2s = swa_of = None
+    if swa:
+        swa_of = torch.randperm(nblocks, generator=gen).to(torch.int64)
+        s = torch.arange(nslots)
+        f2s = (swa_of[s // ps] * ps + s % ps).to(torch.int32)
+    if max_seq_pages is None:
+        max_seq_pages = max_pages if B else 0
+    return MetadataCase(seq_lens=lens, req_to_token=rtt.to(torch.int32), req_pool_indices=rows,
+                        block_tables=bt, page_size=ps, max_seq_pages=int(max_seq_pages),
+                        seq_len_delta=seq_len_delta, full_to_swa=f2s, swa_block_of=swa_of)

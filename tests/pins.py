@@ -17,6 +17,10 @@ What pins what:
   reduce         closed form of a two-partition merge; one partition -> identity
   num_kv_splits  hand evaluations of the sglang formula (golden file)
   page_indices   numpy concatenation of the table rows, incl. strided views
+  decode meta    page table read back from slots laid out by a block table;
+                 prefix-sum identities and int32 wrap; floor division of
+                 negative slots; SWA map invariants (identity, page relabel);
+                 empty batch
 """
 from __future__ import annotations
 
@@ -348,6 +352,99 @@ def pin_mla(o):
     assert np.array_equal(got, got2)
 
 
+def _md(o, c, **kw):
+    """Run the oracle's decode metadata on a MetadataCase (numpy views)."""
+    args = dict(seq_lens=c.seq_lens.numpy(), req_to_token=c.req_to_token.numpy(),
+                req_pool_indices=c.req_pool_indices.numpy(), max_seq_pages=c.max_seq_pages,
+                page_size=c.page_size, seq_len_delta=c.seq_len_delta,
+                full_to_swa=None if c.full_to_swa is None else c.full_to_swa.numpy())
+    args.update(kw)
+    return o.decode_metadata(**args)
+
+
+def pin_metadata_roundtrip(o):
+    """Token slots laid out page by page from a block table: reading every
+    page_size-th slot and dividing by the page size gives the block table
+    back (the page table's meaning), for shuffled pool rows and strided
+    inputs. Columns past a row's pages hold its stale slots, divided."""
+    for ps in (1, 4, 16):
+        c = workloads.metadata_case(seed=60 + ps, seq_lens=[37, 1, 0, 64, 19], page_size=ps,
+                                    seq_len_delta=1)
+        _, _, pt, swa = _md(o, c)
+        assert swa is None
+        rows = c.req_pool_indices.numpy()
+        rtt = c.req_to_token.numpy()
+        for b, L in enumerate(c.seq_lens.tolist()):
+            n = (L + ps - 1) // ps
+            assert np.array_equal(pt[b, :n], c.block_tables.numpy()[b, :n]), (ps, b)
+            for col in range(n, c.max_seq_pages):  # stale slots, floor-divided
+                assert pt[b, col] == math.floor(int(rtt[rows[b], col * ps]) / ps)
+        # strided views of every input give the same tables
+        big = np.zeros((rtt.shape[0], 2 * rtt.shape[1]), np.int32)
+        big[:, ::2] = rtt
+        sl = np.zeros(2 * c.batch, np.int64)
+        sl[::2] = c.seq_lens.numpy()
+        rp = np.zeros(3 * c.batch, np.int64)
+        rp[::3] = rows
+        _, _, pt2, _ = _md(o, c, req_to_token=big[:, ::2], seq_lens=sl[::2], req_pool_indices=rp[::3])
+        assert np.array_equal(pt2, pt)
+
+
+def pin_metadata_prefix(o):
+    """cache_seqlens = seq_len + delta; cu_seqlens_k starts at 0, steps by
+    cache_seqlens and ends at their sum; int32 two's complement wrap."""
+    c = workloads.metadata_case(seed=70, seq_lens=[5, 0, 9, 1, 300], page_size=8, seq_len_delta=1)
+    cs, cu, _, _ = _md(o, c)
+    want = c.seq_lens.numpy() + 1
+    assert np.array_equal(cs, want)
+    assert cu[0] == 0 and np.array_equal(np.diff(cu), want) and cu[-1] == want.sum()
+    cs, cu, _, _ = _md(o, c, seq_len_delta=-1)
+    assert np.array_equal(cs, c.seq_lens.numpy() - 1)
+    # 2^31 - 1 + 1 wraps to -2^31; the running sum wraps the same way
+    big = np.array([2**31 - 1, 2**31 - 2], np.int64)
+    cs, cu, _, _ = o.decode_metadata(big, np.zeros((2, 4), np.int32), np.array([0, 1], np.int64),
+                                     0, 4, seq_len_delta=1)
+    assert cs.tolist() == [-2**31, 2**31 - 1]
+    assert cu.tolist() == [0, -2**31, -1]
+
+
+def pin_metadata_floor(o):
+    """Negative slots divide toward minus infinity: floor(-5/4) = -2,
+    floor(-1/4) = -1, floor(-4/4) = -1, floor(3/4) = 0, floor(8/4) = 2."""
+    slots = [-5, -1, -4, 3, 8]
+    rtt = np.zeros((1, 4 * len(slots)), np.int32)
+    rtt[0, ::4] = slots
+    _, _, pt, _ = o.decode_metadata(np.array([20], np.int64), rtt, np.array([0], np.int64),
+                                    len(slots), 4)
+    assert pt[0].tolist() == [-2, -1, -1, 0, 2]
+
+
+def pin_metadata_swa(o):
+    """The SWA table follows the map from full-pool slots to SWA slots: with
+    the identity map it equals the page table; with a map that relabels whole
+    pages by sigma it is sigma applied to the page table."""
+    for ps in (1, 8):
+        c = workloads.metadata_case(seed=80 + ps, seq_lens=[33, 2, 17], page_size=ps, swa=True)
+        _, _, pt, swa = _md(o, c)
+        assert np.array_equal(swa, c.swa_block_of.numpy()[pt])
+        nslots = c.full_to_swa.shape[0]
+        _, _, pt2, swa2 = _md(o, c, full_to_swa=np.arange(nslots, dtype=np.int32))
+        assert np.array_equal(swa2, pt2) and np.array_equal(pt2, pt)
+
+
+def pin_metadata_empty(o):
+    """An empty batch still writes cu_seqlens_k[0] = 0; max_seq_pages = 0
+    leaves the page table untouched and still fills the lengths."""
+    cs, cu, pt, _ = o.decode_metadata(np.zeros(0, np.int64), np.zeros((1, 4), np.int32),
+                                      np.zeros(0, np.int64), 4, 4)
+    assert cu.tolist() == [0] and cs.size == 0 and pt.size == 0
+    c = workloads.metadata_case(seed=90, seq_lens=[3, 4], page_size=2, seq_len_delta=2)
+    cs, cu, pt, _ = _md(o, c, max_seq_pages=0)
+    assert cs.tolist() == [5, 6] and cu.tolist() == [0, 5, 11] and pt.shape == (2, 0)
+
+
 ALL_PINS = [pin_worked_example, pin_offsets_bruteforce, pin_attention_bruteforce,
             pin_attention_sdpa, pin_closed_forms, pin_block_permutation, pin_partitions,
-            pin_reduce_closed_form, pin_num_kv_splits, pin_page_indices, pin_mla]
+            pin_reduce_closed_form, pin_num_kv_splits, pin_page_indices, pin_mla,
+            pin_metadata_roundtrip, pin_metadata_prefix, pin_metadata_floor, pin_metadata_swa,
+            pin_metadata_empty]

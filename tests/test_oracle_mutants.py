@@ -4,7 +4,10 @@ Each mutant is a build of oracle/oracle.c with ORACLE_MUTANT=k, which swaps
 in one plausible mistake (off-by-one slot, ignored stride, reversed length
 rule, unclamped log2, wrong GQA map, transposed key packing, unnormalised
 output, merge without the partition sums, partition dropping a token, value
-rows read token-major). Mistakes are planted in the oracle only, on the CPU.
+rows read token-major; for the decode metadata: inclusive prefix sum, delta
+dropped, column not scaled to a token position, SWA map applied to the page
+instead of the slot, pool row index ignored). Mistakes are planted in the
+oracle only, on the CPU.
 """
 import pytest
 
