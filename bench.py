@@ -126,31 +126,128 @@ def recorded_traffic(workload: str, kind: str, launches_kv_bytes: int):
     return float(m.group(1)) if m else None
 
 
-def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int):
-    """The oracle, as it stands, timed on the first `sample_seqs` sequences."""
+def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int, min_seconds: float):
+    """The oracle, as it stands, on the first `sample_seqs` sequences (all of
+    them by default), run repeatedly until `min_seconds` of CPU time have
+    passed; KV bytes per second of the mean run."""
     import ctypes
 
     import oracle
 
     orc = oracle.get()
-    sub = w.subset(range(sample_seqs))
+    n = w.num_seqs if sample_seqs <= 0 else min(sample_seqs, w.num_seqs)
+    sub = w.subset(range(n))
     args = (sub.query.float().numpy(), sub.key_cache.float().numpy(),
             sub.value_cache.float().numpy(), sub.block_tables.numpy(), sub.seq_lens.numpy(),
             sub.scale)
-    t0 = time.perf_counter()
-    ref = orc.attention(*args)
-    dt = time.perf_counter() - t0
+    runs, total = 0, 0.0
+    while runs == 0 or total < min_seconds:
+        t0 = time.perf_counter()
+        ref = orc.attention(*args)
+        total += time.perf_counter() - t0
+        runs += 1
+    dt = total / runs
     try:
         threads = int(ctypes.CDLL(orc.lib._name).omp_get_max_threads())
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    threads = min(threads, sample_seqs * w.num_kv_heads)
+    threads = min(threads, n * w.num_kv_heads)  # one (sequence, kv head) per thread
     kv = sub.kv_bytes()
-    err = float(np.abs(out[:sample_seqs].float().cpu().numpy() - ref).max())
+    err = float(np.abs(out[:n].float().cpu().numpy() - ref).max())
     return ({"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-             "sample": f"{sample_seqs} of {w.num_seqs} sequences (all heads), "
-                       f"{kv} KV bytes, {dt:.2f} s", "seconds": dt},
-            {"sample_seqs": sample_seqs, "max_abs_err": err})
+             "sample": f"{n} of {w.num_seqs} sequences (all heads), {kv} KV bytes, "
+                       f"{runs} runs in {total:.1f} s", "seconds": dt},
+            {"sample_seqs": n, "max_abs_err": err})
+
+
+# Decode-metadata workloads: the batches of configs 4 and 5 as a serving
+# engine's request -> token-slot table (page size 32 with a sliding-window
+# map, and page size 1).
+MD_WORKLOADS = {
+    "metadata_skewed_ps32_swa": dict(cfg=4, page_size=32, swa=True, pool_rows=512, delta=1),
+    "metadata_mla_ps1": dict(cfg=5, page_size=1, swa=False, pool_rows=128, delta=1),
+}
+
+
+def bench_metadata(args):
+    """One JSON line for normal_decode_set_metadata: GPU µs per launch
+    (launches queued back to back on one stream) and algorithmic bytes against
+    HBM peak; the rate of back-to-back calls from Python is reported beside it."""
+    spec = MD_WORKLOADS[args.md_workload]
+    lens = workloads.config_lengths(spec["cfg"]).to(torch.int64)
+    c = workloads.metadata_case(seed=100 + spec["cfg"], seq_lens=lens, page_size=spec["page_size"],
+                                pool_rows=spec["pool_rows"], seq_len_delta=spec["delta"],
+                                swa=spec["swa"])
+    B, P = c.batch, c.max_seq_pages
+    dev = "cuda"
+    sl, rtt, rows = c.seq_lens.to(dev), c.req_to_token.to(dev), c.req_pool_indices.to(dev)
+    f2s = c.full_to_swa.to(dev) if spec["swa"] else None
+    cs = torch.empty(B, dtype=torch.int32, device=dev)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    pt = torch.empty((B, P), dtype=torch.int32, device=dev)
+    sw = torch.empty((B, P), dtype=torch.int32, device=dev) if spec["swa"] else None
+
+    def launch():
+        pad.normal_decode_set_metadata(cs, cu, pt, rtt, rows, P, sl, c.seq_len_delta, c.page_size,
+                                       swa_page_table=sw, full_to_swa=f2s)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    K = args.steps
+    # GPU time per launch: the K launches are queued behind a short GPU spin
+    # (longer than it takes the host to enqueue them), so the events bracket
+    # the launches running back to back on the GPU and no host time.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(50e6))  # ~20 ms of GPU cycles
+    start.record()
+    for _ in range(K):
+        launch()
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) / K * 1e3
+    # back-to-back calls from Python (bound by the host-side argument marshalling)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        launch()
+    stop.record()
+    torch.cuda.synchronize()
+    us_b2b = start.elapsed_time(stop) / K * 1e3
+    tables = 2 if spec["swa"] else 1
+    # reads: lengths and pool rows (8 B each), one slot per page entry (+ one
+    # map entry with SWA); writes: lengths, prefix sum, the table(s)
+    nbytes = B * 16 + B * P * 4 * tables + B * 4 + (B + 1) * 4 + B * P * 4 * tables
+    res = {
+        "metric": "decode-metadata µs/launch",
+        "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(us * 1e-3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": args.md_workload, "batch": B, "max_seq_pages": P,
+                   "page_size": c.page_size, "swa": spec["swa"], "seq_len_delta": c.seq_len_delta,
+                   "pool_rows": spec["pool_rows"], "bytes_per_launch": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "normal_decode_set_metadata",
+                     "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(us, 3)},
+        "back_to_back_us_per_call": round(us_b2b, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        orc = oracle.get()
+        a = (c.seq_lens.numpy(), c.req_to_token.numpy(), c.req_pool_indices.numpy(), P,
+             c.page_size, c.seq_len_delta, None if f2s is None else c.full_to_swa.numpy())
+        t0 = time.perf_counter()
+        want = orc.decode_metadata(*a)
+        dt = time.perf_counter() - t0
+        got = [cs.cpu().numpy(), cu.cpu().numpy(), pt.cpu().numpy(),
+               None if sw is None else sw.cpu().numpy()]
+        same = all((g is None and w is None) or np.array_equal(g, w) for g, w in zip(got, want))
+        res["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us", "cores": 1,
+                               "kind": "oracle", "sample": "the whole launch, one call"}
+        res["parity_sample"] = {"bit_exact": bool(same)}
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -159,16 +256,23 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = long-context GQA)")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0,
+                    help="sequences the CPU oracle baseline runs (0 = all)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle baseline until this many seconds have passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a kernel of known "
                          "traffic for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--op", choices=("decode", "metadata"), default="decode",
+                    help="decode: one decode step of --config (the default); metadata: the "
+                         "decode-metadata launch on --md-workload")
+    ap.add_argument("--md-workload", choices=sorted(MD_WORKLOADS), default="metadata_skewed_ps32_swa")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not "
-                                   "part of this build (see the sharding notes in DESIGN.md)",
+        print(json.dumps({"error": "this benchmark measures one GPU only: the decode path has no "
+                                   "multi-GPU mode, run it with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -184,6 +288,10 @@ def main():
         torch.cuda.synchronize()
         log(f"bench: calibration copy of {n} bytes done")
         del src, dst
+
+    if args.op == "metadata":
+        bench_metadata(args)
+        return
 
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config)
@@ -259,7 +367,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
-        cb, parity = cpu_baseline(w, step.out, args.cpu_sample_seqs)
+        cb, parity = cpu_baseline(w, step.out, args.cpu_sample_seqs, args.cpu_seconds)
         res["cpu_baseline"] = cb
         res["parity_sample"] = parity
     print(json.dumps(res), flush=True)

@@ -12,7 +12,8 @@
  *   [PR35765] vLLM PR 35765, "AITER MLA backend: Avoid CPU sync in
  *             _build_decode" (_copy_page_indices_kernel, stride-robust form).
  *   [SGMETA]  sglang kernels/ops/attention/metadata.py
- *             (get_num_kv_splits_triton).
+ *             (get_num_kv_splits_triton; normal_decode_set_metadata and its
+ *             fused metadata kernels).
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers (HBM of the current HIP device) unless
@@ -202,6 +203,59 @@ int paged_token_offsets(int64_t* out, int64_t out_stride_s, const int32_t* block
                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                         int32_t block_size, int64_t block_stride, int64_t slot_stride,
                         void* stream);
+
+/*
+ * Decode metadata, the step before the path ([SGMETA]
+ * normal_decode_set_metadata; the five steps of its docstring, the index
+ * arithmetic of its two fused kernels), in one launch:
+ *   cache_seqlens[b] = int32(seq_lens[b] + seq_len_delta)
+ *   cu_seqlens_k[b]  = cache_seqlens[0] + ... + cache_seqlens[b-1]  (b <= B)
+ *   slot             = req_to_token[req_pool_indices[b], col * page_size]
+ *   page_table[b, col]     = floor(slot / page_size)
+ *   swa_page_table[b, col] = floor(full_to_swa[slot] / page_size)   (optional)
+ * for 0 <= b < batch and 0 <= col < max_seq_pages. Every column below
+ * max_seq_pages is written for every row, whatever the row's length.
+ *
+ * Types and layout: seq_lens and req_pool_indices int64; req_to_token,
+ * full_to_swa and every output int32; all arrays strided in elements (any
+ * stride values). int32 results wrap in two's complement (the lengths are
+ * the low 32 bits of the int64 sum; the prefix sum runs in int32). Slots are
+ * divided with an arithmetic right shift by log2(page_size), i.e. toward
+ * minus infinity.
+ *
+ * page_size must be a power of two >= 1, batch >= 0, max_seq_pages >= 0
+ * (PA_EINVAL otherwise). cu_seqlens_k (batch + 1 entries) is always written,
+ * cu_seqlens_k[0] = 0 even for an empty batch. The SWA table is built only
+ * when both swa_page_table and full_to_swa are non-NULL. Device-side values
+ * must index inside the caller's arrays: req_pool_indices[b] a row of
+ * req_to_token, which holds at least (max_seq_pages - 1) * page_size + 1
+ * columns; every gathered slot an entry of full_to_swa when it is given.
+ */
+typedef struct pa_metadata_args {
+    int32_t* cache_seqlens;      /* [batch] */
+    int64_t cache_seqlens_stride;
+    int32_t* cu_seqlens_k;       /* [batch + 1] */
+    int64_t cu_seqlens_k_stride;
+    int32_t* page_table;         /* [batch, max_seq_pages] */
+    int64_t page_table_stride0, page_table_stride1;
+    int32_t* swa_page_table;     /* [batch, max_seq_pages] or NULL */
+    int64_t swa_page_table_stride0, swa_page_table_stride1;
+    const int64_t* seq_lens;     /* [batch] */
+    int64_t seq_lens_stride;
+    const int32_t* req_to_token; /* [pool rows, context] token slots */
+    int64_t req_to_token_stride0, req_to_token_stride1;
+    const int64_t* req_pool_indices; /* [batch] row of req_to_token per request */
+    int64_t req_pool_indices_stride;
+    const int32_t* full_to_swa;  /* [slots] full-pool slot -> SWA slot, or NULL */
+    int64_t full_to_swa_stride;
+    int32_t batch;
+    int32_t max_seq_pages;
+    int32_t page_size;
+    int32_t reserved;            /* must be 0 */
+    int64_t seq_len_delta;
+} pa_metadata_args;
+
+int normal_decode_set_metadata(const pa_metadata_args* args, void* stream);
 
 /* Message describing the last non-OK return on the calling thread. */
 const char* pa_last_error(void);

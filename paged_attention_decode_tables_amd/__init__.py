@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     build_page_indices,
     library_path,
     load_library,
+    normal_decode_set_metadata,
     num_kv_splits,
     paged_attn_decode,
     paged_attn_reduce,

@@ -69,6 +69,21 @@ class ReduceArgs(ctypes.Structure):
     ]
 
 
+class MetadataArgs(ctypes.Structure):
+    _fields_ = [
+        ("cache_seqlens", _vp), ("cache_seqlens_stride", _i64),
+        ("cu_seqlens_k", _vp), ("cu_seqlens_k_stride", _i64),
+        ("page_table", _vp), ("page_table_stride0", _i64), ("page_table_stride1", _i64),
+        ("swa_page_table", _vp), ("swa_page_table_stride0", _i64), ("swa_page_table_stride1", _i64),
+        ("seq_lens", _vp), ("seq_lens_stride", _i64),
+        ("req_to_token", _vp), ("req_to_token_stride0", _i64), ("req_to_token_stride1", _i64),
+        ("req_pool_indices", _vp), ("req_pool_indices_stride", _i64),
+        ("full_to_swa", _vp), ("full_to_swa_stride", _i64),
+        ("batch", _i32), ("max_seq_pages", _i32), ("page_size", _i32), ("reserved", _i32),
+        ("seq_len_delta", _i64),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -92,6 +107,7 @@ def load_library() -> ctypes.CDLL:
     lib.num_kv_splits.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.paged_token_offsets.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32,
                                         _i64, _i64, _vp]
+    lib.normal_decode_set_metadata.argtypes = [ctypes.POINTER(MetadataArgs), _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     _lib = lib
@@ -209,6 +225,49 @@ def build_page_indices(page_indices: torch.Tensor, block_table: torch.Tensor,
     s0, s1 = block_table.stride()
     _check(lib.build_page_indices(_ptr(page_indices), _ptr(block_table), s0, s1,
                                   _ptr(cu_num_blocks), num_reqs, _stream(stream)))
+
+
+def normal_decode_set_metadata(cache_seqlens: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                               page_table: torch.Tensor, req_to_token: torch.Tensor,
+                               req_pool_indices: torch.Tensor, max_seq_pages: int,
+                               seq_lens: torch.Tensor, seq_len_delta: int, page_size: int,
+                               swa_page_table: Optional[torch.Tensor] = None,
+                               full_to_swa: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Decode metadata in one launch (sglang metadata.py,
+    normal_decode_set_metadata): cache_seqlens = int32(seq_lens + delta),
+    cu_seqlens_k = their exclusive prefix sum, page_table[b, col] =
+    req_to_token[req_pool_indices[b], col * page_size] // page_size, and the
+    SWA table through full_to_swa when both SWA tensors are given. seq_lens
+    and req_pool_indices are int64, the rest int32; any strides."""
+    lib = load_library()
+    for name, t, dt in (("cache_seqlens", cache_seqlens, torch.int32),
+                        ("cu_seqlens_k", cu_seqlens_k, torch.int32),
+                        ("page_table", page_table, torch.int32),
+                        ("req_to_token", req_to_token, torch.int32),
+                        ("req_pool_indices", req_pool_indices, torch.int64),
+                        ("seq_lens", seq_lens, torch.int64),
+                        ("swa_page_table", swa_page_table, torch.int32),
+                        ("full_to_swa", full_to_swa, torch.int32)):
+        if t is not None and t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+    B = seq_lens.shape[0]
+    a = MetadataArgs()
+    a.cache_seqlens, a.cache_seqlens_stride = _ptr(cache_seqlens), cache_seqlens.stride(0)
+    a.cu_seqlens_k, a.cu_seqlens_k_stride = _ptr(cu_seqlens_k), cu_seqlens_k.stride(0)
+    a.page_table = _ptr(page_table)
+    a.page_table_stride0, a.page_table_stride1 = page_table.stride()
+    if swa_page_table is not None:
+        a.swa_page_table = _ptr(swa_page_table)
+        a.swa_page_table_stride0, a.swa_page_table_stride1 = swa_page_table.stride()
+    a.seq_lens, a.seq_lens_stride = _ptr(seq_lens), seq_lens.stride(0)
+    a.req_to_token = _ptr(req_to_token)
+    a.req_to_token_stride0, a.req_to_token_stride1 = req_to_token.stride()
+    a.req_pool_indices, a.req_pool_indices_stride = _ptr(req_pool_indices), req_pool_indices.stride(0)
+    if full_to_swa is not None:
+        a.full_to_swa, a.full_to_swa_stride = _ptr(full_to_swa), full_to_swa.stride(0)
+    a.batch, a.max_seq_pages, a.page_size = B, max_seq_pages, page_size
+    a.seq_len_delta = seq_len_delta
+    _check(lib.normal_decode_set_metadata(ctypes.byref(a), _stream(stream)))
 
 
 def num_kv_splits(out: torch.Tensor, seq_lens: torch.Tensor, num_group: int, num_head: int,

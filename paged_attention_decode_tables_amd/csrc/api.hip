@@ -201,6 +201,54 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
                     "paged_attn_reduce");
 }
 
+PA_EXPORT int normal_decode_set_metadata(const pa_metadata_args* a, void* stream)
+{
+    if (!a) return fail(PA_EINVAL, "normal_decode_set_metadata: args is NULL");
+    if (a->reserved != 0) return fail(PA_EINVAL, "normal_decode_set_metadata: reserved must be 0");
+    if (a->batch < 0) return fail(PA_EINVAL, "normal_decode_set_metadata: batch < 0");
+    if (a->max_seq_pages < 0) return fail(PA_EINVAL, "normal_decode_set_metadata: max_seq_pages < 0");
+    if (a->page_size < 1 || (a->page_size & (a->page_size - 1)))
+        return fail(PA_EINVAL, "normal_decode_set_metadata: page_size %d is not a power of two", a->page_size);
+    if (!a->cu_seqlens_k) return fail(PA_EINVAL, "normal_decode_set_metadata: cu_seqlens_k is NULL");
+    if (a->batch > 0 && (!a->cache_seqlens || !a->seq_lens))
+        return fail(PA_EINVAL, "normal_decode_set_metadata: cache_seqlens or seq_lens is NULL");
+    if (a->batch > 0 && a->max_seq_pages > 0 && (!a->page_table || !a->req_to_token || !a->req_pool_indices))
+        return fail(PA_EINVAL, "normal_decode_set_metadata: page_table, req_to_token or req_pool_indices is NULL");
+    const int64_t grid = pa::metadata_grid(a->batch, a->max_seq_pages);
+    if (grid > 0x7fffffff)
+        return fail(PA_ENOTSUP, "normal_decode_set_metadata: batch x column blocks too large (%lld workgroups)",
+                    (long long)grid);
+    pa::MetadataParams p{};
+    p.cache_seqlens = a->cache_seqlens;
+    p.cache_seqlens_stride = a->cache_seqlens_stride;
+    p.cu_seqlens_k = a->cu_seqlens_k;
+    p.cu_seqlens_k_stride = a->cu_seqlens_k_stride;
+    p.page_table = a->page_table;
+    p.page_table_stride0 = a->page_table_stride0;
+    p.page_table_stride1 = a->page_table_stride1;
+    const bool swa = a->swa_page_table && a->full_to_swa;
+    p.swa_page_table = swa ? a->swa_page_table : nullptr;
+    p.swa_page_table_stride0 = a->swa_page_table_stride0;
+    p.swa_page_table_stride1 = a->swa_page_table_stride1;
+    p.seq_lens = a->seq_lens;
+    p.seq_lens_stride = a->seq_lens_stride;
+    p.req_to_token = a->req_to_token;
+    p.req_to_token_stride0 = a->req_to_token_stride0;
+    p.req_to_token_stride1 = a->req_to_token_stride1;
+    p.req_pool_indices = a->req_pool_indices;
+    p.req_pool_indices_stride = a->req_pool_indices_stride;
+    p.full_to_swa = a->full_to_swa;
+    p.full_to_swa_stride = a->full_to_swa_stride;
+    p.seq_len_delta = a->seq_len_delta;
+    p.batch = a->batch;
+    p.max_seq_pages = a->batch > 0 ? a->max_seq_pages : 0;
+    int shift = 0;
+    while ((1 << shift) < a->page_size) ++shift;
+    p.shift = shift;
+    return launched(pa::launch_decode_metadata(p, reinterpret_cast<hipStream_t>(stream)),
+                    "normal_decode_set_metadata");
+}
+
 PA_EXPORT int build_page_indices(int32_t* page_indices, const int32_t* block_table, int64_t bt_stride0,
                                  int64_t bt_stride1, const int32_t* cu_num_blocks, int32_t num_reqs,
                                  void* stream)

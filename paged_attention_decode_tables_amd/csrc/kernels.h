@@ -45,6 +45,28 @@ struct ReduceParams {
     int num_seqs, num_heads, partition_size, max_num_parts;
 };
 
+// Decode-metadata parameters (validated copy of pa_metadata_args).
+struct MetadataParams {
+    int32_t* cache_seqlens;
+    int64_t cache_seqlens_stride;
+    int32_t* cu_seqlens_k;
+    int64_t cu_seqlens_k_stride;
+    int32_t* page_table;
+    int64_t page_table_stride0, page_table_stride1;
+    int32_t* swa_page_table;  // NULL: no SWA table
+    int64_t swa_page_table_stride0, swa_page_table_stride1;
+    const int64_t* seq_lens;
+    int64_t seq_lens_stride;
+    const int32_t* req_to_token;
+    int64_t req_to_token_stride0, req_to_token_stride1;
+    const int64_t* req_pool_indices;
+    int64_t req_pool_indices_stride;
+    const int32_t* full_to_swa;
+    int64_t full_to_swa_stride;
+    int64_t seq_len_delta;
+    int batch, max_seq_pages, shift, col_blocks;
+};
+
 // Which phase-1 kernel family serves a problem.
 enum class DecodeKernel { VALU, MFMA };
 
@@ -60,6 +82,9 @@ bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size);
 
 hipError_t launch_reduce(const ReduceParams& p, int out_dtype, int Dv, hipStream_t st);
 bool reduce_supported(int Dv);
+
+hipError_t launch_decode_metadata(MetadataParams p, hipStream_t st);
+int64_t metadata_grid(int batch, int max_seq_pages);  // workgroups of one launch
 
 hipError_t launch_page_indices(int32_t* out, const int32_t* bt, int64_t s0, int64_t s1,
                                const int32_t* cu, int num_reqs, hipStream_t st);

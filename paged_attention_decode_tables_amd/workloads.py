@@ -201,6 +201,25 @@ CONFIG_NAMES = {
 }
 
 
+def _draw_lengths(cfg: int, gen: torch.Generator) -> torch.Tensor:
+    """The first draw of configs 2-5: the sequence lengths (int32)."""
+    if cfg == 2:
+        return torch.randint(1, 2049, (32,), generator=gen, dtype=torch.int64).to(torch.int32)
+    if cfg == 3:
+        return torch.full((8,), 32768, dtype=torch.int32)
+    if cfg == 4:
+        z = torch.randn((256,), generator=gen, dtype=torch.float64)
+        return torch.exp(math.log(1024.0) + 1.0 * z).round().clamp(1, 16384).to(torch.int32)
+    if cfg == 5:
+        return torch.randint(1024, 8193, (64,), generator=gen, dtype=torch.int64).to(torch.int32)
+    raise ValueError(f"config {cfg} has no length draw")
+
+
+def config_lengths(cfg: int) -> torch.Tensor:
+    """Sequence lengths of config 2-5 alone (the same values config() draws)."""
+    return _draw_lengths(cfg, torch.Generator().manual_seed(cfg))
+
+
 def config(cfg: int, *, poison: bool = False) -> Workload:
     """The five reference workloads (seed = config number)."""
     gen = torch.Generator().manual_seed(cfg)
@@ -227,16 +246,15 @@ def config(cfg: int, *, poison: bool = False) -> Workload:
             _poison(w, [2, 2])
         return w
     if cfg == 2:
-        lens = torch.randint(1, 2049, (32,), generator=gen, dtype=torch.int64).to(torch.int32)
+        lens = _draw_lengths(2, gen)
         return _standard(gen, CONFIG_NAMES[2], "MHA decode fp16", lens, H=32, Hkv=32, D=128,
                          bs=16, dt=torch.float16, nb=8192, poison=poison)
     if cfg == 3:
-        lens = torch.full((8,), 32768, dtype=torch.int32)
+        lens = _draw_lengths(3, gen)
         return _standard(gen, CONFIG_NAMES[3], "long-context GQA decode bf16", lens, H=64, Hkv=8,
                          D=128, bs=16, dt=torch.bfloat16, nb=20000, poison=poison)
     if cfg == 4:
-        z = torch.randn((256,), generator=gen, dtype=torch.float64)
-        lens = torch.exp(math.log(1024.0) + 1.0 * z).round().clamp(1, 16384).to(torch.int32)
+        lens = _draw_lengths(4, gen)
         w = _standard(gen, CONFIG_NAMES[4], "skewed-batch GQA decode bf16", lens, H=32, Hkv=8,
                       D=128, bs=32, dt=torch.bfloat16, nb=None, poison=poison)
         w.max_kv_splits = 32
@@ -271,7 +289,7 @@ def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison):
 
 def _mla(gen, *, poison):
     S, H, D, Dv = 64, 128, 576, 512
-    lens = torch.randint(1024, 8193, (S,), generator=gen, dtype=torch.int64).to(torch.int32)
+    lens = _draw_lengths(5, gen)
     total = int(lens.sum())
     nb = total + (1 if poison else 0)
     perm = torch.randperm(nb, generator=gen)

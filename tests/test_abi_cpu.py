@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
-    for n in ("paged_attn_decode", "paged_attn_reduce", "build_page_indices", "num_kv_splits"):
+    for n in ("paged_attn_decode", "paged_attn_reduce", "build_page_indices", "num_kv_splits",
+              "normal_decode_set_metadata"):
         assert n in names
     assert len(names) >= 6, names
 
@@ -59,7 +60,8 @@ def _c_layout(struct: str, fields):
     return vals[0], vals[1:]
 
 
-@pytest.mark.parametrize("cls,cname", [(api.DecodeArgs, "pa_decode_args"), (api.ReduceArgs, "pa_reduce_args")])
+@pytest.mark.parametrize("cls,cname", [(api.DecodeArgs, "pa_decode_args"), (api.ReduceArgs, "pa_reduce_args"),
+                                       (api.MetadataArgs, "pa_metadata_args")])
 def test_argument_block_layout_matches_header(cls, cname):
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -197,6 +199,37 @@ def test_index_helpers_reject(lib):
     assert lib.num_kv_splits(None, None, 0, 1, 8, 1, 16, 256, None) == api.PA_OK
     assert lib.paged_token_offsets(FAKE, 8, FAKE, 8, 1, None, FAKE, 2, 8, 3, 1, 1, None) == api.PA_EINVAL
     assert lib.paged_token_offsets(None, 8, FAKE, 8, 1, None, FAKE, 2, 8, 4, 1, 1, None) == api.PA_EINVAL
+
+
+def good_metadata(B=4, pages=10, ps=16):
+    a = api.MetadataArgs()
+    a.cache_seqlens, a.cache_seqlens_stride = FAKE, 1
+    a.cu_seqlens_k, a.cu_seqlens_k_stride = FAKE, 1
+    a.page_table, a.page_table_stride0, a.page_table_stride1 = FAKE, pages, 1
+    a.seq_lens, a.seq_lens_stride = FAKE, 1
+    a.req_to_token, a.req_to_token_stride0, a.req_to_token_stride1 = FAKE, pages * ps, 1
+    a.req_pool_indices, a.req_pool_indices_stride = FAKE, 1
+    a.batch, a.max_seq_pages, a.page_size = B, pages, ps
+    return a
+
+
+@pytest.mark.parametrize("name,change", [
+    ("page_size_not_pow2", dict(page_size=12)),
+    ("page_size_zero", dict(page_size=0)),
+    ("negative_batch", dict(batch=-1)),
+    ("negative_pages", dict(max_seq_pages=-2)),
+    ("reserved_set", dict(reserved=1)),
+    ("no_cu", dict(cu_seqlens_k=None)),
+    ("no_lengths_out", dict(cache_seqlens=None)),
+    ("no_seq_lens", dict(seq_lens=None)),
+    ("no_page_table", dict(page_table=None)),
+    ("no_req_to_token", dict(req_to_token=None)),
+    ("no_pool_indices", dict(req_pool_indices=None)),
+])
+def test_metadata_rejects(lib, name, change):
+    a = _mut(good_metadata(), **change)
+    assert lib.normal_decode_set_metadata(ctypes.byref(a), None) == api.PA_EINVAL
+    assert lib.normal_decode_set_metadata(None, None) == api.PA_EINVAL
 
 
 def test_binding_raises_on_error():
