@@ -81,6 +81,8 @@ class Oracle:
         L.orc_decode_metadata.argtypes = [_I32P, _I64, _I32P, _I64, _I32P, _I64, _I64,
                                           _I32P, _I64, _I64, _I64P, _I64, _I32P, _I64, _I64,
                                           _I64P, _I64, _I32P, _I64, _I32, _I32, _I32, _I64]
+        L.orc_swa_spec_page_table.argtypes = [_I32P, _I64, _I64, _I32P, _I64, _I64, _I32P, _I64, _I64,
+                                              _I32P, _I32P, _I32, _I32, _I32, _I32]
         self.mutant = L.orc_mutant_id()
 
     # -- integer helpers ----------------------------------------------------
@@ -162,6 +164,27 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"orc_decode_metadata: invalid arguments (rc={rc})")
         return cs, cu, pt, swa
+
+    def swa_spec_page_table(self, page_table_a, page_table_b, seq_len_a, seq_len_b,
+                            draft_tokens, fill=-1):
+        """Speculative SWA page table (sglang metadata.py,
+        prepare_swa_spec_page_table_triton): [bs * R, LEN_A + LEN_B] int32,
+        `fill` where nothing is written. Inputs may be strided int32 views."""
+        a = np.asarray(page_table_a)
+        b = np.asarray(page_table_b)
+        la = np.ascontiguousarray(seq_len_a, dtype=np.int32)
+        lb = np.ascontiguousarray(seq_len_b, dtype=np.int32)
+        assert a.dtype == np.int32 and b.dtype == np.int32 and a.ndim == 2 and b.ndim == 2
+        bs = la.shape[0]
+        assert lb.shape[0] == bs * draft_tokens
+        out = np.full((bs * draft_tokens, a.shape[1] + b.shape[1]), fill, dtype=np.int32)
+        rc = self.lib.orc_swa_spec_page_table(_ptr(out, _I32P), max(out.shape[1], 1), 1,
+                                              _ptr(a, _I32P), *_estrides(a), _ptr(b, _I32P),
+                                              *_estrides(b), _ptr(la, _I32P), _ptr(lb, _I32P), bs,
+                                              a.shape[1], b.shape[1], draft_tokens)
+        if rc != 0:
+            raise ValueError(f"orc_swa_spec_page_table: invalid arguments (rc={rc})")
+        return out
 
     # -- attention ----------------------------------------------------------
     def _problem(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr):

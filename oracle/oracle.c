@@ -20,9 +20,11 @@
  *            _build_decode": _copy_page_indices_kernel and the review's
  *            stride-robust version of it.
  *   [SGMETA] sglang kernels/ops/attention/metadata.py:
- *            get_num_kv_splits_triton, and normal_decode_set_metadata with
- *            its two fused metadata kernels (the docstring lists the five
- *            steps; the kernels fix the index arithmetic).
+ *            get_num_kv_splits_triton, normal_decode_set_metadata with its
+ *            two fused metadata kernels (the docstring lists the five steps;
+ *            the kernels fix the index arithmetic), and the speculative SWA
+ *            page-table concat (prepare_swa_spec_page_table_triton and its
+ *            kernel).
  *
  * Precision: attention is accumulated in double. The split heuristic follows
  * the fp32 arithmetic its page prescribes (tl.float32 cast, fp32 log2 and
@@ -60,6 +62,11 @@
  *       prefix sum of nothing).
  *   R11 the SWA table is built only when both it and the full-to-SWA map are
  *       given; it maps the raw slot (before the division) and then divides.
+ *   R12 speculative SWA page table: the destination has LEN_A + LEN_B columns
+ *       (the wrapper's LEN_OUT) and only columns below
+ *       min(seq_len_a + seq_len_b, LEN_A + LEN_B) are written (the page's
+ *       grid would write to the end of the last 256-column block when the
+ *       lengths exceed the tables); lengths are int32.
  */
 #include <math.h>
 #include <stdint.h>
@@ -568,6 +575,52 @@ int orc_decode_metadata(int32_t* cache_seqlens, int64_t cs_stride,
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Speculative SWA page table, [SGMETA] prepare_swa_spec_page_table_triton:
+ * the page table of each of the bs requests is concatenated with the
+ * expanded page table of each of its R = draft_tokens draft rows. Row m of
+ * the destination (0 <= m < bs * R) belongs to request m / R; with
+ * la = seq_len_a[m / R] and lb = seq_len_b[m], column n < la + lb is
+ *   a[m / R, n]        for n < la   (0 when n >= LEN_A)
+ *   b[m, n - la]       for n >= la  (0 when n - la >= LEN_B)
+ * and columns n >= la + lb are left untouched (R12 for the table widths).
+ * ------------------------------------------------------------------------ */
+int orc_swa_spec_page_table(int32_t* dst, int64_t d0, int64_t d1,
+                            const int32_t* a, int64_t a0, int64_t a1,
+                            const int32_t* b, int64_t b0, int64_t b1,
+                            const int32_t* seq_len_a, const int32_t* seq_len_b,
+                            int32_t bs, int32_t len_a, int32_t len_b, int32_t draft_tokens)
+{
+    if (bs < 0 || len_a < 0 || len_b < 0 || draft_tokens < 1) return ORC_EINVAL;
+    if (bs == 0) return ORC_OK;
+    if (!dst || !seq_len_a || !seq_len_b || (len_a > 0 && !a) || (len_b > 0 && !b)) return ORC_EINVAL;
+    const int64_t rows = (int64_t)bs * draft_tokens;
+    for (int64_t m = 0; m < rows; ++m) {
+#if ORACLE_MUTANT == 16
+        const int64_t ia = m; /* planted: draft row used as the request row */
+#else
+        const int64_t ia = m / draft_tokens;
+#endif
+        const int64_t la = seq_len_a[ia], lb = seq_len_b[m];
+        const int64_t end = min64(la + lb, (int64_t)len_a + len_b);
+        for (int64_t n = 0; n < end; ++n) {
+            int32_t v;
+            if (n < la) {
+                v = n < len_a ? a[ia * a0 + n * a1] : 0;
+            } else {
+#if ORACLE_MUTANT == 17
+                const int64_t j = n; /* planted: b column not shifted by la */
+#else
+                const int64_t j = n - la;
+#endif
+                v = j < len_b ? b[m * b0 + j * b1] : 0;
+            }
+            dst[m * d0 + n * d1] = v;
+        }
+    }
+    return ORC_OK;
+}
+
 /* Number of planted-mistake variants this file defines (for the tests). */
-int orc_num_mutants(void) { return 15; }
+int orc_num_mutants(void) { return 17; }
 int orc_mutant_id(void) { return ORACLE_MUTANT; }

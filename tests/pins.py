@@ -21,6 +21,8 @@ What pins what:
                  prefix-sum identities and int32 wrap; floor division of
                  negative slots; SWA map invariants (identity, page relabel);
                  empty batch
+  spec page tbl  numpy concatenation of the two prefixes per draft row;
+                 zeros past the table widths; untouched past the total
 """
 from __future__ import annotations
 
@@ -443,8 +445,46 @@ def pin_metadata_empty(o):
     assert cs.tolist() == [5, 6] and cu.tolist() == [0, 5, 11] and pt.shape == (2, 0)
 
 
+def pin_spec_page_table(o):
+    """Each destination row is the concatenation of its request's page-table
+    prefix and its draft row's prefix (numpy concatenate), nothing written
+    past the total; with one draft token and empty drafts it is the plain
+    page table, with empty request rows the draft table."""
+    rng = np.random.default_rng(21)
+    bs, R, LA, LB = 5, 3, 37, 11
+    a = rng.integers(0, 10**6, (bs, LA)).astype(np.int32)
+    bt = rng.integers(0, 10**6, (LB, bs * R)).astype(np.int32)
+    for b in (bt.T.copy(), bt.T):  # contiguous, then a transposed view
+        la = rng.integers(0, LA + 1, bs).astype(np.int32)
+        lb = rng.integers(0, LB + 1, bs * R).astype(np.int32)
+        la[1], lb[4] = 0, 0
+        out = o.swa_spec_page_table(a, b, la, lb, R, fill=-9)
+        for m in range(bs * R):
+            n = la[m // R] + lb[m]
+            want = np.concatenate([a[m // R, :la[m // R]], np.asarray(b)[m, :lb[m]]])
+            assert np.array_equal(out[m, :n], want), m
+            assert (out[m, n:] == -9).all(), m
+    out = o.swa_spec_page_table(a, np.zeros((bs, 4), np.int32), np.full(bs, 20, np.int32),
+                                np.zeros(bs, np.int32), 1, fill=-9)
+    assert np.array_equal(out[:, :20], a[:, :20]) and (out[:, 20:] == -9).all()
+    out = o.swa_spec_page_table(a, bt.T.copy(), np.zeros(bs, np.int32), np.full(bs * R, LB, np.int32),
+                                R, fill=-9)
+    assert np.array_equal(out[:, :LB], bt.T) and (out[:, LB:] == -9).all()
+
+
+def pin_spec_page_table_widths(o):
+    """Lengths past a table's width read zeros there (the masked loads), and
+    the destination stops at LEN_A + LEN_B columns."""
+    a = np.arange(1, 5, dtype=np.int32)[None, :]          # LEN_A = 4
+    b = np.arange(101, 104, dtype=np.int32)[None, :]      # LEN_B = 3
+    out = o.swa_spec_page_table(a, b, np.array([6], np.int32), np.array([2], np.int32), 1, fill=-9)
+    assert out.tolist() == [[1, 2, 3, 4, 0, 0, 101]]
+    out = o.swa_spec_page_table(a, b, np.array([2], np.int32), np.array([1], np.int32), 1, fill=-9)
+    assert out.tolist() == [[1, 2, 101, -9, -9, -9, -9]]
+
+
 ALL_PINS = [pin_worked_example, pin_offsets_bruteforce, pin_attention_bruteforce,
             pin_attention_sdpa, pin_closed_forms, pin_block_permutation, pin_partitions,
             pin_reduce_closed_form, pin_num_kv_splits, pin_page_indices, pin_mla,
             pin_metadata_roundtrip, pin_metadata_prefix, pin_metadata_floor, pin_metadata_swa,
-            pin_metadata_empty]
+            pin_metadata_empty, pin_spec_page_table, pin_spec_page_table_widths]

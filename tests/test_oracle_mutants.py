@@ -6,8 +6,9 @@ rule, unclamped log2, wrong GQA map, transposed key packing, unnormalised
 output, merge without the partition sums, partition dropping a token, value
 rows read token-major; for the decode metadata: inclusive prefix sum, delta
 dropped, column not scaled to a token position, SWA map applied to the page
-instead of the slot, pool row index ignored). Mistakes are planted in the
-oracle only, on the CPU.
+instead of the slot, pool row index ignored; for the speculative page
+table: draft row used as the request row, draft column not shifted).
+Mistakes are planted in the oracle only, on the CPU.
 """
 import pytest
 
