@@ -250,6 +250,67 @@ def bench_metadata(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_spec_table(args):
+    """One JSON line for prepare_swa_spec_page_table on the MLA batch: 64
+    requests (page size 1, so a page table row per token), 4 draft tokens
+    each with up to 4 extra pages; GPU µs per launch as in bench_metadata."""
+    lens = workloads.config_lengths(5).numpy().astype(np.int32)
+    bs, R, LB = lens.shape[0], 4, 4
+    LA = int(lens.max())
+    rng = np.random.default_rng(105)
+    a = torch.from_numpy(rng.integers(0, 2**31 - 1, (bs, LA)).astype(np.int32)).cuda()
+    b = torch.from_numpy(rng.integers(0, 2**31 - 1, (bs * R, LB)).astype(np.int32)).cuda()
+    la = torch.from_numpy(lens).cuda()
+    lb_np = rng.integers(1, LB + 1, bs * R).astype(np.int32)
+    lb = torch.from_numpy(lb_np).cuda()
+    dst = torch.empty((bs * R, LA + LB), dtype=torch.int32, device="cuda")
+
+    def launch():
+        pad.prepare_swa_spec_page_table(dst, a, b, la, lb, R)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    K = args.steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(50e6))
+    start.record()
+    for _ in range(K):
+        launch()
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) / K * 1e3
+    # each written entry is one 4-byte read and one 4-byte write, plus the lengths
+    written = int(np.repeat(lens, R).astype(np.int64).sum() + lb_np.astype(np.int64).sum())
+    nbytes = 8 * written + 4 * (bs + bs * R)
+    res = {
+        "metric": "speculative SWA page table µs/launch",
+        "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(us * 1e-3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "spec_table_mla_batch", "bs": bs, "draft_tokens": R, "len_a": LA,
+                   "len_b": LB, "entries_written": written, "bytes_per_launch": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "prepare_swa_spec_page_table",
+                     "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        orc = oracle.get()
+        an, bn = a.cpu().numpy(), b.cpu().numpy()
+        t0 = time.perf_counter()
+        want = orc.swa_spec_page_table(an, bn, lens, lb_np, R)
+        dt = time.perf_counter() - t0
+        got = dst.cpu().numpy()
+        mask = want != -1  # entries the call writes
+        res["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us", "cores": 1,
+                               "kind": "oracle", "sample": "the whole launch, one call"}
+        res["parity_sample"] = {"bit_exact": bool(np.array_equal(got[mask], want[mask]))}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,9 +325,10 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a kernel of known "
                          "traffic for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--op", choices=("decode", "metadata"), default="decode",
+    ap.add_argument("--op", choices=("decode", "metadata", "spec_table"), default="decode",
                     help="decode: one decode step of --config (the default); metadata: the "
-                         "decode-metadata launch on --md-workload")
+                         "decode-metadata launch on --md-workload; spec_table: the speculative "
+                         "SWA page-table concat on the MLA batch")
     ap.add_argument("--md-workload", choices=sorted(MD_WORKLOADS), default="metadata_skewed_ps32_swa")
     args = ap.parse_args()
 
@@ -291,6 +353,9 @@ def main():
 
     if args.op == "metadata":
         bench_metadata(args)
+        return
+    if args.op == "spec_table":
+        bench_spec_table(args)
         return
 
     log(f"bench: generating workload {args.config}")

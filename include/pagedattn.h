@@ -13,7 +13,7 @@
  *             _build_decode" (_copy_page_indices_kernel, stride-robust form).
  *   [SGMETA]  sglang kernels/ops/attention/metadata.py
  *             (get_num_kv_splits_triton; normal_decode_set_metadata and its
- *             fused metadata kernels).
+ *             fused metadata kernels; prepare_swa_spec_page_table_triton).
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers (HBM of the current HIP device) unless
@@ -256,6 +256,27 @@ typedef struct pa_metadata_args {
 } pa_metadata_args;
 
 int normal_decode_set_metadata(const pa_metadata_args* args, void* stream);
+
+/*
+ * Speculative SWA page table ([SGMETA] prepare_swa_spec_page_table_triton
+ * and its kernel): concatenates each request's page table with the
+ * expanded page tables of its draft rows. With R = draft_tokens, row m of
+ * dst (0 <= m < bs*R) belongs to request m / R; with la = seq_len_a[m / R],
+ * lb = seq_len_b[m], for n < min(la + lb, len_a + len_b):
+ *     dst[m, n] = page_table_a[m / R, n]   if n < la  (0 if n >= len_a)
+ *                 page_table_b[m, n - la]  otherwise (0 if n - la >= len_b)
+ * Columns n >= la + lb are not written. Shapes: page_table_a [bs, len_a],
+ * page_table_b [bs*R, len_b], dst [bs*R, len_a + len_b], seq_len_a [bs],
+ * seq_len_b [bs*R]; int32 throughout, element strides. Reads are masked by
+ * the table widths and writes by the destination width, so any length
+ * values are memory-safe. bs, len_a, len_b >= 0 and draft_tokens >= 1
+ * (PA_EINVAL otherwise); bs == 0 or len_a + len_b == 0 is a no-op.
+ */
+int prepare_swa_spec_page_table(int32_t* dst, int64_t dst_stride0, int64_t dst_stride1,
+                                const int32_t* page_table_a, int64_t a_stride0, int64_t a_stride1,
+                                const int32_t* page_table_b, int64_t b_stride0, int64_t b_stride1,
+                                const int32_t* seq_len_a, const int32_t* seq_len_b, int32_t bs,
+                                int32_t len_a, int32_t len_b, int32_t draft_tokens, void* stream);
 
 /* Message describing the last non-OK return on the calling thread. */
 const char* pa_last_error(void);

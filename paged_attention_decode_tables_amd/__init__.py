@@ -15,4 +15,5 @@ from .api import (  # noqa: F401
     paged_attn_decode,
     paged_attn_reduce,
     paged_token_offsets,
+    prepare_swa_spec_page_table,
 )

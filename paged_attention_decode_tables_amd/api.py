@@ -108,6 +108,8 @@ def load_library() -> ctypes.CDLL:
     lib.paged_token_offsets.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32,
                                         _i64, _i64, _vp]
     lib.normal_decode_set_metadata.argtypes = [ctypes.POINTER(MetadataArgs), _vp]
+    lib.prepare_swa_spec_page_table.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                                _vp, _vp, _i32, _i32, _i32, _i32, _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     _lib = lib
@@ -268,6 +270,33 @@ def normal_decode_set_metadata(cache_seqlens: torch.Tensor, cu_seqlens_k: torch.
     a.batch, a.max_seq_pages, a.page_size = B, max_seq_pages, page_size
     a.seq_len_delta = seq_len_delta
     _check(lib.normal_decode_set_metadata(ctypes.byref(a), _stream(stream)))
+
+
+def prepare_swa_spec_page_table(page_table_dst: torch.Tensor, page_table_a: torch.Tensor,
+                                page_table_b: torch.Tensor, seq_len_a: torch.Tensor,
+                                seq_len_b: torch.Tensor, speculative_num_draft_tokens: int,
+                                stream=None) -> None:
+    """Concatenate each request's page table with its draft rows' tables
+    (sglang metadata.py, prepare_swa_spec_page_table_triton). All int32;
+    page_table_dst is [bs * R, LEN_A + LEN_B]."""
+    lib = load_library()
+    for name, t in (("page_table_dst", page_table_dst), ("page_table_a", page_table_a),
+                    ("page_table_b", page_table_b), ("seq_len_a", seq_len_a),
+                    ("seq_len_b", seq_len_b)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32, got {t.dtype}")
+    bs, R = seq_len_a.numel(), speculative_num_draft_tokens
+    if seq_len_b.numel() != bs * R:
+        raise ValueError("seq_len_b must hold bs * speculative_num_draft_tokens entries")
+    if not (seq_len_a.is_contiguous() and seq_len_b.is_contiguous()):
+        raise ValueError("seq_len_a and seq_len_b must be contiguous")
+    LA, LB = page_table_a.shape[1], page_table_b.shape[1]
+    if tuple(page_table_dst.shape) != (bs * R, LA + LB):
+        raise ValueError(f"page_table_dst must be [{bs * R}, {LA + LB}]")
+    _check(lib.prepare_swa_spec_page_table(
+        _ptr(page_table_dst), *page_table_dst.stride(), _ptr(page_table_a), *page_table_a.stride(),
+        _ptr(page_table_b), *page_table_b.stride(), _ptr(seq_len_a), _ptr(seq_len_b), bs, LA, LB, R,
+        _stream(stream)))
 
 
 def num_kv_splits(out: torch.Tensor, seq_lens: torch.Tensor, num_group: int, num_head: int,

@@ -249,6 +249,42 @@ PA_EXPORT int normal_decode_set_metadata(const pa_metadata_args* a, void* stream
                     "normal_decode_set_metadata");
 }
 
+PA_EXPORT int prepare_swa_spec_page_table(int32_t* dst, int64_t dst_stride0, int64_t dst_stride1,
+                                          const int32_t* page_table_a, int64_t a_stride0, int64_t a_stride1,
+                                          const int32_t* page_table_b, int64_t b_stride0, int64_t b_stride1,
+                                          const int32_t* seq_len_a, const int32_t* seq_len_b, int32_t bs,
+                                          int32_t len_a, int32_t len_b, int32_t draft_tokens, void* stream)
+{
+    if (bs < 0 || len_a < 0 || len_b < 0)
+        return fail(PA_EINVAL, "prepare_swa_spec_page_table: bs, len_a and len_b must be >= 0");
+    if (draft_tokens < 1) return fail(PA_EINVAL, "prepare_swa_spec_page_table: draft_tokens < 1");
+    if (bs == 0 || len_a + (int64_t)len_b == 0) return PA_OK;
+    if (!dst || !seq_len_a || !seq_len_b || (len_a > 0 && !page_table_a) || (len_b > 0 && !page_table_b))
+        return fail(PA_EINVAL, "prepare_swa_spec_page_table: a required pointer is NULL");
+    const int64_t grid = pa::spec_table_grid((int64_t)bs * draft_tokens, len_a, len_b);
+    if (grid > 0x7fffffff)
+        return fail(PA_ENOTSUP, "prepare_swa_spec_page_table: too many rows x column blocks (%lld)",
+                    (long long)grid);
+    pa::SpecTableParams p{};
+    p.dst = dst;
+    p.dst_stride0 = dst_stride0;
+    p.dst_stride1 = dst_stride1;
+    p.a = page_table_a;
+    p.a_stride0 = a_stride0;
+    p.a_stride1 = a_stride1;
+    p.b = page_table_b;
+    p.b_stride0 = b_stride0;
+    p.b_stride1 = b_stride1;
+    p.seq_len_a = seq_len_a;
+    p.seq_len_b = seq_len_b;
+    p.bs = bs;
+    p.len_a = len_a;
+    p.len_b = len_b;
+    p.draft_tokens = draft_tokens;
+    return launched(pa::launch_swa_spec_page_table(p, reinterpret_cast<hipStream_t>(stream)),
+                    "prepare_swa_spec_page_table");
+}
+
 PA_EXPORT int build_page_indices(int32_t* page_indices, const int32_t* block_table, int64_t bt_stride0,
                                  int64_t bt_stride1, const int32_t* cu_num_blocks, int32_t num_reqs,
                                  void* stream)

@@ -67,6 +67,19 @@ struct MetadataParams {
     int batch, max_seq_pages, shift, col_blocks;
 };
 
+// Speculative SWA page-table parameters.
+struct SpecTableParams {
+    int32_t* dst;
+    int64_t dst_stride0, dst_stride1;
+    const int32_t* a;
+    int64_t a_stride0, a_stride1;
+    const int32_t* b;
+    int64_t b_stride0, b_stride1;
+    const int32_t* seq_len_a;
+    const int32_t* seq_len_b;
+    int bs, len_a, len_b, draft_tokens, col_blocks;
+};
+
 // Which phase-1 kernel family serves a problem.
 enum class DecodeKernel { VALU, MFMA };
 
@@ -85,6 +98,9 @@ bool reduce_supported(int Dv);
 
 hipError_t launch_decode_metadata(MetadataParams p, hipStream_t st);
 int64_t metadata_grid(int batch, int max_seq_pages);  // workgroups of one launch
+
+hipError_t launch_swa_spec_page_table(SpecTableParams p, hipStream_t st);
+int64_t spec_table_grid(int64_t rows, int len_a, int len_b);
 
 hipError_t launch_page_indices(int32_t* out, const int32_t* bt, int64_t s0, int64_t s1,
                                const int32_t* cu, int num_reqs, hipStream_t st);

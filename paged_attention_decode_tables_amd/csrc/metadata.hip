@@ -2,7 +2,8 @@
 // kernels/ops/attention/metadata.py, normal_decode_set_metadata and its fused
 // metadata kernels): per-request lengths, their exclusive prefix sum, and the
 // page table gathered from the request -> token-slot table, with the optional
-// sliding-window (SWA) table.
+// sliding-window (SWA) table; and the speculative SWA page-table concat of the
+// same page (prepare_swa_spec_page_table_triton).
 //
 // Workgroup 0 computes the lengths and the prefix sum; every other workgroup
 // gathers kMetaCols columns of one request's row. The prefix sum is a block
@@ -101,6 +102,55 @@ __global__ __launch_bounds__(kMetaThreads) void k_decode_metadata(MetadataParams
                              (int64_t)col * p.swa_page_table_stride1] = s >> p.shift;
         }
     }
+}
+
+// Speculative SWA page table (prepare_swa_spec_page_table_triton): one
+// workgroup per (destination row, kMetaCols columns). Row m belongs to
+// request m / draft; its columns below la + lb take the request's page
+// table, then the draft row's, with zeros past either table's width, and the
+// row stops at len_a + len_b columns. Reads are masked by the table widths
+// and writes by the destination width, so any length values are safe.
+__global__ __launch_bounds__(kMetaThreads) void k_swa_spec_page_table(SpecTableParams p)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t m = wg / p.col_blocks;
+    const int cb = (int)(wg % p.col_blocks);
+    const int64_t ia = m / p.draft_tokens;
+    const int64_t la = p.seq_len_a[ia], lb = p.seq_len_b[m];
+    const int64_t width = (int64_t)p.len_a + p.len_b;
+    const int64_t end = la + lb < width ? la + lb : width;
+    int32_t v[kMetaColsPerThread];
+#pragma unroll
+    for (int j = 0; j < kMetaColsPerThread; ++j) {
+        const int64_t n = (int64_t)cb * kMetaCols + j * kMetaThreads + threadIdx.x;
+        v[j] = 0;
+        if (n < end) {
+            if (n < la) {
+                if (n < p.len_a) v[j] = p.a[ia * p.a_stride0 + n * p.a_stride1];
+            } else if (n - la < p.len_b) {
+                v[j] = p.b[m * p.b_stride0 + (n - la) * p.b_stride1];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kMetaColsPerThread; ++j) {
+        const int64_t n = (int64_t)cb * kMetaCols + j * kMetaThreads + threadIdx.x;
+        if (n < end) p.dst[m * p.dst_stride0 + n * p.dst_stride1] = v[j];
+    }
+}
+
+int64_t spec_table_grid(int64_t rows, int len_a, int len_b)
+{
+    return rows * ((((int64_t)len_a + len_b) + kMetaCols - 1) / kMetaCols);
+}
+
+hipError_t launch_swa_spec_page_table(SpecTableParams p, hipStream_t st)
+{
+    p.col_blocks = (int)((((int64_t)p.len_a + p.len_b) + kMetaCols - 1) / kMetaCols);
+    const int64_t grid = spec_table_grid((int64_t)p.bs * p.draft_tokens, p.len_a, p.len_b);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_swa_spec_page_table, dim3((unsigned)grid), dim3(kMetaThreads), 0, st, p);
+    return hipGetLastError();
 }
 
 int64_t metadata_grid(int batch, int max_seq_pages)

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for n in ("paged_attn_decode", "paged_attn_reduce", "build_page_indices", "num_kv_splits",
-              "normal_decode_set_metadata"):
+              "normal_decode_set_metadata", "prepare_swa_spec_page_table"):
         assert n in names
     assert len(names) >= 6, names
 
@@ -230,6 +230,17 @@ def test_metadata_rejects(lib, name, change):
     a = _mut(good_metadata(), **change)
     assert lib.normal_decode_set_metadata(ctypes.byref(a), None) == api.PA_EINVAL
     assert lib.normal_decode_set_metadata(None, None) == api.PA_EINVAL
+
+
+def test_spec_page_table_rejects(lib):
+    f = lib.prepare_swa_spec_page_table
+    assert f(FAKE, 8, 1, FAKE, 4, 1, FAKE, 4, 1, FAKE, FAKE, -1, 4, 4, 2, None) == api.PA_EINVAL
+    assert f(FAKE, 8, 1, FAKE, 4, 1, FAKE, 4, 1, FAKE, FAKE, 3, -4, 4, 2, None) == api.PA_EINVAL
+    assert f(FAKE, 8, 1, FAKE, 4, 1, FAKE, 4, 1, FAKE, FAKE, 3, 4, 4, 0, None) == api.PA_EINVAL
+    assert f(None, 8, 1, FAKE, 4, 1, FAKE, 4, 1, FAKE, FAKE, 3, 4, 4, 2, None) == api.PA_EINVAL
+    assert f(FAKE, 8, 1, None, 4, 1, FAKE, 4, 1, FAKE, FAKE, 3, 4, 4, 2, None) == api.PA_EINVAL
+    assert f(FAKE, 8, 1, FAKE, 4, 1, FAKE, 4, 1, FAKE, None, 3, 4, 4, 2, None) == api.PA_EINVAL
+    assert f(None, 8, 1, None, 4, 1, None, 4, 1, None, None, 0, 4, 4, 2, None) == api.PA_OK
 
 
 def test_binding_raises_on_error():

@@ -155,3 +155,64 @@ def test_metadata_negative_slots_and_wrap(orc):
                                max_seq_pages=P, seq_len_delta=3)
     cs, cu, pt, _ = check(orc, c)
     assert (pt < 0).any() and (cu < 0).any()  # the cases this test is for occurred
+
+
+# ---------------------------------------------------------------------------
+# speculative SWA page table (prepare_swa_spec_page_table)
+# ---------------------------------------------------------------------------
+def _spec_inputs(seed, bs, R, LA, LB, over=False):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 2**31 - 1, (bs, LA)).astype(np.int32)
+    b = rng.integers(0, 2**31 - 1, (bs * R, LB)).astype(np.int32)
+    hi_a, hi_b = (LA + 40, LB + 7) if over else (LA, LB)
+    la = rng.integers(-3 if over else 0, hi_a + 1, bs).astype(np.int32)
+    lb = rng.integers(0, hi_b + 1, bs * R).astype(np.int32)
+    return a, b, la, lb
+
+
+def run_spec(a, b, la, lb, R, strided=False):
+    bs, LA, LB = a.shape[0], a.shape[1], b.shape[1]
+    ta, tb = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    if strided:  # a as a transposed view, b with a column stride of 2, dst with padded rows
+        ta = ta.t().contiguous().t()
+        tb = _strided(tb, 2)
+        buf = torch.full((bs * R, LA + LB + 9), SENTINEL, dtype=torch.int32, device=DEV)
+        dst = buf[:, :LA + LB]
+    else:
+        dst = torch.full((bs * R, LA + LB), SENTINEL, dtype=torch.int32, device=DEV)
+    pad.prepare_swa_spec_page_table(dst, ta, tb, torch.from_numpy(la).to(DEV),
+                                    torch.from_numpy(lb).to(DEV), R)
+    torch.cuda.synchronize()
+    if strided:
+        assert (buf[:, LA + LB:] == SENTINEL).all()
+    return dst.cpu().numpy()
+
+
+SPEC_CASES = [
+    # name, seed, bs, R, LA, LB, lengths past the widths / negative
+    ("mla_like", 31, 64, 4, 8192, 8, False),
+    ("small_ragged", 32, 7, 3, 300, 17, False),
+    ("over_widths", 33, 9, 2, 1030, 5, True),
+    ("one_draft", 34, 33, 1, 2049, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", SPEC_CASES, ids=[c[0] for c in SPEC_CASES])
+@pytest.mark.parametrize("strided", [False, True])
+def test_spec_page_table_matches_oracle(orc, case, strided):
+    name, seed, bs, R, LA, LB, over = case
+    say(f"spec page table {name} strided={strided}")
+    a, b, la, lb = _spec_inputs(seed, bs, R, LA, LB, over)
+    got = run_spec(a, b, la, lb, R, strided=strided)
+    want = orc.swa_spec_page_table(a, b, la, lb, R, fill=SENTINEL)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+def test_spec_page_table_empty():
+    say("spec page table empty")
+    dst = torch.full((0, 12), SENTINEL, dtype=torch.int32, device=DEV)
+    e = torch.zeros(0, dtype=torch.int32, device=DEV)
+    pad.prepare_swa_spec_page_table(dst, torch.zeros((0, 8), dtype=torch.int32, device=DEV),
+                                    torch.zeros((0, 4), dtype=torch.int32, device=DEV), e, e, 3)
+    torch.cuda.synchronize()
