@@ -67,11 +67,14 @@ def kernel_source_hash(kind: str) -> str:
 class Step:
     """Device buffers and the launches of one decode step."""
 
-    def __init__(self, w: workloads.Workload, out_dtype=torch.bfloat16):
+    def __init__(self, w: workloads.Workload, out_dtype=torch.bfloat16, balanced_workers=0):
         self.w = w
         self.g = g = w.to("cuda")
         self.ns = None
         self.indptr = None
+        # balanced splits: equal token ranges, one per worker (partition_size 0)
+        self.workers = balanced_workers
+        self.partition = 0 if balanced_workers else w.partition_size
         if w.max_kv_splits is not None:
             self.max_parts = w.max_kv_splits
             self.ns = torch.empty(w.num_seqs, dtype=torch.int32, device="cuda")
@@ -98,13 +101,13 @@ class Step:
         w, g = self.w, self.g
         bt = self.flat if self.indptr is not None else g.block_tables
         pad.paged_attn_decode(self.tmp, self.es, self.ml, g.query, g.key_cache, g.value_cache, bt,
-                              g.seq_lens, w.scale, w.max_seq_len, partition_size=w.partition_size,
-                              num_splits=self.ns, kv_indptr=self.indptr)
+                              g.seq_lens, w.scale, w.max_seq_len, partition_size=self.partition,
+                              num_splits=self.ns, kv_indptr=self.indptr, num_workers=self.workers)
 
     def reduce(self):
         w, g = self.w, self.g
         pad.paged_attn_reduce(self.out, self.tmp, self.es, self.ml, g.seq_lens,
-                              partition_size=w.partition_size, num_splits=self.ns)
+                              partition_size=self.partition, num_splits=self.ns)
 
     def run(self):
         self.pre()
@@ -325,6 +328,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a kernel of known "
                          "traffic for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--fixed-splits", action="store_true",
+                    help="run the MLA workload with its fixed 512-token partitions instead of "
+                         "balanced splits")
     ap.add_argument("--op", choices=("decode", "metadata", "spec_table"), default="decode",
                     help="decode: one decode step of --config (the default); metadata: the "
                          "decode-metadata launch on --md-workload; spec_table: the speculative "
@@ -360,8 +366,12 @@ def main():
 
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config)
-    step = Step(w)
     kind = kernel_kind(w)
+    # The MLA workload's split policy is not fixed by its definition: it runs
+    # with balanced splits, one token range per compute unit.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    workers = cus if (kind == "mla" and not args.fixed_splits) else 0
+    step = Step(w, balanced_workers=workers)
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup}")
@@ -421,7 +431,8 @@ def main():
                    "tokens": w.total_tokens, "heads": w.num_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_size, "v_head_dim": w.v_head_size,
                    "block_size": w.block_size, "num_blocks": w.num_blocks,
-                   "partition": w.partition_size if w.max_kv_splits is None else "num_kv_splits",
+                   "partition": (f"balanced ({workers} token ranges)" if workers else
+                                 w.partition_size if w.max_kv_splits is None else "num_kv_splits"),
                    "kv_bytes_per_step": kv},
         "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -69,6 +69,18 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
  * of 64 tokens, and split p covers [p*len, min((p+1)*len, L)). A split with
  * no tokens (p*len >= L) stores m = -inf, l = 0 and leaves tmp_output
  * untouched, as the page's early exit does.
+ *
+ * Balanced splits (partition_size == 0, num_splits == NULL, num_workers >= 1;
+ * served by the MLA matrix-core kernel only, PA_ENOTSUP otherwise): the
+ * tokens of all sequences, concatenated in sequence order (lengths <= 0
+ * count as 0), total T, are cut into ranges of U tokens,
+ *     U = round_up(max(cdiv(T, num_workers), cdiv(max_s L_s, max_num_parts - 1)), 32),
+ * range w = [w*U, (w+1)*U). The k-th range that meets sequence s is its
+ * split k, and slots k >= (number of such ranges) store m = -inf, l = 0. So
+ * every worker gets the same number of tokens whatever the length mix, and
+ * a sequence never has more than max_num_parts splits (max_num_parts >= 2).
+ * Phase 2 with partition_size == 0 merges every non-empty slot; the final
+ * output is the same as with any other split.
  */
 typedef struct pa_decode_args {
     /* outputs: fp32 workspaces */
@@ -119,6 +131,9 @@ typedef struct pa_decode_args {
                                     vector-ALU kernel; PA_KERNEL_MFMA: the matrix-core kernel
                                     (PA_ENOTSUP where it does not apply). Results agree
                                     within the documented tolerance either way. */
+    int32_t num_workers;         /* balanced splits only (partition_size == 0): number of
+                                    token ranges, typically the compute-unit count;
+                                    ignored otherwise */
 } pa_decode_args;
 
 #define PA_KERNEL_AUTO 0
@@ -155,7 +170,8 @@ typedef struct pa_reduce_args {
     const int32_t* seq_lens;     /* [num_seqs] */
     const int32_t* num_splits;   /* optional, as given to paged_attn_decode */
     int32_t num_seqs, num_heads, v_head_size;
-    int32_t partition_size;      /* as given to paged_attn_decode */
+    int32_t partition_size;      /* as given to paged_attn_decode; 0 = balanced splits:
+                                    merge every slot whose max_logits is not -inf */
     int32_t max_num_parts;
 } pa_reduce_args;
 

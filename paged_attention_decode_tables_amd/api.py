@@ -51,7 +51,7 @@ class DecodeArgs(ctypes.Structure):
         ("num_seqs", _i32), ("num_heads", _i32), ("num_kv_heads", _i32),
         ("head_size", _i32), ("v_head_size", _i32), ("block_size", _i32), ("x", _i32),
         ("partition_size", _i32), ("max_num_parts", _i32), ("max_seq_len", _i32),
-        ("dtype", _i32), ("kernel_hint", _i32),
+        ("dtype", _i32), ("kernel_hint", _i32), ("num_workers", _i32),
     ]
 
 
@@ -149,13 +149,14 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
                       max_seq_len: int, *, partition_size: int = 512,
                       num_splits: Optional[torch.Tensor] = None,
                       kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
-                      stream=None) -> None:
+                      num_workers: int = 0, stream=None) -> None:
     """Phase 1: per-split max logits, exp sums and normalised outputs.
 
     Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
     fp32; query [S, H, D]; key_cache [NB, Hkv, D/x, bs, x]; value_cache
     [NB, Hkv, Dv, bs]; block_tables [S, max_blocks] int32 (or the flat page
-    list when kv_indptr is given); seq_lens [S] int32.
+    list when kv_indptr is given); seq_lens [S] int32. partition_size=0 with
+    num_workers > 0 asks for balanced splits (equal token ranges).
     """
     lib = load_library()
     if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
@@ -190,6 +191,7 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     a.max_seq_len = int(max_seq_len)
     a.dtype = _dtype(query)
     a.kernel_hint = PA_KERNEL[kernel]
+    a.num_workers = num_workers
     _check(lib.paged_attn_decode(ctypes.byref(a), _stream(stream)))
 
 

@@ -77,7 +77,12 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if (a->max_num_parts < 1) return fail(PA_EINVAL, "paged_attn_decode: max_num_parts < 1");
     if (a->max_seq_len < 0) return fail(PA_EINVAL, "paged_attn_decode: max_seq_len < 0");
     int64_t parts;
-    if (!a->num_splits) {
+    const bool balanced = !a->num_splits && a->partition_size == 0;
+    if (balanced) {
+        if (a->num_workers < 1) return fail(PA_EINVAL, "paged_attn_decode: balanced splits need num_workers >= 1");
+        if (a->max_num_parts < 2) return fail(PA_EINVAL, "paged_attn_decode: balanced splits need max_num_parts >= 2");
+        parts = a->num_workers;  // grid dimension: one workgroup per token range
+    } else if (!a->num_splits) {
         if (a->partition_size < 64 || a->partition_size % 64)
             return fail(PA_EINVAL, "paged_attn_decode: partition_size %d is not a positive multiple of 64", a->partition_size);
         parts = cdiv(a->max_seq_len, a->partition_size);
@@ -140,6 +145,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     p.bs_shift = log2i(bs);
     p.partition_size = a->partition_size;
     p.max_num_parts = a->max_num_parts;
+    p.num_seqs = a->num_seqs;
+    p.num_workers = balanced ? a->num_workers : 0;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // latent rows: the value cache is the leading v_head_size columns of the key rows
@@ -149,6 +156,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size);
     if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok && !mla_ok)
         return fail(PA_ENOTSUP, "paged_attn_decode: no matrix-core kernel serves this problem");
+    if (balanced && (!mla_ok || a->kernel_hint == PA_KERNEL_VALU))
+        return fail(PA_ENOTSUP, "paged_attn_decode: balanced splits are built for the MLA matrix-core kernel only");
     if (a->kernel_hint != PA_KERNEL_VALU && mla_ok)
         return launched(pa::launch_decode_mla(p, a->dtype, a->num_seqs, (int)parts, st),
                         "paged_attn_decode (mla)");
@@ -165,8 +174,9 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
     if (!elem_size(a->out_dtype)) return fail(PA_EINVAL, "paged_attn_reduce: unknown out_dtype %d", a->out_dtype);
     if (a->num_seqs < 0 || a->num_heads < 1 || a->v_head_size < 1 || a->max_num_parts < 1)
         return fail(PA_EINVAL, "paged_attn_reduce: num_seqs >= 0, num_heads, v_head_size, max_num_parts >= 1 required");
-    if (!a->num_splits && (a->partition_size < 64 || a->partition_size % 64))
-        return fail(PA_EINVAL, "paged_attn_reduce: partition_size %d is not a positive multiple of 64", a->partition_size);
+    if (!a->num_splits && a->partition_size != 0 && (a->partition_size < 64 || a->partition_size % 64))
+        return fail(PA_EINVAL, "paged_attn_reduce: partition_size %d is neither 0 nor a positive multiple of 64",
+                    a->partition_size);
     if (a->num_seqs == 0) return PA_OK;
     if (!a->output || !a->tmp_output || !a->exp_sums || !a->max_logits || !a->seq_lens)
         return fail(PA_EINVAL, "paged_attn_reduce: a required pointer is NULL");

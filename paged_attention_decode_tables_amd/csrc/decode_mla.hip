@@ -1,36 +1,41 @@
 // decode_mla.hip -- phase 1 of split-KV decode for the MLA-style layout:
 // many query heads (G = 64 or 128) over one latent kv head whose cache row
-// holds both the key (all D values) and the value (its first Dv values),
-// page size 1. What is computed is the phase-1 algorithm of
+// holds both the key (all D = 576 values) and the value (its first Dv = 512
+// values), page size 1. What is computed is the phase-1 algorithm of
 // paged_attention_v2_triton.py (module docstring: per split, scores
 // q.K^T * scale, online softmax, weighted V; stores m, l and the normalised
 // split output); the value rows are the leading Dv columns of the key rows,
 // so every latent byte is read from HBM once per split.
 //
-// One 4-wave workgroup per (seq, kv head, head group of 64, split); wave w
-// owns query heads 16w .. 16w+15 of its group (lane = 16*g + r, head r of
-// the wave). At one wave per SIMD a wave keeps its heads' q (72 VGPRs) and
-// accumulators (128) in registers. The split is walked in 16-token chunks:
+// One workgroup per (seq, kv head, split) serves all G heads with NW = G/32
+// waves; wave w owns query heads 32w .. 32w+31 (lane = 32*hl + c32, head c32
+// of the wave). The 32x32 matrix-core tiles make every latent byte staged in
+// LDS feed 32 heads per read. The split is walked in 32-token chunks:
 //
-//   staging  the chunk's 16 latent rows are copied HBM -> LDS by direct
+//   staging  the chunk's 32 latent rows are copied HBM -> LDS by direct
 //            global-to-LDS loads (no registers hold data in flight) into a
-//            ring of NBUF chunk buffers, NBUF-1 chunks ahead. 16-byte piece
-//            pc of row t sits at column pc ^ ((t >> 1) & 7) of its LDS row,
-//            which spreads the 16 rows a QK operand read touches over
-//            distinct LDS banks. Page ids of the split are staged in LDS.
-//   QK       S^T[t][h] = sum_d K[t][d] Q[h][d]: v_mfma_f32_16x16x32 with the
-//            chunk's 16 tokens as rows (A operand: one 16-byte piece of a K
-//            row from LDS) and the wave's 16 heads as columns (B operand: q in
-//            registers). Lane (g, r) receives tokens 4g..4g+3 of head r.
-//   softmax  running max per head over the lane's 4 scores and the lanes r,
-//            r+16, r+32, r+48; probabilities rounded to the cache type.
-//   PV       O^T[dv][h] = sum_t V[t][dv] P[t][h]: v_mfma_f32_16x16x16 per 16
-//            value columns. The B operand (P[4g..4g+3][r]) is what the softmax
-//            left in lane (g, r); the A operand (V[4g..4g+3][16mt + r]) is a
-//            column of the token-major rows, read with ds_read_b64_tr_b16:
-//            within a 16-lane group, lane i receives value (i mod 4) of the
-//            8-byte chunks addressed by lanes i/4 + 4j, so lane a addresses
-//            row 4g + a/4, columns 16mt + 4(a%4) .. +3.
+//            ring of kMlaBuf chunk slots, kMlaBuf-1 chunks ahead. 16-byte
+//            piece pc of row t sits at column pc ^ swz(t), swz(t) =
+//            (t & 6) | ((t >> 3) & 1), which puts the rows one operand read
+//            touches on distinct LDS banks (rows two apart share a bank
+//            offset, 1152 B = 32 mod 64 dwords). Page ids are staged in LDS.
+//   QK       S^T[t][h] = sum_d K[t][d] Q[h][d] on v_mfma_f32_32x32x16: the 32
+//            tokens are the rows (A operand: 16 bytes of a latent row from
+//            LDS), the wave's 32 heads the columns (B operand: q in
+//            registers). A-row m reads token perm(m) = 16*(m>>4) +
+//            8*((m>>2)&1) + 4*((m>>3)&1) + (m&3); with the accumulator layout
+//            (lane 32*hl + c32, register r: row 8*(r>>2) + 4*hl + (r&3),
+//            column c32) lane (hl, c32) then holds head c32's scores of tokens
+//            16*(r>>3) + 8*hl + (r&7): tokens 8hl..8hl+7 and 16+8hl..16+8hl+7,
+//            i.e. the two P.V B operands of the chunk, with no data movement.
+//   softmax  running max per head over the lane's 16 scores and lane l^32;
+//            probabilities rounded to the cache type.
+//   PV       O^T[dv][h] = sum_t V[t][dv] P[t][h] on v_mfma_f32_32x32x16 per 32
+//            value columns and 16 tokens: A = V[t0..t0+7][dv] for the lane's
+//            column, two ds_read_b64_tr_b16 of the token-major rows (within
+//            a 16-lane group, lane i receives value (i mod 4) of the 8-byte
+//            pieces addressed by lanes i/4 + 4j, so lane a addresses row
+//            t0 + a/4, columns 4(a%4) .. +3 of its 16-column half).
 // Tokens past the split end are loaded from the last valid row (a real,
 // finite row) and masked: scores -inf, probabilities 0.
 #include <utility>
@@ -40,31 +45,21 @@
 namespace pa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <class E> struct MlaOps;
 template <> struct MlaOps<BF16> {
     typedef bf16x8 vec8;
-    typedef __bf16 vec4 __attribute__((ext_vector_type(4)));
-    static __device__ __forceinline__ f32x4 mma32(vec8 a, vec8 b, f32x4 c)
+    static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c)
     {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ f32x4 mma16(vec4 a, vec4 b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                        __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
 };
 template <> struct MlaOps<F16> {
     typedef f16x8 vec8;
-    typedef _Float16 vec4 __attribute__((ext_vector_type(4)));
-    static __device__ __forceinline__ f32x4 mma32(vec8 a, vec8 b, f32x4 c)
+    static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c)
     {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ f32x4 mma16(vec4 a, vec4 b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
 };
 
@@ -110,14 +105,20 @@ __device__ __forceinline__ s16x4 lds_read_tr16(uint32_t lds_addr)
 }
 
 // Waits until at most N LDS operations of this wave are outstanding. LDS
-// operations complete in issue order, so the read N places before the last
-// one issued has landed; its value is threaded through the wait so nothing
-// that uses it can be scheduled above it.
+// operations complete in issue order, so every read issued before the last
+// N has landed; the values are threaded through the wait so nothing that
+// uses them can be scheduled above it.
 template <int N, class V>
 __device__ __forceinline__ void lds_wait(V& v)
 {
     static_assert(N >= 0 && N <= 15, "lgkmcnt is a 4-bit field");
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+template <int N, class V>
+__device__ __forceinline__ void lds_wait(V& v0, V& v1)
+{
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is a 4-bit field");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v0), "+v"(v1) : "n"(N));
 }
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order
@@ -132,18 +133,17 @@ __device__ __forceinline__ void static_for(F&& f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// max of x over lanes l, l^16, l^32, l^48 (the four 16-lane rows)
-__device__ __forceinline__ float row_max4(float x)
+// max and sum of x over lanes l and l ^ 32
+__device__ __forceinline__ float half_max(float x)
 {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
-
-// LDS reads kept in flight ahead of their MFMAs (at most 15 can be
-// outstanding per wave)
-constexpr int kMlaReadAhead = 12;
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
 
 // Largest divisor of `ins` that is at most `nw` (waves issuing the copies).
 __host__ __device__ constexpr int loader_waves(int ins, int nw)
@@ -154,62 +154,82 @@ __host__ __device__ constexpr int loader_waves(int ins, int nw)
     return best;
 }
 
-constexpr int kMlaChunk = 16;    // tokens per chunk
-constexpr int kMlaBuf = 6;       // chunk buffers in the LDS ring
-constexpr int kMlaPageWin = 2048;  // page ids staged in LDS at a time
+// LDS column offset of the pieces of ring row t (XORed into the piece index)
+__host__ __device__ constexpr int mla_swz(int t) { return (t & 6) | ((t >> 3) & 1); }
 
-template <class E, int D, int DV, int NW>
-__global__ __launch_bounds__(64 * NW) void k_decode_mla(DecodeParams p)
+constexpr int kMlaChunk = 32;      // tokens per chunk
+constexpr int kMlaBuf = 4;         // chunk slots in the LDS ring
+constexpr int kMlaPageWin = 1024;  // page ids staged in LDS at a time
+constexpr int kMlaKAhead = 8;      // QK operand reads in flight ahead of their MFMAs
+constexpr int kMlaVAhead = 6;      // PV MFMAs whose operand reads are in flight ahead
+constexpr int kMlaHeadsPerWave = 32;
+
+// Wave-wide int64 inclusive prefix sum and max of an int.
+__device__ __forceinline__ int64_t wave_incl_sum_i64(int64_t v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t up = __shfl_up(v, d, kWave);
+        if (lane >= d) v += up;
+    }
+    return v;
+}
+__device__ __forceinline__ int wave_max_i32(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// BAL = false: one workgroup per (seq, kv head, split) of the fixed or
+// per-sequence split rule. BAL = true: balanced splits, one workgroup per
+// (token range, kv head).
+template <class E, int NW, bool BAL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_decode_mla(DecodeParams p)
 {
     using T = typename E::storage;
     using Ops = MlaOps<E>;
     using vec8 = typename Ops::vec8;
-    using vec4 = typename Ops::vec4;
+    constexpr int D = 576, DV = 512;
     constexpr int CT = kMlaChunk;
-    constexpr int PR = D * (int)sizeof(T) / 16;  // 16-byte pieces per latent row
-    constexpr int INS = CT * PR / 64;              // copy instructions per chunk
+    constexpr int PR = D * (int)sizeof(T) / 16;  // 16-byte pieces per latent row (72)
+    constexpr int RB = PR * 16;                   // bytes per latent row
+    constexpr int INS = CT * PR / 64;             // copy instructions per chunk
     constexpr int LW = loader_waves(INS, NW);     // waves that issue copies
     constexpr int IPW = INS / LW;                 // copies per loader wave per chunk
-    constexpr int KS = D / 32;                    // QK k-steps
-    constexpr int MT = DV / 16;                   // PV value-column tiles
+    constexpr int KS = D / 16;                    // QK k-steps
+    constexpr int MT = DV / 32;                   // PV value-column tiles
     constexpr int NB = kMlaBuf;
+    constexpr int HPW = kMlaHeadsPerWave;
     static_assert(CT * PR % 64 == 0, "chunk must be a whole number of copy instructions");
     static_assert(PR % 8 == 0, "row pieces must be a multiple of 8 for the swizzle");
-    static_assert(DV % 16 == 0 && DV <= D, "value columns are a prefix of the key row");
+    static_assert(KS % 4 == 0 && MT % 2 == 0, "tiling");
+    static_assert(IPW * (NB - 2) <= 63, "vmcnt is a 6-bit field");
 
     __shared__ u32x4 ring[NB][CT * PR];
     __shared__ int32_t page_lds[kMlaPageWin];
+    __shared__ int rerun_flag;
 
-    // grid (seq, kv head x head group, split): a workgroup serves 16*NW of
-    // the kv head's G query heads; the head groups of one split read the
-    // same latent rows, which the second reader finds in L2.
-    const int ngroups = p.group / (16 * NW);
-    const int s = blockIdx.x, kvh = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, part = blockIdx.z;
+    const int ngroups = p.group / (HPW * NW);
+    const int kvh = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
     const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-    const int h = kvh * p.group + hg * 16 * NW + wave * 16 + r;
+    const int lane = threadIdx.x & 63, c32 = lane & 31, hl = lane >> 5;
+    const int h0 = kvh * p.group + hg * HPW * NW;  // first head of the workgroup
+    const int h = h0 + wave * HPW + c32;
 
-    const int L = p.seq_lens[s];
-    const int64_t len64 = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
-    const int64_t start64 = (int64_t)part * len64;
-    if (start64 >= (int64_t)L) {
-        if (g == 0) {
-            const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
-            p.max_logits[mloff] = -INFINITY;
-            p.exp_sums[mloff] = 0.0f;
-        }
-        return;
-    }
-    const int start = (int)start64;
-    const int end = (int)((int64_t)L < start64 + len64 ? (int64_t)L : start64 + len64);
+    // One split (or balanced piece): tokens [start, end) of sequence s, its
+    // statistics and normalised output stored in split slot `part`.
+    auto piece = [&](const int s, const int part, const int start, const int end) {
+    __syncthreads();  // the previous piece's LDS reads are done
     const int nc = (end - start + CT - 1) / CT;
 
-    // B operand of QK: lane (g, r) holds q[h][32*ks + 8g .. +8]
+    // B operand of QK: lane (hl, c32) holds q[h][16*ks + 8*hl .. +8]
     vec8 qv[KS];
     {
-        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh + g * 8;
+        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh + 8 * hl;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(vec8, load16(q + ks * 32));
+        for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(vec8, load16(q + ks * 16));
     }
 
     const int32_t* row = page_row(p.pl, s);
@@ -241,106 +261,127 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mla(DecodeParams p)
             const int ins = wave * IPW + j;
             const int piece = ins * 64 + lane;
             const int t = piece / PR, pc = piece % PR;
-            const T* src = kc + (int64_t)pg[j] * p.k_sb + (int64_t)((pc ^ ((t >> 1) & 7)) * 8);
+            const T* src = kc + (int64_t)pg[j] * p.k_sb + (int64_t)((pc ^ mla_swz(t)) * 8);
             lds_copy16(src, dst + ins * 64);
         }
     };
 
-    // Lazy rescaling: probabilities are taken against a reference max mref
-    // that only moves when a chunk's max exceeds it by more than 2^8, so the
-    // 128 accumulator values are rescaled rarely (p <= 256 meanwhile, well
-    // inside fp32 / bf16 range). The true max is kept apart and (m, l) are
-    // brought to it at the end, so the stored statistics are the exact
-    // max logit and sum of exp(z - max).
-    constexpr float kLazy = 8.0f;
-    float mref = -INFINITY;  // reference max of head r (base 2)
-    float mtrue = -INFINITY; // true running max of head r (base 2)
+    // Fixed reference: probabilities are taken against mref, head c32's max
+    // over the split's first chunk, and never rescaled, so the 256
+    // accumulators are only ever touched by MFMAs. While no later score
+    // passes mref by more than kHeadroom (base 2), p <= 2^kHeadroom and the
+    // fp32 sums stay finite for value magnitudes below 2^(126 - kHeadroom -
+    // log2 tokens). A split where some score does pass it is run a second
+    // time with mref = the split's true max (known after the first pass), so
+    // every p <= 1. The true max is kept apart and (m, l) are brought to it
+    // at the end, so the stored statistics are the exact max logit and sum
+    // of exp(z - max).
+    constexpr float kHeadroom = 64.0f;
+    float mref = -INFINITY;  // reference max of head c32 (base 2)
+    float mtrue = -INFINITY; // true running max of head c32 (base 2)
     float l = 0.0f;          // this lane's share of sum_t exp2(z_t - mref)
-    f32x4 acc[MT];
+    bool over = false;       // a score of head c32 passed mref + kHeadroom
+    f32x16 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
 
-    // scores of chunk c for this lane's four tokens (base 2, masked past
-    // the split end) and their max over the wave's tokens for head r
-    auto scores = [&](int c, float (&sc)[4]) -> float {
+    // QK operand addresses: A-row c32 reads ring row perm(c32); piece
+    // 2*ks + hl of it sits at column 8*(ks>>2) + ((2*(ks&3) + hl) ^ swz), i.e.
+    // four base addresses (ks mod 4) plus 128*(ks/4) as the immediate.
+    const int trow = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
+    const int ksw = mla_swz(trow);
+    uint32_t kb_lane[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) kb_lane[q4] = trow * RB + 16 * ((2 * q4 + hl) ^ ksw);
+    // PV operand addresses: read (kk, rd) of value tile mt covers rows
+    // t = 16kk + 8hl + 4rd + a/4 (a = lane & 15) and value columns
+    // 32mt + 16*g16 + 4*(a&3) .. +3 (g16 = (lane >> 4) & 1): piece
+    // 4mt + 2*g16 + ((a&3) >> 1) at column 4*(mt ^ rd) + low, low =
+    // 2*(g16 ^ (a >> 3)) + (((a & 3) >> 1) ^ hl), 8 bytes in when a is odd.
+    // One lane base plus kk*16*RB + rd*4*RB + 64*(mt ^ rd) as the immediate.
+    uint32_t vb_lane;
+    {
+        const int a = lane & 15, g16 = (lane >> 4) & 1;
+        const int low = 2 * (g16 ^ (a >> 3)) + (((a & 3) >> 1) ^ hl);
+        vb_lane = (8 * hl + (a >> 2)) * RB + 16 * low + 8 * (a & 1);
+    }
+
+    // scores of chunk c for this lane's 16 tokens (base 2, masked past the
+    // split end) and their max over both lane halves (head c32). One
+    // accumulator: a second does not fit beside q and the 256 output
+    // accumulators without spilling.
+    auto scores = [&](int c, float (&sc)[16]) -> float {
         const int c0 = start + CT * c;
-        const u32x4* buf = &ring[c % NB][0];
-        // ---- scores. Piece (4ks + g) of row r sits at column (4ks + g) ^ rsw;
-        // with rsw = 4*b + a' that is 4*(ks ^ b) + (g ^ a'), i.e. two base
-        // addresses (even and odd k-steps) plus 128*(ks/2) as the immediate.
-        // The 18 reads stream kMlaReadAhead ahead of their MFMAs, which
-        // alternate between two accumulators to keep the matrix core fed.
-        const uint32_t bufa = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)buf);
-        const int rsw = (r >> 1) & 7;
-        const uint32_t kbase = bufa + r * PR * 16 + 16 * (g ^ (rsw & 3));
-        const uint32_t kb0 = kbase + 64 * (rsw >> 2);        // even k-steps
-        const uint32_t kb1 = kbase + 64 * ((rsw >> 2) ^ 1);  // odd k-steps
-        constexpr int RA = kMlaReadAhead < KS ? kMlaReadAhead : KS;
+        const uint32_t bufa =
+            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+        constexpr int RA = kMlaKAhead < KS ? kMlaKAhead : KS;
         u32x4 kr[KS];
         auto kread = [&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
-            kr[ks] = lds_read_b128<128 * (ks >> 1)>((ks & 1) ? kb1 : kb0);
+            kr[ks] = lds_read_b128<128 * (ks >> 2)>(bufa + kb_lane[ks & 3]);
         };
         static_for<RA>(kread);
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        f32x16 sacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
         static_for<KS>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             constexpr int issued = (i + RA < KS) ? i + RA : KS;
             lds_wait<issued - i - 1>(kr[i]);
-            if constexpr (i & 1)
-                s1 = Ops::mma32(__builtin_bit_cast(vec8, kr[i]), qv[i], s1);
-            else
-                s0 = Ops::mma32(__builtin_bit_cast(vec8, kr[i]), qv[i], s0);
+            sacc = Ops::mma(__builtin_bit_cast(vec8, kr[i]), qv[i], sacc);
             if constexpr (i + RA < KS) kread(std::integral_constant<int, i + RA>{});
             __builtin_amdgcn_sched_barrier(0);  // keep wait -> MFMA -> next read in order
         });
-        const f32x4 sacc = s0 + s1;
-        const int t0 = c0 + 4 * g;
+        float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = (t0 + i < end) ? sacc[i] * p.scale_log2 : -INFINITY;
-        return row_max4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        for (int r = 0; r < 16; ++r) {
+            const int t = c0 + 16 * (r >> 3) + 8 * hl + (r & 7);
+            sc[r] = t < end ? sacc[r] * p.scale_log2 : -INFINITY;
+            mloc = fmaxf(mloc, sc[r]);
+        }
+        return half_max(mloc);
     };
 
     // probabilities of chunk c against mref, and their weighted value rows
-    auto weigh = [&](int c, const float (&sc)[4]) {
-        const u32x4* buf = &ring[c % NB][0];
-        // Value tile mt of this lane lives in piece 2mt + c1 (c1 = (r & 3) >> 1)
-        // of row vrow, at column (2mt + c1) ^ vsw = 2*(mt ^ (vsw >> 1)) +
-        // (c1 ^ (vsw & 1)): four base addresses (mt mod 4) plus 128*(mt/4)
-        // as the immediate. The first reads are issued before the
-        // probabilities are formed, so their latency overlaps that work.
-        const uint32_t bufa = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)buf);
-        const int vrow = 4 * g + (r >> 2);
-        const int vsw = (vrow >> 1) & 7;
-        const uint32_t vbase = bufa + vrow * PR * 16 + (r & 1) * 8 + 16 * ((((r & 3) >> 1)) ^ (vsw & 1));
-        const int vx = vsw >> 1;
-        const uint32_t vb4[4] = {vbase + 32 * (0 ^ vx), vbase + 32 * (1 ^ vx), vbase + 32 * (2 ^ vx),
-                                 vbase + 32 * (3 ^ vx)};
-        constexpr int RA = kMlaReadAhead < MT ? kMlaReadAhead : MT;
-        s16x4 vr[MT];
-        auto vread = [&](auto mtc) {
-            constexpr int mt = decltype(mtc)::value;
-            vr[mt] = lds_read_tr16<128 * (mt >> 2)>(vb4[mt & 3]);
+    auto weigh = [&](int c, const float (&sc)[16]) {
+        const uint32_t vbase =
+            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]) + vb_lane;
+        // MFMA j (0 .. 2*MT-1) is (kk = j / MT, mt = j % MT): all tiles of the
+        // first 16 tokens, then of the second, so consecutive MFMAs update
+        // different accumulators
+        constexpr int NJ = 2 * MT;
+        constexpr int RA = kMlaVAhead < NJ ? kMlaVAhead : NJ;
+        s16x4 vr[NJ][2];
+        auto vread = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int kk = j / MT, mt = j % MT;
+            vr[j][0] = lds_read_tr16<kk * 16 * RB + 64 * mt>(vbase);
+            vr[j][1] = lds_read_tr16<kk * 16 * RB + 4 * RB + 64 * (mt ^ 1)>(vbase);
         };
         static_for<RA>(vread);
         __builtin_amdgcn_sched_barrier(0);
 
-        vec4 pv;
+        vec8 pv[2];
         float psum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const T e = (T)fast_exp2(sc[i] - mref);
-            pv[i] = e;
+        for (int r = 0; r < 16; ++r) {
+            const T e = (T)fast_exp2(sc[r] - mref);
+            pv[r >> 3][r & 7] = e;
             psum += (float)e;
         }
         l += psum;
-        // O^T[dv][h] += V^T[dv][t] P[t][h], one value tile per MFMA
-        static_for<MT>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            constexpr int issued = (i + RA < MT) ? i + RA : MT;
-            lds_wait<issued - i - 1>(vr[i]);
-            acc[i] = Ops::mma16(__builtin_bit_cast(vec4, vr[i]), pv, acc[i]);
-            if constexpr (i + RA < MT) vread(std::integral_constant<int, i + RA>{});
+        static_for<NJ>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int issued = (j + RA < NJ) ? j + RA : NJ;
+            lds_wait<2 * (issued - j - 1)>(vr[j][0], vr[j][1]);
+            const u32x4 a = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][0], vr[j][0], 0, 1)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][0], vr[j][0], 2, 3)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][1], vr[j][1], 0, 1)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][1], vr[j][1], 2, 3))};
+            acc[j % MT] = Ops::mma(__builtin_bit_cast(vec8, a), pv[j / MT], acc[j % MT]);
+            if constexpr (j + RA < NJ) vread(std::integral_constant<int, j + RA>{});
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -351,10 +392,6 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mla(DecodeParams p)
     // (all of them in the last NB-2 chunks); the barrier then makes every
     // wave's copies visible and frees the slot chunk c-1 used, which the
     // copy of chunk c+NB-1 reuses.
-    // q is in registers before the ring starts, so no wait inside the loop
-    // has to cover its loads
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    for (int c = 0; c < NB - 1 && c < nc; ++c) issue(c);
     // chunk c's copies are visible to every wave; chunk c+NB-1 is issued
     auto advance = [&](int c) {
         if (c + NB - 2 < nc)
@@ -379,49 +416,171 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mla(DecodeParams p)
             issue(cn);
         }
     };
-
-    // The steady-state loop touches the accumulators only through MFMAs, so
-    // they stay in accumulation registers across chunks; a chunk whose max
-    // passes mref + kLazy leaves it, the accumulators are rescaled here
-    // (every wave passes one barrier per chunk on either path), and the
-    // loop resumes after that chunk.
-    int c = 0;
-    while (c < nc) {
-        float sc[4];
-        float mloc = -INFINITY;
-        bool rescale = false;
-        for (; c < nc; ++c) {
+    // one pass over the split
+    auto run = [&]() {
+        // q (first pass) or the previous pass's copies are complete, so no
+        // wait inside the loop has to cover them
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        for (int c = 0; c < NB - 1 && c < nc; ++c) issue(c);
+        for (int c = 0; c < nc; ++c) {
+            float sc[16];
             advance(c);
-            mloc = scores(c, sc);
+            const float mloc = scores(c, sc);
             mtrue = fmaxf(mtrue, mloc);
-            if (__builtin_amdgcn_ballot_w64(mloc > mref + kLazy)) {
-                rescale = true;
-                break;
-            }
+            mref = mref == -INFINITY ? mloc : mref;
+            over |= mloc > mref + kHeadroom;
             weigh(c, sc);
         }
-        if (!rescale) break;
-        const float mn = fmaxf(mref, mloc);
-        const float alpha = fast_exp2(mref - mn);  // 0 on the first chunk
-        mref = mn;
-        l *= alpha;
+    };
+
+    if (threadIdx.x == 0) rerun_flag = 0;
+    run();
+    if (over) rerun_flag = 1;  // benign race: every writer stores 1
+    __syncthreads();
+    if (rerun_flag) {  // uniform across the workgroup
+        mref = mtrue;
+        l = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-        weigh(c, sc);
-        ++c;
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
+        if (wbase != start) {
+            wbase = start;
+            stage_pages(wbase);
+        }
+        __syncthreads();  // every wave is done with the ring and the page window
+        run();
     }
 
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    l = half_sum(l);
     const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
-    if (g == 0) {
+    if (hl == 0) {
         p.max_logits[mloff] = mtrue * kLn2;
         p.exp_sums[mloff] = l * fast_exp2(mref - mtrue);
     }
+    // lane (hl, c32), register 4i + j of tile mt holds value column
+    // 32mt + 8i + 4hl + j of head c32
     const float inv = 1.0f / l;
-    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp + 4 * g;
+    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp + 4 * hl;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(out + 16 * mt) = acc[mt] * inv;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(out + 32 * mt + 8 * i) =
+                f32x4{acc[mt][4 * i], acc[mt][4 * i + 1], acc[mt][4 * i + 2], acc[mt][4 * i + 3]} * inv;
+    };
+
+    if constexpr (!BAL) {
+        const int s = blockIdx.x, part = blockIdx.z;
+        const int L = p.seq_lens[s];
+        const int64_t len64 = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+        const int64_t start64 = (int64_t)part * len64;
+        if (start64 >= (int64_t)L) {  // empty split: the page's early exit
+            if (hl == 0) {
+                const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
+                p.max_logits[mloff] = -INFINITY;
+                p.exp_sums[mloff] = 0.0f;
+            }
+            return;
+        }
+        piece(s, part, (int)start64, (int)((int64_t)L < start64 + len64 ? (int64_t)L : start64 + len64));
+        return;
+    }
+
+    // ---- balanced splits: worker w = blockIdx.x takes tokens [w*U, (w+1)*U)
+    // of all sequences concatenated (lengths <= 0 count as 0)
+    constexpr int BT = 64 * NW;
+    constexpr int GH = HPW * NW;  // heads of this workgroup
+    __shared__ int64_t bal_w64[NW];
+    __shared__ int bal_w32[NW];
+    __shared__ int64_t bal_off[BT];
+    __shared__ int bal_len[BT];
+    __shared__ int bal_first, bal_last;
+    const int tid = threadIdx.x;
+    const int w = blockIdx.x;
+    // m = -inf, l = 0 in slots [k0, max_num_parts) of sequence s, all heads
+    // here (all threads of the workgroup together)
+    auto mark_empty = [&](int s, int k0) {
+        for (int e = tid; e < GH * (p.max_num_parts - k0); e += BT) {
+            const int64_t off = (int64_t)s * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + k0 + e / GH;
+            p.max_logits[off] = -INFINITY;
+            p.exp_sums[off] = 0.0f;
+        }
+    };
+
+    int64_t tsum = 0;
+    int tmax = 0;
+    for (int i = tid; i < p.num_seqs; i += BT) {
+        const int Li = max(p.seq_lens[i], 0);
+        tsum += Li;
+        tmax = max(tmax, Li);
+        if (w == 0 && Li == 0) {  // worker 0 covers the empty sequences, one thread each
+            for (int e = 0; e < GH * p.max_num_parts; ++e) {
+                const int64_t off = (int64_t)i * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + e / GH;
+                p.max_logits[off] = -INFINITY;
+                p.exp_sums[off] = 0.0f;
+            }
+        }
+    }
+    tsum = __shfl(wave_incl_sum_i64(tsum, lane), kWave - 1, kWave);
+    tmax = wave_max_i32(tmax);
+    if (lane == 0) {
+        bal_w64[wave] = tsum;
+        bal_w32[wave] = tmax;
+    }
+    __syncthreads();
+    int64_t total_tokens = 0;
+    int maxL = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        total_tokens += bal_w64[i];
+        maxL = max(maxL, bal_w32[i]);
+    }
+    __syncthreads();  // bal_w64 is reused by the scan below
+    const int64_t W = p.num_workers;
+    int64_t U = max((total_tokens + W - 1) / W, ((int64_t)maxL + p.max_num_parts - 2) / (p.max_num_parts - 1));
+    U = max((U + 31) & ~int64_t(31), int64_t(32));
+    if (total_tokens == 0 || (int64_t)w * U >= total_tokens) return;
+    const int64_t r0 = (int64_t)w * U, r1 = min(r0 + U, total_tokens);
+
+    // sequences in batches of BT: block scan of the lengths gives their
+    // offsets; the ones meeting [r0, r1) form a contiguous run
+    int64_t base = 0;
+    for (int b0 = 0; b0 < p.num_seqs && base < r1; b0 += BT) {
+        const int i = b0 + tid;
+        const int Li = i < p.num_seqs ? max(p.seq_lens[i], 0) : 0;
+        const int64_t inc = wave_incl_sum_i64(Li, lane);
+        if (lane == kWave - 1) bal_w64[wave] = inc;
+        if (tid == 0) {
+            bal_first = BT;
+            bal_last = -1;
+        }
+        __syncthreads();
+        int64_t off = base + inc - Li, total = 0;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < wave) off += bal_w64[j];
+            total += bal_w64[j];
+        }
+        bal_off[tid] = off;
+        bal_len[tid] = Li;
+        if (Li > 0 && off < r1 && off + Li > r0) {
+            atomicMin(&bal_first, tid);
+            atomicMax(&bal_last, tid);
+        }
+        __syncthreads();
+        const int first = bal_first, last = bal_last;
+        for (int j = first; j <= last; ++j) {
+            const int64_t so = bal_off[j];
+            const int Ls = bal_len[j];
+            if (Ls <= 0) continue;
+            const int k = (int)(w - so / U);
+            piece(b0 + j, k, (int)(max(r0, so) - so), (int)(min(r1, so + Ls) - so));
+            if ((so + Ls - 1) / U == w) mark_empty(b0 + j, k + 1);  // this worker has the last piece
+        }
+        base += total;
+        __syncthreads();  // bal_* are rewritten by the next batch
+    }
 }
 
 bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size)
@@ -430,16 +589,24 @@ bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size)
            (group == 64 || group == 128);
 }
 
-// One 4-wave workgroup (64 query heads) per head group: at 1 wave per SIMD a
-// wave holds its 16 heads' q (72 VGPRs) and accumulators (128) with room to
-// spare; with 8 waves (2 per SIMD) the same state spills.
-constexpr int kMlaWaves = 4;
+template <class E, int NW>
+static void launch_mla_nw(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
+{
+    if (p.num_workers > 0)
+        hipLaunchKernelGGL((k_decode_mla<E, NW, true>), dim3(p.num_workers, p.num_kv_heads, 1), dim3(64 * NW),
+                           0, st, p);
+    else
+        hipLaunchKernelGGL((k_decode_mla<E, NW, false>), dim3(num_seqs, p.num_kv_heads, parts), dim3(64 * NW),
+                           0, st, p);
+}
 
 template <class E>
 static hipError_t launch_mla_e(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    dim3 grid(num_seqs, p.num_kv_heads * (p.group / (16 * kMlaWaves)), parts);
-    hipLaunchKernelGGL((k_decode_mla<E, 576, 512, kMlaWaves>), grid, dim3(64 * kMlaWaves), 0, st, p);
+    if (p.group == 128)
+        launch_mla_nw<E, 4>(p, num_seqs, parts, st);
+    else
+        launch_mla_nw<E, 2>(p, num_seqs, parts, st);
     return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@ struct DecodeParams {
     int num_heads, num_kv_heads, group;
     int bs_shift;
     int partition_size, max_num_parts;
+    int num_seqs;
+    int num_workers;  // > 0: balanced splits (grid z = workers), see pagedattn.h
 };
 
 struct ReduceParams {

@@ -31,11 +31,17 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
     const int64_t obase = (int64_t)s * p.out_ss + (int64_t)h * p.out_sh + 4 * col;
 
     const int L = p.seq_lens[s];
+    // balanced splits (partition_size 0): every slot, empty ones skipped below
+    const bool balanced = !p.num_splits && p.partition_size == 0;
     int64_t n = 0;
     if (L > 0) {
-        const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
-        n = ((int64_t)L + len - 1) / len;
-        n = n < p.max_num_parts ? n : p.max_num_parts;
+        if (balanced) {
+            n = p.max_num_parts;
+        } else {
+            const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+            n = ((int64_t)L + len - 1) / len;
+            n = n < p.max_num_parts ? n : p.max_num_parts;
+        }
     }
     if (n == 0) {
         if (grp == 0)
@@ -54,29 +60,48 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
     for (int64_t q0 = grp; q0 < n; q0 += (int64_t)NG * kRedBatch) {
         f32x4 rows[kRedBatch];
         float mv[kRedBatch], lv[kRedBatch];
+        if (!balanced) {  // every split below n is live: all loads at once
 #pragma unroll
-        for (int r = 0; r < kRedBatch; ++r) {
-            const int64_t q = q0 + (int64_t)r * NG;
-            if (q < n) {
-                rows[r] = *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp);
-                mv[r] = ml[q];
-                lv[r] = es[q];
-            } else {
-                rows[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mv[r] = -INFINITY;
-                lv[r] = 0.0f;
+            for (int r = 0; r < kRedBatch; ++r) {
+                const int64_t q = q0 + (int64_t)r * NG;
+                if (q < n) {
+                    rows[r] = *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp);
+                    mv[r] = ml[q];
+                    lv[r] = es[q];
+                } else {
+                    rows[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    mv[r] = -INFINITY;
+                    lv[r] = 0.0f;
+                }
+            }
+        } else {  // most slots are empty: statistics first, rows of live slots only
+#pragma unroll
+            for (int r = 0; r < kRedBatch; ++r) {
+                const int64_t q = q0 + (int64_t)r * NG;
+                mv[r] = q < n ? ml[q] : -INFINITY;
+                lv[r] = q < n ? es[q] : 0.0f;
+            }
+#pragma unroll
+            for (int r = 0; r < kRedBatch; ++r) {
+                const int64_t q = q0 + (int64_t)r * NG;
+                rows[r] = mv[r] != -INFINITY ? *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp)
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
         float mb = M;
 #pragma unroll
         for (int r = 0; r < kRedBatch; ++r) mb = fmaxf(mb, mv[r]);
-        const float f = fast_exp2((M - mb) * kLog2e);
+        // mb = -inf: nothing live yet (acc, W are 0); avoids exp2(-inf + inf)
+        const float f = mb == -INFINITY ? 1.0f : fast_exp2((M - mb) * kLog2e);
         acc *= f;
         W *= f;
 #pragma unroll
         for (int r = 0; r < kRedBatch; ++r) {
-            const float w = fast_exp2((mv[r] - mb) * kLog2e) * lv[r];
-            acc += w * rows[r];
+            // an empty split (m = -inf) adds nothing; its row was never
+            // written, so it is dropped by a select, not a multiply
+            const bool live = mv[r] != -INFINITY;
+            const float w = live ? fast_exp2((mv[r] - mb) * kLog2e) * lv[r] : 0.0f;
+            acc += live ? w * rows[r] : f32x4{0.f, 0.f, 0.f, 0.f};
             W += w;
         }
         M = mb;
@@ -96,11 +121,11 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
     float Wt = 0.0f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        const float f = fast_exp2((m_lds[g] - Mt) * kLog2e);  // empty groups: exp2(-inf) = 0
+        const float f = m_lds[g] == -INFINITY ? 0.0f : fast_exp2((m_lds[g] - Mt) * kLog2e);
         a += f * acc_lds[g][col];
         Wt += f * w_lds[g];
     }
-    const float inv = 1.0f / Wt;
+    const float inv = Wt > 0.0f ? 1.0f / Wt : 0.0f;  // no live split: zero row
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, a[i] * inv);
 }

@@ -382,3 +382,112 @@ def test_full_config(orc, cfg, seqs):
     check_output(w, orc, out, seqs=seqs)
     check_partials(w, orc, tmp, ml, es, num_splits=ns, seqs=seqs if seqs is not None else None)
     assert torch.isfinite(out).all()
+
+
+# ---------------------------------------------------------------------------
+# balanced splits (partition_size 0): equal token ranges over the batch
+# ---------------------------------------------------------------------------
+def balanced_pieces(lens, workers, max_parts):
+    """Per sequence, the (slot, start, end) pieces of the balanced split rule
+    stated in pagedattn.h."""
+    L = [max(0, int(x)) for x in lens]
+    T, maxL = sum(L), max(L + [0])
+    U = max(-(-T // workers), -(-maxL // (max_parts - 1)))
+    U = max(-(-U // 32) * 32, 32)
+    out, off = [], 0
+    for Ls in L:
+        pieces = []
+        if Ls > 0:
+            w0, w1 = off // U, (off + Ls - 1) // U
+            for w in range(w0, w1 + 1):
+                pieces.append((w - w0, max(w * U, off) - off, min((w + 1) * U, off + Ls) - off))
+        out.append(pieces)
+        off += Ls
+    return out
+
+
+def run_balanced(w, workers, max_parts, out_dtype=torch.float32):
+    g = w.to(DEV)
+    tmp, ml, es = workspace_nan(w, max_parts)
+    cu = torch.zeros(w.num_seqs + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(w.seq_lens.clamp(min=0), 0)
+    indptr = cu.to(DEV)
+    flat = torch.full((max(int(cu[-1]), 1),), -1, dtype=torch.int32, device=DEV)
+    pad.build_page_indices(flat, g.block_tables, indptr)
+    pad.paged_attn_decode(tmp, es, ml, g.query, g.key_cache, g.value_cache, flat, g.seq_lens,
+                          w.scale, w.max_seq_len, partition_size=0, num_workers=workers,
+                          kv_indptr=indptr)
+    out = torch.full((w.num_seqs, w.num_heads, w.v_head_size), float("nan"), dtype=out_dtype,
+                     device=DEV)
+    pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens, partition_size=0)
+    torch.cuda.synchronize()
+    return out.cpu(), tmp.cpu(), ml.cpu(), es.cpu()
+
+
+def workspace_nan(w, max_parts):
+    S, H, Dv = w.num_seqs, w.num_heads, w.v_head_size
+    return (torch.full((S, H, max_parts, Dv), float("nan"), device=DEV),
+            torch.full((S, H, max_parts), float("nan"), device=DEV),
+            torch.full((S, H, max_parts), float("nan"), device=DEV))
+
+
+def check_balanced_pieces(w, orc, tmp, ml, es, workers, max_parts):
+    """Each piece's statistics and normalised row against the oracle on that
+    token range alone; slots past a sequence's pieces marked empty."""
+    K, V = np64(w.key_cache), np64(w.value_cache)
+    pieces = balanced_pieces(w.seq_lens.tolist(), workers, max_parts)
+    for s, ps in enumerate(pieces):
+        for slot, a, b in ps:
+            P = -(-(b - a) // 64) * 64
+            t_o, m_o, l_o = orc.partials(np64(w.query[s:s + 1]), K, V,
+                                         w.block_tables[s:s + 1, a:b].numpy(),
+                                         np.array([b - a], np.int32), w.scale, 1, partition_size=P)
+            m_g, l_g, t_g = ml[s, :, slot].double().numpy(), es[s, :, slot].double().numpy(), tmp[s, :, slot].double().numpy()
+            assert np.all(np.abs(m_g - m_o[0, :, 0]) <= 2e-4 + 1e-5 * np.abs(m_o[0, :, 0])), (s, slot)
+            assert np.all(np.abs(l_g - l_o[0, :, 0]) <= 4e-3 * np.abs(l_o[0, :, 0])), (s, slot)
+            assert np.abs(t_g - t_o[0, :, 0]).max() <= 1e-2, (s, slot)
+        for slot in range(len(ps), max_parts):
+            assert torch.all(ml[s, :, slot] == -math.inf) and torch.all(es[s, :, slot] == 0), (s, slot)
+
+
+BAL_CASES = [
+    # name, heads, lens, workers, max_parts
+    ("g128_w1", 128, [1, 15, 16, 17, 100, 513, 1030, 0, 700, 33], 1, 8),
+    ("g128_w5", 128, [1, 15, 16, 17, 100, 513, 1030, 0, 700, 33], 5, 8),
+    ("g128_w64_p2", 128, [1, 15, 16, 17, 100, 513, 1030, 0, 700, 33], 64, 2),
+    ("g64_w3", 64, [64, 65, 300, 7], 3, 4),
+    ("g128_one_long", 128, [2100], 7, 16),
+]
+
+
+@pytest.mark.parametrize("case", BAL_CASES, ids=[c[0] for c in BAL_CASES])
+def test_decode_mla_balanced(orc, case):
+    name, H, lens, workers, max_parts = case
+    say(f"decode mla balanced {name}")
+    w = workloads.mla_custom(seed=zlib.crc32(name.encode()) % 10007, seq_lens=lens, num_heads=H,
+                             poison=True)
+    out, tmp, ml, es = run_balanced(w, workers, max_parts)
+    check_balanced_pieces(w, orc, tmp, ml, es, workers, max_parts)
+    check_output(w, orc, out)
+
+
+def test_decode_mla_balanced_all_empty():
+    say("decode mla balanced, all sequences empty")
+    w = workloads.mla_custom(seed=5, seq_lens=[0, 0, 0], num_heads=128, max_blocks=4, poison=True)
+    out, tmp, ml, es = run_balanced(w, 4, 3)
+    assert torch.all(out == 0)
+    assert torch.all(ml == -math.inf) and torch.all(es == 0)
+
+
+def test_decode_mla_balanced_config5(orc):
+    """The MLA workload as the benchmark runs it (256 workers): final output
+    on a sample of sequences, slots marked as the rule says."""
+    say("decode mla balanced config5")
+    w = workloads.config(5, poison=True)
+    max_parts = -(-w.max_seq_len // 512)
+    out, tmp, ml, es = run_balanced(w, 256, max_parts)
+    pieces = balanced_pieces(w.seq_lens.tolist(), 256, max_parts)
+    for s, ps in enumerate(pieces):
+        assert torch.all(torch.isfinite(ml[s, :, :len(ps)]))
+        assert torch.all(ml[s, :, len(ps):] == -math.inf)
+    check_output(subset(w, [0, 17, 63]), orc, out[[0, 17, 63]])
