@@ -113,6 +113,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
         return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
     if (parts > kMaxGridYZ || a->num_heads > kMaxGridYZ)
         return fail(PA_ENOTSUP, "paged_attn_decode: partitions and num_heads must be <= %d", kMaxGridYZ);
+    if ((int64_t)a->num_seqs * a->num_heads > 0x7fffffff)
+        return fail(PA_ENOTSUP, "paged_attn_decode: num_seqs * num_heads must be < 2^31");
     const int D = a->head_size, Dv = a->v_head_size, group = a->num_heads / a->num_kv_heads;
     if (!pa::decode_valu_supported(a->dtype, D, Dv))
         return fail(PA_ENOTSUP, "paged_attn_decode: (head_size, v_head_size) = (%d, %d) is not built", D, Dv);

@@ -84,11 +84,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     constexpr int MT = DV / 16;  // PV value-row tiles
     constexpr int W = kMfmaWaves;
 
-    // grid (seq, kv head, split): workgroups are dealt to the XCDs round-robin
-    // by linear id, so putting the sequence first spreads the work of every
-    // split index (split 0 is never empty, high splits often are) over all
-    // XCDs instead of piling the non-empty splits onto a few of them.
-    const int s = blockIdx.x, kvh = blockIdx.y, part = blockIdx.z;
+    // grid (kv head + Hkv * seq, split): workgroups are dealt to the XCDs
+    // round-robin by linear id. With the kv head fastest, every XCD gets an
+    // equal share of every sequence's tokens (Hkv a multiple of 8: exactly
+    // one kv head's), whatever the length mix; the split index last keeps
+    // each split index's work (split 0 is never empty, high splits often
+    // are) spread over all XCDs.
+    const int kvh = blockIdx.x % p.num_kv_heads, s = blockIdx.x / p.num_kv_heads, part = blockIdx.y;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int G = p.group;
@@ -364,7 +366,7 @@ bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
 template <class E, int D>
 static hipError_t launch_mfma_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    dim3 grid(num_seqs, p.num_kv_heads, parts), block(kWave * kMfmaWaves);
+    dim3 grid(num_seqs * p.num_kv_heads, parts), block(kWave * kMfmaWaves);
     switch (p.bs_shift) {
     case 4: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 16>), grid, block, 0, st, p); break;
     case 5: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 32>), grid, block, 0, st, p); break;

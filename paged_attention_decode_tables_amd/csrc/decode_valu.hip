@@ -33,9 +33,14 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
     __shared__ float q_lds[D];
     __shared__ float p_lds[kWave];
 
-    // grid (seq, head, split): sequence first so each split index's work is
-    // spread over all XCDs (workgroups are dealt to XCDs by linear id)
-    const int s = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
+    // grid (kv head + Hkv * (g + G * seq), split), g the head within its kv
+    // head's group: workgroups are dealt to the XCDs round-robin by linear
+    // id, so with the kv head fastest every XCD gets an equal share of every
+    // sequence's tokens whatever the length mix, and (Hkv a multiple of 8)
+    // the G heads sharing a kv head's rows run on one XCD and share them in
+    // its L2; the split index last spreads each split index over all XCDs.
+    const int kvh_ = blockIdx.x % p.num_kv_heads, rest = blockIdx.x / p.num_kv_heads;
+    const int s = rest / p.group, h = kvh_ * p.group + rest % p.group, part = blockIdx.y;
     const int lane = threadIdx.x;
     const int L = p.seq_lens[s];
     const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
@@ -169,7 +174,7 @@ bool decode_valu_supported(int dtype, int D, int Dv)
 template <class E, int D, int DV>
 static hipError_t launch_valu_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    dim3 grid(num_seqs, p.num_heads, parts), block(kWave);
+    dim3 grid(num_seqs * p.num_heads, parts), block(kWave);
     const bool stream = p.group == 1;
     if (p.bs_shift == 0) {
         if (stream) hipLaunchKernelGGL((k_decode_valu<E, D, DV, true, true>), grid, block, 0, st, p);
