@@ -46,6 +46,7 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _F32P = ctypes.POINTER(ctypes.c_float)
 _F64P = ctypes.POINTER(ctypes.c_double)
+_U8P = ctypes.POINTER(ctypes.c_uint8)
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 
@@ -76,7 +77,10 @@ class Oracle:
                   _I32P, _I64, _I64, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                   ctypes.c_double]
         L.orc_attention.argtypes = [_F64P] + common
+        ext = [_F32P, _U8P, _U8P, ctypes.c_double, ctypes.c_double]
+        L.orc_attention_v.argtypes = [_F64P] + common + ext
         L.orc_partials.argtypes = [_F64P, _F64P, _F64P] + common + [_I32P, _I32, _I32]
+        L.orc_partials_v.argtypes = [_F64P, _F64P, _F64P] + common + [_I32P, _I32, _I32] + ext
         L.orc_reduce.argtypes = [_F64P, _F64P, _F64P, _F64P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32]
         L.orc_decode_metadata.argtypes = [_I32P, _I64, _I32P, _I64, _I32P, _I64, _I64,
                                           _I32P, _I64, _I64, _I64P, _I64, _I32P, _I64, _I64,
@@ -189,8 +193,13 @@ class Oracle:
     # -- attention ----------------------------------------------------------
     def _problem(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr):
         q = np.asarray(query, dtype=np.float32)
-        kc = np.asarray(key_cache, dtype=np.float32)
-        vc = np.asarray(value_cache, dtype=np.float32)
+        kc = np.asarray(key_cache)
+        vc = np.asarray(value_cache)
+        fp8 = kc.dtype == np.uint8  # fp8 E4M3 codes (both caches)
+        assert (vc.dtype == np.uint8) == fp8
+        if not fp8:
+            kc = kc.astype(np.float32, copy=False)
+            vc = vc.astype(np.float32, copy=False)
         assert q.ndim == 3 and kc.ndim == 5 and vc.ndim == 4
         qs = _estrides(q)
         ks = _estrides(kc)
@@ -209,25 +218,43 @@ class Oracle:
             ip = None
             ps, pb = _estrides(pages)
         seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
-        args = [_ptr(q, _F32P), qs[0], qs[1], _ptr(kc, _F32P), ks[0], ks[1], _ptr(vc, _F32P),
-                vs[0], vs[1], _ptr(pages, _I32P), ps, pb, _ptr(ip, _I32P), _ptr(seq, _I32P),
-                S, H, Hkv, D, Dv, bs, x, float(scale)]
+        args = [_ptr(q, _F32P), qs[0], qs[1], None if fp8 else _ptr(kc, _F32P), ks[0], ks[1],
+                None if fp8 else _ptr(vc, _F32P), vs[0], vs[1], _ptr(pages, _I32P), ps, pb,
+                _ptr(ip, _I32P), _ptr(seq, _I32P), S, H, Hkv, D, Dv, bs, x, float(scale)]
         keep = (q, kc, vc, pages, ip, seq)
+        self._codes = (kc, vc) if fp8 else (None, None)
         return args, keep, (S, H, Dv)
 
-    def attention(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr=None):
+    def _variant(self, alibi, k_scale, v_scale):
+        """Extra arguments of the _v entry points, or None for the plain ones."""
+        kc, vc = self._codes
+        if alibi is None and kc is None:
+            return None
+        al = None if alibi is None else np.ascontiguousarray(alibi, dtype=np.float32)
+        self._alibi = al
+        return [_ptr(al, _F32P), None if kc is None else kc.ctypes.data_as(_U8P),
+                None if vc is None else vc.ctypes.data_as(_U8P), float(k_scale), float(v_scale)]
+
+    def attention(self, query, key_cache, value_cache, pages, seq_lens, scale, indptr=None,
+                  alibi=None, k_scale=1.0, v_scale=1.0):
         """[S, H, Dv] float64 softmax attention of each query over its paged
         K/V rows (paged_attention_v2_triton.py, phase-1 docstring steps 1-4
-        applied to the whole sequence)."""
+        applied to the whole sequence). alibi: optional slopes [H]; uint8
+        caches are fp8 E4M3 codes dequantized with k_scale / v_scale."""
         args, keep, (S, H, Dv) = self._problem(query, key_cache, value_cache, pages, seq_lens,
                                                scale, indptr)
         out = np.empty((S, H, Dv), dtype=np.float64)
-        rc = self.lib.orc_attention(_ptr(out, _F64P), *args)
+        ext = self._variant(alibi, k_scale, v_scale)
+        if ext is None:
+            rc = self.lib.orc_attention(_ptr(out, _F64P), *args)
+        else:
+            rc = self.lib.orc_attention_v(_ptr(out, _F64P), *args, *ext)
         assert rc == 0, rc
         return out
 
     def partials(self, query, key_cache, value_cache, pages, seq_lens, scale, max_num_parts,
-                 partition_size=512, num_splits=None, indptr=None):
+                 partition_size=512, num_splits=None, indptr=None, alibi=None, k_scale=1.0,
+                 v_scale=1.0):
         """Phase-1 intermediates (tmp [S,H,P,Dv], max_logits, exp_sums
         [S,H,P]) in float64; tmp of empty partitions is NaN."""
         args, keep, (S, H, Dv) = self._problem(query, key_cache, value_cache, pages, seq_lens,
@@ -236,8 +263,13 @@ class Oracle:
         ml = np.empty((S, H, max_num_parts), dtype=np.float64)
         es = np.empty((S, H, max_num_parts), dtype=np.float64)
         ns = None if num_splits is None else np.ascontiguousarray(num_splits, dtype=np.int32)
-        rc = self.lib.orc_partials(_ptr(tmp, _F64P), _ptr(ml, _F64P), _ptr(es, _F64P), *args,
-                                   _ptr(ns, _I32P), partition_size, max_num_parts)
+        ext = self._variant(alibi, k_scale, v_scale)
+        if ext is None:
+            rc = self.lib.orc_partials(_ptr(tmp, _F64P), _ptr(ml, _F64P), _ptr(es, _F64P), *args,
+                                       _ptr(ns, _I32P), partition_size, max_num_parts)
+        else:
+            rc = self.lib.orc_partials_v(_ptr(tmp, _F64P), _ptr(ml, _F64P), _ptr(es, _F64P), *args,
+                                         _ptr(ns, _I32P), partition_size, max_num_parts, *ext)
         assert rc == 0, rc
         return tmp, ml, es
 

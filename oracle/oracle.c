@@ -62,6 +62,19 @@
  *       prefix sum of nothing).
  *   R11 the SWA table is built only when both it and the full-to-SWA map are
  *       given; it maps the raw slot (before the division) and then divides.
+ *   R13 ALiBi ([PAv2] wrapper argument alibi_slopes, no math on the page):
+ *       the standard linear bias, z_t = scale * q . K_t + slope[h] * (t - (L-1))
+ *       with t the token's position in its sequence of length L (the query is
+ *       the last position, so its own token gets no bias and earlier ones a
+ *       penalty growing with the distance, for a positive slope).
+ *   R14 fp8 cache ([PAv2] wrapper arguments kv_cache_dtype, k_scale, v_scale,
+ *       no math on the page): both caches hold OCP FP8 E4M3 codes, packed with
+ *       x = 16 (16 / element size, as for every dtype), and the dequantized
+ *       values are K_t[d] = e4m3(code) * k_scale, V_t[d] = e4m3(code) *
+ *       v_scale; the query keeps its own dtype.
+ *   R15 e4m3(code): sign bit, 4-bit exponent e (bias 7), 3-bit mantissa m:
+ *       e = 0 gives m * 2^-9, e = 15 with m = 7 is NaN, otherwise
+ *       (1 + m/8) * 2^(e-7) (the OCP E4M3 definition: no infinities).
  *   R12 speculative SWA page table: the destination has LEN_A + LEN_B columns
  *       (the wrapper's LEN_OUT) and only columns below
  *       min(seq_len_a + seq_len_b, LEN_A + LEN_B) are written (the page's
@@ -241,7 +254,30 @@ typedef struct {
     const int32_t* seq_lens;
     int32_t S, H, Hkv, D, Dv, bs, x;
     double scale;
+    /* R13, R14: optional ALiBi slopes [H]; fp8 caches (codes addressed with
+       the same strides as the float caches, which are then unused) */
+    const float* alibi;
+    const uint8_t* key_u8;
+    const uint8_t* value_u8;
+    double k_scale, v_scale;
 } orc_problem;
+
+/* R15: OCP FP8 E4M3 code -> value */
+static double e4m3(uint8_t c)
+{
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+#if ORACLE_MUTANT == 18
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = ldexp((double)m, -10);              /* planted: exponent bias 8 */
+    else v = ldexp(1.0 + m / 8.0, e - 8);
+#else
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+#endif
+    return sgn ? -v : v;
+}
 
 static int kv_head_of(const orc_problem* p, int h)
 {
@@ -258,21 +294,29 @@ static void gather_seq(const orc_problem* p, int s, int kvh, int64_t L, double* 
     for (int64_t t = 0; t < L; ++t) {
         int64_t blk = physical_block(p->pages, p->pg_s, p->pg_b, p->indptr, s, t / p->bs);
         int64_t slot = t % p->bs;
-        const float* kb = p->key_cache + blk * p->k_b + (int64_t)kvh * p->k_h;
-        const float* vb = p->value_cache + blk * p->v_b + (int64_t)kvh * p->v_h;
+        const int64_t kbase = blk * p->k_b + (int64_t)kvh * p->k_h;
+        const int64_t vbase = blk * p->v_b + (int64_t)kvh * p->v_h;
         for (int d = 0; d < p->D; ++d) {
 #if ORACLE_MUTANT == 6
             int64_t e = ((int64_t)(d % p->x) * p->bs + slot) * p->x + d / p->x; /* planted: packing transposed */
 #else
             int64_t e = ((int64_t)(d / p->x) * p->bs + slot) * p->x + d % p->x;
 #endif
-            K[t * p->D + d] = (double)kb[e];
+            K[t * p->D + d] = p->key_u8 ? e4m3(p->key_u8[kbase + e]) * p->k_scale
+                                        : (double)p->key_cache[kbase + e];
         }
         for (int d = 0; d < p->Dv; ++d) {
 #if ORACLE_MUTANT == 10
-            V[t * p->Dv + d] = (double)vb[slot * (int64_t)p->Dv + d]; /* planted: V read token-major */
+            int64_t e = slot * (int64_t)p->Dv + d; /* planted: V read token-major */
 #else
-            V[t * p->Dv + d] = (double)vb[(int64_t)d * p->bs + slot];
+            int64_t e = (int64_t)d * p->bs + slot;
+#endif
+#if ORACLE_MUTANT == 19
+            V[t * p->Dv + d] = p->value_u8 ? e4m3(p->value_u8[vbase + e]) * p->k_scale /* planted: k_scale on V */
+                                           : (double)p->value_cache[vbase + e];
+#else
+            V[t * p->Dv + d] = p->value_u8 ? e4m3(p->value_u8[vbase + e]) * p->v_scale
+                                           : (double)p->value_cache[vbase + e];
 #endif
         }
     }
@@ -284,10 +328,16 @@ static void logits(const orc_problem* p, int s, int h, const double* K, int64_t 
                    double* z)
 {
     const float* q = p->query + (int64_t)s * p->q_s + (int64_t)h * p->q_h;
+    const int64_t L = p->seq_lens[s];
     for (int64_t t = t0; t < t1; ++t) {
         double acc = 0.0;
         for (int d = 0; d < p->D; ++d) acc += (double)q[d] * K[t * p->D + d];
         z[t - t0] = p->scale * acc;
+#if ORACLE_MUTANT == 20
+        if (p->alibi) z[t - t0] += (double)p->alibi[h] * (double)((L - 1) - t); /* planted: bias sign */
+#else
+        if (p->alibi) z[t - t0] += (double)p->alibi[h] * (double)(t - (L - 1)); /* R13 */
+#endif
     }
 }
 
@@ -317,7 +367,9 @@ static void softmax_average(const orc_problem* p, const double* z, const double*
 
 static int check_problem(const orc_problem* p)
 {
-    if (!p->query || !p->key_cache || !p->value_cache || !p->pages || !p->seq_lens) return 0;
+    if (!p->query || !(p->key_cache || p->key_u8) || !(p->value_cache || p->value_u8) || !p->pages ||
+        !p->seq_lens)
+        return 0;
     if (p->S < 0 || p->H < 1 || p->Hkv < 1 || p->H % p->Hkv || p->D < 1 || p->Dv < 1 ||
         p->bs < 1 || p->x < 1 || p->D % p->x)
         return 0;
@@ -326,15 +378,11 @@ static int check_problem(const orc_problem* p)
 
 /* Unpartitioned definition ([PAv2] docstring steps 1-4 over the whole
  * sequence): out[s, h, :] = sum_t softmax(z)_t v_t. out is [S][H][Dv]. */
-int orc_attention(double* out, const float* query, int64_t q_s, int64_t q_h,
-                  const float* key_cache, int64_t k_b, int64_t k_h,
-                  const float* value_cache, int64_t v_b, int64_t v_h,
-                  const int32_t* pages, int64_t pg_s, int64_t pg_b, const int32_t* indptr,
-                  const int32_t* seq_lens, int32_t S, int32_t H, int32_t Hkv, int32_t D,
-                  int32_t Dv, int32_t bs, int32_t x, double scale)
+static int attention_impl(double* out, const orc_problem* pp)
 {
-    orc_problem p = {query, q_s, q_h, key_cache, k_b, k_h, value_cache, v_b, v_h,
-                     pages, pg_s, pg_b, indptr, seq_lens, S, H, Hkv, D, Dv, bs, x, scale};
+    const orc_problem p = *pp;
+    const int32_t S = p.S, H = p.H, Hkv = p.Hkv, D = p.D, Dv = p.Dv;
+    const int32_t* seq_lens = p.seq_lens;
     if (!out || !check_problem(&p)) return ORC_EINVAL;
     int G = H / Hkv;
     int failed = 0;
@@ -388,17 +436,12 @@ static int64_t split_len(int64_t L, const int32_t* num_splits, int s, int32_t pa
  * Empty partitions (start >= L) store max = -inf, sum = 0 and leave tmp
  * untouched, as the page's early exit does. Layouts: tmp [S][H][Pmax][Dv],
  * max_logits and exp_sums [S][H][Pmax]. tmp holds acc / l (reading R1). */
-int orc_partials(double* tmp, double* max_logits, double* exp_sums,
-                 const float* query, int64_t q_s, int64_t q_h,
-                 const float* key_cache, int64_t k_b, int64_t k_h,
-                 const float* value_cache, int64_t v_b, int64_t v_h,
-                 const int32_t* pages, int64_t pg_s, int64_t pg_b, const int32_t* indptr,
-                 const int32_t* seq_lens, int32_t S, int32_t H, int32_t Hkv, int32_t D,
-                 int32_t Dv, int32_t bs, int32_t x, double scale,
-                 const int32_t* num_splits, int32_t partition_size, int32_t max_num_parts)
+static int partials_impl(double* tmp, double* max_logits, double* exp_sums, const orc_problem* pp,
+                         const int32_t* num_splits, int32_t partition_size, int32_t max_num_parts)
 {
-    orc_problem p = {query, q_s, q_h, key_cache, k_b, k_h, value_cache, v_b, v_h,
-                     pages, pg_s, pg_b, indptr, seq_lens, S, H, Hkv, D, Dv, bs, x, scale};
+    const orc_problem p = *pp;
+    const int32_t S = p.S, H = p.H, Hkv = p.Hkv, D = p.D, Dv = p.Dv;
+    const int32_t* seq_lens = p.seq_lens;
     if (!tmp || !max_logits || !exp_sums || !check_problem(&p) || max_num_parts < 1) return ORC_EINVAL;
     if (!num_splits && partition_size < 1) return ORC_EINVAL;
     int failed = 0;
@@ -443,6 +486,46 @@ int orc_partials(double* tmp, double* max_logits, double* exp_sums,
         free(K); free(V); free(z);
     }
     return failed ? ORC_ENOMEM : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Entry points: the plain problem, and the variants of R13 / R14 (optional
+ * ALiBi slopes; fp8 caches as uint8 codes with the float-cache strides).
+ * ------------------------------------------------------------------------ */
+#define ORC_PROBLEM_ARGS                                                             \
+    const float *query, int64_t q_s, int64_t q_h, const float *key_cache, int64_t k_b, \
+        int64_t k_h, const float *value_cache, int64_t v_b, int64_t v_h,              \
+        const int32_t *pages, int64_t pg_s, int64_t pg_b, const int32_t *indptr,      \
+        const int32_t *seq_lens, int32_t S, int32_t H, int32_t Hkv, int32_t D,        \
+        int32_t Dv, int32_t bs, int32_t x, double scale
+#define ORC_PROBLEM_INIT(alibi, ku8, vu8, ks, vs)                                                \
+    {query, q_s, q_h, key_cache, k_b, k_h, value_cache, v_b, v_h, pages, pg_s, pg_b, indptr,    \
+     seq_lens, S, H, Hkv, D, Dv, bs, x, scale, alibi, ku8, vu8, ks, vs}
+
+int orc_attention(double* out, ORC_PROBLEM_ARGS)
+{
+    const orc_problem p = ORC_PROBLEM_INIT(NULL, NULL, NULL, 1.0, 1.0);
+    return attention_impl(out, &p);
+}
+int orc_attention_v(double* out, ORC_PROBLEM_ARGS, const float* alibi, const uint8_t* key_u8,
+                    const uint8_t* value_u8, double k_scale, double v_scale)
+{
+    const orc_problem p = ORC_PROBLEM_INIT(alibi, key_u8, value_u8, k_scale, v_scale);
+    return attention_impl(out, &p);
+}
+int orc_partials(double* tmp, double* max_logits, double* exp_sums, ORC_PROBLEM_ARGS,
+                 const int32_t* num_splits, int32_t partition_size, int32_t max_num_parts)
+{
+    const orc_problem p = ORC_PROBLEM_INIT(NULL, NULL, NULL, 1.0, 1.0);
+    return partials_impl(tmp, max_logits, exp_sums, &p, num_splits, partition_size, max_num_parts);
+}
+int orc_partials_v(double* tmp, double* max_logits, double* exp_sums, ORC_PROBLEM_ARGS,
+                   const int32_t* num_splits, int32_t partition_size, int32_t max_num_parts,
+                   const float* alibi, const uint8_t* key_u8, const uint8_t* value_u8,
+                   double k_scale, double v_scale)
+{
+    const orc_problem p = ORC_PROBLEM_INIT(alibi, key_u8, value_u8, k_scale, v_scale);
+    return partials_impl(tmp, max_logits, exp_sums, &p, num_splits, partition_size, max_num_parts);
 }
 
 /* Phase 2 ([PAv2] _paged_attn_v2_reduce_kernel): over the n nonempty
@@ -622,5 +705,5 @@ int orc_swa_spec_page_table(int32_t* dst, int64_t d0, int64_t d1,
 }
 
 /* Number of planted-mistake variants this file defines (for the tests). */
-int orc_num_mutants(void) { return 17; }
+int orc_num_mutants(void) { return 20; }
 int orc_mutant_id(void) { return ORACLE_MUTANT; }

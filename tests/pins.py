@@ -23,6 +23,10 @@ What pins what:
                  empty batch
   spec page tbl  numpy concatenation of the two prefixes per draft row;
                  zeros past the table widths; untouched past the total
+  fp8 caches     every E4M3 code against torch's float8_e4m3fn, through a
+                 value row and through one-hot queries on keys
+  ALiBi          geometric-series closed form with zero scores (weights,
+                 max logit, exp sum, both slope signs); zero slopes = plain
 """
 from __future__ import annotations
 
@@ -483,8 +487,74 @@ def pin_spec_page_table_widths(o):
     assert out.tolist() == [[1, 2, 101, -9, -9, -9, -9]]
 
 
+def _fp8_values(codes):
+    """float32 values of OCP E4M3 codes (torch's float8_e4m3fn)."""
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def pin_fp8_dequant(o):
+    """fp8 caches: one token of 256 value codes comes back as v_scale times
+    the E4M3 value of each code (NaN codes included); keys: with a one-hot
+    query per head the max logit is scale * k_scale * E4M3(code)."""
+    codes = np.arange(256, dtype=np.uint8)
+    # values: Dv = 256, one token, one block
+    vc = codes.reshape(1, 1, 256, 1)
+    kc = np.full((1, 1, 1, 1, 16), 0x38, np.uint8)  # keys 1.0
+    q = np.zeros((1, 1, 16), np.float32)
+    out = o.attention(q, kc, vc, np.zeros((1, 1), np.int32), [1], 1.0, k_scale=0.5, v_scale=0.25)
+    want = 0.25 * _fp8_values(codes).astype(np.float64)
+    assert np.array_equal(np.isnan(out[0, 0]), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(out[0, 0][fin], want[fin])
+    # keys: 16 heads over one kv head, block s holds codes 16s .. 16s+15 of token 0 of seq s
+    finite = codes[(codes & 0x7F) != 0x7F]
+    n = len(finite) // 16
+    kc = finite[:16 * n].reshape(n, 1, 1, 1, 16)
+    vc = np.full((n, 1, 1, 1), 0x38, np.uint8)
+    q = np.tile(np.eye(16, dtype=np.float32)[None], (n, 1, 1))
+    pages = np.arange(n, dtype=np.int32).reshape(n, 1)
+    _, ml, _ = o.partials(q, kc, vc, pages, np.ones(n, np.int32), 2.0, 1, partition_size=64,
+                          k_scale=0.75, v_scale=1.0)
+    want = 2.0 * 0.75 * _fp8_values(finite[:16 * n]).astype(np.float64).reshape(n, 16)
+    assert np.array_equal(ml[:, :, 0], want)
+
+
+def pin_alibi_geometric(o):
+    """ALiBi with zero scores: the weights of tokens 0..L-1 are r^(L-1-t)
+    normalised, r = exp(-slope) (a geometric series), the max logit is the
+    bias of the best token (0 at t = L-1 for a positive slope, -slope*(L-1)
+    at t = 0 for a negative one) and the exp sum (1 - r^L) / (1 - r)."""
+    L, H = 7, 4
+    slopes = np.array([0.5, 1.0, 0.125, -0.25], np.float32)
+    q = np.zeros((1, H, 4), np.float32)
+    kc = np.ones((L, 1, 1, 1, 4), np.float32)
+    vc = np.zeros((L, 1, L, 1), np.float32)
+    for t in range(L):
+        vc[t, 0, t, 0] = 1.0  # V_t = e_t
+    pages = np.arange(L, dtype=np.int32)[None]
+    out = o.attention(q, kc, vc, pages, [L], 1.0, alibi=slopes)
+    _, ml, es = o.partials(q, kc, vc, pages, [L], 1.0, 1, partition_size=64, alibi=slopes)
+    for h, sl in enumerate(slopes.astype(np.float64)):
+        r = math.exp(-sl)
+        w = np.array([r ** (L - 1 - t) for t in range(L)]) * (1 - r) / (1 - r ** L)
+        assert np.allclose(out[0, h], w, rtol=1e-12, atol=0), h
+        m = 0.0 if sl >= 0 else -sl * (L - 1)
+        assert abs(ml[0, h, 0] - m) < 1e-12, h
+        assert abs(es[0, h, 0] * math.exp(m) - (1 - r ** L) / (1 - r)) < 1e-9, h
+
+
+def pin_alibi_zero_slopes(o):
+    """Zero slopes leave the plain result unchanged (bit for bit)."""
+    w = workloads.custom(seed=33, seq_lens=[9, 30], num_heads=4, num_kv_heads=2, head_size=16,
+                         block_size=4)
+    a = (_np(w.query), _np(w.key_cache), _np(w.value_cache), w.block_tables.numpy(),
+         w.seq_lens.numpy(), w.scale)
+    assert np.array_equal(o.attention(*a), o.attention(*a, alibi=np.zeros(4, np.float32)))
+
+
 ALL_PINS = [pin_worked_example, pin_offsets_bruteforce, pin_attention_bruteforce,
             pin_attention_sdpa, pin_closed_forms, pin_block_permutation, pin_partitions,
             pin_reduce_closed_form, pin_num_kv_splits, pin_page_indices, pin_mla,
             pin_metadata_roundtrip, pin_metadata_prefix, pin_metadata_floor, pin_metadata_swa,
-            pin_metadata_empty, pin_spec_page_table, pin_spec_page_table_widths]
+            pin_metadata_empty, pin_spec_page_table, pin_spec_page_table_widths,
+            pin_fp8_dequant, pin_alibi_geometric, pin_alibi_zero_slopes]

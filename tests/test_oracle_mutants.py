@@ -7,7 +7,8 @@ output, merge without the partition sums, partition dropping a token, value
 rows read token-major; for the decode metadata: inclusive prefix sum, delta
 dropped, column not scaled to a token position, SWA map applied to the page
 instead of the slot, pool row index ignored; for the speculative page
-table: draft row used as the request row, draft column not shifted).
+table: draft row used as the request row, draft column not shifted; fp8
+exponent bias 8, k_scale applied to values, ALiBi bias sign flipped).
 Mistakes are planted in the oracle only, on the CPU.
 """
 import pytest
