@@ -45,7 +45,8 @@ extern "C" {
 #define PA_ENOTSUP (-2)  /* valid, but this dtype/size/layout combination is not built */
 #define PA_ELAUNCH (-3)  /* the HIP launch itself failed */
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
+/* PA_FP8_E4M3 is a cache dtype only (pa_decode_args.kv_dtype). */
 
 /*
  * Phase 1 of split-KV decode ([PAv2] _paged_attn_v2_partition_kernel and the
@@ -81,6 +82,18 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
  * a sequence never has more than max_num_parts splits (max_num_parts >= 2).
  * Phase 2 with partition_size == 0 merges every non-empty slot; the final
  * output is the same as with any other split.
+ *
+ * Variants of phase 1 named by the [PAv2] wrapper arguments (alibi_slopes,
+ * kv_cache_dtype, k_scale, v_scale), whose math the page does not give; the
+ * readings implemented:
+ *   ALiBi: with alibi_slopes (fp32 [num_heads]) each score gets
+ *     slope[h] * (t - (L - 1)), t the token's position in its sequence of
+ *     length L (the query is the last position).
+ *   fp8 cache: with kv_dtype = PA_FP8_E4M3 both caches hold OCP FP8 E4M3
+ *     codes (sign, 4-bit exponent with bias 7, 3-bit mantissa, no
+ *     infinities, NaN = exponent 15 and mantissa 7), packed with x = 16, and
+ *     K_t[d] = E4M3(code) * k_scale, V_t[d] = E4M3(code) * v_scale. The query
+ *     (and every output) keeps dtype.
  */
 typedef struct pa_decode_args {
     /* outputs: fp32 workspaces */
@@ -134,6 +147,10 @@ typedef struct pa_decode_args {
     int32_t num_workers;         /* balanced splits only (partition_size == 0): number of
                                     token ranges, typically the compute-unit count;
                                     ignored otherwise */
+    const float* alibi_slopes;   /* optional, [num_heads] fp32 (see "Variants") */
+    int32_t kv_dtype;            /* 0 (or equal to dtype): caches hold dtype;
+                                    PA_FP8_E4M3: fp8 caches with the scales below */
+    float k_scale, v_scale;      /* fp8 caches only; must be finite and nonzero */
 } pa_decode_args;
 
 #define PA_KERNEL_AUTO 0
@@ -146,6 +163,10 @@ typedef struct pa_decode_args {
  *   (head_size, v_head_size) in {(64,64), (128,128), (256,256), (576,512)};
  *   any group size num_heads / num_kv_heads (grouped heads of f16/bf16 caches
  *   run on MFMA when block_size >= 8 and the group is at most 16).
+ * fp8 caches (any query dtype, x = 16) run on the vector kernel; asking for
+ * a matrix-core kernel with them returns PA_ENOTSUP. ALiBi slopes run on the
+ * grouped-head matrix-core kernel and the vector kernel; latent rows with
+ * slopes go to the vector kernel. Balanced splits take neither.
  */
 int paged_attn_decode(const pa_decode_args* args, void* stream);
 

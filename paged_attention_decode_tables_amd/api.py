@@ -18,9 +18,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libpagedattn.so"
 
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_ELAUNCH = 0, -1, -2, -3
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_KERNEL = {"auto": 0, "valu": 1, "mfma": 2}
 _DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_FP8_CACHE = (torch.uint8, torch.float8_e4m3fn)  # cache tensors holding E4M3 codes
 _CODE_NAMES = {PA_EINVAL: "PA_EINVAL", PA_ENOTSUP: "PA_ENOTSUP", PA_ELAUNCH: "PA_ELAUNCH"}
 
 _vp = ctypes.c_void_p
@@ -52,6 +53,8 @@ class DecodeArgs(ctypes.Structure):
         ("head_size", _i32), ("v_head_size", _i32), ("block_size", _i32), ("x", _i32),
         ("partition_size", _i32), ("max_num_parts", _i32), ("max_seq_len", _i32),
         ("dtype", _i32), ("kernel_hint", _i32), ("num_workers", _i32),
+        ("alibi_slopes", _vp), ("kv_dtype", _i32), ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -149,7 +152,8 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
                       max_seq_len: int, *, partition_size: int = 512,
                       num_splits: Optional[torch.Tensor] = None,
                       kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
-                      num_workers: int = 0, stream=None) -> None:
+                      num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
     """Phase 1: per-split max logits, exp sums and normalised outputs.
 
     Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
@@ -157,10 +161,17 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     [NB, Hkv, Dv, bs]; block_tables [S, max_blocks] int32 (or the flat page
     list when kv_indptr is given); seq_lens [S] int32. partition_size=0 with
     num_workers > 0 asks for balanced splits (equal token ranges).
+    Caches of dtype uint8 or float8_e4m3fn hold FP8 E4M3 codes (x = 16),
+    dequantized with k_scale / v_scale; alibi_slopes is an fp32 [H] tensor.
     """
     lib = load_library()
-    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
-        raise TypeError("query, key_cache and value_cache must share one dtype")
+    fp8 = key_cache.dtype in _FP8_CACHE
+    if value_cache.dtype != key_cache.dtype or (not fp8 and key_cache.dtype != query.dtype):
+        raise TypeError("key_cache and value_cache must share the query's dtype, or both be fp8 codes")
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.shape != (query.shape[1],) \
+                or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous fp32 tensor of shape [num_heads]")
     S, H, D = query.shape
     NB, Hkv, Dx, bs, x = key_cache.shape
     Dv = value_cache.shape[2]
@@ -192,6 +203,9 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     a.dtype = _dtype(query)
     a.kernel_hint = PA_KERNEL[kernel]
     a.num_workers = num_workers
+    a.alibi_slopes = _ptr(alibi_slopes)
+    a.kv_dtype = PA_FP8_E4M3 if fp8 else 0
+    a.k_scale, a.v_scale = float(k_scale), float(v_scale)
     _check(lib.paged_attn_decode(ctypes.byref(a), _stream(stream)))
 
 

@@ -1,6 +1,7 @@
 // api.hip -- the exported C ABI of libpagedattn.so (declared in pagedattn.h).
 // Every entry point validates its arguments on the host, then enqueues its
 // kernels on the caller's stream. Nothing here allocates or synchronises.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -62,6 +63,12 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if (!a) return fail(PA_EINVAL, "paged_attn_decode: args is NULL");
     const int esz = elem_size(a->dtype);
     if (!esz) return fail(PA_EINVAL, "paged_attn_decode: unknown dtype %d", a->dtype);
+    const bool fp8 = a->kv_dtype == PA_FP8_E4M3;
+    if (a->kv_dtype != 0 && a->kv_dtype != a->dtype && !fp8)
+        return fail(PA_EINVAL, "paged_attn_decode: kv_dtype %d is neither 0, dtype nor PA_FP8_E4M3", a->kv_dtype);
+    const int kv_esz = fp8 ? 1 : esz;  // cache element size
+    if (fp8 && (!isfinite(a->k_scale) || !isfinite(a->v_scale) || a->k_scale == 0.0f || a->v_scale == 0.0f))
+        return fail(PA_EINVAL, "paged_attn_decode: fp8 caches need finite nonzero k_scale and v_scale");
     if (a->num_seqs < 0) return fail(PA_EINVAL, "paged_attn_decode: num_seqs < 0");
     if (a->num_heads < 1 || a->num_kv_heads < 1 || a->num_heads % a->num_kv_heads)
         return fail(PA_EINVAL, "paged_attn_decode: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
@@ -72,8 +79,9 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
         return fail(PA_EINVAL, "paged_attn_decode: block_size %d is not a power of two in [1, 1024]", a->block_size);
     if (a->x < 1 || a->head_size % a->x)
         return fail(PA_EINVAL, "paged_attn_decode: x = %d must divide head_size %d", a->x, a->head_size);
-    if (a->x * esz != 16)
-        return fail(PA_ENOTSUP, "paged_attn_decode: key packing x = %d, only 16 / element size (%d) is built", a->x, 16 / esz);
+    if (a->x * kv_esz != 16)
+        return fail(PA_ENOTSUP, "paged_attn_decode: key packing x = %d, only 16 / cache element size (%d) is built",
+                    a->x, 16 / kv_esz);
     if (a->max_num_parts < 1) return fail(PA_EINVAL, "paged_attn_decode: max_num_parts < 1");
     if (a->max_seq_len < 0) return fail(PA_EINVAL, "paged_attn_decode: max_seq_len < 0");
     int64_t parts;
@@ -107,8 +115,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if (!aligned16(a->query) || !aligned16(a->key_cache) || !aligned16(a->value_cache) ||
         !aligned16(a->tmp_output))
         return fail(PA_ENOTSUP, "paged_attn_decode: query, caches and tmp_output must be 16-byte aligned");
-    if ((a->q_stride_s * esz) % 16 || (a->q_stride_h * esz) % 16 || (a->k_stride_b * esz) % 16 ||
-        (a->k_stride_h * esz) % 16 || (a->v_stride_b * esz) % 16 || (a->v_stride_h * esz) % 16 ||
+    if ((a->q_stride_s * esz) % 16 || (a->q_stride_h * esz) % 16 || (a->k_stride_b * kv_esz) % 16 ||
+        (a->k_stride_h * kv_esz) % 16 || (a->v_stride_b * kv_esz) % 16 || (a->v_stride_h * kv_esz) % 16 ||
         a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
         return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
     if (parts > kMaxGridYZ || a->num_heads > kMaxGridYZ)
@@ -140,7 +148,10 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     p.pl = pa::PageList{a->block_tables, a->bt_stride_s, a->bt_stride_b, a->kv_indptr};
     p.seq_lens = a->seq_lens;
     p.num_splits = a->num_splits;
-    p.scale_log2 = a->scale * pa::kLog2e;
+    p.scale_log2 = a->scale * (fp8 ? a->k_scale : 1.0f) * pa::kLog2e;
+    p.alibi = a->alibi_slopes;
+    p.v_scale = fp8 ? a->v_scale : 1.0f;
+    p.kv_fp8 = fp8;
     p.num_heads = a->num_heads;
     p.num_kv_heads = a->num_kv_heads;
     p.group = group;
@@ -152,14 +163,17 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // latent rows: the value cache is the leading v_head_size columns of the key rows
+    // The matrix-core kernels read caches of the query's dtype; ALiBi is
+    // built into the grouped-head one, not the latent-row one.
     const bool mla_ok = pa::decode_mla_supported(a->dtype, D, Dv, group, a->block_size) &&
                         a->value_cache == a->key_cache && a->v_stride_b == a->k_stride_b &&
-                        a->v_stride_h == a->k_stride_h;
-    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size);
+                        a->v_stride_h == a->k_stride_h && !fp8 && !a->alibi_slopes;
+    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size) && !fp8;
     if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok && !mla_ok)
         return fail(PA_ENOTSUP, "paged_attn_decode: no matrix-core kernel serves this problem");
     if (balanced && (!mla_ok || a->kernel_hint == PA_KERNEL_VALU))
-        return fail(PA_ENOTSUP, "paged_attn_decode: balanced splits are built for the MLA matrix-core kernel only");
+        return fail(PA_ENOTSUP, "paged_attn_decode: balanced splits are built for the MLA matrix-core kernel only "
+                                "(query-dtype caches, no ALiBi)");
     if (a->kernel_hint != PA_KERNEL_VALU && mla_ok)
         return launched(pa::launch_decode_mla(p, a->dtype, a->num_seqs, (int)parts, st),
                         "paged_attn_decode (mla)");

@@ -37,8 +37,28 @@ struct BF16 {
     static constexpr int size = 2;
     static constexpr int dtype = PA_BF16;
 };
+// OCP FP8 E4M3 cache codes (caches only; dequantized with a scale)
+struct FP8E4M3 {
+    using storage = uint8_t;
+    static constexpr int size = 1;
+    static constexpr int dtype = PA_FP8_E4M3;
+};
+
+// E4M3 code (low 8 bits of c) -> fp32: sign, exponent e (4 bits, bias 7),
+// mantissa m (3 bits). e >= 1: (1 + m/8) * 2^(e-7), i.e. the 7 bits moved to
+// the fp32 exponent / mantissa position with the bias raised by 120; e = 0:
+// m * 2^-9; e = 15 with m = 7: NaN. No infinities.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+{
+    const uint32_t em = c & 0x7Fu;
+    float v = __uint_as_float((em << 20) + (120u << 23));
+    if (em < 8u) v = (float)em * 0x1p-9f;
+    if (em == 0x7Fu) v = __uint_as_float(0x7FC00000u);
+    return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+}
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint8_t v) { return e4m3_to_f32(v); }  // fp8 cache code
 __device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(__bf16 v)
 {
@@ -62,7 +82,10 @@ template <> __device__ __forceinline__ float hi16<F16>(uint32_t w)
 // Element i (0-based) of a 16-byte vector holding 16/size elements.
 template <class E> __device__ __forceinline__ float elem16(const u32x4& v, int i)
 {
-    if constexpr (E::size == 4) {
+    if constexpr (E::size == 1) {
+        const uint32_t w = v[i >> 2];
+        return e4m3_to_f32(w >> (8 * (i & 3)));
+    } else if constexpr (E::size == 4) {
         // copy the element out first: bit-casting the vector-element lvalue
         // directly reads element 0 with this compiler
         const uint32_t w = v[i];

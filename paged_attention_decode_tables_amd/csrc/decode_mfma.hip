@@ -133,6 +133,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
     const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)kvh * p.v_sh;
     const int last_group = (end - 1) & ~7;
+    // ALiBi: slope of head r in base-2 units (0 without slopes or past the group)
+    const float slope = (p.alibi && head_ok) ? p.alibi[h] * kLog2e : 0.0f;
 
     // Block-table window held in a register: lane i has the id of block
     // blk0 + wb + i of this wave's run; the next 64 ids are fetched one window
@@ -206,6 +208,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             sc[4 + i] = s1[i] * p.scale_log2;
         }
         const int t0 = c0 + 8 * g;  // this lane's first token
+        if (p.alibi) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sc[j] += slope * (float)(t0 + j - (L - 1));
+        }
         if (end - c0 < 32) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) sc[j] = (t0 + j < end) ? sc[j] : -INFINITY;

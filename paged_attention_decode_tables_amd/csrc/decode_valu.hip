@@ -17,6 +17,11 @@
 //          row. The chunk's probabilities are broadcast from LDS.
 // Tokens past the split end are masked: their scores are -inf and their
 // values are replaced by 0 before use, so NaN padding never propagates.
+//
+// The cache element type KE is the query's E or FP8E4M3 (codes dequantized
+// as code value * k_scale / v_scale: k_scale is folded into the score scale,
+// v_scale into the final normalisation). With ALiBi slopes each score gets
+// slope[h] * (t - (L - 1)) (base 2 here, like the scores).
 #include "kernels.h"
 
 namespace pa {
@@ -24,11 +29,12 @@ namespace pa {
 // STREAM: every K/V byte is read by exactly one wave (group size 1), so the
 // loads carry the nontemporal hint; with grouped heads the G waves of a kv
 // head share the lines through the caches and use plain loads.
-template <class E, int D, int DV, bool ROWV, bool STREAM>
+template <class E, class KE, int D, int DV, bool ROWV, bool STREAM>
 __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
 {
     using T = typename E::storage;
-    constexpr int X = 16 / E::size;       // key packing
+    using KT = typename KE::storage;
+    constexpr int X = 16 / KE::size;      // key packing
     constexpr int DVR = DV / kWave;       // value rows (or values) per lane
     __shared__ float q_lds[D];
     __shared__ float p_lds[kWave];
@@ -65,8 +71,9 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
 
     const int32_t* row = page_row(p.pl, s);
     const int64_t sb = p.pl.stride_b;
-    const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
-    const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)kvh * p.v_sh;
+    const KT* kc = reinterpret_cast<const KT*>(p.kc) + (int64_t)kvh * p.k_sh;
+    const KT* vc = reinterpret_cast<const KT*>(p.vc) + (int64_t)kvh * p.v_sh;
+    const float slope = p.alibi ? p.alibi[h] * kLog2e : 0.0f;
 
     float m = -INFINITY;  // running max (base 2)
     float l = 0.0f;       // per-lane partial sum
@@ -78,15 +85,15 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
         const int n = (int)((end - c0) < kWave ? (end - c0) : kWave);
         // ---- scores: lane <-> token (clamped to a valid token for the load)
         const int64_t t = c0 + (lane < n ? lane : n - 1);
-        const T* kp = kc + token_block(row, sb, t, bs_shift) * p.k_sb + (t & (bs - 1)) * X;
+        const KT* kp = kc + token_block(row, sb, t, bs_shift) * p.k_sb + (t & (bs - 1)) * X;
         float dot = 0.0f;
 #pragma unroll 8
         for (int c = 0; c < D / X; ++c) {
             const u32x4 kv = STREAM ? load16_stream(kp + (int64_t)c * bs * X) : load16(kp + (int64_t)c * bs * X);
 #pragma unroll
-            for (int j = 0; j < X; ++j) dot += q_lds[c * X + j] * elem16<E>(kv, j);
+            for (int j = 0; j < X; ++j) dot += q_lds[c * X + j] * elem16<KE>(kv, j);
         }
-        const float sc = lane < n ? dot * p.scale_log2 : -INFINITY;
+        const float sc = lane < n ? dot * p.scale_log2 + slope * (float)(t - (L - 1)) : -INFINITY;
         const float mn = fmaxf(m, wave_max(sc));
         const float alpha = fast_exp2(m - mn);
         const float pl = lane < n ? fast_exp2(sc - mn) : 0.0f;
@@ -105,18 +112,18 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
                 const int nv = (n + VT - 1) / VT;
                 for (int v = 0; v < nv; ++v) {
                     const int64_t tv = c0 + v * VT;
-                    const T* vp = vc + token_block(row, sb, tv, bs_shift) * p.v_sb + (tv & (bs - 1));
+                    const KT* vp = vc + token_block(row, sb, tv, bs_shift) * p.v_sb + (tv & (bs - 1));
                     float pv[VT];
 #pragma unroll
                     for (int j = 0; j < VT; ++j) pv[j] = p_lds[v * VT + j];
                     const bool full = (v + 1) * VT <= n;
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) {
-                        const T* vr = vp + (int64_t)(lane + kWave * r) * bs;
+                        const KT* vr = vp + (int64_t)(lane + kWave * r) * bs;
                         const u32x4 vv = STREAM ? load16_stream(vr) : load16(vr);
 #pragma unroll
                         for (int j = 0; j < VT; ++j) {
-                            float x = elem16<E>(vv, j);
+                            float x = elem16<KE>(vv, j);
                             if (!full) x = (v * VT + j < n) ? x : 0.0f;
                             acc[r] += pv[j] * x;
                         }
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
                 // small blocks: one token at a time, one element per row
                 for (int j = 0; j < n; ++j) {
                     const int64_t tj = c0 + j;
-                    const T* vp = vc + token_block(row, sb, tj, bs_shift) * p.v_sb + (tj & (bs - 1));
+                    const KT* vp = vc + token_block(row, sb, tj, bs_shift) * p.v_sb + (tj & (bs - 1));
                     const float pj = p_lds[j];
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) acc[r] += pj * to_f32(vp[(int64_t)(lane + kWave * r) * bs]);
@@ -136,12 +143,12 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
             // page size 1: lane <-> values [lane*DVR, lane*DVR + DVR) of each row
             for (int j = 0; j < n; ++j) {
                 const int64_t tj = c0 + j;
-                const T* vp = vc + token_block(row, sb, tj, 0) * p.v_sb + lane * DVR;
+                const KT* vp = vc + token_block(row, sb, tj, 0) * p.v_sb + lane * DVR;
                 const float pj = p_lds[j];
-                if constexpr (DVR * E::size == 16) {
+                if constexpr (DVR * KE::size == 16) {
                     const u32x4 vv = STREAM ? load16_stream(vp) : load16(vp);
 #pragma unroll
-                    for (int r = 0; r < DVR; ++r) acc[r] += pj * elem16<E>(vv, r);
+                    for (int r = 0; r < DVR; ++r) acc[r] += pj * elem16<KE>(vv, r);
                 } else {
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) acc[r] += pj * to_f32(vp[r]);
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
         *mlp = m * kLn2;
         *esp = lsum;
     }
-    const float inv = 1.0f / lsum;
+    const float inv = p.v_scale / lsum;
     float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp;
 #pragma unroll
     for (int r = 0; r < DVR; ++r) {
@@ -171,39 +178,47 @@ bool decode_valu_supported(int dtype, int D, int Dv)
     return (D == Dv && (D == 64 || D == 128 || D == 256)) || (D == 576 && Dv == 512);
 }
 
-template <class E, int D, int DV>
+template <class E, class KE, int D, int DV>
 static hipError_t launch_valu_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
     dim3 grid(num_seqs * p.num_heads, parts), block(kWave);
     const bool stream = p.group == 1;
     if (p.bs_shift == 0) {
-        if (stream) hipLaunchKernelGGL((k_decode_valu<E, D, DV, true, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((k_decode_valu<E, D, DV, true, false>), grid, block, 0, st, p);
+        if (stream) hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, true, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, true, false>), grid, block, 0, st, p);
     } else {
-        if (stream) hipLaunchKernelGGL((k_decode_valu<E, D, DV, false, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((k_decode_valu<E, D, DV, false, false>), grid, block, 0, st, p);
+        if (stream) hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, false, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, false, false>), grid, block, 0, st, p);
     }
     return hipGetLastError();
 }
 
-template <class E>
+template <class E, class KE>
 static hipError_t launch_valu_e(const DecodeParams& p, int D, int Dv, int num_seqs, int parts,
                                 hipStream_t st)
 {
-    if (D == 64 && Dv == 64) return launch_valu_t<E, 64, 64>(p, num_seqs, parts, st);
-    if (D == 128 && Dv == 128) return launch_valu_t<E, 128, 128>(p, num_seqs, parts, st);
-    if (D == 256 && Dv == 256) return launch_valu_t<E, 256, 256>(p, num_seqs, parts, st);
-    if (D == 576 && Dv == 512) return launch_valu_t<E, 576, 512>(p, num_seqs, parts, st);
+    if (D == 64 && Dv == 64) return launch_valu_t<E, KE, 64, 64>(p, num_seqs, parts, st);
+    if (D == 128 && Dv == 128) return launch_valu_t<E, KE, 128, 128>(p, num_seqs, parts, st);
+    if (D == 256 && Dv == 256) return launch_valu_t<E, KE, 256, 256>(p, num_seqs, parts, st);
+    if (D == 576 && Dv == 512) return launch_valu_t<E, KE, 576, 512>(p, num_seqs, parts, st);
     return hipErrorInvalidValue;
+}
+
+template <class E>
+static hipError_t launch_valu_kv(const DecodeParams& p, int D, int Dv, int num_seqs, int parts,
+                                 hipStream_t st)
+{
+    return p.kv_fp8 ? launch_valu_e<E, FP8E4M3>(p, D, Dv, num_seqs, parts, st)
+                    : launch_valu_e<E, E>(p, D, Dv, num_seqs, parts, st);
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, int Dv, int num_seqs,
                               int parts, hipStream_t st)
 {
     switch (dtype) {
-    case PA_F32: return launch_valu_e<F32>(p, D, Dv, num_seqs, parts, st);
-    case PA_F16: return launch_valu_e<F16>(p, D, Dv, num_seqs, parts, st);
-    case PA_BF16: return launch_valu_e<BF16>(p, D, Dv, num_seqs, parts, st);
+    case PA_F32: return launch_valu_kv<F32>(p, D, Dv, num_seqs, parts, st);
+    case PA_F16: return launch_valu_kv<F16>(p, D, Dv, num_seqs, parts, st);
+    case PA_BF16: return launch_valu_kv<BF16>(p, D, Dv, num_seqs, parts, st);
     default: return hipErrorInvalidValue;
     }
 }

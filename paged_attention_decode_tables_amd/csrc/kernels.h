@@ -32,6 +32,9 @@ struct DecodeParams {
     int partition_size, max_num_parts;
     int num_seqs;
     int num_workers;  // > 0: balanced splits (grid z = workers), see pagedattn.h
+    const float* alibi;  // optional ALiBi slopes [num_heads] (natural units)
+    float v_scale;       // fp8 caches: value scale (1 otherwise); k_scale is in scale_log2
+    bool kv_fp8;         // caches hold FP8 E4M3 codes
 };
 
 struct ReduceParams {

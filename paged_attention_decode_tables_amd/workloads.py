@@ -20,6 +20,13 @@ The MLA-style workload stores one latent row of 576 values per page (page
 size 1); its key cache is that row viewed as [NB, 1, 72, 1, 8] and its value
 cache the first 512 values of the same row ([NB, 1, 512, 1], strides
 (576, 576, 1, 1)).
+
+FP8 caches (``custom(kv_cache="fp8" | "fp8_codes")``) are uint8 tensors of
+E4M3 codes in the same layouts with x = 16. "fp8": N(0, 1) draws divided by
+the scale and rounded to E4M3 by torch's float8_e4m3fn cast, the way a
+serving engine quantises its cache; "fp8_codes": codes uniform over the 254
+that are not NaN. ALiBi slopes, when asked for, are 2^(-8 i / H), i = 1..H
+(no draw).
 """
 from __future__ import annotations
 
@@ -59,6 +66,11 @@ class Workload:
     latent: Optional[torch.Tensor] = None
     poison_block: Optional[int] = None
     notes: List[str] = field(default_factory=list)
+    # FP8 E4M3 caches: kv_dtype torch.uint8 (None: caches hold dtype)
+    kv_dtype: Optional[torch.dtype] = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    alibi_slopes: Optional[torch.Tensor] = None  # fp32 [H]
 
     @property
     def num_seqs(self) -> int:
@@ -67,6 +79,10 @@ class Workload:
     @property
     def elem_size(self) -> int:
         return torch.tensor([], dtype=self.dtype).element_size()
+
+    @property
+    def kv_elem_size(self) -> int:
+        return 1 if self.kv_dtype is not None else self.elem_size
 
     @property
     def total_tokens(self) -> int:
@@ -84,7 +100,7 @@ class Workload:
         """Algorithmic KV bytes of one decode step: every live token's K and V
         read once per kv head ((D + Dv) * elem), or D * elem when V aliases K."""
         per_tok = self.head_size if self.kv_aliased else self.head_size + self.v_head_size
-        return self.total_tokens * self.num_kv_heads * per_tok * self.elem_size
+        return self.total_tokens * self.num_kv_heads * per_tok * self.kv_elem_size
 
     def subset(self, seqs) -> "Workload":
         """The same workload restricted to some sequences (shares the caches)."""
@@ -99,7 +115,7 @@ class Workload:
 
     def to(self, device) -> "Workload":
         kw = {k: getattr(self, k) for k in self.__dataclass_fields__}
-        for k in ("seq_lens", "block_tables", "query", "cu_num_blocks"):
+        for k in ("seq_lens", "block_tables", "query", "cu_num_blocks", "alibi_slopes"):
             if kw[k] is not None:
                 kw[k] = kw[k].to(device)
         if self.latent is not None:
@@ -125,6 +141,29 @@ def _randn(gen, shape, dtype):
     return torch.randn(shape, generator=gen, dtype=torch.float32).to(dtype)
 
 
+FP8_NAN_CODE = 0x7F
+
+
+def _fp8_cache(gen, shape, kind: str, scale: float) -> torch.Tensor:
+    """uint8 E4M3 codes: "fp8" quantises N(0, 1) / scale (clamped to the
+    largest finite value, 448), "fp8_codes" draws the 254 non-NaN codes
+    uniformly."""
+    if kind == "fp8":
+        z = torch.randn(shape, generator=gen, dtype=torch.float32) / scale
+        return z.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    if kind == "fp8_codes":
+        c = torch.randint(0, 254, shape, generator=gen, dtype=torch.int64)
+        c = c + (c >= FP8_NAN_CODE).to(torch.int64)  # skip 0x7F; 0xFF is past the range
+        return c.to(torch.uint8)
+    raise ValueError(f"unknown fp8 cache kind {kind}")
+
+
+def alibi_slopes(num_heads: int) -> torch.Tensor:
+    """fp32 [H]: 2^(-8 i / H), i = 1..H."""
+    i = torch.arange(1, num_heads + 1, dtype=torch.float64)
+    return torch.pow(2.0, -8.0 * i / num_heads).to(torch.float32)
+
+
 def _assign_blocks(perm: torch.Tensor, nblocks: List[int], max_blocks: int, pad: int) -> torch.Tensor:
     """Block table rows filled from perm in order (seq, then logical block)."""
     bt = torch.full((len(nblocks), max(max_blocks, 1)), pad, dtype=torch.int32)
@@ -142,10 +181,15 @@ def _blocks_needed(lens, bs):
 def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size: int,
            v_head_size: Optional[int] = None, block_size: int, dtype="f32",
            num_blocks: Optional[int] = None, partition_size: int = 512,
-           max_blocks: Optional[int] = None, poison: bool = False, name="custom") -> Workload:
-    """Standard layout workload with the given lengths (drawn in the standard order)."""
+           max_blocks: Optional[int] = None, poison: bool = False, name="custom",
+           kv_cache: str = "same", k_scale: float = 1.0, v_scale: float = 1.0,
+           alibi: bool = False) -> Workload:
+    """Standard layout workload with the given lengths (drawn in the standard
+    order). kv_cache "fp8" / "fp8_codes" gives uint8 E4M3 caches (see the
+    module docstring) with the given scales; alibi adds ALiBi slopes."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
-    esz = torch.tensor([], dtype=dt).element_size()
+    fp8 = kv_cache != "same"
+    esz = 1 if fp8 else torch.tensor([], dtype=dt).element_size()
     x = 16 // esz
     dv = v_head_size or head_size
     gen = torch.Generator().manual_seed(seed)
@@ -158,8 +202,12 @@ def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size:
     perm = torch.randperm(nb, generator=gen)
     S = lens.shape[0]
     q = _randn(gen, (S, num_heads, head_size), dt)
-    kc = _randn(gen, (nb, num_kv_heads, head_size // x, block_size, x), dt)
-    vc = _randn(gen, (nb, num_kv_heads, dv, block_size), dt)
+    kshape, vshape = (nb, num_kv_heads, head_size // x, block_size, x), (nb, num_kv_heads, dv, block_size)
+    if fp8:
+        kc = _fp8_cache(gen, kshape, kv_cache, k_scale)
+        vc = _fp8_cache(gen, vshape, kv_cache, v_scale)
+    else:
+        kc, vc = _randn(gen, kshape, dt), _randn(gen, vshape, dt)
     poison_block = int(perm[total]) if poison else None
     mb = max_blocks if max_blocks is not None else max(need + [1])
     bt = _assign_blocks(perm, need, mb, poison_block if poison else 0)
@@ -167,7 +215,9 @@ def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size:
                  key_cache=kc, value_cache=vc, scale=1.0 / math.sqrt(head_size),
                  num_heads=num_heads, num_kv_heads=num_kv_heads, head_size=head_size,
                  v_head_size=dv, block_size=block_size, x=x, num_blocks=nb,
-                 partition_size=partition_size, poison_block=poison_block)
+                 partition_size=partition_size, poison_block=poison_block,
+                 kv_dtype=torch.uint8 if fp8 else None, k_scale=k_scale, v_scale=v_scale,
+                 alibi_slopes=alibi_slopes(num_heads) if alibi else None)
     if poison:
         _poison(w, need)
     return w
@@ -179,7 +229,7 @@ def _poison(w: Workload, need: List[int]):
     used = torch.zeros(w.num_blocks, dtype=torch.bool)
     for s, n in enumerate(need):
         used[w.block_tables[s, :n].long()] = True
-    nan = float("nan")
+    nan = FP8_NAN_CODE if w.key_cache.dtype == torch.uint8 else float("nan")
     w.key_cache[~used] = nan
     w.value_cache[~used] = nan
     bs = w.block_size

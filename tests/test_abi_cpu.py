@@ -144,6 +144,57 @@ def test_decode_mfma_hint_rejected_where_it_does_not_apply(lib):
     assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
 
 
+def good_fp8(**kw):
+    """A valid bf16-query problem over FP8 E4M3 caches (x = 16, byte strides)."""
+    a = good_decode(**kw)
+    D, Dv, Hkv, bs = a.head_size, a.v_head_size, a.num_kv_heads, a.block_size
+    a.x = 16
+    a.k_stride_b, a.k_stride_h, a.k_stride_dx, a.k_stride_bs, a.k_stride_x = Hkv * D * bs, D * bs, bs * 16, 16, 1
+    a.kv_dtype = api.PA_FP8_E4M3
+    a.k_scale, a.v_scale = 0.05, 0.1
+    return a
+
+
+FP8_BAD = [
+    ("k_scale_zero", dict(k_scale=0.0), api.PA_EINVAL),
+    ("v_scale_zero", dict(v_scale=0.0), api.PA_EINVAL),
+    ("k_scale_inf", dict(k_scale=float("inf")), api.PA_EINVAL),
+    ("v_scale_nan", dict(v_scale=float("nan")), api.PA_EINVAL),
+    ("kv_dtype_unknown", dict(kv_dtype=9), api.PA_EINVAL),
+    ("x_of_query_dtype", dict(x=8, k_stride_bs=8, k_stride_dx=16 * 8), api.PA_ENOTSUP),
+    ("mfma_hint", dict(kernel_hint=api.PA_KERNEL["mfma"]), api.PA_ENOTSUP),
+    ("misaligned_block", dict(k_stride_b=2 * 128 * 16 + 8), api.PA_ENOTSUP),
+]
+
+
+@pytest.mark.parametrize("name,change,code", FP8_BAD, ids=[c[0] for c in FP8_BAD])
+def test_decode_fp8_rejects(lib, name, change, code):
+    a = _mut(good_fp8(), **change)
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == code
+    assert lib.pa_last_error()
+
+
+def test_decode_kv_dtype_must_be_query_dtype_or_fp8(lib):
+    a = _mut(good_decode(), kv_dtype=api.PA_F16)  # bf16 query over f16 caches
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_EINVAL
+    a = _mut(good_decode(), kv_dtype=api.PA_BF16, num_seqs=0)  # equal to dtype: accepted
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_OK
+    a = _mut(good_fp8(), num_seqs=0)
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_OK
+
+
+def test_decode_balanced_splits_need_the_mla_kernel(lib):
+    """Balanced splits are built into the latent-row kernel only, which takes
+    neither ALiBi nor fp8 caches."""
+    a = good_decode(D=576, Dv=512, H=16, Hkv=1, bs=1)
+    a.value_cache = a.key_cache
+    a.v_stride_b, a.v_stride_h = a.k_stride_b, a.k_stride_h
+    a.partition_size, a.num_workers, a.max_num_parts = 0, 256, 256
+    a.alibi_slopes = FAKE
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
+    assert "ALiBi" in lib.pa_last_error().decode()
+
+
 def test_decode_empty_batch_is_a_noop(lib):
     a = _mut(good_decode(), num_seqs=0, query=None)
     assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_OK

@@ -1,0 +1,149 @@
+"""Parity of the phase-1 variants with the CPU oracle: FP8 E4M3 caches with
+k_scale / v_scale, and ALiBi slopes, on every kernel that serves them.
+
+The fp8 path decodes codes exactly to fp32 and computes in fp32, so its
+outputs take the fp32-cache tolerances; ALiBi on the matrix-core kernel
+keeps the bf16/f16 ones. Unused cache slots and unreferenced blocks are
+poisoned (NaN, or the E4M3 NaN code 0x7F) where the case says so.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_decode_tables_amd as pad
+from paged_attention_decode_tables_amd import workloads
+from gpu_util import (check_output, check_partials, oracle_args, oracle_kw,
+                      run_gpu, say, tolerances)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pad.load_library()
+
+
+CASES = [
+    # name, workload kwargs, run kwargs
+    ("fp8_gqa_bf16", dict(seed=101, seq_lens=[1, 17, 300, 1000, 2049, 0, 64], num_heads=8,
+                          num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+                          kv_cache="fp8", k_scale=0.05, v_scale=0.08, poison=True), {}),
+    ("fp8_gqa_bf16_splits", dict(seed=102, seq_lens=[3000, 5, 700, 1], num_heads=16,
+                                 num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+                                 kv_cache="fp8", k_scale=0.03, v_scale=0.1, poison=True),
+     dict(num_splits=[7, 1, 3, 2], max_parts=8)),
+    ("fp8_bs8_f32_group4", dict(seed=103, seq_lens=[100, 513, 7], num_heads=4, num_kv_heads=1,
+                                head_size=128, block_size=8, dtype="f32", kv_cache="fp8",
+                                k_scale=0.05, v_scale=0.05, poison=True), {}),
+    ("fp8_bs1_rows_f16", dict(seed=104, seq_lens=[300, 45], num_heads=2, num_kv_heads=2,
+                              head_size=128, block_size=1, dtype="f16", kv_cache="fp8",
+                              k_scale=0.05, v_scale=0.2, poison=True), dict(partition_size=128)),
+    ("fp8_latent_576", dict(seed=105, seq_lens=[600, 31], num_heads=16, num_kv_heads=1,
+                            head_size=576, v_head_size=512, block_size=1, dtype="bf16",
+                            kv_cache="fp8", k_scale=0.02, v_scale=0.05), {}),
+    ("fp8_bs64_mha_f16", dict(seed=106, seq_lens=[2000, 129, 64, 63], num_heads=4, num_kv_heads=4,
+                              head_size=64, block_size=64, dtype="f16", kv_cache="fp8",
+                              k_scale=0.05, v_scale=0.05, poison=True), dict(partition_size=256)),
+    ("alibi_mfma_bf16", dict(seed=111, seq_lens=[1, 2, 33, 1000, 3000], num_heads=32,
+                             num_kv_heads=4, head_size=128, block_size=16, dtype="bf16",
+                             alibi=True, poison=True), dict(kernel="mfma")),
+    ("alibi_mfma_f16_d64_g16", dict(seed=112, seq_lens=[513, 77, 4096], num_heads=32,
+                                    num_kv_heads=2, head_size=64, block_size=32, dtype="f16",
+                                    alibi=True, poison=True), dict(kernel="mfma")),
+    ("alibi_mfma_bf16_splits", dict(seed=113, seq_lens=[5000, 40, 900], num_heads=16,
+                                    num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+                                    alibi=True), dict(kernel="mfma", num_splits=[9, 1, 4],
+                                                      max_parts=12)),
+    ("alibi_valu_f32", dict(seed=114, seq_lens=[700, 3, 64], num_heads=4, num_kv_heads=4,
+                            head_size=128, block_size=16, dtype="f32", alibi=True, poison=True),
+     dict(kernel="valu")),
+    ("alibi_valu_bf16_group", dict(seed=115, seq_lens=[1500, 9], num_heads=16, num_kv_heads=2,
+                                   head_size=128, block_size=16, dtype="bf16", alibi=True),
+     dict(kernel="valu")),
+    ("alibi_fp8_bf16", dict(seed=116, seq_lens=[2500, 1, 130], num_heads=8, num_kv_heads=1,
+                            head_size=128, block_size=16, dtype="bf16", kv_cache="fp8",
+                            k_scale=0.05, v_scale=0.05, alibi=True, poison=True), {}),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_variant_matches_oracle(orc, case):
+    name, wkw, rkw = case
+    say(f"variant {name}")
+    w = workloads.custom(name=name, **wkw)
+    P = rkw.get("partition_size", 512)
+    out, tmp, ml, es = run_gpu(w, **rkw)
+    check_partials(w, orc, tmp, ml, es, partition_size=P, num_splits=rkw.get("num_splits"))
+    check_output(w, orc, out)
+
+
+def _live_codes(cache: torch.Tensor, w: workloads.Workload, value: bool) -> torch.Tensor:
+    """Codes of every live token of a paged fp8 cache."""
+    bs = w.block_size
+    parts = []
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        for i in range((L + bs - 1) // bs):
+            n = min(bs, L - i * bs)
+            blk = cache[int(w.block_tables[s, i])]
+            parts.append((blk[:, :, :n] if value else blk[:, :, :n, :]).flatten())
+    return torch.cat(parts)
+
+
+def test_fp8_every_code(orc):
+    """Codes uniform over all 254 non-NaN E4M3 codes (subnormals, both zeros,
+    448), each present in the live keys and values."""
+    say("fp8 every code")
+    w = workloads.custom(seed=120, seq_lens=[700, 5, 129], num_heads=4, num_kv_heads=4,
+                         head_size=64, block_size=32, dtype="f16", kv_cache="fp8_codes",
+                         k_scale=1.0 / 448, v_scale=1.0 / 448, poison=True)
+    for value, c in ((False, w.key_cache), (True, w.value_cache)):
+        seen = torch.bincount(_live_codes(c, w, value).long(), minlength=256)
+        assert int((seen > 0).sum()) == 254 and seen[0x7F] == 0 and seen[0xFF] == 0
+    out, tmp, ml, es = run_gpu(w, partition_size=256)
+    check_partials(w, orc, tmp, ml, es, partition_size=256)
+    check_output(w, orc, out)
+
+
+def test_alibi_moves_the_output(orc):
+    """The slopes are applied: the result is far from the no-ALiBi one."""
+    say("alibi changes the output")
+    w = workloads.custom(seed=121, seq_lens=[400, 1200], num_heads=16, num_kv_heads=2,
+                         head_size=128, block_size=16, dtype="bf16", alibi=True)
+    out = run_gpu(w, kernel="mfma")[0].double().numpy()
+    plain = orc.attention(*oracle_args(w))
+    assert np.abs(out - plain).max() > 20 * tolerances(w)[0]
+    ref = orc.attention(*oracle_args(w), **oracle_kw(w))
+    assert np.abs(out - ref).max() <= tolerances(w)[0]
+
+
+def test_alibi_latent_rows_run_on_the_vector_kernel(orc):
+    """Latent rows (V aliasing K, page size 1) with ALiBi: the latent-row
+    matrix-core kernel does not take slopes, so auto dispatch serves them on
+    the vector kernel, and asking for a matrix-core kernel is refused."""
+    say("alibi latent rows")
+    w = workloads.mla_custom(seed=122, seq_lens=[300, 1, 1000], num_heads=16, poison=True)
+    w.alibi_slopes = workloads.alibi_slopes(16)
+    out, tmp, ml, es = run_gpu(w)
+    check_partials(w, orc, tmp, ml, es)
+    check_output(w, orc, out)
+    with pytest.raises(pad.PagedAttnError):
+        run_gpu(w, kernel="mfma")
+
+
+def test_fp8_scales_scale_linearly(orc):
+    """Halving v_scale halves the output; k_scale only reshapes the softmax."""
+    say("fp8 scales")
+    w = workloads.custom(seed=123, seq_lens=[800, 50], num_heads=4, num_kv_heads=1,
+                         head_size=128, block_size=16, dtype="bf16", kv_cache="fp8",
+                         k_scale=0.05, v_scale=0.1)
+    a = run_gpu(w)[0].double()
+    b = run_gpu(dataclasses.replace(w, v_scale=0.05))[0].double()  # the same codes
+    assert torch.allclose(b * 2, a, rtol=1e-6, atol=1e-7)
+    c = run_gpu(dataclasses.replace(w, k_scale=0.1))[0].double()
+    assert (c - a).abs().max() > 1e-2
+    check_output(dataclasses.replace(w, k_scale=0.1), orc, c.float())
