@@ -49,7 +49,8 @@ def kernel_kind(w) -> str:
     group = w.num_heads // w.num_kv_heads
     low = w.dtype in (torch.float16, torch.bfloat16)
     if low and w.head_size == 576 and w.v_head_size == 512 and w.block_size == 1 \
-            and group in (64, 128) and w.latent is not None:
+            and group in (64, 128) and w.latent is not None and w.alibi_slopes is None \
+            and w.kv_dtype is None:
         return "mla"
     if low and group > 1 and w.block_size >= 8 and w.head_size in (64, 128):
         return "mfma"
@@ -102,7 +103,8 @@ class Step:
         bt = self.flat if self.indptr is not None else g.block_tables
         pad.paged_attn_decode(self.tmp, self.es, self.ml, g.query, g.key_cache, g.value_cache, bt,
                               g.seq_lens, w.scale, w.max_seq_len, partition_size=self.partition,
-                              num_splits=self.ns, kv_indptr=self.indptr, num_workers=self.workers)
+                              num_splits=self.ns, kv_indptr=self.indptr, num_workers=self.workers,
+                              alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale)
 
     def reduce(self):
         w, g = self.w, self.g
@@ -140,13 +142,17 @@ def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int, min
     orc = oracle.get()
     n = w.num_seqs if sample_seqs <= 0 else min(sample_seqs, w.num_seqs)
     sub = w.subset(range(n))
-    args = (sub.query.float().numpy(), sub.key_cache.float().numpy(),
-            sub.value_cache.float().numpy(), sub.block_tables.numpy(), sub.seq_lens.numpy(),
-            sub.scale)
+    def cache(t):  # fp8 caches go to the oracle as their codes
+        return t.numpy() if t.dtype == torch.uint8 else t.float().numpy()
+
+    args = (sub.query.float().numpy(), cache(sub.key_cache), cache(sub.value_cache),
+            sub.block_tables.numpy(), sub.seq_lens.numpy(), sub.scale)
+    kw = dict(alibi=None if w.alibi_slopes is None else w.alibi_slopes.numpy(),
+              k_scale=w.k_scale, v_scale=w.v_scale)
     runs, total = 0, 0.0
     while runs == 0 or total < min_seconds:
         t0 = time.perf_counter()
-        ref = orc.attention(*args)
+        ref = orc.attention(*args, **kw)
         total += time.perf_counter() - t0
         runs += 1
     dt = total / runs
@@ -336,6 +342,9 @@ def main():
                          "decode-metadata launch on --md-workload; spec_table: the speculative "
                          "SWA page-table concat on the MLA batch")
     ap.add_argument("--md-workload", choices=sorted(MD_WORKLOADS), default="metadata_skewed_ps32_swa")
+    ap.add_argument("--kv-cache", choices=("same", "fp8"), default="same",
+                    help="fp8: the same workload with FP8 E4M3 caches (configs 2-4)")
+    ap.add_argument("--alibi", action="store_true", help="the same workload with ALiBi slopes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -365,7 +374,7 @@ def main():
         return
 
     log(f"bench: generating workload {args.config}")
-    w = workloads.config(args.config)
+    w = workloads.config(args.config, kv_cache=args.kv_cache, alibi=args.alibi)
     kind = kernel_kind(w)
     # The MLA workload's split policy is not fixed by its definition: it runs
     # with balanced splits, one token range per compute unit.
@@ -425,7 +434,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype],
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype]
+                 + ("/kv-fp8-e4m3" if w.kv_dtype is not None else ""),
         "data": "synthetic",
         "config": {"workload": w.name, "seqs": w.num_seqs, "seq_len_max": w.max_seq_len,
                    "tokens": w.total_tokens, "heads": w.num_heads, "kv_heads": w.num_kv_heads,
@@ -433,7 +443,10 @@ def main():
                    "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "partition": (f"balanced ({workers} token ranges)" if workers else
                                  w.partition_size if w.max_kv_splits is None else "num_kv_splits"),
-                   "kv_bytes_per_step": kv},
+                   "kv_bytes_per_step": kv,
+                   "kv_cache": (f"fp8 e4m3, k_scale = v_scale = {w.k_scale}" if w.kv_dtype is not None
+                                else "query dtype"),
+                   "alibi": w.alibi_slopes is not None},
         "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

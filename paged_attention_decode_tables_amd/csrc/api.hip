@@ -163,12 +163,12 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // latent rows: the value cache is the leading v_head_size columns of the key rows
-    // The matrix-core kernels read caches of the query's dtype; ALiBi is
-    // built into the grouped-head one, not the latent-row one.
+    // The grouped-head matrix-core kernel takes ALiBi and fp8 caches; the
+    // latent-row one takes neither.
     const bool mla_ok = pa::decode_mla_supported(a->dtype, D, Dv, group, a->block_size) &&
                         a->value_cache == a->key_cache && a->v_stride_b == a->k_stride_b &&
                         a->v_stride_h == a->k_stride_h && !fp8 && !a->alibi_slopes;
-    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size) && !fp8;
+    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size);
     if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok && !mla_ok)
         return fail(PA_ENOTSUP, "paged_attn_decode: no matrix-core kernel serves this problem");
     if (balanced && (!mla_ok || a->kernel_hint == PA_KERNEL_VALU))

@@ -44,21 +44,23 @@ struct FP8E4M3 {
     static constexpr int dtype = PA_FP8_E4M3;
 };
 
-// E4M3 code (low 8 bits of c) -> fp32: sign, exponent e (4 bits, bias 7),
-// mantissa m (3 bits). e >= 1: (1 + m/8) * 2^(e-7), i.e. the 7 bits moved to
-// the fp32 exponent / mantissa position with the bias raised by 120; e = 0:
-// m * 2^-9; e = 15 with m = 7: NaN. No infinities.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+// E4M3 codes -> fp32 with gfx950's conversion (two codes, the low or high
+// 16 bits of w, per instruction). It decodes OCP E4M3: sign, 4-bit exponent
+// with bias 7, 3-bit mantissa, subnormals m * 2^-9, NaN for exponent 15 with
+// mantissa 7, no infinities (checked for all 256 codes).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w, bool high)
 {
-    const uint32_t em = c & 0x7Fu;
-    float v = __uint_as_float((em << 20) + (120u << 23));
-    if (em < 8u) v = (float)em * 0x1p-9f;
-    if (em == 0x7Fu) v = __uint_as_float(0x7FC00000u);
-    return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+    return high ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint8_t v) { return e4m3_to_f32(v); }  // fp8 cache code
+__device__ __forceinline__ float to_f32(uint8_t v)  // fp8 cache code
+{
+    const f32x2 f = e4m3x2_to_f32(v, false);
+    return f[0];
+}
 __device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(__bf16 v)
 {
@@ -83,8 +85,8 @@ template <> __device__ __forceinline__ float hi16<F16>(uint32_t w)
 template <class E> __device__ __forceinline__ float elem16(const u32x4& v, int i)
 {
     if constexpr (E::size == 1) {
-        const uint32_t w = v[i >> 2];
-        return e4m3_to_f32(w >> (8 * (i & 3)));
+        const f32x2 f = e4m3x2_to_f32(v[i >> 2], (i & 2) != 0);
+        return (i & 1) ? f[1] : f[0];
     } else if constexpr (E::size == 4) {
         // copy the element out first: bit-casting the vector-element lvalue
         // directly reads element 0 with this compiler
@@ -106,6 +108,11 @@ __device__ __forceinline__ u32x4 load16(const void* p)
 __device__ __forceinline__ u32x4 load16_stream(const void* p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x2 load8_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
 template <class E> __device__ __forceinline__ void store_out(void* base, int64_t idx, float v);

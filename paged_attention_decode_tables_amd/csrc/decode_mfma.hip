@@ -7,13 +7,18 @@
 // heads that share one kv head at once, so each K/V byte is read from HBM
 // once per (seq, kv head) instead of G times.
 //
-// One workgroup per (seq, kv head, split); its waves take contiguous runs of
-// the split's chunks and merge their softmax states at the end. In a wave,
-// lane = 16*g + r (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
+// One single-wave workgroup per (seq, kv head, run of up to four consecutive
+// splits): the load pipeline runs through the whole run, and at each split
+// boundary the split's softmax state is normalised, parked in LDS and
+// reset (the last split's goes straight out); the parked ones are written
+// after the loop. Fewer, longer workgroups cut the per-workgroup start-up
+// and drain that dominated with one workgroup per 512-token split. In the
+// wave, lane = 16*g + r (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
 // unused columns get q = 0 and are never stored). The split is walked in
-// 32-token chunks, all in registers, double-buffered (the next chunk's 16 KB
-// of K/V loads are in flight while the current chunk is used), with the
-// split's block ids held in a register and fetched by lane shuffles:
+// 32-token chunks, loaded in 16 KB tiles of K/V (one chunk of 16-bit caches,
+// two of fp8), all in registers and double-buffered (the next tile's loads
+// are in flight while the current one is used), with the split's block ids
+// held in a register and fetched by lane shuffles:
 //
 //   QK:  S^T[t][h] = sum_d K[t][d] Q[h][d] as two 16x16x32 products per
 //        32 d (tile 0 and tile 1 of the chunk). Lane (g, r) feeds A with 8
@@ -34,16 +39,38 @@
 // Chunks that run past the split end clamp their loads to the last valid
 // 8-token group (always inside an allocated block) and mask: scores -inf,
 // values 0, so NaN padding in unused slots never reaches the output.
+//
+// FP8 E4M3 caches (x = 16) run the same products on the query's 16-bit type:
+// every E4M3 value is exact in bf16 and in f16, so codes are widened in
+// registers (two per conversion instruction) and nothing is rounded that the
+// 16-bit path does not round. A 16-byte key piece then holds 16 d of one
+// token and feeds two k-steps: lane (g, r) takes d = 64p + 16g + 0..7 for
+// k-step 2p and + 8..15 for k-step 2p + 1, and q is loaded in that order. A
+// value operand is 8 codes (8 tokens of one row, an 8-byte load). k_scale is
+// in the score scale, v_scale is applied with the final normalisation.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace pa {
 
 template <class E> struct MfmaOps;
+// from_fp8(lo, hi): the 8 E4M3 codes in the bytes of lo, hi (first code in
+// the low byte of lo) as 8 exact values of the 16-bit type.
 template <> struct MfmaOps<BF16> {
     typedef bf16x8 vec;
     static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ vec from_fp8(uint32_t lo, uint32_t hi)
+    {
+        u32x4 w;
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+        w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+        w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+        return __builtin_bit_cast(vec, w);
     }
 };
 template <> struct MfmaOps<F16> {
@@ -52,76 +79,91 @@ template <> struct MfmaOps<F16> {
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ vec from_fp8(uint32_t lo, uint32_t hi)
+    {
+        u32x4 w;
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+        w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+        w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+        return __builtin_bit_cast(vec, w);
+    }
 };
 
-// Waves per workgroup. The chunks of a split are shared out in contiguous
-// runs, one run per wave, and the waves' softmax states are merged through
-// LDS at the end; several short runs per split keep the tail of the grid
-// short when the splits outnumber the wave slots.
-#ifndef PA_MFMA_WAVES
-#define PA_MFMA_WAVES 1
-#endif
-constexpr int kMfmaWaves = PA_MFMA_WAVES;
-// Pipeline depth: 1 = half-chunk pipeline (one 8 KB half in flight while
-// the other is used), 2 = double buffering (the next 16 KB chunk in flight).
-#ifndef PA_MFMA_PIPE
-#define PA_MFMA_PIPE 2
+// Splits per workgroup at most (the host picks 1..kMfmaMaxRun so that the
+// grid is about one workgroup per SIMD).
+constexpr int kMfmaMaxRun = 4;
+// 32-token chunks per load tile with fp8 caches (1: 8 KB tiles, 2: 16 KB).
+#ifndef PA_MFMA_FP8_SUB
+#define PA_MFMA_FP8_SUB 2
 #endif
 // Waves per SIMD the register budget is sized for.
 #ifndef PA_MFMA_OCCUPANCY
-#define PA_MFMA_OCCUPANCY (PA_MFMA_PIPE == 1 ? 3 : 2)
+#define PA_MFMA_OCCUPANCY 2
 #endif
 
 // BS > 0 fixes the block size at compile time (every load of a chunk is then
 // an immediate offset from two base addresses); BS == 0 reads it at run time.
-template <class E, int D, int DV, int BS>
-__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCUPANCY))) void k_decode_mfma(DecodeParams p)
+template <class E, class KE, int D, int DV, int BS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCUPANCY))) void k_decode_mfma(DecodeParams p)
 {
     using T = typename E::storage;
+    using KT = typename KE::storage;
     using Ops = MfmaOps<E>;
     using vec = typename Ops::vec;
+    constexpr bool F8 = KE::size == 1;  // fp8 codes, x = 16
+    constexpr int KX = F8 ? 16 : 8;     // key packing x
     constexpr int KS = D / 32;   // QK k-steps
     constexpr int MT = DV / 16;  // PV value-row tiles
-    constexpr int W = kMfmaWaves;
+    // A load tile is NSUB 32-token chunks: one for 16-bit caches, two for
+    // fp8 (the same 16 KB of K/V per tile either way).
+    constexpr int NSUB = F8 ? PA_MFMA_FP8_SUB : 1;
+    constexpr int CH = 32 * NSUB;
 
-    // grid (kv head + Hkv * seq, split): workgroups are dealt to the XCDs
-    // round-robin by linear id. With the kv head fastest, every XCD gets an
-    // equal share of every sequence's tokens (Hkv a multiple of 8: exactly
-    // one kv head's), whatever the length mix; the split index last keeps
-    // each split index's work (split 0 is never empty, high splits often
+    // grid (kv head + Hkv * seq, run of splits): workgroups are dealt to the
+    // XCDs round-robin by linear id. With the kv head fastest, every XCD gets
+    // an equal share of every sequence's tokens (Hkv a multiple of 8: exactly
+    // one kv head's), whatever the length mix; the run index last keeps
+    // each run index's work (the first is never empty, late ones often
     // are) spread over all XCDs.
-    const int kvh = blockIdx.x % p.num_kv_heads, s = blockIdx.x / p.num_kv_heads, part = blockIdx.y;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const int kvh = blockIdx.x % p.num_kv_heads, s = blockIdx.x / p.num_kv_heads;
+    const int part0 = blockIdx.y * p.split_run;  // first split of the run
+    const int nrun = min(p.split_run, p.grid_parts - part0);
+    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const int G = p.group;
     const int h = kvh * G + r;
     const bool head_ok = r < G;
+    const int64_t mlbase = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part0;
 
     // token positions fit in 32 bits (lengths are int32)
     const int L = p.seq_lens[s];
     const int64_t len64 = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
-    const int64_t start64 = (int64_t)part * len64;
-    if (start64 >= (int64_t)L) {
-        if (wave == 0 && head_ok && g == 0) {
-            const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
-            p.max_logits[mloff] = -INFINITY;
-            p.exp_sums[mloff] = 0.0f;
+    const int64_t start64 = (int64_t)part0 * len64;
+    // splits of the run that hold tokens: [0, nlive); the rest are empty
+    const int nlive = start64 < (int64_t)L
+                          ? (int)min((int64_t)nrun, ((int64_t)L - start64 + len64 - 1) / len64)
+                          : 0;
+    if (head_ok && g == 0) {
+        for (int j = nlive; j < nrun; ++j) {
+            p.max_logits[mlbase + j] = -INFINITY;
+            p.exp_sums[mlbase + j] = 0.0f;
         }
-        return;
     }
+    if (nlive == 0) return;
     const int start = (int)start64;
-    const int end = (int)((int64_t)L < start64 + len64 ? (int64_t)L : start64 + len64);
-    // this wave's run of 32-token chunks: [ca, cb)
-    const int nc = (end - start + 31) >> 5;
-    const int ca = wave * nc / W, cb = (wave + 1) * nc / W;
+    const int end = (int)min((int64_t)L, start64 + (int64_t)nlive * len64);
+    // the run's CH-token tiles: [ca, cb)
+    const int ca = 0, cb = (end - start + CH - 1) / CH;
 
-    // B operand of QK: lane (g, r) holds q[h][32*ks + 8g .. +8]
+    // B operand of QK: lane (g, r) holds q[h][32*ks + 8g .. +8] (fp8 caches:
+    // q[h][64*(ks/2) + 16g + 8*(ks%2) .. +8], the order the key pieces hold)
     vec qv[KS];
     {
-        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh + g * 8;
+        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 w = head_ok ? load16(q + ks * 32) : u32x4{0, 0, 0, 0};
+            const int d0 = F8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
+            u32x4 w = head_ok ? load16(q + d0) : u32x4{0, 0, 0, 0};
             qv[ks] = __builtin_bit_cast(vec, w);
         }
     }
@@ -130,18 +172,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const int bs = 1 << bs_shift;
     const int32_t* row = page_row(p.pl, s);
     const int64_t sb = p.pl.stride_b;
-    const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
-    const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)kvh * p.v_sh;
+    const KT* kc = reinterpret_cast<const KT*>(p.kc) + (int64_t)kvh * p.k_sh;
+    const KT* vc = reinterpret_cast<const KT*>(p.vc) + (int64_t)kvh * p.v_sh;
     const int last_group = (end - 1) & ~7;
     // ALiBi: slope of head r in base-2 units (0 without slopes or past the group)
     const float slope = (p.alibi && head_ok) ? p.alibi[h] * kLog2e : 0.0f;
 
     // Block-table window held in a register: lane i has the id of block
-    // blk0 + wb + i of this wave's run; the next 64 ids are fetched one window
-    // ahead. Chunks never straddle a window (runs start on 32-token
-    // boundaries, so a window of 64 whole blocks ends on a chunk boundary).
-    const int wstart = start + 32 * ca;
-    const int wend = min(end, start + 32 * cb);
+    // blk0 + wb + i of the run; the next 64 ids are fetched one window
+    // ahead. Tiles never straddle a window: split starts are multiples of 64
+    // tokens, so runs start on tile boundaries, and a window of 64 whole
+    // blocks (block size >= 8) ends on one.
+    const int wstart = start + CH * ca;
+    const int wend = min(end, start + CH * cb);
     const int blk0 = wstart >> bs_shift;
     const int nblk = ca < cb ? ((wend - 1) >> bs_shift) - blk0 + 1 : 0;
     auto fetch_window = [&](int base) -> int32_t {
@@ -165,24 +208,40 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     // tiles), tv: its value group (column group g of the PV tile); both are
     // clamped to the last valid group so every load stays inside a block
     // that holds live tokens.
+    // Key pieces per chunk and MFMA tile: one per k-step, or (fp8) one per
+    // pair of k-steps.
+    constexpr int KP = F8 ? KS / 2 : KS;
+    using VPiece = typename std::conditional<F8, u32x2, u32x4>::type;
     struct Tile {
-        u32x4 k[2 * KS];  // K of the chunk: tile 0 (tokens 8j..8j+3), tile 1 (+4)
-        u32x4 v[MT];      // V of the chunk: 16 value rows per tile
+        u32x4 k[NSUB][2 * KP];  // K of each chunk: MFMA tile 0 (tokens 8j..8j+3), tile 1 (+4)
+        VPiece v[NSUB][MT];     // V of each chunk: 16 value rows per MFMA tile, 8 tokens each
     };
+    // Chunks past the split end (the second chunk of a tail tile) load the
+    // clamped group like any other masked tokens.
     auto issue_k = [&](Tile& t, int c0) {
-        const int tk = min(c0 + 8 * (r >> 2), last_group);
-        const T* kp = kc + block_of(tk) * p.k_sb + (((tk & (bs - 1)) + (r & 3)) * 8 + g * bs * 8);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            t.k[2 * ks] = load16_stream(kp + ks * 4 * bs * 8);
-            t.k[2 * ks + 1] = load16_stream(kp + ks * 4 * bs * 8 + 32);
+        for (int u = 0; u < NSUB; ++u) {
+            const int tk = min(c0 + 32 * u + 8 * (r >> 2), last_group);
+            // piece (4*kp + g) of the token's D/KX pieces
+            const KT* kp = kc + block_of(tk) * p.k_sb + (((tk & (bs - 1)) + (r & 3)) * KX + g * bs * KX);
+#pragma unroll
+            for (int kp_ = 0; kp_ < KP; ++kp_) {
+                t.k[u][2 * kp_] = load16_stream(kp + kp_ * 4 * bs * KX);
+                t.k[u][2 * kp_ + 1] = load16_stream(kp + kp_ * 4 * bs * KX + 4 * KX);
+            }
         }
     };
     auto issue_v = [&](Tile& t, int c0) {
-        const int tv = min(c0 + 8 * g, last_group);
-        const T* vp = vc + block_of(tv) * p.v_sb + (r * bs + (tv & (bs - 1)));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) t.v[mt] = load16_stream(vp + mt * 16 * bs);
+        for (int u = 0; u < NSUB; ++u) {
+            const int tv = min(c0 + 32 * u + 8 * g, last_group);
+            const KT* vp = vc + block_of(tv) * p.v_sb + (r * bs + (tv & (bs - 1)));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (F8) t.v[u][mt] = load8_stream(vp + mt * 16 * bs);
+                else t.v[u][mt] = load16_stream(vp + mt * 16 * bs);
+            }
+        }
     };
 
     float m = -INFINITY;  // running max of head r (base 2)
@@ -194,12 +253,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     // Scores and online-softmax update for the chunk at c0 (uses kt); returns
     // the probabilities as the P.V operand and leaves alpha for the rescale.
     float alpha = 1.0f;
-    auto scores = [&](Tile& t, int c0) -> vec {
+    auto scores = [&](Tile& t, int u, int c0) -> vec {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (F8) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s0 = Ops::mma(__builtin_bit_cast(vec, t.k[2 * ks]), qv[ks], s0);
-            s1 = Ops::mma(__builtin_bit_cast(vec, t.k[2 * ks + 1]), qv[ks], s1);
+            for (int kp_ = 0; kp_ < KP; ++kp_) {
+                const u32x4 a = t.k[u][2 * kp_], b = t.k[u][2 * kp_ + 1];
+                s0 = Ops::mma(Ops::from_fp8(a[0], a[1]), qv[2 * kp_], s0);
+                s1 = Ops::mma(Ops::from_fp8(b[0], b[1]), qv[2 * kp_], s1);
+                s0 = Ops::mma(Ops::from_fp8(a[2], a[3]), qv[2 * kp_ + 1], s0);
+                s1 = Ops::mma(Ops::from_fp8(b[2], b[3]), qv[2 * kp_ + 1], s1);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s0 = Ops::mma(__builtin_bit_cast(vec, t.k[u][2 * ks]), qv[ks], s0);
+                s1 = Ops::mma(__builtin_bit_cast(vec, t.k[u][2 * ks + 1]), qv[ks], s1);
+            }
         }
         float sc[8];
 #pragma unroll
@@ -236,51 +306,80 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         return pv;
     };
     // Rescale and P.V for the chunk at c0 (uses vt).
-    auto weigh = [&](Tile& t, int c0, vec pv) {
+    auto weigh = [&](Tile& t, int u, int c0, vec pv) {
+        // Once the running maxima settle, alpha is 1 in every lane: the
+        // rescale is skipped for the whole wave then (a scalar branch).
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+            for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+        }
         if (end - c0 < 32) {
             const int t0 = c0 + 8 * g;
-            u32x4 keep;
+            if constexpr (F8) {
+                u32x2 keep;  // byte j of word w: token t0 + 4w + j
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                keep[w] = (t0 + 2 * w < end ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < end ? 0xffff0000u : 0u);
+                for (int w = 0; w < 2; ++w) {
+                    uint32_t k = 0;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) t.v[mt] &= keep;
+                    for (int j = 0; j < 4; ++j) k |= (t0 + 4 * w + j < end ? 0xffu : 0u) << (8 * j);
+                    keep[w] = k;
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) t.v[u][mt] &= keep;
+            } else {
+                u32x4 keep;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    keep[w] = (t0 + 2 * w < end ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < end ? 0xffff0000u : 0u);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) t.v[u][mt] &= keep;
+            }
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = Ops::mma(__builtin_bit_cast(vec, t.v[mt]), pv, acc[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (F8) {
+                const u32x2 v = t.v[u][mt];
+                acc[mt] = Ops::mma(Ops::from_fp8(v[0], v[1]), pv, acc[mt]);
+            } else {
+                acc[mt] = Ops::mma(__builtin_bit_cast(vec, t.v[u][mt]), pv, acc[mt]);
+            }
+        }
+    };
+    // Split boundaries inside the run: when a tile ends one (and the run goes
+    // on), the split's state is normalised into LDS slot `parked` and reset.
+    // LDS traffic counts apart from the vector-memory waits of the pipeline.
+    extern __shared__ f32x4 park[];  // [split_run - 1][MT][64] rows, then m, l
+    float* park_ml = reinterpret_cast<float*>(park + (p.split_run - 1) * MT * kWave);
+    int parked = 0;
+    int64_t next_boundary = start64 + len64;
+    auto flush = [&](float* m_out, float* l_out, f32x4* rows) {
+        float lt = l + __shfl_xor(l, 16, kWave);
+        lt += __shfl_xor(lt, 32, kWave);
+        const float inv = p.v_scale / lt;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) rows[mt * kWave] = acc[mt] * inv;
+        if (g == 0) {
+            *m_out = m * kLn2;
+            *l_out = lt;
+        }
+    };
+    // Scores, softmax and P.V of every chunk of the tile at c0.
+    auto use = [&](Tile& t, int c0) {
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) weigh(t, u, c0 + 32 * u, scores(t, u, c0 + 32 * u));
+        if ((int64_t)(c0 + CH) >= next_boundary && c0 + CH < end) {
+            flush(park_ml + 32 * parked + r, park_ml + 32 * parked + 16 + r,
+                  park + parked * MT * kWave + lane);
+            ++parked;
+            next_boundary += len64;
+            m = -INFINITY;
+            l = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     };
 
-#if PA_MFMA_PIPE == 1
-    // Software pipeline at half-chunk granularity: once the scores of chunk
-    // i are formed its K registers receive chunk i+1's keys, and once its
-    // P.V is done its V registers receive chunk i+1's values, so one half of
-    // a chunk (8 KB) is always in flight while the other half is used. The
-    // last chunk is peeled so every wait in the loop is a fixed count; the
-    // scheduling fences keep the next loads from being hoisted above the
-    // math that frees their registers.
-    if (ca < cb) {
-        Tile t;
-        issue_k(t, wstart);
-        issue_v(t, wstart);
-        int c0 = wstart;
-        for (int i = ca; i + 1 < cb; ++i, c0 += 32) {
-            advance_window(c0 + 32);
-            vec pv = scores(t, c0);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_k(t, c0 + 32);
-            __builtin_amdgcn_sched_barrier(0);
-            weigh(t, c0, pv);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_v(t, c0 + 32);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        vec pv = scores(t, c0);
-        weigh(t, c0, pv);
-    }
-#else
-    // Double buffering: the whole next chunk (16 KB) is requested before the
+    // Double buffering: the whole next tile (16 KB) is requested before the
     // current one is used. The loop is unrolled by two so the buffers have
     // fixed registers and every wait is for exactly one tile.
     if (ca < cb) {
@@ -289,78 +388,58 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         issue_v(A, wstart);
         int c0 = wstart;
         int i = ca;
-        for (; i + 2 < cb; i += 2, c0 += 64) {
-            advance_window(c0 + 32);
-            issue_k(B, c0 + 32);
-            issue_v(B, c0 + 32);
+        for (; i + 2 < cb; i += 2, c0 += 2 * CH) {
+            advance_window(c0 + CH);
+            issue_k(B, c0 + CH);
+            issue_v(B, c0 + CH);
             __builtin_amdgcn_sched_barrier(0);
-            weigh(A, c0, scores(A, c0));
+            use(A, c0);
             __builtin_amdgcn_sched_barrier(0);
-            advance_window(c0 + 64);
-            issue_k(A, c0 + 64);
-            issue_v(A, c0 + 64);
+            advance_window(c0 + 2 * CH);
+            issue_k(A, c0 + 2 * CH);
+            issue_v(A, c0 + 2 * CH);
             __builtin_amdgcn_sched_barrier(0);
-            weigh(B, c0 + 32, scores(B, c0 + 32));
+            use(B, c0 + CH);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (i + 1 < cb) {
-            advance_window(c0 + 32);
-            issue_k(B, c0 + 32);
-            issue_v(B, c0 + 32);
+            advance_window(c0 + CH);
+            issue_k(B, c0 + CH);
+            issue_v(B, c0 + CH);
             __builtin_amdgcn_sched_barrier(0);
-            weigh(A, c0, scores(A, c0));
+            use(A, c0);
             __builtin_amdgcn_sched_barrier(0);
-            weigh(B, c0 + 32, scores(B, c0 + 32));
+            use(B, c0 + CH);
         } else {
-            weigh(A, c0, scores(A, c0));
+            use(A, c0);
         }
     }
-#endif
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-
-    // Merge the waves' states (max, sum, accumulator of each head) in wave 0:
-    // M = max_w m_w, l = sum_w exp(m_w - M) l_w, acc = sum_w exp(m_w - M) acc_w.
-    // A wave without chunks holds m = -inf and contributes nothing.
-    if constexpr (W > 1) {
-        __shared__ f32x4 acc_lds[W > 1 ? W - 1 : 1][MT][kWave];
-        __shared__ float m_lds[W > 1 ? W - 1 : 1][16], l_lds[W > 1 ? W - 1 : 1][16];
-        if (wave > 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc_lds[wave - 1][mt][lane] = acc[mt];
-            if (g == 0) {
-                m_lds[wave - 1][r] = m;
-                l_lds[wave - 1][r] = l;
-            }
-        }
-        __syncthreads();
-        if (wave > 0) return;
-        float M = m;
-#pragma unroll
-        for (int w = 0; w < W - 1; ++w) M = fmaxf(M, m_lds[w][r]);
-        const float f0 = fast_exp2(m - M);
-        l *= f0;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= f0;
-        for (int w = 0; w < W - 1; ++w) {
-            const float f = fast_exp2(m_lds[w][r] - M);
-            l += f * l_lds[w][r];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] += f * acc_lds[w][mt][lane];
-        }
-        m = M;
-    }
-
+    // The run's last split straight from registers, then the parked ones.
+    float lt = l + __shfl_xor(l, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
     if (!head_ok) return;
-    const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
-    if (g == 0) {
-        p.max_logits[mloff] = m * kLn2;
-        p.exp_sums[mloff] = l;
-    }
-    const float inv = 1.0f / l;
-    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp + 4 * g;
+    const int64_t tstride = p.tmp_sp;
+    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part0 * tstride + 4 * g;
+    {
+        const float inv = p.v_scale / lt;
+        float* o = out + (int64_t)parked * tstride;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(out + 16 * mt) = acc[mt] * inv;
+        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(o + 16 * mt) = acc[mt] * inv;
+        if (g == 0) {
+            p.max_logits[mlbase + parked] = m * kLn2;
+            p.exp_sums[mlbase + parked] = lt;
+        }
+    }
+    for (int j = 0; j < parked; ++j) {
+        float* o = out + (int64_t)j * tstride;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<f32x4*>(o + 16 * mt) = park[(j * MT + mt) * kWave + lane];
+        if (g == 0) {
+            p.max_logits[mlbase + j] = park_ml[32 * j + r];
+            p.exp_sums[mlbase + j] = park_ml[32 * j + 16 + r];
+        }
+    }
 }
 
 bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
@@ -369,29 +448,62 @@ bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
            group >= 2 && group <= 16 && block_size >= 8;
 }
 
-template <class E, int D>
-static hipError_t launch_mfma_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
+// Splits per workgroup with fixed-size splits: enough that the grid is about
+// one workgroup per SIMD (four per compute unit of the current device), at
+// most kMfmaMaxRun. Per-sequence split counts were already sized for the
+// device by the split heuristic; their splits run one per workgroup (runs
+// of them measured slower on a skewed batch: fewer workgroups for the
+// long sequences).
+static int pick_split_run(int64_t units)
 {
-    dim3 grid(num_seqs * p.num_kv_heads, parts), block(kWave * kMfmaWaves);
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cus[dev] = n;
+    }
+    const int64_t run = units / (4 * (int64_t)cus[dev]);
+    return (int)(run < 1 ? 1 : run > kMfmaMaxRun ? kMfmaMaxRun : run);
+}
+
+template <class E, class KE, int D>
+static hipError_t launch_mfma_t(DecodeParams p, int num_seqs, int parts, hipStream_t st)
+{
+    p.grid_parts = parts;
+    p.split_run = p.num_splits ? 1 : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts);
+    if (p.split_run < 1 || p.split_run > kMfmaMaxRun) return hipErrorInvalidValue;
+    dim3 grid(num_seqs * p.num_kv_heads, (parts + p.split_run - 1) / p.split_run), block(kWave);
+    const size_t lds = (size_t)(p.split_run - 1) * ((D / 16) * kWave * sizeof(f32x4) + 32 * sizeof(float));
     switch (p.bs_shift) {
-    case 4: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 16>), grid, block, 0, st, p); break;
-    case 5: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 32>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((k_decode_mfma<E, D, D, 0>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 16>), grid, block, lds, st, p); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 32>), grid, block, lds, st, p); break;
+    default: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 0>), grid, block, lds, st, p); break;
     }
     return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_mfma_e(const DecodeParams& p, int D, int num_seqs, int parts, hipStream_t st)
+{
+    if (p.kv_fp8) {
+        if (D == 64) return launch_mfma_t<E, FP8E4M3, 64>(p, num_seqs, parts, st);
+        if (D == 128) return launch_mfma_t<E, FP8E4M3, 128>(p, num_seqs, parts, st);
+    } else {
+        if (D == 64) return launch_mfma_t<E, E, 64>(p, num_seqs, parts, st);
+        if (D == 128) return launch_mfma_t<E, E, 128>(p, num_seqs, parts, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int D, int Dv, int num_seqs,
                               int parts, hipStream_t st)
 {
     if (D != Dv) return hipErrorInvalidValue;
-    if (dtype == PA_BF16) {
-        if (D == 64) return launch_mfma_t<BF16, 64>(p, num_seqs, parts, st);
-        if (D == 128) return launch_mfma_t<BF16, 128>(p, num_seqs, parts, st);
-    } else if (dtype == PA_F16) {
-        if (D == 64) return launch_mfma_t<F16, 64>(p, num_seqs, parts, st);
-        if (D == 128) return launch_mfma_t<F16, 128>(p, num_seqs, parts, st);
-    }
+    if (dtype == PA_BF16) return launch_mfma_e<BF16>(p, D, num_seqs, parts, st);
+    if (dtype == PA_F16) return launch_mfma_e<F16>(p, D, num_seqs, parts, st);
     return hipErrorInvalidValue;
 }
 

@@ -35,6 +35,8 @@ struct DecodeParams {
     const float* alibi;  // optional ALiBi slopes [num_heads] (natural units)
     float v_scale;       // fp8 caches: value scale (1 otherwise); k_scale is in scale_log2
     bool kv_fp8;         // caches hold FP8 E4M3 codes
+    int split_run;       // grouped-head matrix-core kernel: consecutive splits per workgroup
+    int grid_parts;      // splits covered by the grid (set by the launcher)
 };
 
 struct ReduceParams {

@@ -270,9 +270,28 @@ def config_lengths(cfg: int) -> torch.Tensor:
     return _draw_lengths(cfg, torch.Generator().manual_seed(cfg))
 
 
-def config(cfg: int, *, poison: bool = False) -> Workload:
-    """The five reference workloads (seed = config number)."""
+# Scales of the fp8 forms of the standard workloads: N(0, 1) values land on
+# codes of magnitude up to about 5 * 32 = 160, inside E4M3's 448.
+FP8_WORKLOAD_SCALE = 1.0 / 32
+
+
+def config(cfg: int, *, poison: bool = False, kv_cache: str = "same",
+           alibi: bool = False) -> Workload:
+    """The five reference workloads (seed = config number). Configs 2-4 also
+    come with fp8 caches (kv_cache "fp8", both scales FP8_WORKLOAD_SCALE,
+    name suffix "_kvfp8") and with ALiBi slopes (suffix "_alibi")."""
+    if kv_cache != "same" and cfg not in (2, 3, 4):
+        raise ValueError("fp8 caches are drawn for configs 2-4")
+    w = _config(cfg, poison=poison, kv_cache=kv_cache)
+    if alibi:
+        w.alibi_slopes = alibi_slopes(w.num_heads)
+        w.name += "_alibi"
+    return w
+
+
+def _config(cfg: int, *, poison: bool, kv_cache: str) -> Workload:
     gen = torch.Generator().manual_seed(cfg)
+    kv = dict(kv_cache=kv_cache)
     if cfg == 1:
         # 2 seqs, lengths 16 and 13, block size 8, 64 physical blocks; seq 0
         # uses the block table [40, 30] of the Triton issue 2522 example, seq 1
@@ -298,15 +317,15 @@ def config(cfg: int, *, poison: bool = False) -> Workload:
     if cfg == 2:
         lens = _draw_lengths(2, gen)
         return _standard(gen, CONFIG_NAMES[2], "MHA decode fp16", lens, H=32, Hkv=32, D=128,
-                         bs=16, dt=torch.float16, nb=8192, poison=poison)
+                         bs=16, dt=torch.float16, nb=8192, poison=poison, **kv)
     if cfg == 3:
         lens = _draw_lengths(3, gen)
         return _standard(gen, CONFIG_NAMES[3], "long-context GQA decode bf16", lens, H=64, Hkv=8,
-                         D=128, bs=16, dt=torch.bfloat16, nb=20000, poison=poison)
+                         D=128, bs=16, dt=torch.bfloat16, nb=20000, poison=poison, **kv)
     if cfg == 4:
         lens = _draw_lengths(4, gen)
         w = _standard(gen, CONFIG_NAMES[4], "skewed-batch GQA decode bf16", lens, H=32, Hkv=8,
-                      D=128, bs=32, dt=torch.bfloat16, nb=None, poison=poison)
+                      D=128, bs=32, dt=torch.bfloat16, nb=None, poison=poison, **kv)
         w.max_kv_splits = 32
         w.device_core_count = 256
         return w
@@ -315,23 +334,32 @@ def config(cfg: int, *, poison: bool = False) -> Workload:
     raise ValueError(f"unknown config {cfg}")
 
 
-def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison):
+def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison, kv_cache="same"):
     need = _blocks_needed(lens.tolist(), bs)
     total = sum(need)
     if nb is None:
         nb = total + (1 if poison else 0)
     perm = torch.randperm(nb, generator=gen)
-    x = 16 // torch.tensor([], dtype=dt).element_size()
+    fp8 = kv_cache != "same"
+    x = 16 if fp8 else 16 // torch.tensor([], dtype=dt).element_size()
     S = lens.shape[0]
     q = _randn(gen, (S, H, D), dt)
-    kc = _randn(gen, (nb, Hkv, D // x, bs, x), dt)
-    vc = _randn(gen, (nb, Hkv, D, bs), dt)
+    if fp8:
+        sc = FP8_WORKLOAD_SCALE
+        kc = _fp8_cache(gen, (nb, Hkv, D // x, bs, x), kv_cache, sc)
+        vc = _fp8_cache(gen, (nb, Hkv, D, bs), kv_cache, sc)
+        name += "_kvfp8"
+    else:
+        kc = _randn(gen, (nb, Hkv, D // x, bs, x), dt)
+        vc = _randn(gen, (nb, Hkv, D, bs), dt)
     poison_block = int(perm[total]) if poison else None
     bt = _assign_blocks(perm, need, max(need), poison_block if poison else 0)
     w = Workload(name=name, description=desc, dtype=dt, seq_lens=lens, block_tables=bt, query=q,
                  key_cache=kc, value_cache=vc, scale=1.0 / math.sqrt(D), num_heads=H,
                  num_kv_heads=Hkv, head_size=D, v_head_size=D, block_size=bs, x=x, num_blocks=nb,
-                 poison_block=poison_block)
+                 poison_block=poison_block, kv_dtype=torch.uint8 if fp8 else None,
+                 k_scale=FP8_WORKLOAD_SCALE if fp8 else 1.0,
+                 v_scale=FP8_WORKLOAD_SCALE if fp8 else 1.0)
     if poison:
         _poison(w, need)
     return w

@@ -162,7 +162,8 @@ FP8_BAD = [
     ("v_scale_nan", dict(v_scale=float("nan")), api.PA_EINVAL),
     ("kv_dtype_unknown", dict(kv_dtype=9), api.PA_EINVAL),
     ("x_of_query_dtype", dict(x=8, k_stride_bs=8, k_stride_dx=16 * 8), api.PA_ENOTSUP),
-    ("mfma_hint", dict(kernel_hint=api.PA_KERNEL["mfma"]), api.PA_ENOTSUP),
+    ("mfma_hint_f32_query", dict(kernel_hint=api.PA_KERNEL["mfma"], dtype=api.PA_F32,
+                                 q_stride_s=8 * 128 * 2), api.PA_ENOTSUP),
     ("misaligned_block", dict(k_stride_b=2 * 128 * 16 + 8), api.PA_ENOTSUP),
 ]
 

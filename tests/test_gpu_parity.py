@@ -491,3 +491,28 @@ def test_decode_mla_balanced_config5(orc):
         assert torch.all(torch.isfinite(ml[s, :, :len(ps)]))
         assert torch.all(ml[s, :, len(ps):] == -math.inf)
     check_output(subset(w, [0, 17, 63]), orc, out[[0, 17, 63]])
+
+
+# ---------------------------------------------------------------------------
+# runs of consecutive splits per workgroup (grouped-head matrix-core kernel,
+# fixed split size): the launcher picks 1-4 splits per workgroup so that the
+# grid is about one workgroup per SIMD; these batches reach runs of 2, 3 and
+# 4 on a 256-CU device. Ragged lengths leave runs partly empty and end runs
+# mid-split.
+# ---------------------------------------------------------------------------
+RUN_LENS = [16384, 1, 513, 2047, 2048, 2049, 5000, 0, 100, 16000, 8191, 3, 700, 12345, 64, 15000]
+
+
+@pytest.mark.parametrize("nseq,kv", [(8, "same"), (12, "same"), (16, "same"), (16, "fp8")])
+def test_split_runs(orc, nseq, kv):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = nseq * 8 * 32
+    say(f"split runs: {nseq} seqs, kv {kv}, run {max(1, min(4, units // (4 * cus)))}")
+    w = workloads.custom(seed=200 + nseq, seq_lens=RUN_LENS[:nseq], num_heads=64, num_kv_heads=8,
+                         head_size=128, block_size=16, dtype="bf16", kv_cache=kv,
+                         k_scale=0.05, v_scale=0.05, poison=True)
+    out, tmp, ml, es = run_gpu(w, max_parts=32)
+    seqs = [0, 1, 2, 5, 7] + ([9, 13] if nseq > 13 else [])
+    check_partials(w, orc, tmp, ml, es, seqs=seqs)
+    check_output(w, orc, out, seqs=seqs)
+    assert torch.isfinite(out).all()

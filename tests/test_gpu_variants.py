@@ -1,9 +1,10 @@
 """Parity of the phase-1 variants with the CPU oracle: FP8 E4M3 caches with
 k_scale / v_scale, and ALiBi slopes, on every kernel that serves them.
 
-The fp8 path decodes codes exactly to fp32 and computes in fp32, so its
-outputs take the fp32-cache tolerances; ALiBi on the matrix-core kernel
-keeps the bf16/f16 ones. Unused cache slots and unreferenced blocks are
+FP8 codes decode exactly. On the vector kernel the rest is fp32, so those
+cases take the fp32-cache tolerances; on the matrix-core kernel the codes
+are widened to the query's 16-bit type and the probabilities rounded to it,
+so those cases take that type's tolerances, as ALiBi there does. Unused cache slots and unreferenced blocks are
 poisoned (NaN, or the E4M3 NaN code 0x7F) where the case says so.
 """
 import dataclasses
@@ -66,7 +67,32 @@ CASES = [
      dict(kernel="valu")),
     ("alibi_fp8_bf16", dict(seed=116, seq_lens=[2500, 1, 130], num_heads=8, num_kv_heads=1,
                             head_size=128, block_size=16, dtype="bf16", kv_cache="fp8",
-                            k_scale=0.05, v_scale=0.05, alibi=True, poison=True), {}),
+                            k_scale=0.05, v_scale=0.05, alibi=True, poison=True),
+     dict(kernel="mfma")),
+    ("alibi_fp8_bf16_valu", dict(seed=116, seq_lens=[2500, 1, 130], num_heads=8, num_kv_heads=1,
+                                 head_size=128, block_size=16, dtype="bf16", kv_cache="fp8",
+                                 k_scale=0.05, v_scale=0.05, alibi=True, poison=True),
+     dict(kernel="valu")),
+    # fp8 caches on the grouped-head matrix-core kernel
+    ("fp8_mfma_bf16_bs16", dict(seed=131, seq_lens=[1, 7, 8, 9, 31, 33, 1000, 2049], num_heads=16,
+                                num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+                                kv_cache="fp8", k_scale=0.05, v_scale=0.08, poison=True),
+     dict(kernel="mfma")),
+    ("fp8_mfma_f16_bs32_d64", dict(seed=132, seq_lens=[4100, 63, 64, 65], num_heads=32,
+                                   num_kv_heads=2, head_size=64, block_size=32, dtype="f16",
+                                   kv_cache="fp8", k_scale=0.04, v_scale=0.1, poison=True),
+     dict(kernel="mfma")),
+    ("fp8_mfma_bf16_bs8_g2", dict(seed=133, seq_lens=[777, 5, 100], num_heads=4, num_kv_heads=2,
+                                  head_size=128, block_size=8, dtype="bf16", kv_cache="fp8",
+                                  k_scale=0.05, v_scale=0.05, poison=True), dict(kernel="mfma")),
+    ("fp8_mfma_bf16_bs64_splits", dict(seed=134, seq_lens=[6000, 300, 2], num_heads=8,
+                                       num_kv_heads=1, head_size=128, block_size=64, dtype="bf16",
+                                       kv_cache="fp8", k_scale=0.05, v_scale=0.05, poison=True),
+     dict(kernel="mfma", num_splits=[11, 2, 1], max_parts=16)),
+    ("fp8_valu_bf16_group", dict(seed=131, seq_lens=[1, 7, 8, 9, 31, 33, 1000, 2049], num_heads=16,
+                                 num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
+                                 kv_cache="fp8", k_scale=0.05, v_scale=0.08, poison=True),
+     dict(kernel="valu")),
 ]
 
 
@@ -77,8 +103,10 @@ def test_variant_matches_oracle(orc, case):
     w = workloads.custom(name=name, **wkw)
     P = rkw.get("partition_size", 512)
     out, tmp, ml, es = run_gpu(w, **rkw)
-    check_partials(w, orc, tmp, ml, es, partition_size=P, num_splits=rkw.get("num_splits"))
-    check_output(w, orc, out)
+    kernel = rkw.get("kernel", "auto")
+    check_partials(w, orc, tmp, ml, es, partition_size=P, num_splits=rkw.get("num_splits"),
+                   kernel=kernel)
+    check_output(w, orc, out, kernel=kernel)
 
 
 def _live_codes(cache: torch.Tensor, w: workloads.Workload, value: bool) -> torch.Tensor:
@@ -107,6 +135,16 @@ def test_fp8_every_code(orc):
     out, tmp, ml, es = run_gpu(w, partition_size=256)
     check_partials(w, orc, tmp, ml, es, partition_size=256)
     check_output(w, orc, out)
+    # grouped heads over the same kinds of codes, on the matrix-core kernel
+    w = workloads.custom(seed=124, seq_lens=[700, 5, 129], num_heads=16, num_kv_heads=2,
+                         head_size=128, block_size=16, dtype="bf16", kv_cache="fp8_codes",
+                         k_scale=1.0 / 448, v_scale=1.0 / 448, poison=True)
+    for value, c in ((False, w.key_cache), (True, w.value_cache)):
+        seen = torch.bincount(_live_codes(c, w, value).long(), minlength=256)
+        assert int((seen > 0).sum()) == 254
+    out, tmp, ml, es = run_gpu(w, kernel="mfma")
+    check_partials(w, orc, tmp, ml, es, kernel="mfma")
+    check_output(w, orc, out, kernel="mfma")
 
 
 def test_alibi_moves_the_output(orc):
