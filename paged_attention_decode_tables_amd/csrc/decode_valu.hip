@@ -64,6 +64,11 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
     const int kvh = h / p.group;
     const int bs_shift = p.bs_shift;
     const int64_t bs = int64_t(1) << bs_shift;
+    // Value rows of a block longer than one 16-byte piece are read piece by
+    // piece; their lines must stay in L2 for the next piece, so only rows of
+    // one piece take the streaming hint (with it, 16-bit rows of 16 tokens
+    // were fetched 1.29x).
+    const bool vstream = STREAM && bs * KE::size <= 16;
 
     const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
     for (int i = lane; i < D; i += kWave) q_lds[i] = to_f32(q[i]);
@@ -109,23 +114,40 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
             // lane <-> row dv = lane + 64*r; VT consecutive tokens per load
             constexpr int VT = X;
             if (bs >= VT) {
+                // Groups of VT tokens in pairs, both pieces requested back to
+                // back (a row of 16 tokens of a 16-bit cache is two pieces of
+                // one line). A missing second group repeats the first one's
+                // address and is not used.
                 const int nv = (n + VT - 1) / VT;
-                for (int v = 0; v < nv; ++v) {
-                    const int64_t tv = c0 + v * VT;
-                    const KT* vp = vc + token_block(row, sb, tv, bs_shift) * p.v_sb + (tv & (bs - 1));
-                    float pv[VT];
-#pragma unroll
-                    for (int j = 0; j < VT; ++j) pv[j] = p_lds[v * VT + j];
-                    const bool full = (v + 1) * VT <= n;
+                for (int v = 0; v < nv; v += 2) {
+                    const bool two = v + 1 < nv;
+                    const int64_t tv0 = c0 + v * VT, tv1 = two ? tv0 + VT : tv0;
+                    const KT* vp0 = vc + token_block(row, sb, tv0, bs_shift) * p.v_sb + (tv0 & (bs - 1));
+                    const KT* vp1 = vc + token_block(row, sb, tv1, bs_shift) * p.v_sb + (tv1 & (bs - 1));
+                    u32x4 va[DVR], vb[DVR];
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) {
-                        const KT* vr = vp + (int64_t)(lane + kWave * r) * bs;
-                        const u32x4 vv = STREAM ? load16_stream(vr) : load16(vr);
+                        const int64_t ro = (int64_t)(lane + kWave * r) * bs;
+                        va[r] = vstream ? load16_stream(vp0 + ro) : load16(vp0 + ro);
+                        vb[r] = vstream ? load16_stream(vp1 + ro) : load16(vp1 + ro);
+                    }
 #pragma unroll
-                        for (int j = 0; j < VT; ++j) {
-                            float x = elem16<KE>(vv, j);
-                            if (!full) x = (v * VT + j < n) ? x : 0.0f;
-                            acc[r] += pv[j] * x;
+                    for (int half = 0; half < 2; ++half) {
+                        if (half == 1 && !two) break;
+                        const int vv_ = v + half;
+                        float pv[VT];
+#pragma unroll
+                        for (int j = 0; j < VT; ++j) pv[j] = p_lds[vv_ * VT + j];
+                        const bool full = (vv_ + 1) * VT <= n;
+#pragma unroll
+                        for (int r = 0; r < DVR; ++r) {
+                            const u32x4 vv = half ? vb[r] : va[r];
+#pragma unroll
+                            for (int j = 0; j < VT; ++j) {
+                                float x = elem16<KE>(vv, j);
+                                if (!full) x = (vv_ * VT + j < n) ? x : 0.0f;
+                                acc[r] += pv[j] * x;
+                            }
                         }
                     }
                 }
