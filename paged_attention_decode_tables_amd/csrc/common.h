@@ -180,6 +180,15 @@ __device__ __forceinline__ int64_t split_length(int L, const int32_t* num_splits
 // ---------------------------------------------------------------------------
 // Wavefront reductions (64 lanes).
 // ---------------------------------------------------------------------------
+// Orders one wave's LDS writes before its later LDS reads (and the reads
+// before later writes) without a workgroup barrier: a wave's LDS operations
+// execute in order, so only the compiler must not move them across.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll

@@ -29,15 +29,20 @@ namespace pa {
 // STREAM: every K/V byte is read by exactly one wave (group size 1), so the
 // loads carry the nontemporal hint; with grouped heads the G waves of a kv
 // head share the lines through the caches and use plain loads.
-template <class E, class KE, int D, int DV, bool ROWV, bool STREAM>
-__global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
+//
+// NW waves per workgroup share one split: wave w takes the w-th of NW equal
+// runs of whole 64-token chunks, and the waves' (max, sum, accumulator)
+// states are merged through LDS at the end. A wave alone streams its chunks
+// one after the other, so several per split keep more loads in flight.
+template <class E, class KE, int D, int DV, bool ROWV, bool STREAM, int NW>
+__global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
 {
     using T = typename E::storage;
     using KT = typename KE::storage;
     constexpr int X = 16 / KE::size;      // key packing
     constexpr int DVR = DV / kWave;       // value rows (or values) per lane
     __shared__ float q_lds[D];
-    __shared__ float p_lds[kWave];
+    __shared__ float p_all[NW][kWave];
 
     // grid (kv head + Hkv * (g + G * seq), split), g the head within its kv
     // head's group: workgroups are dealt to the XCDs round-robin by linear
@@ -47,7 +52,9 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
     // its L2; the split index last spreads each split index over all XCDs.
     const int kvh_ = blockIdx.x % p.num_kv_heads, rest = blockIdx.x / p.num_kv_heads;
     const int s = rest / p.group, h = kvh_ * p.group + rest % p.group, part = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int wave = NW > 1 ? (int)threadIdx.x / kWave : 0;
+    const int lane = (int)threadIdx.x % kWave;
+    float* p_lds = p_all[wave];
     const int L = p.seq_lens[s];
     const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
     const int64_t start = (int64_t)part * len;
@@ -55,7 +62,7 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
     float* mlp = p.max_logits + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
     float* esp = p.exp_sums + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
     if (start >= end) {
-        if (lane == 0) {
+        if (threadIdx.x == 0) {
             *mlp = -INFINITY;
             *esp = 0.0f;
         }
@@ -71,8 +78,12 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
     const bool vstream = STREAM && bs * KE::size <= 16;
 
     const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
-    for (int i = lane; i < D; i += kWave) q_lds[i] = to_f32(q[i]);
+    for (int i = threadIdx.x; i < D; i += kWave * NW) q_lds[i] = to_f32(q[i]);
     __syncthreads();
+    // this wave's run: [wstart, wend), whole chunks from the split start
+    const int64_t sub = NW > 1 ? ((end - start + NW - 1) / NW + kWave - 1) / kWave * kWave : end - start;
+    const int64_t wstart = start + wave * sub;
+    const int64_t wend = end < wstart + sub ? end : wstart + sub;
 
     const int32_t* row = page_row(p.pl, s);
     const int64_t sb = p.pl.stride_b;
@@ -86,8 +97,8 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
 #pragma unroll
     for (int r = 0; r < DVR; ++r) acc[r] = 0.0f;
 
-    for (int64_t c0 = start; c0 < end; c0 += kWave) {
-        const int n = (int)((end - c0) < kWave ? (end - c0) : kWave);
+    for (int64_t c0 = wstart; c0 < wend; c0 += kWave) {
+        const int n = (int)((wend - c0) < kWave ? (wend - c0) : kWave);
         // ---- scores: lane <-> token (clamped to a valid token for the load)
         const int64_t t = c0 + (lane < n ? lane : n - 1);
         const KT* kp = kc + token_block(row, sb, t, bs_shift) * p.k_sb + (t & (bs - 1)) * X;
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
         l = l * alpha + pl;
         m = mn;
         p_lds[lane] = pl;
-        __syncthreads();
+        wave_lds_sync();
 #pragma unroll
         for (int r = 0; r < DVR; ++r) acc[r] *= alpha;
 
@@ -177,10 +188,38 @@ __global__ __launch_bounds__(64) void k_decode_valu(DecodeParams p)
                 }
             }
         }
-        __syncthreads();
+        wave_lds_sync();
     }
 
-    const float lsum = wave_sum(l);
+    float lsum = wave_sum(l);
+    if constexpr (NW > 1) {
+        // merge: M = max_w m_w, l = sum_w exp2(m_w - M) l_w, acc likewise; a
+        // wave without tokens has m = -inf and weight 0 (wave 0 always has some)
+        __shared__ float m_w[NW], l_w[NW];
+        __shared__ float acc_w[NW][DV];
+        if (lane == 0) {
+            m_w[wave] = m;
+            l_w[wave] = lsum;
+        }
+#pragma unroll
+        for (int r = 0; r < DVR; ++r) acc_w[wave][ROWV ? lane * DVR + r : lane + kWave * r] = acc[r];
+        __syncthreads();
+        if (wave != 0) return;
+        float M = m_w[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, m_w[w]);
+        lsum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < DVR; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = m_w[w] == -INFINITY ? 0.0f : fast_exp2(m_w[w] - M);
+            lsum += f * l_w[w];
+#pragma unroll
+            for (int r = 0; r < DVR; ++r) acc[r] += f * acc_w[w][ROWV ? lane * DVR + r : lane + kWave * r];
+        }
+        m = M;
+    }
     if (lane == 0) {
         *mlp = m * kLn2;
         *esp = lsum;
@@ -200,18 +239,31 @@ bool decode_valu_supported(int dtype, int D, int Dv)
     return (D == Dv && (D == 64 || D == 128 || D == 256)) || (D == 576 && Dv == 512);
 }
 
+// Waves per split. Two took the MHA batch's phase 1 from 85 to 79 us (fp8
+// caches: 55 to 49 us); four gave the same as two.
+#ifndef PA_VALU_WAVES
+#define PA_VALU_WAVES 2
+#endif
+
+template <class E, class KE, int D, int DV, int NW>
+static void launch_valu_nw(const DecodeParams& p, dim3 grid, hipStream_t st)
+{
+    const dim3 block(kWave * NW);
+    const bool stream = p.group == 1;
+    if (p.bs_shift == 0) {
+        if (stream) hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, true, true, NW>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, true, false, NW>), grid, block, 0, st, p);
+    } else {
+        if (stream) hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, false, true, NW>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, false, false, NW>), grid, block, 0, st, p);
+    }
+}
+
 template <class E, class KE, int D, int DV>
 static hipError_t launch_valu_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    dim3 grid(num_seqs * p.num_heads, parts), block(kWave);
-    const bool stream = p.group == 1;
-    if (p.bs_shift == 0) {
-        if (stream) hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, true, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, true, false>), grid, block, 0, st, p);
-    } else {
-        if (stream) hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, false, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((k_decode_valu<E, KE, D, DV, false, false>), grid, block, 0, st, p);
-    }
+    const dim3 grid(num_seqs * p.num_heads, parts);
+    launch_valu_nw<E, KE, D, DV, PA_VALU_WAVES>(p, grid, st);
     return hipGetLastError();
 }
 
