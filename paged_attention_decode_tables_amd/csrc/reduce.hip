@@ -2,9 +2,12 @@
 // outputs (paged_attention_v2_triton.py, _paged_attn_v2_reduce_kernel:
 // global max, rescale by exp(m_p - M) * l_p, normalise, weighted sum).
 //
-// One 256-thread workgroup per (seq, head). The Dv-wide rows are read as
-// float4 columns: C = Dv/4 threads cover a row and the NG = 256/C thread
-// groups take every NG-th split. Each thread folds its splits into a local
+// One workgroup per (seq, head). The Dv-wide rows are read as float4
+// columns: C = Dv/4 threads cover a row and NG thread groups take every
+// NG-th split. NG is the smallest power of two that lets every group read
+// its splits in one round (at most 256 threads, at least one wave): with
+// few splits a workgroup stays small and the whole grid fits on the chip at
+// once. Each thread folds its splits into a local
 // (max, sum, row) state, R splits at a time with all their loads in flight,
 // and the groups' states are merged once through LDS with the same rule
 // (M = max m_g, weights exp(m_g - M)), so the whole merge costs one memory
@@ -14,14 +17,13 @@
 
 namespace pa {
 
-constexpr int kRedThreads = 256;
+constexpr int kRedMaxThreads = 256;
 constexpr int kRedBatch = 8;  // splits per thread per round of loads
 
-template <class OutE, int DV>
-__global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
+template <class OutE, int DV, int NG>
+__global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
 {
     constexpr int C = DV / 4;             // threads per row (float4 columns)
-    constexpr int NG = kRedThreads / C;   // split groups
     __shared__ f32x4 acc_lds[NG][C];
     __shared__ float m_lds[NG], w_lds[NG];
 
@@ -132,16 +134,43 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce(ReduceParams p)
 
 bool reduce_supported(int Dv) { return Dv == 64 || Dv == 128 || Dv == 256 || Dv == 512; }
 
+// Split groups for up to max_parts splits: cdiv(max_parts, kRedBatch)
+// rounded up to a power of two, within [max(1, 64 / C), 256 / C].
+static int reduce_groups(int Dv, int max_parts)
+{
+    const int C = Dv / 4;
+    const int lo = C >= 64 ? 1 : 64 / C, hi = kRedMaxThreads / C;
+    const int want = (max_parts + kRedBatch - 1) / kRedBatch;
+    int ng = lo;
+    while (ng < want && ng < hi) ng *= 2;
+    return ng;
+}
+
+template <class OutE, int DV, int NG>
+static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
+{
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_heads)), block(DV / 4 * NG);
+    hipLaunchKernelGGL((k_reduce<OutE, DV, NG>), grid, block, 0, st, p);
+}
+
+template <class OutE, int DV>
+static void launch_reduce_dv(const ReduceParams& p, hipStream_t st)
+{
+    constexpr int C = DV / 4, LO = C >= 64 ? 1 : 64 / C, HI = kRedMaxThreads / C;
+    const int ng = reduce_groups(DV, p.max_num_parts);
+    if (ng <= LO) launch_reduce_ng<OutE, DV, LO>(p, st);
+    else if (ng <= 2 * LO || 2 * LO > HI) launch_reduce_ng<OutE, DV, (2 * LO <= HI ? 2 * LO : HI)>(p, st);
+    else launch_reduce_ng<OutE, DV, HI>(p, st);
+}
+
 template <class OutE>
 static hipError_t launch_reduce_t(const ReduceParams& p, int Dv, hipStream_t st)
 {
-    const int64_t pairs = (int64_t)p.num_seqs * p.num_heads;
-    dim3 grid((unsigned)pairs), block(kRedThreads);
     switch (Dv) {
-    case 64: hipLaunchKernelGGL((k_reduce<OutE, 64>), grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((k_reduce<OutE, 128>), grid, block, 0, st, p); break;
-    case 256: hipLaunchKernelGGL((k_reduce<OutE, 256>), grid, block, 0, st, p); break;
-    case 512: hipLaunchKernelGGL((k_reduce<OutE, 512>), grid, block, 0, st, p); break;
+    case 64: launch_reduce_dv<OutE, 64>(p, st); break;
+    case 128: launch_reduce_dv<OutE, 128>(p, st); break;
+    case 256: launch_reduce_dv<OutE, 256>(p, st); break;
+    case 512: launch_reduce_dv<OutE, 512>(p, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
