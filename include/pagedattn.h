@@ -163,10 +163,10 @@ typedef struct pa_decode_args {
  *   (head_size, v_head_size) in {(64,64), (128,128), (256,256), (576,512)};
  *   any group size num_heads / num_kv_heads (grouped heads of f16/bf16 caches
  *   run on MFMA when block_size >= 8 and the group is at most 16).
- * fp8 caches (x = 16) and ALiBi slopes run on the grouped-head matrix-core
- * kernel (f16/bf16 queries, the conditions above) and on the vector kernel
- * (everything else). The latent-row kernel takes neither: latent rows with
- * them go to the vector kernel, and balanced splits return PA_ENOTSUP.
+ * ALiBi slopes run on every kernel. fp8 caches (x = 16) run on the
+ * grouped-head matrix-core kernel (f16/bf16 queries, the conditions above)
+ * and on the vector kernel; latent rows over fp8 caches go to the vector
+ * kernel, and balanced splits over fp8 caches return PA_ENOTSUP.
  */
 int paged_attn_decode(const pa_decode_args* args, void* stream);
 

@@ -180,6 +180,15 @@ __device__ __forceinline__ int64_t split_length(int L, const int32_t* num_splits
 // ---------------------------------------------------------------------------
 // Wavefront reductions (64 lanes).
 // ---------------------------------------------------------------------------
+// A 64-bit value that is the same in every lane, as a scalar (the compiler
+// cannot tell that a value read from LDS is uniform).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Orders one wave's LDS writes before its later LDS reads (and the reads
 // before later writes) without a workgroup barrier: a wave's LDS operations
 // execute in order, so only the compiler must not move them across.

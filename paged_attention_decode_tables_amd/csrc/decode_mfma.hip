@@ -127,7 +127,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     // each run index's work (the first is never empty, late ones often
     // are) spread over all XCDs.
     const int kvh = blockIdx.x % p.num_kv_heads, s = blockIdx.x / p.num_kv_heads;
-    const int part0 = blockIdx.y * p.split_run;  // first split of the run
+    // runs in reverse order: late runs exist only for long sequences and are
+    // the longest, so they are dispatched first and the grid ends on short work
+    const int part0 = (int)(gridDim.y - 1 - blockIdx.y) * p.split_run;  // first split of the run
     const int nrun = min(p.split_run, p.grid_parts - part0);
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const int G = p.group;
@@ -473,7 +475,11 @@ template <class E, class KE, int D>
 static hipError_t launch_mfma_t(DecodeParams p, int num_seqs, int parts, hipStream_t st)
 {
     p.grid_parts = parts;
-    p.split_run = p.num_splits ? 1 : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts);
+#ifndef PA_MFMA_RUN_NS
+#define PA_MFMA_RUN_NS 1
+#endif
+    p.split_run = p.num_splits ? (PA_MFMA_RUN_NS > 0 ? PA_MFMA_RUN_NS : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts))
+                               : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts);
     if (p.split_run < 1 || p.split_run > kMfmaMaxRun) return hipErrorInvalidValue;
     dim3 grid(num_seqs * p.num_kv_heads, (parts + p.split_run - 1) / p.split_run), block(kWave);
     const size_t lds = (size_t)(p.split_run - 1) * ((D / 16) * kWave * sizeof(f32x4) + 32 * sizeof(float));

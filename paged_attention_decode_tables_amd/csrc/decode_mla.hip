@@ -181,10 +181,12 @@ __device__ __forceinline__ int wave_max_i32(int v)
     return v;
 }
 
+// ALIBI: scores carry the slopes' bias (a separate instance, so the plain
+// kernel keeps its registers).
 // BAL = false: one workgroup per (seq, kv head, split) of the fixed or
 // per-sequence split rule. BAL = true: balanced splits, one workgroup per
 // (token range, kv head).
-template <class E, int NW, bool BAL>
+template <class E, int NW, bool BAL, bool ALIBI>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_decode_mla(DecodeParams p)
 {
@@ -222,6 +224,16 @@ void k_decode_mla(DecodeParams p)
     // statistics and normalised output stored in split slot `part`.
     auto piece = [&](const int s, const int part, const int start, const int end) {
     __syncthreads();  // the previous piece's LDS reads are done
+    // With balanced splits the pieces run in a loop. The lane and head
+    // indices are then re-derived through an opaque zero, so the compiler
+    // cannot hoist what depends on them out of that loop: kept live across
+    // it, they pushed the loop over chunks past the register file (spills
+    // in it cost a quarter of the kernel's time).
+    int opaque = 0;
+    if constexpr (BAL) asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+    const int lane = (int)(threadIdx.x & 63) + opaque, c32 = lane & 31, hl = lane >> 5;
+    const int wave = (int)(threadIdx.x >> 6) + opaque;
+    const int h = h0 + opaque + wave * HPW + c32;
     const int nc = (end - start + CT - 1) / CT;
 
     // B operand of QK: lane (hl, c32) holds q[h][16*ks + 8*hl .. +8]
@@ -235,6 +247,11 @@ void k_decode_mla(DecodeParams p)
     const int32_t* row = page_row(p.pl, s);
     const int64_t sb = p.pl.stride_b;
     const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
+    // ALiBi: head c32's slope in base-2 units (0 without slopes). Scores then
+    // grow toward the end of the sequence, so a split usually passes the
+    // first chunk's reference by more than the headroom and runs twice.
+    const int L = ALIBI ? p.seq_lens[s] : 0;
+    const float slope = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
 
     // page ids of tokens [wbase, wbase + kMlaPageWin) of this split
     int wbase = start;
@@ -338,7 +355,9 @@ void k_decode_mla(DecodeParams p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int t = c0 + 16 * (r >> 3) + 8 * hl + (r & 7);
-            sc[r] = t < end ? sacc[r] * p.scale_log2 : -INFINITY;
+            float z = sacc[r] * p.scale_log2;
+            if constexpr (ALIBI) z += slope * (float)(t - (L - 1));
+            sc[r] = t < end ? z : -INFINITY;
             mloc = fmaxf(mloc, sc[r]);
         }
         return half_max(mloc);
@@ -536,6 +555,8 @@ void k_decode_mla(DecodeParams p)
         total_tokens += bal_w64[i];
         maxL = max(maxL, bal_w32[i]);
     }
+    total_tokens = uniform_i64(total_tokens);
+    maxL = __builtin_amdgcn_readfirstlane(maxL);
     __syncthreads();  // bal_w64 is reused by the scan below
     const int64_t W = p.num_workers;
     int64_t U = max((total_tokens + W - 1) / W, ((int64_t)maxL + p.max_num_parts - 2) / (p.max_num_parts - 1));
@@ -569,10 +590,12 @@ void k_decode_mla(DecodeParams p)
             atomicMax(&bal_last, tid);
         }
         __syncthreads();
-        const int first = bal_first, last = bal_last;
+        const int first = __builtin_amdgcn_readfirstlane(bal_first);
+        const int last = __builtin_amdgcn_readfirstlane(bal_last);
+        total = uniform_i64(total);
         for (int j = first; j <= last; ++j) {
-            const int64_t so = bal_off[j];
-            const int Ls = bal_len[j];
+            const int64_t so = uniform_i64(bal_off[j]);
+            const int Ls = __builtin_amdgcn_readfirstlane(bal_len[j]);
             if (Ls <= 0) continue;
             const int k = (int)(w - so / U);
             piece(b0 + j, k, (int)(max(r0, so) - so), (int)(min(r1, so + Ls) - so));
@@ -589,15 +612,22 @@ bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size)
            (group == 64 || group == 128);
 }
 
+template <class E, int NW, bool ALIBI>
+static void launch_mla_a(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
+{
+    if (p.num_workers > 0)
+        hipLaunchKernelGGL((k_decode_mla<E, NW, true, ALIBI>), dim3(p.num_workers, p.num_kv_heads, 1),
+                           dim3(64 * NW), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_decode_mla<E, NW, false, ALIBI>), dim3(num_seqs, p.num_kv_heads, parts),
+                           dim3(64 * NW), 0, st, p);
+}
+
 template <class E, int NW>
 static void launch_mla_nw(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    if (p.num_workers > 0)
-        hipLaunchKernelGGL((k_decode_mla<E, NW, true>), dim3(p.num_workers, p.num_kv_heads, 1), dim3(64 * NW),
-                           0, st, p);
-    else
-        hipLaunchKernelGGL((k_decode_mla<E, NW, false>), dim3(num_seqs, p.num_kv_heads, parts), dim3(64 * NW),
-                           0, st, p);
+    if (p.alibi) launch_mla_a<E, NW, true>(p, num_seqs, parts, st);
+    else launch_mla_a<E, NW, false>(p, num_seqs, parts, st);
 }
 
 template <class E>

@@ -185,15 +185,14 @@ def test_decode_kv_dtype_must_be_query_dtype_or_fp8(lib):
 
 
 def test_decode_balanced_splits_need_the_mla_kernel(lib):
-    """Balanced splits are built into the latent-row kernel only, which takes
-    neither ALiBi nor fp8 caches."""
-    a = good_decode(D=576, Dv=512, H=16, Hkv=1, bs=1)
+    """Balanced splits are built into the latent-row kernel only, which does
+    not read fp8 caches."""
+    a = good_fp8(D=576, Dv=512, H=16, Hkv=1, bs=1)
     a.value_cache = a.key_cache
-    a.v_stride_b, a.v_stride_h = a.k_stride_b, a.k_stride_h
+    a.v_stride_b, a.v_stride_h, a.v_stride_d = a.k_stride_b, a.k_stride_h, 1
     a.partition_size, a.num_workers, a.max_num_parts = 0, 256, 256
-    a.alibi_slopes = FAKE
     assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
-    assert "ALiBi" in lib.pa_last_error().decode()
+    assert "balanced" in lib.pa_last_error().decode()
 
 
 def test_decode_empty_batch_is_a_noop(lib):

@@ -159,18 +159,19 @@ def test_alibi_moves_the_output(orc):
     assert np.abs(out - ref).max() <= tolerances(w)[0]
 
 
-def test_alibi_latent_rows_run_on_the_vector_kernel(orc):
-    """Latent rows (V aliasing K, page size 1) with ALiBi: the latent-row
-    matrix-core kernel does not take slopes, so auto dispatch serves them on
-    the vector kernel, and asking for a matrix-core kernel is refused."""
-    say("alibi latent rows")
-    w = workloads.mla_custom(seed=122, seq_lens=[300, 1, 1000], num_heads=16, poison=True)
-    w.alibi_slopes = workloads.alibi_slopes(16)
-    out, tmp, ml, es = run_gpu(w)
-    check_partials(w, orc, tmp, ml, es)
-    check_output(w, orc, out)
-    with pytest.raises(pad.PagedAttnError):
-        run_gpu(w, kernel="mfma")
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+def test_alibi_latent_rows(orc, kernel):
+    """Latent rows (V aliasing K, page size 1) with ALiBi, 64 and 128 heads on
+    the latent-row kernel (auto) and on the vector kernel. Slopes make later
+    scores pass the latent-row kernel's first-chunk reference, so its
+    splits take the second, exact-reference pass."""
+    for H, lens in ((64, [300, 1, 1000, 2049]), (128, [700, 33])):
+        say(f"alibi latent rows H={H} kernel={kernel}")
+        w = workloads.mla_custom(seed=122 + H, seq_lens=lens, num_heads=H, poison=True)
+        w.alibi_slopes = workloads.alibi_slopes(H)
+        out, tmp, ml, es = run_gpu(w, kernel=kernel)
+        check_partials(w, orc, tmp, ml, es)
+        check_output(w, orc, out)
 
 
 def test_fp8_scales_scale_linearly(orc):
