@@ -80,8 +80,9 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
  * split k, and slots k >= (number of such ranges) store m = -inf, l = 0. So
  * every worker gets the same number of tokens whatever the length mix, and
  * a sequence never has more than max_num_parts splits (max_num_parts >= 2).
- * Phase 2 with partition_size == 0 merges every non-empty slot; the final
- * output is the same as with any other split.
+ * The live slots of a sequence are always a prefix (slots 0 .. k_max).
+ * Phase 2 with partition_size == 0 merges the slots before the first one
+ * whose max is -inf; the final output is the same as with any other split.
  *
  * Variants of phase 1 named by the [PAv2] wrapper arguments (alibi_slopes,
  * kv_cache_dtype, k_scale, v_scale), whose math the page does not give; the
@@ -192,7 +193,8 @@ typedef struct pa_reduce_args {
     const int32_t* num_splits;   /* optional, as given to paged_attn_decode */
     int32_t num_seqs, num_heads, v_head_size;
     int32_t partition_size;      /* as given to paged_attn_decode; 0 = balanced splits:
-                                    merge every slot whose max_logits is not -inf */
+                                    merge the slots before the first one whose
+                                    max_logits is -inf */
     int32_t max_num_parts;
 } pa_reduce_args;
 

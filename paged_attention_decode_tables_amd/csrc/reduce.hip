@@ -83,6 +83,12 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
                 mv[r] = q < n ? ml[q] : -INFINITY;
                 lv[r] = q < n ? es[q] : 0.0f;
             }
+            // the balanced rule fills a prefix of the slots: once this group
+            // meets an empty one, every later slot is empty too
+            bool ended = false;
+#pragma unroll
+            for (int r = 0; r < kRedBatch; ++r) ended |= mv[r] == -INFINITY;
+            if (ended) n = q0 + 1;  // this batch is the group's last
 #pragma unroll
             for (int r = 0; r < kRedBatch; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
