@@ -157,11 +157,20 @@ __host__ __device__ constexpr int loader_waves(int ins, int nw)
 // LDS column offset of the pieces of ring row t (XORed into the piece index)
 __host__ __device__ constexpr int mla_swz(int t) { return (t & 6) | ((t >> 3) & 1); }
 
-constexpr int kMlaChunk = 32;      // tokens per chunk
-constexpr int kMlaBuf = 4;         // chunk slots in the LDS ring
-constexpr int kMlaPageWin = 1024;  // page ids staged in LDS at a time
-constexpr int kMlaKAhead = 8;      // QK operand reads in flight ahead of their MFMAs
-constexpr int kMlaVAhead = 6;      // PV MFMAs whose operand reads are in flight ahead
+#ifndef PA_MLA_BUF
+#define PA_MLA_BUF 4
+#endif
+#ifndef PA_MLA_KAHEAD
+#define PA_MLA_KAHEAD 8
+#endif
+#ifndef PA_MLA_VAHEAD
+#define PA_MLA_VAHEAD 6
+#endif
+constexpr int kMlaChunk = 32;             // tokens per chunk
+constexpr int kMlaBuf = PA_MLA_BUF;       // chunk slots in the LDS ring
+constexpr int kMlaPageWin = 1024;         // page ids staged in LDS at a time
+constexpr int kMlaKAhead = PA_MLA_KAHEAD; // QK operand reads in flight ahead of their MFMAs
+constexpr int kMlaVAhead = PA_MLA_VAHEAD; // PV MFMAs whose operand reads are in flight ahead
 constexpr int kMlaHeadsPerWave = 32;
 
 // Wave-wide int64 inclusive prefix sum and max of an int.
