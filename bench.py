@@ -51,7 +51,8 @@ def kernel_kind(w) -> str:
     if low and w.head_size == 576 and w.v_head_size == 512 and w.block_size == 1 \
             and group in (64, 128) and w.latent is not None and w.kv_dtype is None:
         return "mla"
-    if low and group > 1 and w.block_size >= 8 and w.head_size in (64, 128):
+    cols = group * w.num_group  # (query token, head) pairs of a kv head
+    if low and 2 <= cols <= 16 and w.block_size >= 8 and w.head_size in (64, 128):
         return "mfma"
     return "valu"
 
@@ -77,13 +78,13 @@ class Step:
         self.partition = 0 if balanced_workers else w.partition_size
         if w.max_kv_splits is not None:
             self.max_parts = w.max_kv_splits
-            self.ns = torch.empty(w.num_seqs, dtype=torch.int32, device="cuda")
+            self.ns = torch.empty(w.num_seqs * w.num_group, dtype=torch.int32, device="cuda")
         else:
             self.max_parts = -(-w.max_seq_len // w.partition_size)
         if w.cu_num_blocks is not None:
             self.indptr = w.cu_num_blocks.to("cuda")
             self.flat = torch.empty(int(w.cu_num_blocks[-1]), dtype=torch.int32, device="cuda")
-        S, H, Dv = w.num_seqs, w.num_heads, w.v_head_size
+        S, H, Dv = w.num_seqs * w.num_group, w.num_heads, w.v_head_size  # query rows
         self.tmp = torch.empty((S, H, self.max_parts, Dv), dtype=torch.float32, device="cuda")
         self.ml = torch.empty((S, H, self.max_parts), dtype=torch.float32, device="cuda")
         self.es = torch.empty((S, H, self.max_parts), dtype=torch.float32, device="cuda")
@@ -92,7 +93,7 @@ class Step:
     def pre(self):
         w, g = self.w, self.g
         if self.ns is not None:
-            pad.num_kv_splits(self.ns, g.seq_lens, 1, w.num_heads, w.num_kv_heads, w.max_kv_splits,
+            pad.num_kv_splits(self.ns, g.seq_lens, w.num_group, w.num_heads, w.num_kv_heads, w.max_kv_splits,
                               w.device_core_count)
         if self.indptr is not None:
             pad.build_page_indices(self.flat, g.block_tables, self.indptr)
@@ -103,12 +104,14 @@ class Step:
         pad.paged_attn_decode(self.tmp, self.es, self.ml, g.query, g.key_cache, g.value_cache, bt,
                               g.seq_lens, w.scale, w.max_seq_len, partition_size=self.partition,
                               num_splits=self.ns, kv_indptr=self.indptr, num_workers=self.workers,
-                              alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale)
+                              alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale,
+                              num_group=w.num_group)
 
     def reduce(self):
         w, g = self.w, self.g
         pad.paged_attn_reduce(self.out, self.tmp, self.es, self.ml, g.seq_lens,
-                              partition_size=self.partition, num_splits=self.ns)
+                              partition_size=self.partition, num_splits=self.ns,
+                              num_group=w.num_group)
 
     def run(self):
         self.pre()
@@ -141,11 +144,13 @@ def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int, min
     orc = oracle.get()
     n = w.num_seqs if sample_seqs <= 0 else min(sample_seqs, w.num_seqs)
     sub = w.subset(range(n))
+    rows = sub.expanded()  # with query groups: one oracle sequence per query row
+
     def cache(t):  # fp8 caches go to the oracle as their codes
         return t.numpy() if t.dtype == torch.uint8 else t.float().numpy()
 
-    args = (sub.query.float().numpy(), cache(sub.key_cache), cache(sub.value_cache),
-            sub.block_tables.numpy(), sub.seq_lens.numpy(), sub.scale)
+    args = (rows.query.float().numpy(), cache(rows.key_cache), cache(rows.value_cache),
+            rows.block_tables.numpy(), rows.seq_lens.numpy(), rows.scale)
     kw = dict(alibi=None if w.alibi_slopes is None else w.alibi_slopes.numpy(),
               k_scale=w.k_scale, v_scale=w.v_scale)
     runs, total = 0, 0.0
@@ -161,7 +166,7 @@ def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int, min
         threads = os.cpu_count() or 1
     threads = min(threads, n * w.num_kv_heads)  # one (sequence, kv head) per thread
     kv = sub.kv_bytes()
-    err = float(np.abs(out[:n].float().cpu().numpy() - ref).max())
+    err = float(np.abs(out[:n * w.num_group].float().cpu().numpy() - ref).max())
     return ({"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
              "sample": f"{n} of {w.num_seqs} sequences (all heads), {kv} KV bytes, "
                        f"{runs} runs in {total:.1f} s", "seconds": dt},
@@ -344,6 +349,9 @@ def main():
     ap.add_argument("--kv-cache", choices=("same", "fp8"), default="same",
                     help="fp8: the same workload with FP8 E4M3 caches (configs 2-4)")
     ap.add_argument("--alibi", action="store_true", help="the same workload with ALiBi slopes")
+    ap.add_argument("--num-group", type=int, default=1,
+                    help="query tokens per sequence (configs 2-5): each attends over the whole "
+                         "sequence; the grouped-head kernel reads the cache once for all of them")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -373,7 +381,8 @@ def main():
         return
 
     log(f"bench: generating workload {args.config}")
-    w = workloads.config(args.config, kv_cache=args.kv_cache, alibi=args.alibi)
+    w = workloads.config(args.config, kv_cache=args.kv_cache, alibi=args.alibi,
+                         num_group=args.num_group)
     kind = kernel_kind(w)
     # The MLA workload's split policy is not fixed by its definition: it runs
     # with balanced splits, one token range per compute unit.
@@ -445,7 +454,8 @@ def main():
                    "kv_bytes_per_step": kv,
                    "kv_cache": (f"fp8 e4m3, k_scale = v_scale = {w.k_scale}" if w.kv_dtype is not None
                                 else "query dtype"),
-                   "alibi": w.alibi_slopes is not None},
+                   "alibi": w.alibi_slopes is not None, "num_group": w.num_group,
+                   "query_tokens_per_s": round(w.num_seqs * w.num_group / (ms_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

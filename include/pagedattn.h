@@ -84,6 +84,17 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
  * Phase 2 with partition_size == 0 merges the slots before the first one
  * whose max is -inf; the final output is the same as with any other split.
  *
+ * Query groups (num_group = g > 1; [SGMETA] get_num_kv_splits_triton's
+ * num_group, its output indexed seq * num_group + group): each sequence has g
+ * query tokens, and every one of them attends over the sequence's whole
+ * cache (the pages define no masks among them). query, tmp_output,
+ * max_logits, exp_sums and output then have num_seqs * g rows, row s * g + j
+ * for token j of sequence s; seq_lens and the page lists stay per sequence;
+ * num_splits, when given, has num_seqs * g entries, and the g entries of a
+ * sequence must be equal (num_kv_splits writes them so). The grouped-head
+ * matrix-core kernel serves the g tokens of a kv head together (g * G <= 16
+ * columns), reading each K/V byte once for all of them.
+ *
  * Variants of phase 1 named by the [PAv2] wrapper arguments (alibi_slopes,
  * kv_cache_dtype, k_scale, v_scale), whose math the page does not give; the
  * readings implemented:
@@ -152,6 +163,8 @@ typedef struct pa_decode_args {
     int32_t kv_dtype;            /* 0 (or equal to dtype): caches hold dtype;
                                     PA_FP8_E4M3: fp8 caches with the scales below */
     float k_scale, v_scale;      /* fp8 caches only; must be finite and nonzero */
+    int32_t num_group;           /* query tokens per sequence (0 or 1: one); see
+                                    "Query groups" */
 } pa_decode_args;
 
 #define PA_KERNEL_AUTO 0
@@ -163,7 +176,7 @@ typedef struct pa_decode_args {
  *   dtype f32, f16, bf16 with x = 16 / element size;
  *   (head_size, v_head_size) in {(64,64), (128,128), (256,256), (576,512)};
  *   any group size num_heads / num_kv_heads (grouped heads of f16/bf16 caches
- *   run on MFMA when block_size >= 8 and the group is at most 16).
+ *   run on MFMA when block_size >= 8 and num_group * group is 2..16).
  * ALiBi slopes run on every kernel. fp8 caches (x = 16) run on the
  * grouped-head matrix-core kernel (f16/bf16 queries, the conditions above)
  * and on the vector kernel; latent rows over fp8 caches go to the vector
@@ -196,6 +209,8 @@ typedef struct pa_reduce_args {
                                     merge the slots before the first one whose
                                     max_logits is -inf */
     int32_t max_num_parts;
+    int32_t num_group;           /* as given to paged_attn_decode: output, tmp_output,
+                                    max_logits and exp_sums have num_seqs * num_group rows */
 } pa_reduce_args;
 
 int paged_attn_reduce(const pa_reduce_args* args, void* stream);

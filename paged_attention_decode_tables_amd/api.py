@@ -54,7 +54,7 @@ class DecodeArgs(ctypes.Structure):
         ("partition_size", _i32), ("max_num_parts", _i32), ("max_seq_len", _i32),
         ("dtype", _i32), ("kernel_hint", _i32), ("num_workers", _i32),
         ("alibi_slopes", _vp), ("kv_dtype", _i32), ("k_scale", ctypes.c_float),
-        ("v_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float), ("num_group", _i32),
     ]
 
 
@@ -68,7 +68,7 @@ class ReduceArgs(ctypes.Structure):
         ("ml_stride_s", _i64), ("ml_stride_h", _i64), ("ml_stride_p", _i64),
         ("seq_lens", _vp), ("num_splits", _vp),
         ("num_seqs", _i32), ("num_heads", _i32), ("v_head_size", _i32),
-        ("partition_size", _i32), ("max_num_parts", _i32),
+        ("partition_size", _i32), ("max_num_parts", _i32), ("num_group", _i32),
     ]
 
 
@@ -153,7 +153,8 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
                       num_splits: Optional[torch.Tensor] = None,
                       kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
                       num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
-                      k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+                      k_scale: float = 1.0, v_scale: float = 1.0, num_group: int = 1,
+                      stream=None) -> None:
     """Phase 1: per-split max logits, exp sums and normalised outputs.
 
     Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
@@ -163,6 +164,9 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     num_workers > 0 asks for balanced splits (equal token ranges).
     Caches of dtype uint8 or float8_e4m3fn hold FP8 E4M3 codes (x = 16),
     dequantized with k_scale / v_scale; alibi_slopes is an fp32 [H] tensor.
+    num_group > 1: each sequence has num_group query tokens; query and the
+    workspaces have num_seqs * num_group rows (row s * num_group + j) while
+    seq_lens and the page lists stay per sequence.
     """
     lib = load_library()
     fp8 = key_cache.dtype in _FP8_CACHE
@@ -172,7 +176,10 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
         if alibi_slopes.dtype != torch.float32 or alibi_slopes.shape != (query.shape[1],) \
                 or not alibi_slopes.is_contiguous():
             raise ValueError("alibi_slopes must be a contiguous fp32 tensor of shape [num_heads]")
-    S, H, D = query.shape
+    R, H, D = query.shape
+    S = seq_lens.shape[0]
+    if num_group < 1 or R != S * num_group:
+        raise ValueError(f"query has {R} rows, expected num_seqs * num_group = {S} * {num_group}")
     NB, Hkv, Dx, bs, x = key_cache.shape
     Dv = value_cache.shape[2]
     a = DecodeArgs()
@@ -206,16 +213,20 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     a.alibi_slopes = _ptr(alibi_slopes)
     a.kv_dtype = PA_FP8_E4M3 if fp8 else 0
     a.k_scale, a.v_scale = float(k_scale), float(v_scale)
+    a.num_group = num_group
     _check(lib.paged_attn_decode(ctypes.byref(a), _stream(stream)))
 
 
 def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: torch.Tensor,
                       max_logits: torch.Tensor, seq_lens: torch.Tensor, *,
                       partition_size: int = 512, num_splits: Optional[torch.Tensor] = None,
-                      stream=None) -> None:
-    """Phase 2: log-sum-exp merge of the splits into output [S, H, Dv]."""
+                      num_group: int = 1, stream=None) -> None:
+    """Phase 2: log-sum-exp merge of the splits into output [S * num_group, H, Dv]."""
     lib = load_library()
-    S, H, P, Dv = tmp_output.shape
+    R, H, P, Dv = tmp_output.shape
+    S = seq_lens.shape[0]
+    if num_group < 1 or R != S * num_group:
+        raise ValueError(f"tmp_output has {R} rows, expected num_seqs * num_group = {S} * {num_group}")
     a = ReduceArgs()
     a.output = _ptr(output)
     a.out_stride_s, a.out_stride_h, a.out_stride_d = output.stride()
@@ -232,6 +243,7 @@ def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: 
     a.num_seqs, a.num_heads, a.v_head_size = S, H, Dv
     a.partition_size = partition_size
     a.max_num_parts = P
+    a.num_group = num_group
     _check(lib.paged_attn_reduce(ctypes.byref(a), _stream(stream)))
 
 

@@ -70,6 +70,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if (fp8 && (!isfinite(a->k_scale) || !isfinite(a->v_scale) || a->k_scale == 0.0f || a->v_scale == 0.0f))
         return fail(PA_EINVAL, "paged_attn_decode: fp8 caches need finite nonzero k_scale and v_scale");
     if (a->num_seqs < 0) return fail(PA_EINVAL, "paged_attn_decode: num_seqs < 0");
+    if (a->num_group < 0) return fail(PA_EINVAL, "paged_attn_decode: num_group < 0");
+    const int ng = a->num_group < 1 ? 1 : a->num_group;  // query tokens per sequence
     if (a->num_heads < 1 || a->num_kv_heads < 1 || a->num_heads % a->num_kv_heads)
         return fail(PA_EINVAL, "paged_attn_decode: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                     a->num_heads, a->num_kv_heads);
@@ -119,10 +121,10 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
         (a->k_stride_h * kv_esz) % 16 || (a->v_stride_b * kv_esz) % 16 || (a->v_stride_h * kv_esz) % 16 ||
         a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
         return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
-    if (parts > kMaxGridYZ || a->num_heads > kMaxGridYZ)
-        return fail(PA_ENOTSUP, "paged_attn_decode: partitions and num_heads must be <= %d", kMaxGridYZ);
-    if ((int64_t)a->num_seqs * a->num_heads > 0x7fffffff)
-        return fail(PA_ENOTSUP, "paged_attn_decode: num_seqs * num_heads must be < 2^31");
+    if (parts > kMaxGridYZ || (int64_t)a->num_heads * ng > kMaxGridYZ)
+        return fail(PA_ENOTSUP, "paged_attn_decode: partitions and num_heads * num_group must be <= %d", kMaxGridYZ);
+    if ((int64_t)a->num_seqs * ng * a->num_heads > 0x7fffffff)
+        return fail(PA_ENOTSUP, "paged_attn_decode: num_seqs * num_group * num_heads must be < 2^31");
     const int D = a->head_size, Dv = a->v_head_size, group = a->num_heads / a->num_kv_heads;
     if (!pa::decode_valu_supported(a->dtype, D, Dv))
         return fail(PA_ENOTSUP, "paged_attn_decode: (head_size, v_head_size) = (%d, %d) is not built", D, Dv);
@@ -159,6 +161,7 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     p.partition_size = a->partition_size;
     p.max_num_parts = a->max_num_parts;
     p.num_seqs = a->num_seqs;
+    p.num_group = ng;
     p.num_workers = balanced ? a->num_workers : 0;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -167,7 +170,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     const bool mla_ok = pa::decode_mla_supported(a->dtype, D, Dv, group, a->block_size) &&
                         a->value_cache == a->key_cache && a->v_stride_b == a->k_stride_b &&
                         a->v_stride_h == a->k_stride_h && !fp8;
-    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group, a->block_size);
+    // its 16 columns hold the (query token, head) pairs of a kv head
+    const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group * ng, a->block_size);
     if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok && !mla_ok)
         return fail(PA_ENOTSUP, "paged_attn_decode: no matrix-core kernel serves this problem");
     if (balanced && (!mla_ok || a->kernel_hint == PA_KERNEL_VALU))
@@ -187,8 +191,10 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
 {
     if (!a) return fail(PA_EINVAL, "paged_attn_reduce: args is NULL");
     if (!elem_size(a->out_dtype)) return fail(PA_EINVAL, "paged_attn_reduce: unknown out_dtype %d", a->out_dtype);
-    if (a->num_seqs < 0 || a->num_heads < 1 || a->v_head_size < 1 || a->max_num_parts < 1)
-        return fail(PA_EINVAL, "paged_attn_reduce: num_seqs >= 0, num_heads, v_head_size, max_num_parts >= 1 required");
+    if (a->num_seqs < 0 || a->num_heads < 1 || a->v_head_size < 1 || a->max_num_parts < 1 || a->num_group < 0)
+        return fail(PA_EINVAL, "paged_attn_reduce: num_seqs, num_group >= 0 and num_heads, v_head_size, "
+                               "max_num_parts >= 1 required");
+    const int ng = a->num_group < 1 ? 1 : a->num_group;
     if (!a->num_splits && a->partition_size != 0 && (a->partition_size < 64 || a->partition_size % 64))
         return fail(PA_EINVAL, "paged_attn_reduce: partition_size %d is neither 0 nor a positive multiple of 64",
                     a->partition_size);
@@ -201,8 +207,8 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
         return fail(PA_ENOTSUP, "paged_attn_reduce: v_head_size %d is not built", a->v_head_size);
     if (!aligned16(a->tmp_output) || a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
         return fail(PA_ENOTSUP, "paged_attn_reduce: tmp_output rows must be 16-byte aligned");
-    const int64_t pairs = (int64_t)a->num_seqs * a->num_heads;
-    if (pairs > 0x7fffffff) return fail(PA_ENOTSUP, "paged_attn_reduce: too many (seq, head) pairs");
+    const int64_t pairs = (int64_t)a->num_seqs * ng * a->num_heads;
+    if (pairs > 0x7fffffff) return fail(PA_ENOTSUP, "paged_attn_reduce: too many (row, head) pairs");
 
     pa::ReduceParams p{};
     p.out = a->output;
@@ -219,6 +225,7 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
     p.seq_lens = a->seq_lens;
     p.num_splits = a->num_splits;
     p.num_seqs = a->num_seqs;
+    p.num_group = ng;
     p.num_heads = a->num_heads;
     p.partition_size = a->partition_size;
     p.max_num_parts = a->max_num_parts;

@@ -132,14 +132,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     const int part0 = (int)(gridDim.y - 1 - blockIdx.y) * p.split_run;  // first split of the run
     const int nrun = min(p.split_run, p.grid_parts - part0);
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    // column r of the MFMA tiles: head hh of the kv head's group, for query
+    // token qg of the sequence (query groups put their tokens side by side,
+    // so every K/V byte serves all of them)
     const int G = p.group;
-    const int h = kvh * G + r;
-    const bool head_ok = r < G;
-    const int64_t mlbase = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part0;
+    const int qg = r / G, hh = r - qg * G;
+    const int h = kvh * G + hh;
+    const bool head_ok = qg < p.num_group;
+    const int qrow = s * p.num_group + qg;  // query / output row
+    const int64_t mlbase = (int64_t)qrow * p.ml_ss + (int64_t)h * p.ml_sh + part0;
 
     // token positions fit in 32 bits (lengths are int32)
     const int L = p.seq_lens[s];
-    const int64_t len64 = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+    const int64_t len64 = split_length(L, p.num_splits, s * p.num_group, p.partition_size, p.max_num_parts);
     const int64_t start64 = (int64_t)part0 * len64;
     // splits of the run that hold tokens: [0, nlive); the rest are empty
     const int nlive = start64 < (int64_t)L
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     // q[h][64*(ks/2) + 16g + 8*(ks%2) .. +8], the order the key pieces hold)
     vec qv[KS];
     {
-        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
+        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int d0 = F8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     lt += __shfl_xor(lt, 32, kWave);
     if (!head_ok) return;
     const int64_t tstride = p.tmp_sp;
-    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part0 * tstride + 4 * g;
+    float* out = p.tmp + (int64_t)qrow * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part0 * tstride + 4 * g;
     {
         const float inv = p.v_scale / lt;
         float* o = out + (int64_t)parked * tstride;

@@ -223,7 +223,9 @@ void k_decode_mla(DecodeParams p)
     __shared__ int rerun_flag;
 
     const int ngroups = p.group / (HPW * NW);
-    const int kvh = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
+    const int hg = blockIdx.y % ngroups, kq = blockIdx.y / ngroups;
+    // query token qg of every sequence (rows s * num_group + qg)
+    const int qg = kq % p.num_group, kvh = kq / p.num_group;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63, c32 = lane & 31, hl = lane >> 5;
     const int h0 = kvh * p.group + hg * HPW * NW;  // first head of the workgroup
@@ -248,7 +250,7 @@ void k_decode_mla(DecodeParams p)
     // B operand of QK: lane (hl, c32) holds q[h][16*ks + 8*hl .. +8]
     vec8 qv[KS];
     {
-        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh + 8 * hl;
+        const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)(s * p.num_group + qg) * p.q_ss + (int64_t)h * p.q_sh + 8 * hl;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(vec8, load16(q + ks * 16));
     }
@@ -481,7 +483,7 @@ void k_decode_mla(DecodeParams p)
     }
 
     l = half_sum(l);
-    const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
+    const int64_t mloff = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)h * p.ml_sh + part;
     if (hl == 0) {
         p.max_logits[mloff] = mtrue * kLn2;
         p.exp_sums[mloff] = l * fast_exp2(mref - mtrue);
@@ -489,7 +491,7 @@ void k_decode_mla(DecodeParams p)
     // lane (hl, c32), register 4i + j of tile mt holds value column
     // 32mt + 8i + 4hl + j of head c32
     const float inv = 1.0f / l;
-    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp + 4 * hl;
+    float* out = p.tmp + (int64_t)(s * p.num_group + qg) * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp + 4 * hl;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -501,11 +503,11 @@ void k_decode_mla(DecodeParams p)
     if constexpr (!BAL) {
         const int s = blockIdx.x, part = blockIdx.z;
         const int L = p.seq_lens[s];
-        const int64_t len64 = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+        const int64_t len64 = split_length(L, p.num_splits, s * p.num_group, p.partition_size, p.max_num_parts);
         const int64_t start64 = (int64_t)part * len64;
         if (start64 >= (int64_t)L) {  // empty split: the page's early exit
             if (hl == 0) {
-                const int64_t mloff = (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh + part;
+                const int64_t mloff = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)h * p.ml_sh + part;
                 p.max_logits[mloff] = -INFINITY;
                 p.exp_sums[mloff] = 0.0f;
             }
@@ -530,7 +532,7 @@ void k_decode_mla(DecodeParams p)
     // here (all threads of the workgroup together)
     auto mark_empty = [&](int s, int k0) {
         for (int e = tid; e < GH * (p.max_num_parts - k0); e += BT) {
-            const int64_t off = (int64_t)s * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + k0 + e / GH;
+            const int64_t off = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + k0 + e / GH;
             p.max_logits[off] = -INFINITY;
             p.exp_sums[off] = 0.0f;
         }
@@ -544,7 +546,7 @@ void k_decode_mla(DecodeParams p)
         tmax = max(tmax, Li);
         if (w == 0 && Li == 0) {  // worker 0 covers the empty sequences, one thread each
             for (int e = 0; e < GH * p.max_num_parts; ++e) {
-                const int64_t off = (int64_t)i * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + e / GH;
+                const int64_t off = (int64_t)(i * p.num_group + qg) * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + e / GH;
                 p.max_logits[off] = -INFINITY;
                 p.exp_sums[off] = 0.0f;
             }
@@ -625,10 +627,10 @@ template <class E, int NW, bool ALIBI>
 static void launch_mla_a(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
     if (p.num_workers > 0)
-        hipLaunchKernelGGL((k_decode_mla<E, NW, true, ALIBI>), dim3(p.num_workers, p.num_kv_heads, 1),
+        hipLaunchKernelGGL((k_decode_mla<E, NW, true, ALIBI>), dim3(p.num_workers, p.num_kv_heads * p.num_group, 1),
                            dim3(64 * NW), 0, st, p);
     else
-        hipLaunchKernelGGL((k_decode_mla<E, NW, false, ALIBI>), dim3(num_seqs, p.num_kv_heads, parts),
+        hipLaunchKernelGGL((k_decode_mla<E, NW, false, ALIBI>), dim3(num_seqs, p.num_kv_heads * p.num_group, parts),
                            dim3(64 * NW), 0, st, p);
 }
 

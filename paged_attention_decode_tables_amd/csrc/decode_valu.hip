@@ -51,11 +51,13 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
     // the G heads sharing a kv head's rows run on one XCD and share them in
     // its L2; the split index last spreads each split index over all XCDs.
     const int kvh_ = blockIdx.x % p.num_kv_heads, rest = blockIdx.x / p.num_kv_heads;
+    // s: query row (token j of sequence seq = s / num_group, row seq * num_group + j)
     const int s = rest / p.group, h = kvh_ * p.group + rest % p.group, part = blockIdx.y;
+    const int seq = s / p.num_group;
     const int wave = NW > 1 ? (int)threadIdx.x / kWave : 0;
     const int lane = (int)threadIdx.x % kWave;
     float* p_lds = p_all[wave];
-    const int L = p.seq_lens[s];
+    const int L = p.seq_lens[seq];
     const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
     const int64_t start = (int64_t)part * len;
     const int64_t end = (int64_t)L < start + len ? (int64_t)L : start + len;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
     const int64_t wstart = start + wave * sub;
     const int64_t wend = end < wstart + sub ? end : wstart + sub;
 
-    const int32_t* row = page_row(p.pl, s);
+    const int32_t* row = page_row(p.pl, seq);
     const int64_t sb = p.pl.stride_b;
     const KT* kc = reinterpret_cast<const KT*>(p.kc) + (int64_t)kvh * p.k_sh;
     const KT* vc = reinterpret_cast<const KT*>(p.vc) + (int64_t)kvh * p.v_sh;
@@ -262,7 +264,7 @@ static void launch_valu_nw(const DecodeParams& p, dim3 grid, hipStream_t st)
 template <class E, class KE, int D, int DV>
 static hipError_t launch_valu_t(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    const dim3 grid(num_seqs * p.num_heads, parts);
+    const dim3 grid(num_seqs * p.num_group * p.num_heads, parts);
     launch_valu_nw<E, KE, D, DV, PA_VALU_WAVES>(p, grid, st);
     return hipGetLastError();
 }

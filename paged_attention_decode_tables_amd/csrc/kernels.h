@@ -35,6 +35,7 @@ struct DecodeParams {
     const float* alibi;  // optional ALiBi slopes [num_heads] (natural units)
     float v_scale;       // fp8 caches: value scale (1 otherwise); k_scale is in scale_log2
     bool kv_fp8;         // caches hold FP8 E4M3 codes
+    int num_group;       // query tokens per sequence (rows s * num_group + j)
     int split_run;       // grouped-head matrix-core kernel: consecutive splits per workgroup
     int grid_parts;      // splits covered by the grid (set by the launcher)
 };
@@ -50,6 +51,7 @@ struct ReduceParams {
     const int32_t* seq_lens;
     const int32_t* num_splits;
     int num_seqs, num_heads, partition_size, max_num_parts;
+    int num_group;  // query tokens per sequence: rows s * num_group + j
 };
 
 // Decode-metadata parameters (validated copy of pa_metadata_args).

@@ -29,8 +29,10 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
 
     const int tid = threadIdx.x;
     const int col = tid % C, grp = tid / C;
-    const int s = blockIdx.x / p.num_heads, h = blockIdx.x % p.num_heads;
-    const int64_t obase = (int64_t)s * p.out_ss + (int64_t)h * p.out_sh + 4 * col;
+    // row = s * num_group + j: query token j of sequence s
+    const int row = blockIdx.x / p.num_heads, h = blockIdx.x % p.num_heads;
+    const int s = row / p.num_group;
+    const int64_t obase = (int64_t)row * p.out_ss + (int64_t)h * p.out_sh + 4 * col;
 
     const int L = p.seq_lens[s];
     // balanced splits (partition_size 0): every slot, empty ones skipped below
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
         if (balanced) {
             n = p.max_num_parts;
         } else {
-            const int64_t len = split_length(L, p.num_splits, s, p.partition_size, p.max_num_parts);
+            const int64_t len = split_length(L, p.num_splits, row, p.partition_size, p.max_num_parts);
             n = ((int64_t)L + len - 1) / len;
             n = n < p.max_num_parts ? n : p.max_num_parts;
         }
@@ -51,9 +53,9 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
             for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, 0.0f);
         return;
     }
-    const float* ml = p.max_logits + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh;
-    const float* es = p.exp_sums + (int64_t)s * p.ml_ss + (int64_t)h * p.ml_sh;
-    const float* tmp = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
+    const float* ml = p.max_logits + (int64_t)row * p.ml_ss + (int64_t)h * p.ml_sh;
+    const float* es = p.exp_sums + (int64_t)row * p.ml_ss + (int64_t)h * p.ml_sh;
+    const float* tmp = p.tmp + (int64_t)row * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
 
     // this thread's splits grp, grp + NG, ...: local max M (base e), sum W
     // of exp(m_p - M) l_p, and acc = sum of exp(m_p - M) l_p tmp_p
@@ -155,7 +157,7 @@ static int reduce_groups(int Dv, int max_parts)
 template <class OutE, int DV, int NG>
 static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
 {
-    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_heads)), block(DV / 4 * NG);
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * p.num_heads)), block(DV / 4 * NG);
     hipLaunchKernelGGL((k_reduce<OutE, DV, NG>), grid, block, 0, st, p);
 }
 

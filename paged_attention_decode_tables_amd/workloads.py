@@ -71,6 +71,8 @@ class Workload:
     k_scale: float = 1.0
     v_scale: float = 1.0
     alibi_slopes: Optional[torch.Tensor] = None  # fp32 [H]
+    # query tokens per sequence: query rows s * num_group + j
+    num_group: int = 1
 
     @property
     def num_seqs(self) -> int:
@@ -105,11 +107,25 @@ class Workload:
     def subset(self, seqs) -> "Workload":
         """The same workload restricted to some sequences (shares the caches)."""
         idx = torch.as_tensor(list(seqs), dtype=torch.long)
+        ng = self.num_group
+        rows = (idx[:, None] * ng + torch.arange(ng)[None, :]).reshape(-1)
         kw = {k: getattr(self, k) for k in self.__dataclass_fields__}
         kw["seq_lens"] = self.seq_lens[idx].clone()
         kw["block_tables"] = self.block_tables[idx].clone()
-        kw["query"] = self.query[idx].clone()
+        kw["query"] = self.query[rows].clone()
         kw["cu_num_blocks"] = None
+        kw["notes"] = list(self.notes)
+        return Workload(**kw)
+
+    def expanded(self) -> "Workload":
+        """With query groups: one sequence per query row (row s * num_group + j
+        gets sequence s's length and pages), num_group 1. Shares the caches."""
+        ng = self.num_group
+        kw = {k: getattr(self, k) for k in self.__dataclass_fields__}
+        kw["seq_lens"] = self.seq_lens.repeat_interleave(ng)
+        kw["block_tables"] = self.block_tables.repeat_interleave(ng, dim=0)
+        kw["cu_num_blocks"] = None
+        kw["num_group"] = 1
         kw["notes"] = list(self.notes)
         return Workload(**kw)
 
@@ -183,10 +199,11 @@ def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size:
            num_blocks: Optional[int] = None, partition_size: int = 512,
            max_blocks: Optional[int] = None, poison: bool = False, name="custom",
            kv_cache: str = "same", k_scale: float = 1.0, v_scale: float = 1.0,
-           alibi: bool = False) -> Workload:
+           alibi: bool = False, num_group: int = 1) -> Workload:
     """Standard layout workload with the given lengths (drawn in the standard
     order). kv_cache "fp8" / "fp8_codes" gives uint8 E4M3 caches (see the
-    module docstring) with the given scales; alibi adds ALiBi slopes."""
+    module docstring) with the given scales; alibi adds ALiBi slopes;
+    num_group > 1 draws num_group query rows per sequence."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     fp8 = kv_cache != "same"
     esz = 1 if fp8 else torch.tensor([], dtype=dt).element_size()
@@ -201,7 +218,7 @@ def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size:
         raise ValueError("not enough physical blocks")
     perm = torch.randperm(nb, generator=gen)
     S = lens.shape[0]
-    q = _randn(gen, (S, num_heads, head_size), dt)
+    q = _randn(gen, (S * num_group, num_heads, head_size), dt)
     kshape, vshape = (nb, num_kv_heads, head_size // x, block_size, x), (nb, num_kv_heads, dv, block_size)
     if fp8:
         kc = _fp8_cache(gen, kshape, kv_cache, k_scale)
@@ -217,7 +234,7 @@ def custom(*, seed: int, seq_lens, num_heads: int, num_kv_heads: int, head_size:
                  v_head_size=dv, block_size=block_size, x=x, num_blocks=nb,
                  partition_size=partition_size, poison_block=poison_block,
                  kv_dtype=torch.uint8 if fp8 else None, k_scale=k_scale, v_scale=v_scale,
-                 alibi_slopes=alibi_slopes(num_heads) if alibi else None)
+                 alibi_slopes=alibi_slopes(num_heads) if alibi else None, num_group=num_group)
     if poison:
         _poison(w, need)
     return w
@@ -276,22 +293,28 @@ FP8_WORKLOAD_SCALE = 1.0 / 32
 
 
 def config(cfg: int, *, poison: bool = False, kv_cache: str = "same",
-           alibi: bool = False) -> Workload:
+           alibi: bool = False, num_group: int = 1) -> Workload:
     """The five reference workloads (seed = config number). Configs 2-4 also
     come with fp8 caches (kv_cache "fp8", both scales FP8_WORKLOAD_SCALE,
-    name suffix "_kvfp8") and with ALiBi slopes (suffix "_alibi")."""
+    name suffix "_kvfp8"), with ALiBi slopes (suffix "_alibi") and with
+    num_group query tokens per sequence (configs 2-5, suffix "_qg<n>"; the
+    query draw has num_group rows per sequence)."""
     if kv_cache != "same" and cfg not in (2, 3, 4):
         raise ValueError("fp8 caches are drawn for configs 2-4")
-    w = _config(cfg, poison=poison, kv_cache=kv_cache)
+    if num_group != 1 and cfg not in (2, 3, 4, 5):
+        raise ValueError("query groups are drawn for configs 2-5")
+    w = _config(cfg, poison=poison, kv_cache=kv_cache, num_group=num_group)
+    if num_group != 1:
+        w.name += f"_qg{num_group}"
     if alibi:
         w.alibi_slopes = alibi_slopes(w.num_heads)
         w.name += "_alibi"
     return w
 
 
-def _config(cfg: int, *, poison: bool, kv_cache: str) -> Workload:
+def _config(cfg: int, *, poison: bool, kv_cache: str, num_group: int = 1) -> Workload:
     gen = torch.Generator().manual_seed(cfg)
-    kv = dict(kv_cache=kv_cache)
+    kv = dict(kv_cache=kv_cache, num_group=num_group)
     if cfg == 1:
         # 2 seqs, lengths 16 and 13, block size 8, 64 physical blocks; seq 0
         # uses the block table [40, 30] of the Triton issue 2522 example, seq 1
@@ -330,11 +353,12 @@ def _config(cfg: int, *, poison: bool, kv_cache: str) -> Workload:
         w.device_core_count = 256
         return w
     if cfg == 5:
-        return _mla(gen, poison=poison)
+        return _mla(gen, poison=poison, num_group=num_group)
     raise ValueError(f"unknown config {cfg}")
 
 
-def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison, kv_cache="same"):
+def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison, kv_cache="same",
+              num_group=1):
     need = _blocks_needed(lens.tolist(), bs)
     total = sum(need)
     if nb is None:
@@ -343,7 +367,7 @@ def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison, kv_cache=
     fp8 = kv_cache != "same"
     x = 16 if fp8 else 16 // torch.tensor([], dtype=dt).element_size()
     S = lens.shape[0]
-    q = _randn(gen, (S, H, D), dt)
+    q = _randn(gen, (S * num_group, H, D), dt)
     if fp8:
         sc = FP8_WORKLOAD_SCALE
         kc = _fp8_cache(gen, (nb, Hkv, D // x, bs, x), kv_cache, sc)
@@ -359,20 +383,20 @@ def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison, kv_cache=
                  num_kv_heads=Hkv, head_size=D, v_head_size=D, block_size=bs, x=x, num_blocks=nb,
                  poison_block=poison_block, kv_dtype=torch.uint8 if fp8 else None,
                  k_scale=FP8_WORKLOAD_SCALE if fp8 else 1.0,
-                 v_scale=FP8_WORKLOAD_SCALE if fp8 else 1.0)
+                 v_scale=FP8_WORKLOAD_SCALE if fp8 else 1.0, num_group=num_group)
     if poison:
         _poison(w, need)
     return w
 
 
-def _mla(gen, *, poison):
+def _mla(gen, *, poison, num_group=1):
     S, H, D, Dv = 64, 128, 576, 512
     lens = _draw_lengths(5, gen)
     total = int(lens.sum())
     nb = total + (1 if poison else 0)
     perm = torch.randperm(nb, generator=gen)
     dt = torch.bfloat16
-    q = _randn(gen, (S, H, D), dt)
+    q = _randn(gen, (S * num_group, H, D), dt)
     latent = _randn(gen, (nb, D), dt)
     poison_block = int(perm[total]) if poison else None
     bt = _assign_blocks(perm, lens.tolist(), 8192, poison_block if poison else 0)
@@ -388,11 +412,11 @@ def _mla(gen, *, poison):
                     seq_lens=lens, block_tables=bt, query=q, key_cache=k, value_cache=v,
                     scale=1.0 / math.sqrt(192.0), num_heads=H, num_kv_heads=1, head_size=D,
                     v_head_size=Dv, block_size=1, x=8, num_blocks=nb, cu_num_blocks=cu,
-                    latent=latent, poison_block=poison_block)
+                    latent=latent, poison_block=poison_block, num_group=num_group)
 
 
 def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512, max_blocks=None,
-               poison=False) -> Workload:
+               poison=False, num_group=1) -> Workload:
     """Smaller MLA-style workload (page size 1, V aliasing the first Dv values of K)."""
     gen = torch.Generator().manual_seed(seed)
     lens = torch.as_tensor(seq_lens, dtype=torch.int32).clone()
@@ -401,7 +425,7 @@ def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512,
     nb = total + (1 if poison else 0)
     perm = torch.randperm(nb, generator=gen)
     dt = torch.bfloat16
-    q = _randn(gen, (S, num_heads, head_size), dt)
+    q = _randn(gen, (S * num_group, num_heads, head_size), dt)
     latent = _randn(gen, (nb, head_size), dt)
     poison_block = int(perm[total]) if poison else None
     mb = max_blocks or max(1, int(lens.max()))
@@ -415,7 +439,8 @@ def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512,
                     block_tables=bt, query=q, key_cache=k, value_cache=v,
                     scale=1.0 / math.sqrt(192.0), num_heads=num_heads, num_kv_heads=1,
                     head_size=head_size, v_head_size=v_head_size, block_size=1, x=8,
-                    num_blocks=nb, cu_num_blocks=cu, latent=latent, poison_block=poison_block)
+                    num_blocks=nb, cu_num_blocks=cu, latent=latent, poison_block=poison_block,
+                    num_group=num_group)
 
 
 # ---------------------------------------------------------------------------

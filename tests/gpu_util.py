@@ -59,7 +59,7 @@ def tolerances(w: workloads.Workload, kernel: str = "auto"):
 
 
 def workspace(w: workloads.Workload, max_parts: int, device=DEV):
-    S, H, Dv = w.num_seqs, w.num_heads, w.v_head_size
+    S, H, Dv = w.num_seqs * w.num_group, w.num_heads, w.v_head_size
     nan = float("nan")
     tmp = torch.full((S, H, max_parts, Dv), nan, dtype=torch.float32, device=device)
     ml = torch.full((S, H, max_parts), nan, dtype=torch.float32, device=device)
@@ -79,6 +79,7 @@ def run_gpu(w: workloads.Workload, *, partition_size=512, num_splits=None, max_p
         max_parts = max_parts_for(w, partition_size) if num_splits is None else 32
     tmp, ml, es = workspace(w, max_parts)
     ns = None if num_splits is None else torch.as_tensor(num_splits, dtype=torch.int32, device=DEV)
+    R = w.num_seqs * w.num_group  # query rows
     bt = g.block_tables if block_tables is None else block_tables.to(DEV)
     indptr = None
     if csr:
@@ -92,11 +93,11 @@ def run_gpu(w: workloads.Workload, *, partition_size=512, num_splits=None, max_p
     pad.paged_attn_decode(tmp, es, ml, g.query, g.key_cache, g.value_cache, bt, g.seq_lens,
                           w.scale, w.max_seq_len, partition_size=partition_size,
                           num_splits=ns, kv_indptr=indptr, kernel=kernel,
-                          alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale)
-    out = torch.full((w.num_seqs, w.num_heads, w.v_head_size), float("nan"), dtype=out_dtype,
-                     device=DEV)
+                          alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale,
+                          num_group=w.num_group)
+    out = torch.full((R, w.num_heads, w.v_head_size), float("nan"), dtype=out_dtype, device=DEV)
     pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens, partition_size=partition_size,
-                          num_splits=ns)
+                          num_splits=ns, num_group=w.num_group)
     torch.cuda.synchronize()
     return out.cpu(), tmp.cpu(), ml.cpu(), es.cpu()
 

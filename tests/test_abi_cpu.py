@@ -127,6 +127,8 @@ DECODE_BAD = [
     ("misaligned_row", dict(k_stride_b=16 * 128 * 2 + 1), api.PA_ENOTSUP),
     ("max_parts0", dict(max_num_parts=0), api.PA_EINVAL),
     ("neg_seqs", dict(num_seqs=-1), api.PA_EINVAL),
+    ("neg_num_group", dict(num_group=-1), api.PA_EINVAL),
+    ("grid_rows", dict(num_group=1 << 27), api.PA_ENOTSUP),
 ]
 
 
@@ -226,6 +228,7 @@ REDUCE_BAD = [
     ("dv", dict(v_head_size=96), api.PA_ENOTSUP),
     ("inner", dict(out_stride_d=2), api.PA_ENOTSUP),
     ("tmp_align", dict(tmp_stride_p=130), api.PA_ENOTSUP),
+    ("neg_num_group", dict(num_group=-1), api.PA_EINVAL),
 ]
 
 
