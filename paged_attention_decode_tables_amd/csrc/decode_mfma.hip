@@ -449,6 +449,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     }
 }
 
+// Two columns at least: with one (MHA, a single query token) the vector
+// kernel measured faster on the MHA batch (f16 82 vs 84 us, fp8 50 vs 54 us).
 bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
 {
     return (dtype == PA_BF16 || dtype == PA_F16) && D == Dv && (D == 64 || D == 128) &&
