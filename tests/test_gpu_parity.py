@@ -416,16 +416,16 @@ def run_balanced(w, workers, max_parts, out_dtype=torch.float32):
     pad.build_page_indices(flat, g.block_tables, indptr)
     pad.paged_attn_decode(tmp, es, ml, g.query, g.key_cache, g.value_cache, flat, g.seq_lens,
                           w.scale, w.max_seq_len, partition_size=0, num_workers=workers,
-                          kv_indptr=indptr)
-    out = torch.full((w.num_seqs, w.num_heads, w.v_head_size), float("nan"), dtype=out_dtype,
-                     device=DEV)
-    pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens, partition_size=0)
+                          kv_indptr=indptr, alibi_slopes=g.alibi_slopes, num_group=w.num_group)
+    out = torch.full((w.num_seqs * w.num_group, w.num_heads, w.v_head_size), float("nan"),
+                     dtype=out_dtype, device=DEV)
+    pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens, partition_size=0, num_group=w.num_group)
     torch.cuda.synchronize()
     return out.cpu(), tmp.cpu(), ml.cpu(), es.cpu()
 
 
 def workspace_nan(w, max_parts):
-    S, H, Dv = w.num_seqs, w.num_heads, w.v_head_size
+    S, H, Dv = w.num_seqs * w.num_group, w.num_heads, w.v_head_size
     return (torch.full((S, H, max_parts, Dv), float("nan"), device=DEV),
             torch.full((S, H, max_parts), float("nan"), device=DEV),
             torch.full((S, H, max_parts), float("nan"), device=DEV))

@@ -15,7 +15,7 @@ import torch
 
 import paged_attention_decode_tables_amd as pad
 from paged_attention_decode_tables_amd import workloads
-from gpu_util import (check_output, check_partials, oracle_args, oracle_kw,
+from gpu_util import (DEV, check_output, check_partials, oracle_args, oracle_kw,
                       run_gpu, say, tolerances)
 
 pytestmark = pytest.mark.gpu
@@ -186,3 +186,55 @@ def test_fp8_scales_scale_linearly(orc):
     c = run_gpu(dataclasses.replace(w, k_scale=0.1))[0].double()
     assert (c - a).abs().max() > 1e-2
     check_output(dataclasses.replace(w, k_scale=0.1), orc, c.float())
+
+
+# ---------------------------------------------------------------------------
+# the variant workloads at full size, in the launch configuration the
+# benchmark times (--kv-cache fp8, --alibi, --num-group); the oracle checks
+# sampled sequences
+# ---------------------------------------------------------------------------
+FULL_VARIANTS = [
+    # config, workload kwargs, sampled sequences
+    (3, dict(kv_cache="fp8"), [1, 6]),
+    (3, dict(alibi=True), [0, 7]),
+    (3, dict(num_group=2), [3]),
+    (2, dict(kv_cache="fp8"), [0, 9, 31]),
+    (2, dict(num_group=4), [5, 30]),
+    (4, dict(kv_cache="fp8"), "sample"),
+]
+
+
+@pytest.mark.parametrize("cfg,kw,seqs", FULL_VARIANTS,
+                         ids=[f"config{c}_" + "_".join(f"{k}{v}" for k, v in kw.items())
+                              for c, kw, _ in FULL_VARIANTS])
+def test_full_variant_config(orc, cfg, kw, seqs):
+    say(f"full variant config {cfg} {kw}")
+    w = workloads.config(cfg, poison=True, **kw)
+    ns, mp = None, None
+    if cfg == 4:
+        g = w.to(DEV)
+        t = torch.empty(w.num_seqs * w.num_group, dtype=torch.int32, device=DEV)
+        pad.num_kv_splits(t, g.seq_lens, w.num_group, w.num_heads, w.num_kv_heads,
+                          w.max_kv_splits, w.device_core_count)
+        ns, mp = t.cpu().numpy(), w.max_kv_splits
+        order = np.argsort(w.seq_lens.numpy())
+        seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    out, tmp, ml, es = run_gpu(w, num_splits=ns, max_parts=mp)
+    rows = [s * w.num_group + j for s in seqs for j in range(w.num_group)]
+    we = w.expanded()
+    check_output(we, orc, out, seqs=rows)
+    check_partials(we, orc, tmp, ml, es, num_splits=ns, seqs=rows)
+    assert torch.isfinite(out).all()
+
+
+def test_full_config5_alibi_balanced(orc):
+    """The MLA workload with ALiBi slopes as the benchmark runs it (balanced
+    splits, one token range per compute unit)."""
+    say("full config 5 alibi balanced")
+    import test_gpu_parity as tp
+    w = workloads.config(5, poison=True, alibi=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    max_parts = -(-w.max_seq_len // 512)
+    out, tmp, ml, es = tp.run_balanced(w, cus, max_parts)
+    check_output(w.subset([0, 40]), orc, out[[0, 40]])
+    assert torch.isfinite(out).all()
