@@ -52,7 +52,7 @@ def kernel_kind(w) -> str:
             and group in (64, 128) and w.latent is not None and w.kv_dtype is None:
         return "mla"
     cols = group * w.num_group  # (query token, head) pairs of a kv head
-    if low and 2 <= cols <= 16 and w.block_size >= 8 and w.head_size in (64, 128):
+    if low and 1 <= cols <= 16 and w.block_size >= 8 and w.head_size in (64, 128):
         return "mfma"
     return "valu"
 

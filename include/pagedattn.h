@@ -175,8 +175,9 @@ typedef struct pa_decode_args {
  * Supported combinations (others return PA_ENOTSUP):
  *   dtype f32, f16, bf16 with x = 16 / element size;
  *   (head_size, v_head_size) in {(64,64), (128,128), (256,256), (576,512)};
- *   any group size num_heads / num_kv_heads (grouped heads of f16/bf16 caches
- *   run on MFMA when block_size >= 8 and num_group * group is 2..16).
+ *   any group size num_heads / num_kv_heads (f16/bf16 queries with D = Dv in
+ *   {64, 128} run on MFMA when block_size >= 8 and num_group * group is
+ *   1..16).
  * ALiBi slopes run on every kernel. fp8 caches (x = 16) run on the
  * grouped-head matrix-core kernel (f16/bf16 queries, the conditions above)
  * and on the vector kernel; latent rows over fp8 caches go to the vector

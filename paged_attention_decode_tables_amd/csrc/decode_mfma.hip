@@ -449,21 +449,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     }
 }
 
-// Two columns at least: with one (MHA, a single query token) the vector
-// kernel measured faster on the MHA batch (f16 82 vs 84 us, fp8 50 vs 54 us).
+// Any 1..16 columns: with a single one (MHA, one query token) the tiles
+// waste 15/16 of the matrix-core work, but the products cost the same per
+// cache byte as with 16, and the load pipeline beats the vector kernel's
+// (MHA batch: f16 79 vs 81 us, fp8 46 vs 50 us per step).
 bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
 {
     return (dtype == PA_BF16 || dtype == PA_F16) && D == Dv && (D == 64 || D == 128) &&
-           group >= 2 && group <= 16 && block_size >= 8;
+           group >= 1 && group <= 16 && block_size >= 8;
 }
 
 // Splits per workgroup with fixed-size splits: enough that the grid is about
 // one workgroup per SIMD (four per compute unit of the current device), at
-// most kMfmaMaxRun. Per-sequence split counts were already sized for the
+// most kMfmaMaxRun, and at most an eighth of the split count, so a run
+// never holds a large share of a sequence (with short ragged sequences,
+// runs measured slower: the MHA batch, 4 splits at most, went 79 -> 83 us
+// with runs of 4). Per-sequence split counts were already sized for the
 // device by the split heuristic; their splits run one per workgroup (runs
 // of them measured slower on a skewed batch: fewer workgroups for the
 // long sequences).
-static int pick_split_run(int64_t units)
+static int pick_split_run(int64_t units, int parts)
 {
     static int cus[64];
     int dev = 0;
@@ -474,7 +479,8 @@ static int pick_split_run(int64_t units)
             n = 256;
         cus[dev] = n;
     }
-    const int64_t run = units / (4 * (int64_t)cus[dev]);
+    int64_t run = units / (4 * (int64_t)cus[dev]);
+    run = run < parts / 8 ? run : parts / 8;
     return (int)(run < 1 ? 1 : run > kMfmaMaxRun ? kMfmaMaxRun : run);
 }
 
@@ -482,11 +488,7 @@ template <class E, class KE, int D>
 static hipError_t launch_mfma_t(DecodeParams p, int num_seqs, int parts, hipStream_t st)
 {
     p.grid_parts = parts;
-#ifndef PA_MFMA_RUN_NS
-#define PA_MFMA_RUN_NS 1
-#endif
-    p.split_run = p.num_splits ? (PA_MFMA_RUN_NS > 0 ? PA_MFMA_RUN_NS : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts))
-                               : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts);
+    p.split_run = p.num_splits ? 1 : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts, parts);
     if (p.split_run < 1 || p.split_run > kMfmaMaxRun) return hipErrorInvalidValue;
     dim3 grid(num_seqs * p.num_kv_heads, (parts + p.split_run - 1) / p.split_run), block(kWave);
     const size_t lds = (size_t)(p.split_run - 1) * ((D / 16) * kWave * sizeof(f32x4) + 32 * sizeof(float));

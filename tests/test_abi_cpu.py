@@ -142,7 +142,11 @@ def test_decode_rejects(lib, name, change, code):
 def test_decode_mfma_hint_rejected_where_it_does_not_apply(lib):
     a = _mut(good_decode(dtype=api.PA_F32, D=64, Dv=64), kernel_hint=api.PA_KERNEL["mfma"])
     assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
-    a = _mut(good_decode(H=2, Hkv=2), kernel_hint=api.PA_KERNEL["mfma"])  # group 1
+    a = _mut(good_decode(D=256, Dv=256), kernel_hint=api.PA_KERNEL["mfma"])  # head size 256
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
+    a = _mut(good_decode(bs=4), kernel_hint=api.PA_KERNEL["mfma"])  # blocks of 4 tokens
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
+    a = _mut(good_decode(H=16, Hkv=1), kernel_hint=api.PA_KERNEL["mfma"], num_group=2)  # 32 columns
     assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
 
 

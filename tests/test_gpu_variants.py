@@ -59,6 +59,12 @@ CASES = [
                                     num_kv_heads=2, head_size=128, block_size=16, dtype="bf16",
                                     alibi=True), dict(kernel="mfma", num_splits=[9, 1, 4],
                                                       max_parts=12)),
+    ("alibi_mha_mfma_f16", dict(seed=117, seq_lens=[800, 2, 129], num_heads=4, num_kv_heads=4,
+                                head_size=128, block_size=16, dtype="f16", alibi=True,
+                                poison=True), dict(kernel="mfma")),
+    ("fp8_mha_mfma_bf16", dict(seed=118, seq_lens=[1500, 64, 3], num_heads=4, num_kv_heads=4,
+                               head_size=64, block_size=32, dtype="bf16", kv_cache="fp8",
+                               k_scale=0.05, v_scale=0.05, poison=True), dict(kernel="mfma")),
     ("alibi_valu_f32", dict(seed=114, seq_lens=[700, 3, 64], num_heads=4, num_kv_heads=4,
                             head_size=128, block_size=16, dtype="f32", alibi=True, poison=True),
      dict(kernel="valu")),
