@@ -338,6 +338,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a kernel of known "
                          "traffic for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="size of the buffer read before each step of the cold-cache pass "
+                         "(0: no cold-cache pass)")
     ap.add_argument("--fixed-splits", action="store_true",
                     help="run the MLA workload with its fixed 512-token partitions instead of "
                          "balanced splits")
@@ -429,6 +432,42 @@ def main():
     achieved = kv / (dec_ms * 1e-3) / 1e9
     traffic = recorded_traffic(w.name, kind, kv)
 
+    # Cold-cache region: before each step a sum reads a buffer larger than
+    # the L2s and the 256 MB Infinity Cache, so no KV byte of the previous
+    # step is still on chip (a read leaves clean lines: the step pays no
+    # write-back of the flush). One pass brackets whole steps with events,
+    # a second pass phase 1 alone (events between the launches of a step
+    # would add their own gaps to the step).
+    cold = None
+    if args.flush_mib:
+        junk = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
+        sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+        def cold_pass(phase1_only):
+            evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+            torch.cuda.synchronize()
+            for k in range(K):
+                torch.sum(junk, dim=0, out=sink)
+                if phase1_only:
+                    step.pre()
+                evc[k][0].record()
+                if phase1_only:
+                    step.decode()
+                else:
+                    step.run()
+                evc[k][1].record()
+                if phase1_only:
+                    step.reduce()
+            torch.cuda.synchronize()
+            return float(np.median([e[0].elapsed_time(e[1]) for e in evc]))
+
+        c_step, c_dec = cold_pass(False), cold_pass(True)
+        del junk, sink
+        cold = {"flush_mib": args.flush_mib, "us_per_step_median": round(c_step * 1e3, 2),
+                "phase1_us_median": round(c_dec * 1e3, 2),
+                "kv_gbs": round(kv / (c_step * 1e-3) / 1e9, 1),
+                "phase1_frac_of_hbm_peak": round(kv / (c_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -463,6 +502,8 @@ def main():
         "phase2_us": round(red_ms * 1e3, 2),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }
+    if cold is not None:
+        res["cold_cache"] = cold
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         cb, parity = cpu_baseline(w, step.out, args.cpu_sample_seqs, args.cpu_seconds)
