@@ -7,12 +7,15 @@
 // heads that share one kv head at once, so each K/V byte is read from HBM
 // once per (seq, kv head) instead of G times.
 //
-// One single-wave workgroup per (seq, kv head, run of up to four consecutive
-// splits): the load pipeline runs through the whole run, and at each split
-// boundary the split's softmax state is normalised, parked in LDS and
-// reset (the last split's goes straight out); the parked ones are written
-// after the loop. Fewer, longer workgroups cut the per-workgroup start-up
-// and drain that dominated with one workgroup per 512-token split. In the
+// Single-wave workgroups, each walking runs of consecutive splits of one
+// (seq, kv head): with fixed-size splits one run of up to four per
+// workgroup; with per-sequence split counts persistent workers, each taking
+// an equal share of the batch's tokens as runs of whole splits. The load
+// pipeline runs through a whole run, and at each split boundary the split's
+// softmax state is normalised, parked in LDS and reset (the last split's
+// goes straight out); the parked ones are written after the loop. Fewer,
+// longer runs cut the per-workgroup start-up and drain that dominated with
+// one workgroup per 512-token split. In the
 // wave, lane = 16*g + r (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
 // unused columns get q = 0 and are never stored). The split is walked in
 // 32-token chunks, loaded in 16 KB tiles of K/V (one chunk of 16-bit caches,
@@ -97,15 +100,33 @@ constexpr int kMfmaMaxRun = 4;
 #ifndef PA_MFMA_FP8_SUB
 #define PA_MFMA_FP8_SUB 2
 #endif
-// Waves per SIMD the register budget is sized for.
+// Waves per SIMD the register budget is sized for (grid / persistent workers).
 #ifndef PA_MFMA_OCCUPANCY
 #define PA_MFMA_OCCUPANCY 2
 #endif
+#ifndef PA_MFMA_PERSIST_OCCUPANCY
+#define PA_MFMA_PERSIST_OCCUPANCY 2
+#endif
 
-// BS > 0 fixes the block size at compile time (every load of a chunk is then
-// an immediate offset from two base addresses); BS == 0 reads it at run time.
-template <class E, class KE, int D, int DV, int BS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCUPANCY))) void k_decode_mfma(DecodeParams p)
+// Rows of the split outputs (tmp_output). PA_PARTIAL_NT: with the
+// nontemporal hint.
+#ifndef PA_PARTIAL_NT
+#define PA_PARTIAL_NT 1
+#endif
+__device__ __forceinline__ void store_partial(float* at, f32x4 v)
+{
+    if constexpr (PA_PARTIAL_NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(at));
+    else *reinterpret_cast<f32x4*>(at) = v;
+}
+
+// One run of nrun consecutive splits [part0, part0 + nrun) of sequence s for
+// kv head kvh (the kernel body). L is the sequence length and len64 its split
+// length. BS > 0 fixes the block size at compile time (every load of a chunk
+// is then an immediate offset from two base addresses); BS == 0 reads it at
+// run time.
+template <class E, class KE, int D, int DV, int BS, bool PERSIST>
+__device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, int part0, int nrun,
+                                         int L, int64_t len64)
 {
     using T = typename E::storage;
     using KT = typename KE::storage;
@@ -120,18 +141,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     constexpr int NSUB = F8 ? PA_MFMA_FP8_SUB : 1;
     constexpr int CH = 32 * NSUB;
 
-    // grid (kv head + Hkv * seq, run of splits): workgroups are dealt to the
-    // XCDs round-robin by linear id. With the kv head fastest, every XCD gets
-    // an equal share of every sequence's tokens (Hkv a multiple of 8: exactly
-    // one kv head's), whatever the length mix; the run index last keeps
-    // each run index's work (the first is never empty, late ones often
-    // are) spread over all XCDs.
-    const int kvh = blockIdx.x % p.num_kv_heads, s = blockIdx.x / p.num_kv_heads;
-    // runs in reverse order: late runs exist only for long sequences and are
-    // the longest, so they are dispatched first and the grid ends on short work
-    const int part0 = (int)(gridDim.y - 1 - blockIdx.y) * p.split_run;  // first split of the run
-    const int nrun = min(p.split_run, p.grid_parts - part0);
-    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    // In the persistent workers' loop the lane index is re-derived through an
+    // opaque zero on every run, so nothing computed from it can be hoisted
+    // out of that loop (kept live across it, such values pushed the kernel
+    // past 256 registers).
+    int opaque = 0;
+    if constexpr (PERSIST) asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+    const int lane = (int)threadIdx.x + opaque, g = lane >> 4, r = lane & 15;
     // column r of the MFMA tiles: head hh of the kv head's group, for query
     // token qg of the sequence (query groups put their tokens side by side,
     // so every K/V byte serves all of them)
@@ -143,8 +159,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
     const int64_t mlbase = (int64_t)qrow * p.ml_ss + (int64_t)h * p.ml_sh + part0;
 
     // token positions fit in 32 bits (lengths are int32)
-    const int L = p.seq_lens[s];
-    const int64_t len64 = split_length(L, p.num_splits, s * p.num_group, p.partition_size, p.max_num_parts);
     const int64_t start64 = (int64_t)part0 * len64;
     // splits of the run that hold tokens: [0, nlive); the rest are empty
     const int nlive = start64 < (int64_t)L
@@ -431,7 +445,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
         const float inv = p.v_scale / lt;
         float* o = out + (int64_t)parked * tstride;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(o + 16 * mt) = acc[mt] * inv;
+        for (int mt = 0; mt < MT; ++mt) store_partial(o + 16 * mt, acc[mt] * inv);
         if (g == 0) {
             p.max_logits[mlbase + parked] = m * kLn2;
             p.exp_sums[mlbase + parked] = lt;
@@ -441,11 +455,173 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_OCCU
         float* o = out + (int64_t)j * tstride;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<f32x4*>(o + 16 * mt) = park[(j * MT + mt) * kWave + lane];
+            store_partial(o + 16 * mt, park[(j * MT + mt) * kWave + lane]);
         if (g == 0) {
             p.max_logits[mlbase + j] = park_ml[32 * j + r];
             p.exp_sums[mlbase + j] = park_ml[32 * j + 16 + r];
         }
+    }
+}
+
+// Live tokens of every sequence (lengths <= 0 count none), summed over the
+// batch by one wave.
+__device__ __forceinline__ int64_t batch_tokens(const int32_t* seq_lens, int S)
+{
+    int64_t t = 0;
+    for (int b = 0; b < S; b += 4 * kWave) {
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = b + j * kWave + (int)threadIdx.x;
+            v[j] = s < S ? seq_lens[s] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t += v[j] > 0 ? v[j] : 0;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, kWave);
+    return uniform_i64(t);
+}
+
+// Lane i's value, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int lane_value(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+__device__ __forceinline__ int64_t lane_value(int64_t v, int i)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, i);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), i);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int64_t wave_scan_i64(int64_t v)
+{
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int64_t u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Persistent workers for per-sequence split counts. The batch's live tokens,
+// in sequence order, are numbered 0..T-1. Worker u (of NU) of kv head kvh
+// takes every split whose first token falls in [u*T/NU, (u+1)*T/NU): each
+// worker gets the same share of tokens to within one split, no workgroup is
+// spent on an empty split, and a worker's consecutive splits of one sequence
+// run through one load pipeline (runs of up to split_run). The splits and
+// their partials are exactly those of the one-workgroup-per-split grid.
+template <class E, class KE, int D, int DV, int BS>
+__device__ __forceinline__ void mfma_worker(const DecodeParams& p)
+{
+    const int Hkv = p.num_kv_heads, S = p.num_seqs, ng = p.num_group;
+    const int NU = (int)(gridDim.x / Hkv);
+    const int kvh = (int)blockIdx.x % Hkv, u = (int)blockIdx.x / Hkv;
+    const int lane = threadIdx.x;
+    const int64_t T = batch_tokens(p.seq_lens, S);
+    // [X0, X1) = [floor(T*u/NU), floor(T*(u+1)/NU)) without overflow
+    const int64_t tq = T / NU, tr = T % NU;
+    const int64_t X0 = tq * u + tr * u / NU;
+    const int64_t X1 = tq * (u + 1) + tr * (u + 1) / NU;
+
+    // Walk the sequences 64 at a time (lane i holds sequence bj + i; the
+    // lengths of four such blocks are loaded together): find the one holding
+    // token X0, then take splits until their starts reach X1.
+    int64_t before = 0;  // live tokens of the sequences before block bj
+    for (int b = 0; b < S && before < X1; b += 4 * kWave) {
+        int Lq[4], nq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int sl = b + j * kWave + lane;
+            Lq[j] = sl < S ? p.seq_lens[sl] : 0;
+            nq[j] = (sl < S && p.num_splits) ? p.num_splits[(int64_t)sl * ng] : 1;
+        }
+#pragma unroll 1
+        for (int j = 0; j < 4; ++j) {
+            const int bj = b + j * kWave;
+            if (bj >= S || before >= X1) break;
+            const int Lr = j == 0 ? Lq[0] : j == 1 ? Lq[1] : j == 2 ? Lq[2] : Lq[3];
+            const int nr = j == 0 ? nq[0] : j == 1 ? nq[1] : j == 2 ? nq[2] : nq[3];
+            const int64_t incl = wave_scan_i64(Lr > 0 ? Lr : 0);
+            const int64_t blk_end = before + lane_value(incl, kWave - 1);
+            if (blk_end > X0) {
+                // sequences of this block that end past X0 and start before X1
+                for (int i = 0; i < kWave && bj + i < S; ++i) {
+                    const int Ls = lane_value(Lr, i);
+                    const int64_t Cs = before + lane_value(incl, i) - (Ls > 0 ? Ls : 0);
+                    if (Cs >= X1) break;
+                    if (Ls <= 0 || Cs + Ls <= X0) continue;
+                    int n = lane_value(nr, i);
+                    n = n < 1 ? 1 : (n > p.max_num_parts ? p.max_num_parts : n);
+                    const int64_t len = p.num_splits ? ((((int64_t)Ls + n - 1) / n + 63) & ~int64_t(63))
+                                                     : (int64_t)p.partition_size;
+                    const int nl = (int)(((int64_t)Ls + len - 1) / len);
+                    int sp = Cs < X0 ? (int)((X0 - Cs + len - 1) / len) : 0;
+                    while (sp < nl) {
+                        const int64_t st = Cs + sp * len;
+                        if (st >= X1) break;
+                        int nrun = (int)min((int64_t)(nl - sp), (X1 - st + len - 1) / len);
+                        nrun = min(nrun, p.split_run);
+                        mfma_run<E, KE, D, DV, BS, true>(p, kvh, bj + i, sp, nrun, Ls, len);
+                        sp += nrun;
+                    }
+                }
+            }
+            before = blk_end;
+        }
+    }
+
+    // Splits at or past a sequence's end hold -inf / 0: worker u marks them
+    // for sequences u, u + NU, ... (its kv head's columns).
+    const int G = p.group, cols = G * ng;
+    for (int s = u; s < S; s += NU) {
+        const int Ls = p.seq_lens[s];
+        int nl = 0;
+        if (Ls > 0) {
+            const int64_t len = split_length(Ls, p.num_splits, s * ng, p.partition_size, p.max_num_parts);
+            nl = (int)(((int64_t)Ls + len - 1) / len);
+        }
+        const int ne = p.max_num_parts - nl;
+        for (int idx = lane; idx < cols * ne; idx += kWave) {
+            const int c = idx / ne, sp = nl + idx % ne;
+            const int qg = c / G, hh = c - qg * G;
+            const int64_t at = (int64_t)(s * ng + qg) * p.ml_ss + (int64_t)(kvh * G + hh) * p.ml_sh + sp;
+            p.max_logits[at] = -INFINITY;
+            p.exp_sums[at] = 0.0f;
+        }
+    }
+}
+
+// Phase-1 kernel. PERSIST: persistent workers (per-sequence split counts).
+// Otherwise the grid is (kv head + Hkv * seq, run of splits): workgroups are
+// dealt to the XCDs round-robin by linear id. With the kv head fastest, every
+// XCD gets an equal share of every sequence's tokens (Hkv a multiple of 8:
+// exactly one kv head's), whatever the length mix; the run index last keeps
+// each run index's work (the first is never empty, late ones often are)
+// spread over all XCDs. Persistent workers keep the kv head fastest too.
+// Waves per SIMD: persistent workers over fp8 caches with a run-time block
+// size take the whole register file (at two they spill a few registers).
+template <class KE, int BS, bool PERSIST>
+constexpr int mfma_occupancy()
+{
+    return !PERSIST ? PA_MFMA_OCCUPANCY : (BS == 0 && KE::size == 1) ? 1 : PA_MFMA_PERSIST_OCCUPANCY;
+}
+
+template <class E, class KE, int D, int DV, int BS, bool PERSIST>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(mfma_occupancy<KE, BS, PERSIST>()))) void k_decode_mfma(DecodeParams p)
+{
+    if constexpr (PERSIST) {
+        mfma_worker<E, KE, D, DV, BS>(p);
+    } else {
+        const int kvh = blockIdx.x % p.num_kv_heads, s = blockIdx.x / p.num_kv_heads;
+        // runs in reverse order: late runs exist only for long sequences and
+        // are the longest, so they are dispatched first and the grid ends on
+        // short work
+        const int part0 = (int)(gridDim.y - 1 - blockIdx.y) * p.split_run;  // first split of the run
+        const int nrun = min(p.split_run, p.grid_parts - part0);
+        const int L = p.seq_lens[s];
+        const int64_t len64 = split_length(L, p.num_splits, s * p.num_group, p.partition_size, p.max_num_parts);
+        mfma_run<E, KE, D, DV, BS, false>(p, kvh, s, part0, nrun, L, len64);
     }
 }
 
@@ -459,44 +635,79 @@ bool decode_mfma_supported(int dtype, int D, int Dv, int group, int block_size)
            group >= 1 && group <= 16 && block_size >= 8;
 }
 
-// Splits per workgroup with fixed-size splits: enough that the grid is about
-// one workgroup per SIMD (four per compute unit of the current device), at
-// most kMfmaMaxRun, and at most an eighth of the split count, so a run
-// never holds a large share of a sequence (with short ragged sequences,
-// runs measured slower: the MHA batch, 4 splits at most, went 79 -> 83 us
-// with runs of 4). Per-sequence split counts were already sized for the
-// device by the split heuristic; their splits run one per workgroup (runs
-// of them measured slower on a skewed batch: fewer workgroups for the
-// long sequences).
-static int pick_split_run(int64_t units, int parts)
+// Compute units of the current device (cached per device).
+static int device_cus()
 {
     static int cus[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
     if (!cus[dev]) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
             n = 256;
         cus[dev] = n;
     }
-    int64_t run = units / (4 * (int64_t)cus[dev]);
+    return cus[dev];
+}
+
+// Splits per workgroup with fixed-size splits: enough that the grid is about
+// one workgroup per SIMD (four per compute unit of the current device), at
+// most kMfmaMaxRun, and at most an eighth of the split count, so a run
+// never holds a large share of a sequence (with short ragged sequences,
+// runs measured slower: the MHA batch, 4 splits at most, went 79 -> 83 us
+// with runs of 4).
+static int pick_split_run(int64_t units, int parts)
+{
+    int64_t run = units / (4 * (int64_t)device_cus());
     run = run < parts / 8 ? run : parts / 8;
     return (int)(run < 1 ? 1 : run > kMfmaMaxRun ? kMfmaMaxRun : run);
+}
+
+// Per-sequence split counts run on persistent workers: this many per
+// compute unit (two per SIMD), each taking runs of up to PA_MFMA_WORKER_RUN
+// splits (three keep eight workers' parked splits within the LDS of a
+// compute unit). A worker scans the batch's lengths once, so very large
+// batches keep the one-workgroup-per-split grid. Measured on the skewed
+// batch (phase 1): one workgroup per split 370 us; workers 4/CU with runs
+// of 4 at one wave per SIMD 329 us, at two 339 us (register-limited);
+// 8/CU with runs of 3, 2, 1: 329, 333, 337 us; 16/CU with runs of 2: 342 us.
+#ifndef PA_MFMA_WORKERS_PER_CU
+#define PA_MFMA_WORKERS_PER_CU 8
+#endif
+#ifndef PA_MFMA_WORKER_RUN
+#define PA_MFMA_WORKER_RUN 3
+#endif
+constexpr int kMfmaPersistMaxSeqs = 2048;
+
+template <class E, class KE, int D, bool PERSIST>
+static void launch_mfma_bs(const DecodeParams& p, dim3 grid, size_t lds, hipStream_t st)
+{
+    switch (p.bs_shift) {
+    case 4: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 16, PERSIST>), grid, dim3(kWave), lds, st, p); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 32, PERSIST>), grid, dim3(kWave), lds, st, p); break;
+    default: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 0, PERSIST>), grid, dim3(kWave), lds, st, p); break;
+    }
 }
 
 template <class E, class KE, int D>
 static hipError_t launch_mfma_t(DecodeParams p, int num_seqs, int parts, hipStream_t st)
 {
     p.grid_parts = parts;
-    p.split_run = p.num_splits ? 1 : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts, parts);
-    if (p.split_run < 1 || p.split_run > kMfmaMaxRun) return hipErrorInvalidValue;
-    dim3 grid(num_seqs * p.num_kv_heads, (parts + p.split_run - 1) / p.split_run), block(kWave);
-    const size_t lds = (size_t)(p.split_run - 1) * ((D / 16) * kWave * sizeof(f32x4) + 32 * sizeof(float));
-    switch (p.bs_shift) {
-    case 4: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 16>), grid, block, lds, st, p); break;
-    case 5: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 32>), grid, block, lds, st, p); break;
-    default: hipLaunchKernelGGL((k_decode_mfma<E, KE, D, D, 0>), grid, block, lds, st, p); break;
+    const bool persist = p.num_splits && num_seqs <= kMfmaPersistMaxSeqs;
+    dim3 grid;
+    if (persist) {
+        p.split_run = PA_MFMA_WORKER_RUN;
+        const int64_t want = (int64_t)PA_MFMA_WORKERS_PER_CU * device_cus();
+        const int64_t nu = (want + p.num_kv_heads - 1) / p.num_kv_heads;  // workers per kv head
+        grid = dim3((unsigned)(nu * p.num_kv_heads));
+    } else {
+        p.split_run = p.num_splits ? 1 : pick_split_run((int64_t)num_seqs * p.num_kv_heads * parts, parts);
+        grid = dim3(num_seqs * p.num_kv_heads, (parts + p.split_run - 1) / p.split_run);
     }
+    if (p.split_run < 1 || p.split_run > kMfmaMaxRun) return hipErrorInvalidValue;
+    const size_t lds = (size_t)(p.split_run - 1) * ((D / 16) * kWave * sizeof(f32x4) + 32 * sizeof(float));
+    if (persist) launch_mfma_bs<E, KE, D, true>(p, grid, lds, st);
+    else launch_mfma_bs<E, KE, D, false>(p, grid, lds, st);
     return hipGetLastError();
 }
 

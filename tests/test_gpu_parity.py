@@ -16,7 +16,7 @@ import torch
 import paged_attention_decode_tables_amd as pad
 from paged_attention_decode_tables_amd import workloads
 from gpu_util import (DEV, check_output, check_partials, max_parts_for, np64, oracle_args,
-                      run_gpu, say, subset)
+                      run_gpu, say, split_lengths, subset)
 import pins
 
 pytestmark = pytest.mark.gpu
@@ -516,3 +516,69 @@ def test_split_runs(orc, nseq, kv):
     check_partials(w, orc, tmp, ml, es, seqs=seqs)
     check_output(w, orc, out, seqs=seqs)
     assert torch.isfinite(out).all()
+
+
+# ---------------------------------------------------------------------------
+# persistent workers (grouped-head matrix-core kernel with per-sequence split
+# counts): each worker takes the splits whose first token falls in its equal
+# share of the batch's tokens. Batches longer than one 256-sequence scan
+# step, more workers than tokens, lengths 0 and 1, counts clamped into
+# [1, max_num_parts], fp8 caches with ALiBi, and above 2048 sequences the
+# one-workgroup-per-split grid.
+# ---------------------------------------------------------------------------
+def _ragged_lens(seed, n, hi):
+    r = np.random.default_rng(seed)
+    lens = r.integers(2, hi, n)
+    lens[::17] = 0
+    lens[5::23] = 1
+    return lens.tolist()
+
+
+PERSIST_CASES = [
+    # name, workload kwargs, split counts, max_num_parts
+    ("s300_heuristic_bs32", dict(seed=401, seq_lens=_ragged_lens(401, 300, 3000), num_heads=32,
+                                 num_kv_heads=8, head_size=128, block_size=32, dtype="bf16"),
+     "heuristic", 32),
+    ("s70_counts_clamped_g8_f16", dict(seed=402, seq_lens=_ragged_lens(402, 70, 5000), num_heads=16,
+                                       num_kv_heads=2, head_size=128, block_size=16, dtype="f16"),
+     "random", 16),
+    ("s5_fewer_tokens_than_workers", dict(seed=403, seq_lens=[1, 3, 0, 64, 65], num_heads=8,
+                                          num_kv_heads=8, head_size=64, block_size=8, dtype="bf16"),
+     "heuristic", 8),
+    ("s40_fp8_alibi", dict(seed=404, seq_lens=_ragged_lens(404, 40, 9000), num_heads=32,
+                           num_kv_heads=4, head_size=128, block_size=16, dtype="bf16",
+                           kv_cache="fp8", k_scale=0.05, v_scale=0.05, alibi=True),
+     "heuristic", 32),
+    ("s2100_grid", dict(seed=405, seq_lens=_ragged_lens(405, 2100, 200), num_heads=8,
+                        num_kv_heads=2, head_size=64, block_size=16, dtype="bf16"),
+     "heuristic", 8),
+]
+
+
+@pytest.mark.parametrize("case", PERSIST_CASES, ids=[c[0] for c in PERSIST_CASES])
+def test_persistent_workers(orc, case):
+    name, wkw, counts, mp = case
+    say(f"persistent workers {name}")
+    w = workloads.custom(name=name, poison=True, **wkw)
+    if counts == "heuristic":
+        t = torch.empty(w.num_seqs, dtype=torch.int32, device=DEV)
+        pad.num_kv_splits(t, w.seq_lens.to(DEV), 1, w.num_heads, w.num_kv_heads, mp, 256)
+        ns = t.cpu().numpy()
+    else:
+        ns = np.random.default_rng(7).integers(-2, 3 * mp, w.num_seqs).astype(np.int32)
+    out, tmp, ml, es = run_gpu(w, num_splits=ns, max_parts=mp)
+    # every sequence: live splits finite, empty ones -inf / 0 with tmp untouched
+    lens = split_lengths(w, 512, ns, mp)
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        n = 0 if L <= 0 else -(-L // lens[s])
+        assert (ml[s, :, n:] == -math.inf).all() and (es[s, :, n:] == 0).all(), (s, n)
+        assert torch.isnan(tmp[s, :, n:]).all(), (s, n)
+        assert torch.isfinite(ml[s, :, :n]).all() and torch.isfinite(tmp[s, :, :n]).all(), (s, n)
+        assert torch.isfinite(out[s]).all(), s
+    L = w.seq_lens.numpy()
+    order = np.argsort(L, kind="stable")
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(L) // 2]),
+                   int(np.flatnonzero(L == L[L > 0].min())[0]), 1, w.num_seqs - 1})
+    check_partials(w, orc, tmp, ml, es, num_splits=ns, seqs=seqs)
+    check_output(w, orc, out, seqs=seqs)
