@@ -463,20 +463,53 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     }
 }
 
-// Live tokens of every sequence (lengths <= 0 count none), summed over the
-// batch by one wave.
-__device__ __forceinline__ int64_t batch_tokens(const int32_t* seq_lens, int S)
+// Work units of a split for the persistent workers' balance: its tokens
+// plus a fixed charge for what every split costs whatever its length
+// (normalising and writing its row, a pipeline restart at run ends).
+// Skewed batch, phase 1 with a charge of 0 / 64 / 128 / 256 / 512 tokens:
+// bf16 caches 334 / 330 / 331 / 333 / 334 us, fp8 200 / 196 / 194 / 200 /
+// 195 us.
+#ifndef PA_MFMA_SPLIT_COST
+#define PA_MFMA_SPLIT_COST 128
+#endif
+
+// A sequence's splits: length, live count and work units (tokens plus the
+// per-split charge; lengths <= 0 have no split).
+struct SeqSplits {
+    int64_t len;
+    int nl;
+    int64_t cost;
+};
+__device__ __forceinline__ SeqSplits seq_splits(const DecodeParams& p, int L, int count)
 {
+    if (L <= 0) return SeqSplits{1, 0, 0};
+    const int n = count < 1 ? 1 : (count > p.max_num_parts ? p.max_num_parts : count);
+    const int64_t len = p.num_splits ? ((((int64_t)L + n - 1) / n + 63) & ~int64_t(63)) : (int64_t)p.partition_size;
+    const int nl = (int)(((int64_t)L + len - 1) / len);
+    return SeqSplits{len, nl, (int64_t)L + (int64_t)PA_MFMA_SPLIT_COST * nl};
+}
+
+// The split count of sequence s (1 without counts).
+__device__ __forceinline__ int seq_count(const DecodeParams& p, int s)
+{
+    return p.num_splits ? p.num_splits[(int64_t)s * p.num_group] : 1;
+}
+
+// Work units of the whole batch, summed by one wave.
+__device__ __forceinline__ int64_t batch_cost(const DecodeParams& p)
+{
+    const int S = p.num_seqs;
     int64_t t = 0;
     for (int b = 0; b < S; b += 4 * kWave) {
-        int v[4];
+        int v[4], c[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = b + j * kWave + (int)threadIdx.x;
-            v[j] = s < S ? seq_lens[s] : 0;
+            v[j] = s < S ? p.seq_lens[s] : 0;
+            c[j] = s < S ? seq_count(p, s) : 1;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t += v[j] > 0 ? v[j] : 0;
+        for (int j = 0; j < 4; ++j) t += seq_splits(p, v[j], c[j]).cost;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, kWave);
@@ -504,13 +537,14 @@ __device__ __forceinline__ int64_t wave_scan_i64(int64_t v)
     return v;
 }
 
-// Persistent workers for per-sequence split counts. The batch's live tokens,
-// in sequence order, are numbered 0..T-1. Worker u (of NU) of kv head kvh
-// takes every split whose first token falls in [u*T/NU, (u+1)*T/NU): each
-// worker gets the same share of tokens to within one split, no workgroup is
-// spent on an empty split, and a worker's consecutive splits of one sequence
-// run through one load pipeline (runs of up to split_run). The splits and
-// their partials are exactly those of the one-workgroup-per-split grid.
+// Persistent workers for per-sequence split counts. The batch's work units
+// (each split's tokens plus a fixed per-split charge), in sequence and
+// split order, are numbered 0..T-1. Worker u (of NU) of kv head kvh takes
+// every split whose first unit falls in [u*T/NU, (u+1)*T/NU): each worker
+// gets the same share of work to within one split, no workgroup is spent on
+// an empty split, and a worker's consecutive splits of one sequence run
+// through one load pipeline (runs of up to split_run). The splits and their
+// partials are exactly those of the one-workgroup-per-split grid.
 template <class E, class KE, int D, int DV, int BS>
 __device__ __forceinline__ void mfma_worker(const DecodeParams& p)
 {
@@ -518,7 +552,7 @@ __device__ __forceinline__ void mfma_worker(const DecodeParams& p)
     const int NU = (int)(gridDim.x / Hkv);
     const int kvh = (int)blockIdx.x % Hkv, u = (int)blockIdx.x / Hkv;
     const int lane = threadIdx.x;
-    const int64_t T = batch_tokens(p.seq_lens, S);
+    const int64_t T = batch_cost(p);
     // [X0, X1) = [floor(T*u/NU), floor(T*(u+1)/NU)) without overflow
     const int64_t tq = T / NU, tr = T % NU;
     const int64_t X0 = tq * u + tr * u / NU;
@@ -526,15 +560,16 @@ __device__ __forceinline__ void mfma_worker(const DecodeParams& p)
 
     // Walk the sequences 64 at a time (lane i holds sequence bj + i; the
     // lengths of four such blocks are loaded together): find the one holding
-    // token X0, then take splits until their starts reach X1.
-    int64_t before = 0;  // live tokens of the sequences before block bj
+    // unit X0, then take splits until their starts reach X1. Split sp of a
+    // sequence whose units start at Cs starts at Cs + sp * (len + charge).
+    int64_t before = 0;  // work units of the sequences before block bj
     for (int b = 0; b < S && before < X1; b += 4 * kWave) {
         int Lq[4], nq[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int sl = b + j * kWave + lane;
             Lq[j] = sl < S ? p.seq_lens[sl] : 0;
-            nq[j] = (sl < S && p.num_splits) ? p.num_splits[(int64_t)sl * ng] : 1;
+            nq[j] = sl < S ? seq_count(p, sl) : 1;
         }
 #pragma unroll 1
         for (int j = 0; j < 4; ++j) {
@@ -542,25 +577,27 @@ __device__ __forceinline__ void mfma_worker(const DecodeParams& p)
             if (bj >= S || before >= X1) break;
             const int Lr = j == 0 ? Lq[0] : j == 1 ? Lq[1] : j == 2 ? Lq[2] : Lq[3];
             const int nr = j == 0 ? nq[0] : j == 1 ? nq[1] : j == 2 ? nq[2] : nq[3];
-            const int64_t incl = wave_scan_i64(Lr > 0 ? Lr : 0);
+            const int64_t incl = wave_scan_i64(seq_splits(p, Lr, nr).cost);
             const int64_t blk_end = before + lane_value(incl, kWave - 1);
             if (blk_end > X0) {
                 // sequences of this block that end past X0 and start before X1
+                // (their splits are recomputed as scalars: fewer registers
+                // live across the runs)
                 for (int i = 0; i < kWave && bj + i < S; ++i) {
                     const int Ls = lane_value(Lr, i);
-                    const int64_t Cs = before + lane_value(incl, i) - (Ls > 0 ? Ls : 0);
+                    const SeqSplits sq = seq_splits(p, Ls, lane_value(nr, i));
+                    const int64_t cost = sq.cost;
+                    const int64_t Cs = before + lane_value(incl, i) - cost;
                     if (Cs >= X1) break;
-                    if (Ls <= 0 || Cs + Ls <= X0) continue;
-                    int n = lane_value(nr, i);
-                    n = n < 1 ? 1 : (n > p.max_num_parts ? p.max_num_parts : n);
-                    const int64_t len = p.num_splits ? ((((int64_t)Ls + n - 1) / n + 63) & ~int64_t(63))
-                                                     : (int64_t)p.partition_size;
-                    const int nl = (int)(((int64_t)Ls + len - 1) / len);
-                    int sp = Cs < X0 ? (int)((X0 - Cs + len - 1) / len) : 0;
+                    if (cost == 0 || Cs + cost <= X0) continue;
+                    const int64_t len = sq.len;
+                    const int nl = sq.nl;
+                    const int64_t unit = len + PA_MFMA_SPLIT_COST;  // units from one split start to the next
+                    int sp = Cs < X0 ? (int)((X0 - Cs + unit - 1) / unit) : 0;
                     while (sp < nl) {
-                        const int64_t st = Cs + sp * len;
+                        const int64_t st = Cs + sp * unit;
                         if (st >= X1) break;
-                        int nrun = (int)min((int64_t)(nl - sp), (X1 - st + len - 1) / len);
+                        int nrun = (int)min((int64_t)(nl - sp), (X1 - st + unit - 1) / unit);
                         nrun = min(nrun, p.split_run);
                         mfma_run<E, KE, D, DV, BS, true>(p, kvh, bj + i, sp, nrun, Ls, len);
                         sp += nrun;

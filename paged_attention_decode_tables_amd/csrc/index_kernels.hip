@@ -8,26 +8,45 @@ namespace pa {
 
 // ---------------------------------------------------------------------------
 // Flat page list (vLLM PR 35765, _copy_page_indices_kernel in its
-// stride-robust form): one workgroup per request copies its
+// stride-robust form): workgroups (request r, part y) copy request r's
 // cu[r+1] - cu[r] table entries to page_indices[cu[r] ...], reading the row
-// with both strides. 1024 lanes per row keep a long row to a few passes.
+// with both strides. The copy is latency-bound: 8 x 256 lanes per row with
+// four loads in flight each cover 8192 entries per memory round trip (the
+// 64-request, ~4600-entry page list of the MLA batch: one round; one
+// 1024-lane workgroup per row took five, 5.3 us).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_page_indices(int32_t* __restrict__ out,
-                                                       const int32_t* __restrict__ bt, int64_t s0,
-                                                       int64_t s1,
-                                                       const int32_t* __restrict__ cu)
+__global__ __launch_bounds__(256) void k_page_indices(int32_t* __restrict__ out,
+                                                      const int32_t* __restrict__ bt, int64_t s0,
+                                                      int64_t s1,
+                                                      const int32_t* __restrict__ cu)
 {
+    // kPageCopyParts workgroups per request row, 4 entries per thread per
+    // round with all four loads in flight before the stores
     const int r = blockIdx.x;
     const int64_t start = cu[r];
     const int64_t n = (int64_t)cu[r + 1] - start;
     const int32_t* row = bt + (int64_t)r * s0;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) out[start + i] = row[i * s1];
+    const int64_t step = (int64_t)gridDim.y * blockDim.x;
+    for (int64_t i0 = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i0 < n; i0 += 4 * step) {
+        int32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t i = i0 + k * step;
+            v[k] = i < n ? row[i * s1] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t i = i0 + k * step;
+            if (i < n) out[start + i] = v[k];
+        }
+    }
 }
 
 hipError_t launch_page_indices(int32_t* out, const int32_t* bt, int64_t s0, int64_t s1,
                                const int32_t* cu, int num_reqs, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_page_indices, dim3(num_reqs), dim3(1024), 0, st, out, bt, s0, s1, cu);
+    constexpr int kPageCopyParts = 8;
+    hipLaunchKernelGGL(k_page_indices, dim3(num_reqs, kPageCopyParts), dim3(256), 0, st, out, bt, s0, s1, cu);
     return hipGetLastError();
 }
 

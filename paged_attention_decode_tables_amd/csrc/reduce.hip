@@ -37,12 +37,13 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
     const int L = p.seq_lens[s];
     // balanced splits (partition_size 0): every slot, empty ones skipped below
     const bool balanced = !p.num_splits && p.partition_size == 0;
+    // the split count is read alongside the length (not behind a test of it)
+    const int64_t len = balanced ? 1 : split_length(L, p.num_splits, row, p.partition_size, p.max_num_parts);
     int64_t n = 0;
     if (L > 0) {
         if (balanced) {
             n = p.max_num_parts;
         } else {
-            const int64_t len = split_length(L, p.num_splits, row, p.partition_size, p.max_num_parts);
             n = ((int64_t)L + len - 1) / len;
             n = n < p.max_num_parts ? n : p.max_num_parts;
         }

@@ -92,6 +92,20 @@ def test_page_indices_match_oracle(orc):
         assert np.array_equal(out.cpu().numpy(), want), contiguous
 
 
+def test_page_indices_long_rows(orc):
+    """Rows longer than one round of the copy (8192 entries per round)."""
+    say("page indices: long rows")
+    rng = np.random.default_rng(4)
+    n = np.array([20000, 8193, 8192, 1, 0, 16385], dtype=np.int64)
+    bt = rng.integers(0, 1 << 30, (len(n), 20001)).astype(np.int32)
+    cu = np.zeros(len(n) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(n)
+    want = orc.page_indices(bt, cu)
+    out = torch.full((int(cu[-1]),), -1, dtype=torch.int32, device=DEV)
+    pad.build_page_indices(out, torch.from_numpy(bt).to(DEV), torch.from_numpy(cu).to(DEV))
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
 def test_page_indices_mla_config(orc):
     say("page indices: MLA config")
     w = workloads.config(5)
