@@ -4,10 +4,13 @@
 //
 // One workgroup per (seq, head). The Dv-wide rows are read as float4
 // columns: C = Dv/4 threads cover a row and NG thread groups take every
-// NG-th split. NG is the smallest power of two that lets every group read
-// its splits in one round (at most 256 threads, at least one wave): with
-// few splits a workgroup stays small and the whole grid fits on the chip at
-// once. Each thread folds its splits into a local
+// NG-th split. With fixed partitions NG is the smallest power of two that
+// lets every group read its splits in one round (at most 256 threads, at
+// least one wave); with split counts or balanced splits, whose sequences
+// mostly have a few splits, NG is the least that fills a wave. Small
+// workgroups keep the whole grid resident at once (skewed batch 13.3 ->
+// 8.5 us, MLA batch 25.0 -> 17.2 us with the smaller load batch below).
+// Each thread folds its splits into a local
 // (max, sum, row) state, R splits at a time with all their loads in flight,
 // and the groups' states are merged once through LDS with the same rule
 // (M = max m_g, weights exp(m_g - M)), so the whole merge costs one memory
@@ -18,9 +21,14 @@
 namespace pa {
 
 constexpr int kRedMaxThreads = 256;
-constexpr int kRedBatch = 8;  // splits per thread per round of loads
+constexpr int kRedBatch = 8;  // splits per thread per round of loads (at most)
 
-template <class OutE, int DV, int NG>
+// RB: splits per thread per round of loads. Eight when fixed partitions give
+// every group that many (one round); four with split counts or balanced
+// splits, whose sequences mostly have a few splits: the smaller batch needs
+// fewer registers, so more waves are resident and fewer rounds of the
+// two dependent loads run one after another.
+template <class OutE, int DV, int NG, int RB>
 __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
 {
     constexpr int C = DV / 4;             // threads per row (float4 columns)
@@ -62,12 +70,12 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
     // of exp(m_p - M) l_p, and acc = sum of exp(m_p - M) l_p tmp_p
     float M = -INFINITY, W = 0.0f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t q0 = grp; q0 < n; q0 += (int64_t)NG * kRedBatch) {
-        f32x4 rows[kRedBatch];
-        float mv[kRedBatch], lv[kRedBatch];
+    for (int64_t q0 = grp; q0 < n; q0 += (int64_t)NG * RB) {
+        f32x4 rows[RB];
+        float mv[RB], lv[RB];
         if (!balanced) {  // every split below n is live: all loads at once
 #pragma unroll
-            for (int r = 0; r < kRedBatch; ++r) {
+            for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 if (q < n) {
                     rows[r] = *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp);
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
             }
         } else {  // most slots are empty: statistics first, rows of live slots only
 #pragma unroll
-            for (int r = 0; r < kRedBatch; ++r) {
+            for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 mv[r] = q < n ? ml[q] : -INFINITY;
                 lv[r] = q < n ? es[q] : 0.0f;
@@ -90,10 +98,10 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
             // meets an empty one, every later slot is empty too
             bool ended = false;
 #pragma unroll
-            for (int r = 0; r < kRedBatch; ++r) ended |= mv[r] == -INFINITY;
+            for (int r = 0; r < RB; ++r) ended |= mv[r] == -INFINITY;
             if (ended) n = q0 + 1;  // this batch is the group's last
 #pragma unroll
-            for (int r = 0; r < kRedBatch; ++r) {
+            for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 rows[r] = mv[r] != -INFINITY ? *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp)
                                              : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -101,13 +109,13 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
         }
         float mb = M;
 #pragma unroll
-        for (int r = 0; r < kRedBatch; ++r) mb = fmaxf(mb, mv[r]);
+        for (int r = 0; r < RB; ++r) mb = fmaxf(mb, mv[r]);
         // mb = -inf: nothing live yet (acc, W are 0); avoids exp2(-inf + inf)
         const float f = mb == -INFINITY ? 1.0f : fast_exp2((M - mb) * kLog2e);
         acc *= f;
         W *= f;
 #pragma unroll
-        for (int r = 0; r < kRedBatch; ++r) {
+        for (int r = 0; r < RB; ++r) {
             // an empty split (m = -inf) adds nothing; its row was never
             // written, so it is dropped by a select, not a multiply
             const bool live = mv[r] != -INFINITY;
@@ -159,14 +167,19 @@ template <class OutE, int DV, int NG>
 static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
 {
     const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * p.num_heads)), block(DV / 4 * NG);
-    hipLaunchKernelGGL((k_reduce<OutE, DV, NG>), grid, block, 0, st, p);
+    const bool few = p.num_splits || p.partition_size == 0 || (p.max_num_parts + NG - 1) / NG <= 4;
+    if (few) hipLaunchKernelGGL((k_reduce<OutE, DV, NG, 4>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((k_reduce<OutE, DV, NG, kRedBatch>), grid, block, 0, st, p);
 }
 
 template <class OutE, int DV>
 static void launch_reduce_dv(const ReduceParams& p, hipStream_t st)
 {
     constexpr int C = DV / 4, LO = C >= 64 ? 1 : 64 / C, HI = kRedMaxThreads / C;
-    const int ng = reduce_groups(DV, p.max_num_parts);
+    // split counts and balanced splits: one wave's worth of groups (most
+    // sequences have a few splits; smaller workgroups keep every one resident)
+    const bool few = p.num_splits || p.partition_size == 0;
+    const int ng = few ? LO : reduce_groups(DV, p.max_num_parts);
     if (ng <= LO) launch_reduce_ng<OutE, DV, LO>(p, st);
     else if (ng <= 2 * LO || 2 * LO > HI) launch_reduce_ng<OutE, DV, (2 * LO <= HI ? 2 * LO : HI)>(p, st);
     else launch_reduce_ng<OutE, DV, HI>(p, st);
