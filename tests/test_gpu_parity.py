@@ -566,6 +566,13 @@ PERSIST_CASES = [
     ("s2100_grid", dict(seed=405, seq_lens=_ragged_lens(405, 2100, 200), num_heads=8,
                         num_kv_heads=2, head_size=64, block_size=16, dtype="bf16"),
      "heuristic", 8),
+    ("s24_one_kv_head_g16", dict(seed=406, seq_lens=_ragged_lens(406, 24, 6000), num_heads=16,
+                                 num_kv_heads=1, head_size=128, block_size=32, dtype="bf16"),
+     "heuristic", 16),
+    ("s30_fp8_bs8_runtime_block", dict(seed=407, seq_lens=_ragged_lens(407, 30, 3000), num_heads=8,
+                                       num_kv_heads=2, head_size=128, block_size=8, dtype="f16",
+                                       kv_cache="fp8_codes", k_scale=0.02, v_scale=0.03),
+     "random", 12),
 ]
 
 
