@@ -438,6 +438,25 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     // The run's last split straight from registers, then the parked ones.
     float lt = l + __shfl_xor(l, 16, kWave);
     lt += __shfl_xor(lt, 32, kWave);
+    // Parked rows go out read across the lanes from LDS, so that consecutive
+    // lanes write consecutive 16-byte pieces of one row and every store
+    // instruction covers whole 128-byte lines (from registers a store covers
+    // 64 bytes of each of its rows).
+    if (parked > 0) {
+        wave_lds_sync();  // other lanes' parked rows
+        const int cols = G * p.num_group;  // live columns
+        constexpr int NCH = DV / 4;        // 16-byte pieces per row
+        for (int j = 0; j < parked; ++j) {
+            for (int e = lane; e < cols * NCH; e += kWave) {
+                const int c = e / NCH, k = e - c * NCH;  // column, piece (dv 4k .. 4k+3)
+                const f32x4 v = park[(j * MT + (k >> 2)) * kWave + 16 * (k & 3) + c];
+                const int cq = c / G, ch = c - cq * G;
+                float* o = p.tmp + (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
+                           (int64_t)(part0 + j) * p.tmp_sp + 4 * k;
+                store_partial(o, v);
+            }
+        }
+    }
     if (!head_ok) return;
     const int64_t tstride = p.tmp_sp;
     float* out = p.tmp + (int64_t)qrow * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part0 * tstride + 4 * g;
@@ -452,10 +471,6 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
         }
     }
     for (int j = 0; j < parked; ++j) {
-        float* o = out + (int64_t)j * tstride;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            store_partial(o + 16 * mt, park[(j * MT + mt) * kWave + lane]);
         if (g == 0) {
             p.max_logits[mlbase + j] = park_ml[32 * j + r];
             p.exp_sums[mlbase + j] = park_ml[32 * j + 16 + r];
