@@ -12,8 +12,8 @@
 // workgroup; with per-sequence split counts persistent workers, each taking
 // an equal share of the batch's tokens as runs of whole splits. The load
 // pipeline runs through a whole run, and at each split boundary the split's
-// softmax state is normalised, parked in LDS and reset (the last split's
-// goes straight out); the parked ones are written after the loop. Fewer,
+// softmax state is normalised, parked in LDS and reset; after the loop the
+// run's rows leave from LDS as whole 128-byte lines. Fewer,
 // longer runs cut the per-workgroup start-up and drain that dominated with
 // one workgroup per 512-token split. In the
 // wave, lane = 16*g + r (g = lane >> 4, r = lane & 15). Heads sit on the 16 MFMA columns (G <= 16,
@@ -369,8 +369,9 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     // Split boundaries inside the run: when a tile ends one (and the run goes
     // on), the split's state is normalised into LDS slot `parked` and reset.
     // LDS traffic counts apart from the vector-memory waits of the pipeline.
-    extern __shared__ f32x4 park[];  // [split_run - 1][MT][64] rows, then m, l
-    float* park_ml = reinterpret_cast<float*>(park + (p.split_run - 1) * MT * kWave);
+    // [max(1, split_run - 1)][MT][64] rows, then [split_run - 1][32] m, l
+    extern __shared__ f32x4 park[];
+    float* park_ml = reinterpret_cast<float*>(park + (p.split_run > 1 ? p.split_run - 1 : 1) * MT * kWave);
     int parked = 0;
     int64_t next_boundary = start64 + len64;
     auto flush = [&](float* m_out, float* l_out, f32x4* rows) {
@@ -435,43 +436,40 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
             use(A, c0);
         }
     }
-    // The run's last split straight from registers, then the parked ones.
+    // The run's rows leave from LDS, read across the lanes, so that
+    // consecutive lanes write consecutive 16-byte pieces of one row and every
+    // store instruction covers whole 128-byte lines (from registers a store
+    // covers 64 bytes of each of its 16 rows). The parked splits go first;
+    // the last split then takes slot 0.
     float lt = l + __shfl_xor(l, 16, kWave);
     lt += __shfl_xor(lt, 32, kWave);
-    // Parked rows go out read across the lanes from LDS, so that consecutive
-    // lanes write consecutive 16-byte pieces of one row and every store
-    // instruction covers whole 128-byte lines (from registers a store covers
-    // 64 bytes of each of its rows).
-    if (parked > 0) {
-        wave_lds_sync();  // other lanes' parked rows
-        const int cols = G * p.num_group;  // live columns
-        constexpr int NCH = DV / 4;        // 16-byte pieces per row
-        for (int j = 0; j < parked; ++j) {
-            for (int e = lane; e < cols * NCH; e += kWave) {
-                const int c = e / NCH, k = e - c * NCH;  // column, piece (dv 4k .. 4k+3)
-                const f32x4 v = park[(j * MT + (k >> 2)) * kWave + 16 * (k & 3) + c];
-                const int cq = c / G, ch = c - cq * G;
-                float* o = p.tmp + (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
-                           (int64_t)(part0 + j) * p.tmp_sp + 4 * k;
-                store_partial(o, v);
-            }
+    const int cols = G * p.num_group;  // live columns
+    constexpr int NCH = DV / 4;        // 16-byte pieces per row
+    auto rows_out = [&](int slot, int split) {
+        for (int e = lane; e < cols * NCH; e += kWave) {
+            const int c = e / NCH, k = e - c * NCH;  // column, piece (dv 4k .. 4k+3)
+            const f32x4 v = park[(slot * MT + (k >> 2)) * kWave + 16 * (k & 3) + c];
+            const int cq = c / G, ch = c - cq * G;
+            float* o = p.tmp + (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
+                       (int64_t)split * p.tmp_sp + 4 * k;
+            store_partial(o, v);
         }
-    }
-    if (!head_ok) return;
-    const int64_t tstride = p.tmp_sp;
-    float* out = p.tmp + (int64_t)qrow * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part0 * tstride + 4 * g;
+    };
+    wave_lds_sync();  // other lanes' parked rows
+    for (int j = 0; j < parked; ++j) rows_out(j, part0 + j);
+    wave_lds_sync();  // slot 0 read out before it is rewritten
     {
         const float inv = p.v_scale / lt;
-        float* o = out + (int64_t)parked * tstride;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) store_partial(o + 16 * mt, acc[mt] * inv);
-        if (g == 0) {
-            p.max_logits[mlbase + parked] = m * kLn2;
-            p.exp_sums[mlbase + parked] = lt;
-        }
+        for (int mt = 0; mt < MT; ++mt) park[mt * kWave + lane] = acc[mt] * inv;
     }
-    for (int j = 0; j < parked; ++j) {
-        if (g == 0) {
+    wave_lds_sync();
+    rows_out(0, part0 + parked);
+    if (!head_ok) return;
+    if (g == 0) {
+        p.max_logits[mlbase + parked] = m * kLn2;
+        p.exp_sums[mlbase + parked] = lt;
+        for (int j = 0; j < parked; ++j) {
             p.max_logits[mlbase + j] = park_ml[32 * j + r];
             p.exp_sums[mlbase + j] = park_ml[32 * j + 16 + r];
         }
@@ -757,7 +755,9 @@ static hipError_t launch_mfma_t(DecodeParams p, int num_seqs, int parts, hipStre
         grid = dim3(num_seqs * p.num_kv_heads, (parts + p.split_run - 1) / p.split_run);
     }
     if (p.split_run < 1 || p.split_run > kMfmaMaxRun) return hipErrorInvalidValue;
-    const size_t lds = (size_t)(p.split_run - 1) * ((D / 16) * kWave * sizeof(f32x4) + 32 * sizeof(float));
+    // row slots (at least one: a run's last split leaves through slot 0), then m, l
+    const size_t slots = p.split_run > 1 ? p.split_run - 1 : 1;
+    const size_t lds = slots * (D / 16) * kWave * sizeof(f32x4) + (size_t)(p.split_run - 1) * 32 * sizeof(float);
     if (persist) launch_mfma_bs<E, KE, D, true>(p, grid, lds, st);
     else launch_mfma_bs<E, KE, D, false>(p, grid, lds, st);
     return hipGetLastError();
