@@ -2,9 +2,9 @@
 // outputs (paged_attention_v2_triton.py, _paged_attn_v2_reduce_kernel:
 // global max, rescale by exp(m_p - M) * l_p, normalise, weighted sum).
 //
-// One workgroup per (seq, head). The Dv-wide rows are read as float4
-// columns: C = Dv/4 threads cover a row and NG thread groups take every
-// NG-th split. With fixed partitions NG is the smallest power of two that
+// C = Dv/4 threads cover a Dv-wide row as float4 columns and NG thread
+// groups take every NG-th split of one (query row, head); a workgroup holds
+// several heads of one query row (below). With fixed partitions NG is the smallest power of two that
 // lets every group read its splits in one round (at most 256 threads, at
 // least one wave); with split counts or balanced splits, whose sequences
 // mostly have a few splits, NG is the least that fills a wave. Small
@@ -30,17 +30,29 @@ constexpr int kRedBatch = 8;  // splits per thread per round of loads (at most)
 // splits, whose sequences mostly have a few splits: the smaller batch needs
 // fewer registers, so more waves are resident and fewer rounds of the
 // two dependent loads run one after another.
+// A workgroup takes HPW = 256 / (C * NG) heads of one query row (up to 256
+// threads), so the row's length and split count are loaded once for all of
+// them and small per-head thread counts do not turn into many tiny
+// workgroups (split counts: 8192 one-wave workgroups on the skewed batch).
+template <int DV, int NG> constexpr int red_heads() { return kRedMaxThreads / (DV / 4 * NG) > 0 ? kRedMaxThreads / (DV / 4 * NG) : 1; }
+
 template <class OutE, int DV, int NG, int RB>
-__global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
+__global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C * NG * HPW = 256
 {
     constexpr int C = DV / 4;             // threads per row (float4 columns)
-    __shared__ f32x4 acc_lds[NG][C];
-    __shared__ float m_lds[NG], w_lds[NG];
+    constexpr int HPW = red_heads<DV, NG>();
+    __shared__ f32x4 acc_lds[HPW][NG][C];
+    __shared__ float m_lds[HPW][NG], w_lds[HPW][NG];
 
-    const int tid = threadIdx.x;
+    const int hs = threadIdx.x / (C * NG), tid = threadIdx.x % (C * NG);
     const int col = tid % C, grp = tid / C;
-    // row = s * num_group + j: query token j of sequence s
-    const int row = blockIdx.x / p.num_heads, h = blockIdx.x % p.num_heads;
+    // row = s * num_group + j: query token j of sequence s; heads
+    // HPW*hb .. HPW*hb + HPW - 1 (past the last head: a repeat of it, not
+    // stored)
+    const int hblocks = (p.num_heads + HPW - 1) / HPW;
+    const int row = blockIdx.x / hblocks, hraw = (blockIdx.x % hblocks) * HPW + hs;
+    const bool head_ok = hraw < p.num_heads;
+    const int h = head_ok ? hraw : p.num_heads - 1;
     const int s = row / p.num_group;
     const int64_t obase = (int64_t)row * p.out_ss + (int64_t)h * p.out_sh + 4 * col;
 
@@ -113,8 +125,8 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
             n = n < p.max_num_parts ? n : p.max_num_parts;
         }
     }
-    if (n == 0) {
-        if (grp == 0)
+    if (n == 0) {  // the same for the whole workgroup (one row)
+        if (grp == 0 && head_ok)
 #pragma unroll
             for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, 0.0f);
         return;
@@ -168,23 +180,23 @@ __global__ __launch_bounds__(DV / 4 * NG) void k_reduce(ReduceParams p)
         fold();
     }
 
-    acc_lds[grp][col] = acc;
+    acc_lds[hs][grp][col] = acc;
     if (col == 0) {
-        m_lds[grp] = M;
-        w_lds[grp] = W;
+        m_lds[hs][grp] = M;
+        w_lds[hs][grp] = W;
     }
     __syncthreads();
-    if (grp != 0) return;
-    float Mt = m_lds[0];
+    if (grp != 0 || !head_ok) return;
+    float Mt = m_lds[hs][0];
 #pragma unroll
-    for (int g = 1; g < NG; ++g) Mt = fmaxf(Mt, m_lds[g]);
+    for (int g = 1; g < NG; ++g) Mt = fmaxf(Mt, m_lds[hs][g]);
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     float Wt = 0.0f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        const float f = m_lds[g] == -INFINITY ? 0.0f : fast_exp2((m_lds[g] - Mt) * kLog2e);
-        a += f * acc_lds[g][col];
-        Wt += f * w_lds[g];
+        const float f = m_lds[hs][g] == -INFINITY ? 0.0f : fast_exp2((m_lds[hs][g] - Mt) * kLog2e);
+        a += f * acc_lds[hs][g][col];
+        Wt += f * w_lds[hs][g];
     }
     const float inv = Wt > 0.0f ? 1.0f / Wt : 0.0f;  // no live split: zero row
 #pragma unroll
@@ -208,7 +220,9 @@ static int reduce_groups(int Dv, int max_parts)
 template <class OutE, int DV, int NG>
 static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
 {
-    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * p.num_heads)), block(DV / 4 * NG);
+    constexpr int HPW = red_heads<DV, NG>();
+    const int64_t hblocks = (p.num_heads + HPW - 1) / HPW;
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * hblocks)), block(DV / 4 * NG * HPW);
     const bool few = p.num_splits || p.partition_size == 0 || (p.max_num_parts + NG - 1) / NG <= 4;
     if (few) hipLaunchKernelGGL((k_reduce<OutE, DV, NG, 4>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_reduce<OutE, DV, NG, kRedBatch>), grid, block, 0, st, p);
