@@ -240,6 +240,8 @@ int build_page_indices(int32_t* page_indices, const int32_t* block_table, int64_
  * min(cdiv(cores_ext, grid), max_kv_splits)); and
  *     out[s*num_group + g] = max(cdiv(L_s, chunk_1), cdiv(L_s, chunk_2)).
  * out holds num_seq * num_group int32 entries. num_seq == 0 is a no-op.
+ * PA_EINVAL for num_head < num_kv_head (a group size of 0) and for counts
+ * below 1.
  */
 int num_kv_splits(int32_t* out, const int32_t* seq_lens, int32_t num_seq, int32_t num_group,
                   int32_t num_head, int32_t num_kv_head, int32_t max_kv_splits,

@@ -337,6 +337,9 @@ PA_EXPORT int num_kv_splits(int32_t* out, const int32_t* seq_lens, int32_t num_s
     if (num_seq < 0 || num_group < 1 || num_head < 1 || num_kv_head < 1 || max_kv_splits < 1 ||
         device_core_count < 1)
         return fail(PA_EINVAL, "num_kv_splits: num_seq >= 0 and positive group/head/split/core counts required");
+    // the heuristic divides by min(16, num_head / num_kv_head)
+    if (num_head < num_kv_head)
+        return fail(PA_EINVAL, "num_kv_splits: num_head %d < num_kv_head %d", num_head, num_kv_head);
     if (num_seq == 0) return PA_OK;
     if (!out || !seq_lens) return fail(PA_EINVAL, "num_kv_splits: a required pointer is NULL");
     return launched(pa::launch_num_kv_splits(out, seq_lens, num_seq, num_group, num_head, num_kv_head,

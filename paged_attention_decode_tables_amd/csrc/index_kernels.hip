@@ -58,17 +58,36 @@ hipError_t launch_page_indices(int32_t* out, const int32_t* bt, int64_t s0, int6
 // fp32 multiply by the core count, truncation to int32.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// cdiv for 1 <= a, b < 2^31 (a + b - 1 < 2^32): 32-bit unsigned division
+__device__ __forceinline__ uint32_t cdiv_u32(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
-__global__ __launch_bounds__(1024) void k_num_kv_splits(int32_t* __restrict__ out,
-                                                        const int32_t* __restrict__ seq_lens,
-                                                        int num_seq, int num_group, int num_head,
-                                                        int num_kv_head, int max_kv_splits,
-                                                        int cores)
+// 256 threads; a thread keeps the lengths it loads (kSplitHold per thread,
+// all batches up to 1024 sequences) for the second pass instead of reading
+// them again.
+constexpr int kSplitThreads = 256, kSplitHold = 4;
+
+__global__ __launch_bounds__(kSplitThreads) void k_num_kv_splits(int32_t* __restrict__ out,
+                                                                 const int32_t* __restrict__ seq_lens,
+                                                                 int num_seq, int num_group, int num_head,
+                                                                 int num_kv_head, int max_kv_splits,
+                                                                 int cores)
 {
-    __shared__ int s_max[16], s_min[16];
+    __shared__ int s_max[kSplitThreads / kWave], s_min[kSplitThreads / kWave];
     const int tid = threadIdx.x;
+    int held[kSplitHold];  // lengths of sequences tid + kSplitThreads * j, clamped to >= 1
     int mx = 1, mn = INT_MAX;
-    for (int i = tid; i < num_seq; i += blockDim.x) {
+#pragma unroll
+    for (int j = 0; j < kSplitHold; ++j) {
+        const int i = tid + kSplitThreads * j;
+        int L = i < num_seq ? seq_lens[i] : 1;
+        L = L < 1 ? 1 : L;
+        held[j] = L;
+        if (i < num_seq) {
+            mx = L > mx ? L : mx;
+            mn = L < mn ? L : mn;
+        }
+    }
+    for (int i = tid + kSplitThreads * kSplitHold; i < num_seq; i += kSplitThreads) {
         int L = seq_lens[i];
         L = L < 1 ? 1 : L;
         mx = L > mx ? L : mx;
@@ -80,21 +99,22 @@ __global__ __launch_bounds__(1024) void k_num_kv_splits(int32_t* __restrict__ ou
         mx = a > mx ? a : mx;
         mn = b < mn ? b : mn;
     }
-    const int wave = tid / kWave, nwaves = blockDim.x / kWave;
+    const int wave = tid / kWave;
     if ((tid & (kWave - 1)) == 0) {
         s_max[wave] = mx;
         s_min[wave] = mn;
     }
     __syncthreads();
     int64_t max_len = s_max[0], min_len = s_min[0];
-    for (int w = 1; w < nwaves; ++w) {
+#pragma unroll
+    for (int w = 1; w < kSplitThreads / kWave; ++w) {
         max_len = s_max[w] > max_len ? s_max[w] : max_len;
         min_len = s_min[w] < min_len ? s_min[w] : min_len;
     }
     if (max_len * 8 < min_len * 10) min_len = max_len;
-    int64_t splits1 = cdiv(max_len, min_len);
+    int64_t splits1 = cdiv_u32((uint32_t)max_len, (uint32_t)min_len);
     splits1 = splits1 < max_kv_splits ? splits1 : max_kv_splits;
-    const int64_t chunk1 = cdiv(max_len, splits1);
+    const uint32_t chunk1 = cdiv_u32((uint32_t)max_len, (uint32_t)splits1);
 
     const float ext = (float)max_len / 64.0f;
     const float lg = (float)log2((double)ext);
@@ -111,14 +131,21 @@ __global__ __launch_bounds__(1024) void k_num_kv_splits(int32_t* __restrict__ ou
     }
     int64_t splits2 = cdiv(cores_ext, grid);
     splits2 = splits2 < max_kv_splits ? splits2 : max_kv_splits;
-    const int64_t chunk2 = cdiv(max_len, splits2);
+    const uint32_t chunk2 = cdiv_u32((uint32_t)max_len, (uint32_t)splits2);
 
-    for (int i = tid; i < num_seq; i += blockDim.x) {
-        int64_t L = seq_lens[i];
-        L = L < 1 ? 1 : L;
-        const int64_t a = cdiv(L, chunk1), b = cdiv(L, chunk2);
+    auto put = [&](int i, uint32_t L) {
+        const uint32_t a = cdiv_u32(L, chunk1), b = cdiv_u32(L, chunk2);
         const int32_t n = (int32_t)(a > b ? a : b);
         for (int g = 0; g < num_group; ++g) out[(int64_t)i * num_group + g] = n;
+    };
+#pragma unroll
+    for (int j = 0; j < kSplitHold; ++j) {
+        const int i = tid + kSplitThreads * j;
+        if (i < num_seq) put(i, (uint32_t)held[j]);
+    }
+    for (int i = tid + kSplitThreads * kSplitHold; i < num_seq; i += kSplitThreads) {
+        const int L = seq_lens[i];
+        put(i, (uint32_t)(L < 1 ? 1 : L));
     }
 }
 
@@ -126,7 +153,7 @@ hipError_t launch_num_kv_splits(int32_t* out, const int32_t* seq_lens, int num_s
                                 int num_head, int num_kv_head, int max_kv_splits, int cores,
                                 hipStream_t st)
 {
-    hipLaunchKernelGGL(k_num_kv_splits, dim3(1), dim3(1024), 0, st, out, seq_lens, num_seq,
+    hipLaunchKernelGGL(k_num_kv_splits, dim3(1), dim3(kSplitThreads), 0, st, out, seq_lens, num_seq,
                        num_group, num_head, num_kv_head, max_kv_splits, cores);
     return hipGetLastError();
 }

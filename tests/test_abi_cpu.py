@@ -255,6 +255,8 @@ def test_index_helpers_reject(lib):
     assert lib.num_kv_splits(FAKE, FAKE, 4, 0, 8, 1, 16, 256, None) == api.PA_EINVAL
     assert lib.num_kv_splits(FAKE, FAKE, 4, 1, 8, 1, 16, 0, None) == api.PA_EINVAL
     assert lib.num_kv_splits(None, None, 0, 1, 8, 1, 16, 256, None) == api.PA_OK
+    # fewer query heads than kv heads: the heuristic's group size would be 0
+    assert lib.num_kv_splits(FAKE, FAKE, 4, 1, 2, 4, 16, 256, None) == api.PA_EINVAL
     assert lib.paged_token_offsets(FAKE, 8, FAKE, 8, 1, None, FAKE, 2, 8, 3, 1, 1, None) == api.PA_EINVAL
     assert lib.paged_token_offsets(None, 8, FAKE, 8, 1, None, FAKE, 2, 8, 4, 1, 1, None) == api.PA_EINVAL
 
