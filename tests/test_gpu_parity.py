@@ -517,13 +517,14 @@ def test_decode_mla_balanced_config5(orc):
 RUN_LENS = [16384, 1, 513, 2047, 2048, 2049, 5000, 0, 100, 16000, 8191, 3, 700, 12345, 64, 15000]
 
 
-@pytest.mark.parametrize("nseq,kv", [(8, "same"), (12, "same"), (16, "same"), (16, "fp8")])
-def test_split_runs(orc, nseq, kv):
+@pytest.mark.parametrize("nseq,kv,d", [(8, "same", 128), (12, "same", 128), (16, "same", 128),
+                                       (16, "fp8", 128), (16, "same", 64)])
+def test_split_runs(orc, nseq, kv, d):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     units = nseq * 8 * 32
-    say(f"split runs: {nseq} seqs, kv {kv}, run {max(1, min(4, units // (4 * cus)))}")
-    w = workloads.custom(seed=200 + nseq, seq_lens=RUN_LENS[:nseq], num_heads=64, num_kv_heads=8,
-                         head_size=128, block_size=16, dtype="bf16", kv_cache=kv,
+    say(f"split runs: {nseq} seqs, kv {kv}, head size {d}, run {max(1, min(4, units // (4 * cus)))}")
+    w = workloads.custom(seed=(200 if d == 128 else 300) + nseq, seq_lens=RUN_LENS[:nseq], num_heads=64, num_kv_heads=8,
+                         head_size=d, block_size=16, dtype="bf16", kv_cache=kv,
                          k_scale=0.05, v_scale=0.05, poison=True)
     out, tmp, ml, es = run_gpu(w, max_parts=32)
     seqs = [0, 1, 2, 5, 7] + ([9, 13] if nseq > 13 else [])
@@ -569,6 +570,9 @@ PERSIST_CASES = [
     ("s24_one_kv_head_g16", dict(seed=406, seq_lens=_ragged_lens(406, 24, 6000), num_heads=16,
                                  num_kv_heads=1, head_size=128, block_size=32, dtype="bf16"),
      "heuristic", 16),
+    ("s20_d64_runs", dict(seed=408, seq_lens=_ragged_lens(408, 20, 9000), num_heads=16,
+                          num_kv_heads=4, head_size=64, block_size=16, dtype="bf16"),
+     "random", 24),
     ("s30_fp8_bs8_runtime_block", dict(seed=407, seq_lens=_ragged_lens(407, 30, 3000), num_heads=8,
                                        num_kv_heads=2, head_size=128, block_size=8, dtype="f16",
                                        kv_cache="fp8_codes", k_scale=0.02, v_scale=0.03),
