@@ -15,10 +15,11 @@
 //   staging  the chunk's 32 latent rows are copied HBM -> LDS by direct
 //            global-to-LDS loads (no registers hold data in flight) into a
 //            ring of kMlaBuf chunk slots, kMlaBuf-1 chunks ahead. 16-byte
-//            piece pc of row t sits at column pc ^ swz(t), swz(t) =
-//            (t & 6) | ((t >> 3) & 1), which puts the rows one operand read
-//            touches on distinct LDS banks (rows two apart share a bank
-//            offset, 1152 B = 32 mod 64 dwords). Page ids are staged in LDS.
+//            piece pc of row t sits at column pc ^ swz(t) (within groups of
+//            8 pieces), swz(t) = ((t2 ^ t1) << 2) | (t1 << 1) | t3, which
+//            puts the rows one operand read touches on distinct LDS banks
+//            (rows two apart share a bank offset, 1152 B = 32 mod 64
+//            dwords). Page ids are staged in LDS.
 //   QK       S^T[t][h] = sum_d K[t][d] Q[h][d] on v_mfma_f32_32x32x16: the 32
 //            tokens are the rows (A operand: 16 bytes of a latent row from
 //            LDS), the wave's 32 heads the columns (B operand: q in
@@ -154,8 +155,15 @@ __host__ __device__ constexpr int loader_waves(int ins, int nw)
     return best;
 }
 
-// LDS column offset of the pieces of ring row t (XORed into the piece index)
-__host__ __device__ constexpr int mla_swz(int t) { return (t & 6) | ((t >> 3) & 1); }
+// LDS column offset of the pieces of ring row t (XORed into the piece index
+// within each group of 8 pieces): bit 2 = t2 ^ t1, bit 1 = t1, bit 0 = t3.
+// Rows t and t + 2 share LDS banks (a row is 1152 B, 32 mod 64 dwords); bit
+// 2 puts their 64-byte value groups on different banks, so the transposed
+// P.V reads (rows t0 .. t0 + 3 in one instruction) are conflict-free. With
+// t2 alone there, they took two extra cycles each (measured). Over the 8
+// rows of one parity the offsets are a permutation, so the 16-row QK reads
+// stay conflict-free.
+__host__ __device__ constexpr int mla_swz(int t) { return ((((t >> 2) ^ (t >> 1)) & 1) << 2) | (t & 2) | ((t >> 3) & 1); }
 
 #ifndef PA_MLA_BUF
 #define PA_MLA_BUF 4
@@ -326,14 +334,19 @@ void k_decode_mla(DecodeParams p)
     // PV operand addresses: read (kk, rd) of value tile mt covers rows
     // t = 16kk + 8hl + 4rd + a/4 (a = lane & 15) and value columns
     // 32mt + 16*g16 + 4*(a&3) .. +3 (g16 = (lane >> 4) & 1): piece
-    // 4mt + 2*g16 + ((a&3) >> 1) at column 4*(mt ^ rd) + low, low =
-    // 2*(g16 ^ (a >> 3)) + (((a & 3) >> 1) ^ hl), 8 bytes in when a is odd.
-    // One lane base plus kk*16*RB + rd*4*RB + 64*(mt ^ rd) as the immediate.
-    uint32_t vb_lane;
+    // 4mt + 2*g16 + ((a&3) >> 1) at column 4*(mt ^ rd ^ t1) + low, with
+    // t1 = (a >> 3) & 1 (bit 1 of the row) and low = 2*(g16 ^ (a >> 3)) +
+    // (((a & 3) >> 1) ^ hl), 8 bytes in when a is odd. As the immediate
+    // kk*16*RB + rd*4*RB + 64*(mt ^ rd); the lane's t1 then moves the
+    // address by +64 when mt ^ rd is even and -64 when it is odd, so there
+    // are two lane bases (vb_lane for even, vb_lane_odd for odd).
+    uint32_t vb_lane, vb_lane_odd;
     {
-        const int a = lane & 15, g16 = (lane >> 4) & 1;
+        const int a = lane & 15, g16 = (lane >> 4) & 1, t1 = (a >> 3) & 1;
         const int low = 2 * (g16 ^ (a >> 3)) + (((a & 3) >> 1) ^ hl);
-        vb_lane = (8 * hl + (a >> 2)) * RB + 16 * low + 8 * (a & 1);
+        const uint32_t vb = (8 * hl + (a >> 2)) * RB + 16 * low + 8 * (a & 1);
+        vb_lane = vb + 64 * t1;
+        vb_lane_odd = vb - 64 * t1;  // t1 = 1 only for rows >= 2: no wrap
     }
 
     // scores of chunk c for this lane's 16 tokens (base 2, masked past the
@@ -376,8 +389,9 @@ void k_decode_mla(DecodeParams p)
 
     // probabilities of chunk c against mref, and their weighted value rows
     auto weigh = [&](int c, const float (&sc)[16]) {
-        const uint32_t vbase =
-            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]) + vb_lane;
+        const uint32_t slot =
+            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+        const uint32_t vbase = slot + vb_lane, vbase_odd = slot + vb_lane_odd;
         // MFMA j (0 .. 2*MT-1) is (kk = j / MT, mt = j % MT): all tiles of the
         // first 16 tokens, then of the second, so consecutive MFMAs update
         // different accumulators
@@ -387,8 +401,8 @@ void k_decode_mla(DecodeParams p)
         auto vread = [&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr int kk = j / MT, mt = j % MT;
-            vr[j][0] = lds_read_tr16<kk * 16 * RB + 64 * mt>(vbase);
-            vr[j][1] = lds_read_tr16<kk * 16 * RB + 4 * RB + 64 * (mt ^ 1)>(vbase);
+            vr[j][0] = lds_read_tr16<kk * 16 * RB + 64 * mt>((mt & 1) ? vbase_odd : vbase);
+            vr[j][1] = lds_read_tr16<kk * 16 * RB + 4 * RB + 64 * (mt ^ 1)>(((mt ^ 1) & 1) ? vbase_odd : vbase);
         };
         static_for<RA>(vread);
         __builtin_amdgcn_sched_barrier(0);
