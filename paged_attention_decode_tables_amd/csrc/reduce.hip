@@ -3,21 +3,21 @@
 // global max, rescale by exp(m_p - M) * l_p, normalise, weighted sum).
 //
 // C = Dv/4 threads cover a Dv-wide row as float4 columns and NG thread
-// groups take every NG-th split of one (query row, head); a workgroup holds
-// several heads of one query row (below). With fixed partitions NG is the smallest power of two that
-// lets every group read its splits in one round (at most 256 threads, at
-// least one wave); with split counts or balanced splits, whose sequences
-// mostly have a few splits, NG is the least that fills a wave. Small
-// workgroups keep the whole grid resident at once (skewed batch 13.3 ->
-// 8.5 us, MLA batch 25.0 -> 17.2 us with the smaller load batch below).
-// Each thread folds its splits into a local
-// (max, sum, row) state, R splits at a time with all their loads in flight,
-// and the groups' states are merged once through LDS with the same rule
-// (M = max m_g, weights exp(m_g - M)), so the whole merge costs one memory
-// round trip and one barrier. With fixed partitions the first batch is
-// requested together with the sequence's length (slots past the split count
-// are inside the workspaces; what they hold is dropped by a select, never
-// multiplied). Otherwise only splits below the count are read.
+// groups take every NG-th split of one (query row, head); a 256-thread
+// workgroup holds 256 / (C * NG) heads of one query row. With fixed
+// partitions NG is the smallest power of two that lets every group read its
+// splits in one round; with split counts or balanced splits, whose
+// sequences mostly have a few splits, NG is the least that fills a wave.
+// Each thread folds its splits into a local (max, sum, row) state, RB
+// splits at a time with all their loads in flight, and the groups' states
+// are merged once through LDS with the same rule (M = max m_g, weights
+// exp(m_g - M)): one memory round trip and one barrier. With fixed
+// partitions the first batch is requested together with the sequence's
+// length (slots past the split count are inside the workspaces; what they
+// hold is dropped by a select, never multiplied). Otherwise only splits
+// below the count are read. Skewed batch 13.3 -> 7.2 us and MLA batch
+// 25.0 -> 17.2 us against one workgroup per head, 8 splits per batch and
+// groups sized by max_num_parts.
 #include "kernels.h"
 
 namespace pa {
