@@ -146,6 +146,46 @@ def _page_strides(block_tables: torch.Tensor, kv_indptr):
     return block_tables.stride(0), block_tables.stride(1)
 
 
+def _need(t: Optional[torch.Tensor], name: str, dtype=None, ndim=None, shape=None,
+          contiguous: bool = False, optional: bool = False):
+    """Host-side checks the C ABI cannot make: element type, rank, shape and
+    (for arrays the library indexes without strides) contiguity."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_gpu(stream, **tensors):
+    """Every tensor must live on one GPU, the device of `stream` when it is a
+    torch stream (the library hands their addresses to kernels on it)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+    sdev = getattr(stream, "device", None)
+    if dev is not None and sdev is not None and torch.device(sdev) != dev:
+        raise ValueError(f"the tensors are on {dev}, the stream on {sdev}")
+
+
 def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
                       query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                       block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
@@ -169,6 +209,9 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     seq_lens and the page lists stay per sequence.
     """
     lib = load_library()
+    _need(query, "query", tuple(_DTYPE), ndim=3)
+    _need(key_cache, "key_cache", ndim=5)
+    _need(value_cache, "value_cache", ndim=4)
     fp8 = key_cache.dtype in _FP8_CACHE
     if value_cache.dtype != key_cache.dtype or (not fp8 and key_cache.dtype != query.dtype):
         raise TypeError("key_cache and value_cache must share the query's dtype, or both be fp8 codes")
@@ -176,12 +219,27 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
         if alibi_slopes.dtype != torch.float32 or alibi_slopes.shape != (query.shape[1],) \
                 or not alibi_slopes.is_contiguous():
             raise ValueError("alibi_slopes must be a contiguous fp32 tensor of shape [num_heads]")
+    _need(seq_lens, "seq_lens", torch.int32, ndim=1, contiguous=True)
     R, H, D = query.shape
     S = seq_lens.shape[0]
     if num_group < 1 or R != S * num_group:
         raise ValueError(f"query has {R} rows, expected num_seqs * num_group = {S} * {num_group}")
     NB, Hkv, Dx, bs, x = key_cache.shape
     Dv = value_cache.shape[2]
+    _need(tmp_output, "tmp_output", torch.float32, ndim=4)
+    P = tmp_output.shape[2]
+    _need(tmp_output, "tmp_output", shape=(R, H, P, Dv))
+    _need(exp_sums, "exp_sums", torch.float32, shape=(R, H, P))
+    _need(max_logits, "max_logits", torch.float32, shape=(R, H, P))
+    _need(block_tables, "block_tables", torch.int32, ndim=1 if kv_indptr is not None else None)
+    if kv_indptr is None and block_tables.dim() != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks] without kv_indptr")
+    _need(kv_indptr, "kv_indptr", torch.int32, shape=(S + 1,), contiguous=True, optional=True)
+    _need(num_splits, "num_splits", torch.int32, shape=(R,), contiguous=True, optional=True)
+    _same_gpu(stream, tmp_output=tmp_output, exp_sums=exp_sums, max_logits=max_logits,
+              query=query, key_cache=key_cache, value_cache=value_cache,
+              block_tables=block_tables, seq_lens=seq_lens, kv_indptr=kv_indptr,
+              num_splits=num_splits, alibi_slopes=alibi_slopes)
     a = DecodeArgs()
     a.tmp_output = _ptr(tmp_output)
     a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
@@ -205,7 +263,7 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     a.num_seqs, a.num_heads, a.num_kv_heads = S, H, Hkv
     a.head_size, a.v_head_size, a.block_size, a.x = D, Dv, bs, x
     a.partition_size = partition_size
-    a.max_num_parts = tmp_output.shape[2]
+    a.max_num_parts = P
     a.max_seq_len = int(max_seq_len)
     a.dtype = _dtype(query)
     a.kernel_hint = PA_KERNEL[kernel]
@@ -223,10 +281,18 @@ def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: 
                       num_group: int = 1, stream=None) -> None:
     """Phase 2: log-sum-exp merge of the splits into output [S * num_group, H, Dv]."""
     lib = load_library()
+    _need(tmp_output, "tmp_output", torch.float32, ndim=4)
+    _need(seq_lens, "seq_lens", torch.int32, ndim=1, contiguous=True)
     R, H, P, Dv = tmp_output.shape
     S = seq_lens.shape[0]
     if num_group < 1 or R != S * num_group:
         raise ValueError(f"tmp_output has {R} rows, expected num_seqs * num_group = {S} * {num_group}")
+    _need(output, "output", tuple(_DTYPE), shape=(R, H, Dv))
+    _need(exp_sums, "exp_sums", torch.float32, shape=(R, H, P))
+    _need(max_logits, "max_logits", torch.float32, shape=(R, H, P))
+    _need(num_splits, "num_splits", torch.int32, shape=(R,), contiguous=True, optional=True)
+    _same_gpu(stream, output=output, tmp_output=tmp_output, exp_sums=exp_sums,
+              max_logits=max_logits, seq_lens=seq_lens, num_splits=num_splits)
     a = ReduceArgs()
     a.output = _ptr(output)
     a.out_stride_s, a.out_stride_h, a.out_stride_d = output.stride()
@@ -251,6 +317,12 @@ def build_page_indices(page_indices: torch.Tensor, block_table: torch.Tensor,
                        cu_num_blocks: torch.Tensor, stream=None) -> None:
     """page_indices[cu[r] + i] = block_table[r, i] for i < cu[r+1] - cu[r]."""
     lib = load_library()
+    _need(page_indices, "page_indices", torch.int32, ndim=1, contiguous=True)
+    _need(block_table, "block_table", torch.int32, ndim=2)
+    _need(cu_num_blocks, "cu_num_blocks", torch.int32, ndim=1, contiguous=True)
+    if cu_num_blocks.shape[0] < 1:
+        raise ValueError("cu_num_blocks must hold num_reqs + 1 >= 1 entries")
+    _same_gpu(stream, page_indices=page_indices, block_table=block_table, cu_num_blocks=cu_num_blocks)
     num_reqs = cu_num_blocks.shape[0] - 1
     s0, s1 = block_table.stride()
     _check(lib.build_page_indices(_ptr(page_indices), _ptr(block_table), s0, s1,
@@ -280,6 +352,9 @@ def normal_decode_set_metadata(cache_seqlens: torch.Tensor, cu_seqlens_k: torch.
                         ("full_to_swa", full_to_swa, torch.int32)):
         if t is not None and t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+    _same_gpu(stream, cache_seqlens=cache_seqlens, cu_seqlens_k=cu_seqlens_k, page_table=page_table,
+              req_to_token=req_to_token, req_pool_indices=req_pool_indices, seq_lens=seq_lens,
+              swa_page_table=swa_page_table, full_to_swa=full_to_swa)
     B = seq_lens.shape[0]
     a = MetadataArgs()
     a.cache_seqlens, a.cache_seqlens_stride = _ptr(cache_seqlens), cache_seqlens.stride(0)
@@ -318,6 +393,8 @@ def prepare_swa_spec_page_table(page_table_dst: torch.Tensor, page_table_a: torc
         raise ValueError("seq_len_b must hold bs * speculative_num_draft_tokens entries")
     if not (seq_len_a.is_contiguous() and seq_len_b.is_contiguous()):
         raise ValueError("seq_len_a and seq_len_b must be contiguous")
+    _same_gpu(stream, page_table_dst=page_table_dst, page_table_a=page_table_a,
+              page_table_b=page_table_b, seq_len_a=seq_len_a, seq_len_b=seq_len_b)
     LA, LB = page_table_a.shape[1], page_table_b.shape[1]
     if tuple(page_table_dst.shape) != (bs * R, LA + LB):
         raise ValueError(f"page_table_dst must be [{bs * R}, {LA + LB}]")
@@ -332,6 +409,9 @@ def num_kv_splits(out: torch.Tensor, seq_lens: torch.Tensor, num_group: int, num
                   stream=None) -> None:
     """Per-(seq, group) split counts from the sglang heuristic, on the device."""
     lib = load_library()
+    _need(seq_lens, "seq_lens", torch.int32, ndim=1, contiguous=True)
+    _need(out, "out", torch.int32, shape=(seq_lens.shape[0] * num_group,), contiguous=True)
+    _same_gpu(stream, out=out, seq_lens=seq_lens)
     _check(lib.num_kv_splits(_ptr(out), _ptr(seq_lens), seq_lens.shape[0], num_group, num_head,
                              num_kv_head, max_kv_splits, device_core_count, _stream(stream)))
 
@@ -341,7 +421,14 @@ def paged_token_offsets(out: torch.Tensor, block_tables: torch.Tensor, seq_lens:
                         kv_indptr: Optional[torch.Tensor] = None, stream=None) -> None:
     """Test hook: out[s, t] = pages[t // bs] * block_stride + (t % bs) * slot_stride."""
     lib = load_library()
+    _need(out, "out", torch.int64, ndim=2)
+    if out.shape[1] > 1 and out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous (element stride 1)")
     S, max_len = out.shape
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(S,), contiguous=True)
+    _need(kv_indptr, "kv_indptr", torch.int32, shape=(S + 1,), contiguous=True, optional=True)
+    _same_gpu(stream, out=out, block_tables=block_tables, seq_lens=seq_lens, kv_indptr=kv_indptr)
     bs_s, bs_b = _page_strides(block_tables, kv_indptr)
     _check(lib.paged_token_offsets(_ptr(out), out.stride(0), _ptr(block_tables), bs_s, bs_b,
                                    _ptr(kv_indptr), _ptr(seq_lens), S, max_len, block_size,

@@ -39,6 +39,7 @@
 //            t0 + a/4, columns 4(a%4) .. +3 of its 16-column half).
 // Tokens past the split end are loaded from the last valid row (a real,
 // finite row) and masked: scores -inf, probabilities 0.
+#include <type_traits>
 #include <utility>
 
 #include "kernels.h"
@@ -311,8 +312,10 @@ void k_decode_mla(DecodeParams p)
     // time with mref = the split's true max (known after the first pass), so
     // every p <= 1. The true max is kept apart and (m, l) are brought to it
     // at the end, so the stored statistics are the exact max logit and sum
-    // of exp(z - max).
-    constexpr float kHeadroom = 64.0f;
+    // of exp(z - max). p is rounded to the cache type before the P.V product,
+    // so the headroom must keep 2^kHeadroom finite there: bf16 reaches 2^127,
+    // f16 only 65504 < 2^16 (2^16 would round to +inf).
+    constexpr float kHeadroom = std::is_same<E, F16>::value ? 15.0f : 64.0f;
     float mref = -INFINITY;  // reference max of head c32 (base 2)
     float mtrue = -INFINITY; // true running max of head c32 (base 2)
     float l = 0.0f;          // this lane's share of sum_t exp2(z_t - mref)

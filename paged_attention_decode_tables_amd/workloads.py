@@ -416,7 +416,7 @@ def _mla(gen, *, poison, num_group=1):
 
 
 def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512, max_blocks=None,
-               poison=False, num_group=1) -> Workload:
+               poison=False, num_group=1, dtype="bf16") -> Workload:
     """Smaller MLA-style workload (page size 1, V aliasing the first Dv values of K)."""
     gen = torch.Generator().manual_seed(seed)
     lens = torch.as_tensor(seq_lens, dtype=torch.int32).clone()
@@ -424,7 +424,7 @@ def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512,
     total = int(lens.clamp(min=0).sum())
     nb = total + (1 if poison else 0)
     perm = torch.randperm(nb, generator=gen)
-    dt = torch.bfloat16
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     q = _randn(gen, (S * num_group, num_heads, head_size), dt)
     latent = _randn(gen, (nb, head_size), dt)
     poison_block = int(perm[total]) if poison else None

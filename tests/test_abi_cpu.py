@@ -307,3 +307,90 @@ def test_binding_raises_on_error():
     with pytest.raises(api.PagedAttnError) as e:
         api._check(api.PA_EINVAL)
     assert e.value.code == api.PA_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# the Python binding checks what the C ABI cannot see (element types, shapes,
+# contiguity of arrays read without strides, the device) before any call
+# ---------------------------------------------------------------------------
+def _decode_tensors(S=3, H=8, Hkv=2, D=128, bs=16, P=2, NB=10, dtype=torch.bfloat16):
+    x = 16 // torch.tensor([], dtype=dtype).element_size()
+    return dict(
+        tmp_output=torch.zeros(S, H, P, D), exp_sums=torch.zeros(S, H, P),
+        max_logits=torch.zeros(S, H, P), query=torch.zeros(S, H, D, dtype=dtype),
+        key_cache=torch.zeros(NB, Hkv, D // x, bs, x, dtype=dtype),
+        value_cache=torch.zeros(NB, Hkv, D, bs, dtype=dtype),
+        block_tables=torch.zeros(S, 4, dtype=torch.int32),
+        seq_lens=torch.ones(S, dtype=torch.int32), scale=0.1, max_seq_len=64)
+
+
+def _bad_decode(**change):
+    t = _decode_tensors()
+    t.update(change)
+    return t
+
+
+@pytest.mark.parametrize("name,change,exc", [
+    ("seq_lens_int64", dict(seq_lens=torch.ones(3, dtype=torch.int64)), TypeError),
+    ("seq_lens_sliced", dict(seq_lens=torch.ones(6, dtype=torch.int32)[::2]), ValueError),
+    ("workspace_bf16", dict(tmp_output=torch.zeros(3, 8, 2, 128, dtype=torch.bfloat16)), TypeError),
+    ("workspace_short", dict(tmp_output=torch.zeros(3, 8, 2, 64)), ValueError),
+    ("exp_sums_shape", dict(exp_sums=torch.zeros(3, 8, 1)), ValueError),
+    ("max_logits_f16", dict(max_logits=torch.zeros(3, 8, 2, dtype=torch.float16)), TypeError),
+    ("block_tables_int64", dict(block_tables=torch.zeros(3, 4, dtype=torch.int64)), TypeError),
+    ("block_tables_1d", dict(block_tables=torch.zeros(12, dtype=torch.int32)), ValueError),
+    ("query_rank", dict(query=torch.zeros(3, 8 * 128, dtype=torch.bfloat16)), ValueError),
+    ("query_int", dict(query=torch.zeros(3, 8, 128, dtype=torch.int16)), TypeError),
+    ("host_tensors", {}, ValueError),  # every shape right, but nothing is on a GPU
+])
+def test_binding_rejects_decode(name, change, exc):
+    t = _bad_decode(**change)
+    with pytest.raises(exc):
+        api.paged_attn_decode(**t)
+
+
+def test_binding_rejects_decode_options():
+    with pytest.raises(TypeError):  # split counts as int64
+        api.paged_attn_decode(**_decode_tensors(), num_splits=torch.ones(3, dtype=torch.int64))
+    with pytest.raises(ValueError):  # one split count per query row
+        api.paged_attn_decode(**_decode_tensors(), num_splits=torch.ones(4, dtype=torch.int32))
+    t = _decode_tensors()
+    t["block_tables"] = torch.zeros(12, dtype=torch.int32)
+    with pytest.raises(ValueError):  # indptr of num_seqs + 1 entries
+        api.paged_attn_decode(**t, kv_indptr=torch.zeros(3, dtype=torch.int32))
+
+
+def test_binding_rejects_reduce():
+    t = _decode_tensors()
+    ok = dict(output=torch.zeros(3, 8, 128), tmp_output=t["tmp_output"], exp_sums=t["exp_sums"],
+              max_logits=t["max_logits"], seq_lens=t["seq_lens"])
+    for change, exc in ((dict(output=torch.zeros(3, 8, 64)), ValueError),
+                        (dict(output=torch.zeros(3, 8, 128, dtype=torch.int32)), TypeError),
+                        (dict(exp_sums=torch.zeros(3, 8, 2, dtype=torch.float64)), TypeError),
+                        (dict(seq_lens=torch.ones(3, dtype=torch.int64)), TypeError),
+                        (dict(tmp_output=torch.zeros(3, 8, 2, 128, dtype=torch.bfloat16)), TypeError),
+                        ({}, ValueError)):
+        with pytest.raises(exc):
+            api.paged_attn_reduce(**{**ok, **change})
+
+
+def test_binding_rejects_index_helpers():
+    bt = torch.zeros(4, 8, dtype=torch.int32)
+    cu = torch.zeros(5, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        api.build_page_indices(torch.zeros(32, dtype=torch.int64), bt, cu)
+    with pytest.raises(ValueError):
+        api.build_page_indices(torch.zeros(64, dtype=torch.int32)[::2], bt, cu)
+    with pytest.raises(TypeError):
+        api.build_page_indices(torch.zeros(32, dtype=torch.int32), bt, cu.long())
+    with pytest.raises(ValueError):
+        api.build_page_indices(torch.zeros(32, dtype=torch.int32), bt, cu)  # host tensors
+    lens = torch.ones(4, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        api.num_kv_splits(torch.zeros(4, dtype=torch.int32), lens.long(), 1, 8, 2, 16, 256)
+    with pytest.raises(ValueError):  # one count per (sequence, group)
+        api.num_kv_splits(torch.zeros(4, dtype=torch.int32), lens, 2, 8, 2, 16, 256)
+    with pytest.raises(TypeError):
+        api.paged_token_offsets(torch.zeros(4, 16, dtype=torch.int32), bt, lens, 8, 1, 1)
+    with pytest.raises(ValueError):
+        api.paged_token_offsets(torch.zeros(4, 16, dtype=torch.int64), bt, lens, 8, 1, 1)

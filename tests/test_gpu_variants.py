@@ -200,20 +200,21 @@ def test_fp8_scales_scale_linearly(orc):
 # sampled sequences
 # ---------------------------------------------------------------------------
 FULL_VARIANTS = [
-    # config, workload kwargs, sampled sequences
-    (3, dict(kv_cache="fp8"), [1, 6]),
-    (3, dict(alibi=True), [0, 7]),
-    (3, dict(num_group=2), [3]),
-    (2, dict(kv_cache="fp8"), [0, 9, 31]),
-    (2, dict(num_group=4), [5, 30]),
-    (4, dict(kv_cache="fp8"), "sample"),
+    # config, workload kwargs
+    (3, dict(kv_cache="fp8")),
+    (3, dict(alibi=True)),
+    (3, dict(num_group=2)),
+    (2, dict(kv_cache="fp8")),
+    (2, dict(num_group=4)),
+    (4, dict(kv_cache="fp8")),
 ]
 
 
-@pytest.mark.parametrize("cfg,kw,seqs", FULL_VARIANTS,
+@pytest.mark.parametrize("cfg,kw", FULL_VARIANTS,
                          ids=[f"config{c}_" + "_".join(f"{k}{v}" for k, v in kw.items())
-                              for c, kw, _ in FULL_VARIANTS])
-def test_full_variant_config(orc, cfg, kw, seqs):
+                              for c, kw in FULL_VARIANTS])
+def test_full_variant_config(orc, cfg, kw):
+    """Every query row's output and every split's statistics."""
     say(f"full variant config {cfg} {kw}")
     w = workloads.config(cfg, poison=True, **kw)
     ns, mp = None, None
@@ -223,24 +224,21 @@ def test_full_variant_config(orc, cfg, kw, seqs):
         pad.num_kv_splits(t, g.seq_lens, w.num_group, w.num_heads, w.num_kv_heads,
                           w.max_kv_splits, w.device_core_count)
         ns, mp = t.cpu().numpy(), w.max_kv_splits
-        order = np.argsort(w.seq_lens.numpy())
-        seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
     out, tmp, ml, es = run_gpu(w, num_splits=ns, max_parts=mp)
-    rows = [s * w.num_group + j for s in seqs for j in range(w.num_group)]
     we = w.expanded()
-    check_output(we, orc, out, seqs=rows)
-    check_partials(we, orc, tmp, ml, es, num_splits=ns, seqs=rows)
-    assert torch.isfinite(out).all()
+    err = check_output(we, orc, out)
+    check_partials(we, orc, tmp, ml, es, num_splits=ns)
+    say(f"full variant config {cfg} {kw}: all {we.num_seqs} rows, max abs err {err:.2e}")
 
 
 def test_full_config5_alibi_balanced(orc):
     """The MLA workload with ALiBi slopes as the benchmark runs it (balanced
-    splits, one token range per compute unit)."""
+    splits, one token range per compute unit): every sequence's output."""
     say("full config 5 alibi balanced")
     import test_gpu_parity as tp
     w = workloads.config(5, poison=True, alibi=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     max_parts = -(-w.max_seq_len // 512)
     out, tmp, ml, es = tp.run_balanced(w, cus, max_parts)
-    check_output(w.subset([0, 40]), orc, out[[0, 40]])
-    assert torch.isfinite(out).all()
+    err = check_output(w, orc, out)
+    say(f"full config 5 alibi balanced: max abs err {err:.2e}")
