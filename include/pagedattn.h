@@ -335,6 +335,33 @@ int prepare_swa_spec_page_table(int32_t* dst, int64_t dst_stride0, int64_t dst_s
                                 const int32_t* seq_len_a, const int32_t* seq_len_b, int32_t bs,
                                 int32_t len_a, int32_t len_b, int32_t draft_tokens, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * paged_attn_decode() followed by paged_attn_reduce() in one call, with the
+ * split partials (tmp_output, max_logits, exp_sums) in a scratch buffer the
+ * library holds in device memory, PA_STATIC_SCRATCH_BYTES per GPU, from the
+ * first load of its code on that GPU until the process ends. Nothing is
+ * allocated per call.
+ *
+ * args is as for paged_attn_decode() except that tmp_output, exp_sums and
+ * max_logits must be NULL (their strides are ignored); max_num_parts sizes
+ * the partials, which need num_seqs * max(num_group, 1) * num_heads *
+ * max_num_parts * (v_head_size + 2) * 4 bytes. More than
+ * PA_STATIC_SCRATCH_BYTES returns PA_EINVAL before any work is queued.
+ * output [num_seqs * max(num_group, 1), num_heads, v_head_size] of out_dtype
+ * (f32, f16 or bf16), row strides out_stride_s, out_stride_h, innermost
+ * stride 1, receives the merged result of paged_attn_reduce().
+ *
+ * Every call on one GPU shares that GPU's buffer and leaves its partials in
+ * it; nothing in it needs to start at zero (phase 1 writes every statistic
+ * phase 2 reads). Calls that overlap in time on one GPU (other streams,
+ * other host threads) race on the buffer: the caller must order them.
+ */
+#define PA_STATIC_SCRATCH_BYTES (256u << 20)
+int paged_attn_decode_static(const pa_decode_args* args, void* output, int64_t out_stride_s,
+                             int64_t out_stride_h, int32_t out_dtype, void* stream);
+
 /* Message describing the last non-OK return on the calling thread. */
 const char* pa_last_error(void);
 

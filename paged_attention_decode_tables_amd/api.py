@@ -106,6 +106,7 @@ def load_library() -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.paged_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
     lib.paged_attn_reduce.argtypes = [ctypes.POINTER(ReduceArgs), _vp]
+    lib.paged_attn_decode_static.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _i64, _i64, _i32, _vp]
     lib.build_page_indices.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp]
     lib.num_kv_splits.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.paged_token_offsets.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32,
@@ -186,29 +187,12 @@ def _same_gpu(stream, **tensors):
         raise ValueError(f"the tensors are on {dev}, the stream on {sdev}")
 
 
-def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
-                      query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                      block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
-                      max_seq_len: int, *, partition_size: int = 512,
-                      num_splits: Optional[torch.Tensor] = None,
-                      kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
-                      num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
-                      k_scale: float = 1.0, v_scale: float = 1.0, num_group: int = 1,
-                      stream=None) -> None:
-    """Phase 1: per-split max logits, exp sums and normalised outputs.
-
-    Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
-    fp32; query [S, H, D]; key_cache [NB, Hkv, D/x, bs, x]; value_cache
-    [NB, Hkv, Dv, bs]; block_tables [S, max_blocks] int32 (or the flat page
-    list when kv_indptr is given); seq_lens [S] int32. partition_size=0 with
-    num_workers > 0 asks for balanced splits (equal token ranges).
-    Caches of dtype uint8 or float8_e4m3fn hold FP8 E4M3 codes (x = 16),
-    dequantized with k_scale / v_scale; alibi_slopes is an fp32 [H] tensor.
-    num_group > 1: each sequence has num_group query tokens; query and the
-    workspaces have num_seqs * num_group rows (row s * num_group + j) while
-    seq_lens and the page lists stay per sequence.
-    """
-    lib = load_library()
+def _decode_args(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                 seq_lens, scale, max_seq_len, partition_size, num_splits, kv_indptr, kernel,
+                 num_workers, alibi_slopes, k_scale, v_scale, num_group, stream,
+                 max_num_parts=None) -> DecodeArgs:
+    """Checked DecodeArgs for paged_attn_decode (workspaces given) or
+    paged_attn_decode_static (workspaces None, max_num_parts given)."""
     _need(query, "query", tuple(_DTYPE), ndim=3)
     _need(key_cache, "key_cache", ndim=5)
     _need(value_cache, "value_cache", ndim=4)
@@ -226,11 +210,14 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
         raise ValueError(f"query has {R} rows, expected num_seqs * num_group = {S} * {num_group}")
     NB, Hkv, Dx, bs, x = key_cache.shape
     Dv = value_cache.shape[2]
-    _need(tmp_output, "tmp_output", torch.float32, ndim=4)
-    P = tmp_output.shape[2]
-    _need(tmp_output, "tmp_output", shape=(R, H, P, Dv))
-    _need(exp_sums, "exp_sums", torch.float32, shape=(R, H, P))
-    _need(max_logits, "max_logits", torch.float32, shape=(R, H, P))
+    if max_num_parts is None:
+        _need(tmp_output, "tmp_output", torch.float32, ndim=4)
+        P = tmp_output.shape[2]
+        _need(tmp_output, "tmp_output", shape=(R, H, P, Dv))
+        _need(exp_sums, "exp_sums", torch.float32, shape=(R, H, P))
+        _need(max_logits, "max_logits", torch.float32, shape=(R, H, P))
+    else:
+        P = int(max_num_parts)
     _need(block_tables, "block_tables", torch.int32, ndim=1 if kv_indptr is not None else None)
     if kv_indptr is None and block_tables.dim() != 2:
         raise ValueError("block_tables must be [num_seqs, max_blocks] without kv_indptr")
@@ -241,13 +228,14 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
               block_tables=block_tables, seq_lens=seq_lens, kv_indptr=kv_indptr,
               num_splits=num_splits, alibi_slopes=alibi_slopes)
     a = DecodeArgs()
-    a.tmp_output = _ptr(tmp_output)
-    a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
-    a.exp_sums = _ptr(exp_sums)
-    a.max_logits = _ptr(max_logits)
-    if exp_sums.stride() != max_logits.stride():
-        raise ValueError("exp_sums and max_logits must share strides")
-    a.ml_stride_s, a.ml_stride_h, a.ml_stride_p = exp_sums.stride()
+    if tmp_output is not None:
+        a.tmp_output = _ptr(tmp_output)
+        a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
+        a.exp_sums = _ptr(exp_sums)
+        a.max_logits = _ptr(max_logits)
+        if exp_sums.stride() != max_logits.stride():
+            raise ValueError("exp_sums and max_logits must share strides")
+        a.ml_stride_s, a.ml_stride_h, a.ml_stride_p = exp_sums.stride()
     a.query = _ptr(query)
     a.q_stride_s, a.q_stride_h, a.q_stride_d = query.stride()
     a.key_cache = _ptr(key_cache)
@@ -272,7 +260,63 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
     a.kv_dtype = PA_FP8_E4M3 if fp8 else 0
     a.k_scale, a.v_scale = float(k_scale), float(v_scale)
     a.num_group = num_group
+    return a
+
+
+def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
+                      query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                      max_seq_len: int, *, partition_size: int = 512,
+                      num_splits: Optional[torch.Tensor] = None,
+                      kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
+                      num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0, num_group: int = 1,
+                      stream=None) -> None:
+    """Phase 1: per-split max logits, exp sums and normalised outputs.
+
+    Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
+    fp32; query [S, H, D]; key_cache [NB, Hkv, D/x, bs, x]; value_cache
+    [NB, Hkv, Dv, bs]; block_tables [S, max_blocks] int32 (or the flat page
+    list when kv_indptr is given); seq_lens [S] int32. partition_size=0 with
+    num_workers > 0 asks for balanced splits (equal token ranges).
+    Caches of dtype uint8 or float8_e4m3fn hold FP8 E4M3 codes (x = 16),
+    dequantized with k_scale / v_scale; alibi_slopes is an fp32 [H] tensor.
+    num_group > 1: each sequence has num_group query tokens; query and the
+    workspaces have num_seqs * num_group rows (row s * num_group + j) while
+    seq_lens and the page lists stay per sequence.
+    """
+    lib = load_library()
+    a = _decode_args(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                     seq_lens, scale, max_seq_len, partition_size, num_splits, kv_indptr, kernel,
+                     num_workers, alibi_slopes, k_scale, v_scale, num_group, stream)
     _check(lib.paged_attn_decode(ctypes.byref(a), _stream(stream)))
+
+
+def paged_attn_decode_static(output: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, block_tables: torch.Tensor,
+                             seq_lens: torch.Tensor, scale: float, max_seq_len: int, *,
+                             max_num_parts: int, partition_size: int = 512,
+                             num_splits: Optional[torch.Tensor] = None,
+                             kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
+                             num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
+                             k_scale: float = 1.0, v_scale: float = 1.0, num_group: int = 1,
+                             stream=None) -> None:
+    """Phase 1 and phase 2 in one call with the split partials in the
+    library's own device buffer (PA_STATIC_SCRATCH_BYTES per GPU), for
+    callers that cannot allocate: output [S * num_group, H, Dv] receives the
+    merged result. Arguments as for paged_attn_decode; max_num_parts sizes
+    the partials. Overlapping calls on one GPU race on that buffer."""
+    lib = load_library()
+    a = _decode_args(None, None, None, query, key_cache, value_cache, block_tables, seq_lens, scale,
+                     max_seq_len, partition_size, num_splits, kv_indptr, kernel, num_workers,
+                     alibi_slopes, k_scale, v_scale, num_group, stream, max_num_parts=max_num_parts)
+    R, H, Dv = query.shape[0], query.shape[1], value_cache.shape[2]
+    _need(output, "output", tuple(_DTYPE), shape=(R, H, Dv))
+    if Dv > 1 and output.stride(2) != 1:
+        raise ValueError("output rows must be contiguous (element stride 1)")
+    _same_gpu(stream, output=output, query=query)
+    _check(lib.paged_attn_decode_static(ctypes.byref(a), _ptr(output), output.stride(0),
+                                        output.stride(1), _dtype(output), _stream(stream)))
 
 
 def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: torch.Tensor,

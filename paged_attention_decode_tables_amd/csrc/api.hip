@@ -58,6 +58,10 @@ constexpr int kMaxGridYZ = 65535;
 
 PA_EXPORT const char* pa_last_error(void) { return g_last_error.c_str(); }
 
+namespace pa {
+void set_last_error(const char* msg) { g_last_error = msg; }
+}  // namespace pa
+
 PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
 {
     if (!a) return fail(PA_EINVAL, "paged_attn_decode: args is NULL");

@@ -89,6 +89,9 @@ struct SpecTableParams {
     int bs, len_a, len_b, draft_tokens, col_blocks;
 };
 
+// Message returned by pa_last_error() on this thread.
+void set_last_error(const char* msg);
+
 // Which phase-1 kernel family serves a problem.
 enum class DecodeKernel { VALU, MFMA };
 

@@ -394,3 +394,23 @@ def test_binding_rejects_index_helpers():
         api.paged_token_offsets(torch.zeros(4, 16, dtype=torch.int32), bt, lens, 8, 1, 1)
     with pytest.raises(ValueError):
         api.paged_token_offsets(torch.zeros(4, 16, dtype=torch.int64), bt, lens, 8, 1, 1)
+
+
+def test_static_scratch_entry_rejects_on_the_host(lib):
+    """paged_attn_decode_static checks its arguments before any device call:
+    partials larger than the scratch buffer, caller workspaces given, and an
+    empty batch (a no-op)."""
+    lib.paged_attn_decode_static.argtypes = [ctypes.POINTER(api.DecodeArgs), ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_void_p]
+    a = good_decode()
+    a.tmp_output = a.exp_sums = a.max_logits = None
+    a.max_num_parts = 1 << 20  # 3 x 8 x 2^20 x 130 x 4 bytes
+    assert lib.paged_attn_decode_static(ctypes.byref(a), FAKE, 1024, 128, api.PA_F32, None) == api.PA_EINVAL
+    assert b"scratch buffer" in lib.pa_last_error()
+    a = good_decode()  # workspaces given
+    assert lib.paged_attn_decode_static(ctypes.byref(a), FAKE, 1024, 128, api.PA_F32, None) == api.PA_EINVAL
+    a.tmp_output = a.exp_sums = a.max_logits = None
+    a.num_seqs = 0
+    assert lib.paged_attn_decode_static(ctypes.byref(a), None, 0, 0, api.PA_F32, None) == api.PA_OK
+    assert lib.paged_attn_decode_static(None, None, 0, 0, api.PA_F32, None) == api.PA_EINVAL
