@@ -73,13 +73,17 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
  *
  * Balanced splits (partition_size == 0, num_splits == NULL, num_workers >= 1;
  * served by the MLA matrix-core kernel only, PA_ENOTSUP otherwise): the
- * tokens of all sequences, concatenated in sequence order (lengths <= 0
- * count as 0), total T, are cut into ranges of U tokens,
- *     U = round_up(max(cdiv(T, num_workers), cdiv(max_s L_s, max_num_parts - 1)), 32),
- * range w = [w*U, (w+1)*U). The k-th range that meets sequence s is its
- * split k, and slots k >= (number of such ranges) store m = -inf, l = 0. So
- * every worker gets the same number of tokens whatever the length mix, and
- * a sequence never has more than max_num_parts splits (max_num_parts >= 2).
+ * tokens of all sequences in sequence order, each sequence with L_s >= 1
+ * preceded by C = 256 virtual tokens (the cost of starting a split), total
+ * T' = sum over L_s >= 1 of (L_s + C), are cut into ranges of U positions,
+ *     U = round_up(max(cdiv(T', num_workers), cdiv(max_s L_s, max_num_parts - 1)), 32),
+ * range w = [w*U, (w+1)*U). Token t of sequence s sits at position
+ * V_s + C + t, V_s = sum over earlier sequences with L >= 1 of (L + C). The
+ * k-th range that meets sequence s's tokens is its split k, and slots k >=
+ * (number of such ranges) store m = -inf, l = 0. So every worker gets the
+ * same amount of work, counting the splits it starts, whatever the length
+ * mix, and a sequence never has more than max_num_parts splits
+ * (max_num_parts >= 2).
  * The live slots of a sequence are always a prefix (slots 0 .. k_max).
  * Phase 2 with partition_size == 0 merges the slots before the first one
  * whose max is -inf; the final output is the same as with any other split.

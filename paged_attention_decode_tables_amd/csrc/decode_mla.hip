@@ -7,36 +7,41 @@
 // split output); the value rows are the leading Dv columns of the key rows,
 // so every latent byte is read from HBM once per split.
 //
-// One workgroup per (seq, kv head, split) serves all G heads with NW = G/32
-// waves; wave w owns query heads 32w .. 32w+31 (lane = 32*hl + c32, head c32
-// of the wave). The 32x32 matrix-core tiles make every latent byte staged in
-// LDS feed 32 heads per read. The split is walked in 32-token chunks:
+// One workgroup per (seq, kv head, split), or per balanced token range,
+// serves all G heads with NW = G/32 waves, one per SIMD. The split is walked
+// in 32-token chunks:
 //
 //   staging  the chunk's 32 latent rows are copied HBM -> LDS by direct
-//            global-to-LDS loads (no registers hold data in flight) into a
-//            ring of kMlaBuf chunk slots, kMlaBuf-1 chunks ahead. 16-byte
-//            piece pc of row t sits at column pc ^ swz(t) (within groups of
-//            8 pieces), swz(t) = ((t2 ^ t1) << 2) | (t1 << 1) | t3, which
-//            puts the rows one operand read touches on distinct LDS banks
-//            (rows two apart share a bank offset, 1152 B = 32 mod 64
-//            dwords). Page ids are staged in LDS.
-//   QK       S^T[t][h] = sum_d K[t][d] Q[h][d] on v_mfma_f32_32x32x16: the 32
-//            tokens are the rows (A operand: 16 bytes of a latent row from
-//            LDS), the wave's 32 heads the columns (B operand: q in
-//            registers). A-row m reads token perm(m) = 16*(m>>4) +
-//            8*((m>>2)&1) + 4*((m>>3)&1) + (m&3); with the accumulator layout
-//            (lane 32*hl + c32, register r: row 8*(r>>2) + 4*hl + (r&3),
-//            column c32) lane (hl, c32) then holds head c32's scores of tokens
-//            16*(r>>3) + 8*hl + (r&7): tokens 8hl..8hl+7 and 16+8hl..16+8hl+7,
-//            i.e. the two P.V B operands of the chunk, with no data movement.
-//   softmax  running max per head over the lane's 16 scores and lane l^32;
-//            probabilities rounded to the cache type.
-//   PV       O^T[dv][h] = sum_t V[t][dv] P[t][h] on v_mfma_f32_32x32x16 per 32
-//            value columns and 16 tokens: A = V[t0..t0+7][dv] for the lane's
-//            column, two ds_read_b64_tr_b16 of the token-major rows (within
-//            a 16-lane group, lane i receives value (i mod 4) of the 8-byte
-//            pieces addressed by lanes i/4 + 4j, so lane a addresses row
-//            t0 + a/4, columns 4(a%4) .. +3 of its 16-column half).
+//            global-to-LDS loads (no registers hold data in flight, the
+//            nontemporal hint on) into a ring of kMlaBuf chunk slots,
+//            kMlaBuf-1 chunks ahead. A slot holds the rows' first 64 16-byte
+//            pieces as 1 KB rows and their last 8 pieces as 128-byte rows
+//            (see mla_fmain / mla_ftail for the bank swizzle), so each copy
+//            instruction is one row from one page: wave w copies rows
+//            TPW*w .. +TPW-1 with scalar base addresses. Page ids are read
+//            by scalar loads, one chunk ahead.
+//   QK       wave w, heads 32w .. 32w+31 (lane = 32*hl + c32, head c32):
+//            S^T[t][h] = sum_d K[t][d] Q[h][d] on v_mfma_f32_32x32x16, the 32
+//            tokens the rows (A operand: 16 bytes of a latent row from LDS),
+//            the wave's 32 heads the columns (B operand: q in registers).
+//            A-row m reads token perm(m) = 16*(m>>4) + 8*((m>>2)&1) +
+//            4*((m>>3)&1) + (m&3), so with the accumulator layout (lane
+//            32*hl + c32, register r: row 8*(r>>2) + 4*hl + (r&3), column
+//            c32) lane (hl, c32) holds head c32's scores of tokens
+//            16*(r>>3) + 8*hl + (r&7).
+//   softmax  per head against a fixed reference (the split's first-chunk
+//            max; see the kernel), probabilities rounded to the cache type
+//            and written to an LDS buffer of [G heads][32 tokens].
+//   PV       split by value columns: wave w owns column tiles NW*dt + w
+//            for all G heads, O^T[dv][h] += V^T[dv][t] P[t][h] on
+//            v_mfma_f32_32x32x16 per 32 columns, 32 heads and 16 tokens: A =
+//            8 tokens of one value column (two ds_read_b64_tr_b16 of the
+//            token-major rows: within a 16-lane group, lane i receives value
+//            (i mod 4) of the 8-byte pieces addressed by lanes i/4 + 4j, so
+//            lane a addresses row t0 + a/4, columns 4(a%4) .. +3 of its
+//            16-column half), B = 16 bytes of the probability buffer. Each
+//            wave reads a quarter of the chunk's value rows, and every
+//            operand feeds four MFMAs.
 // Tokens past the split end are loaded from the last valid row (a real,
 // finite row) and masked: scores -inf, probabilities 0.
 #include <type_traits>
@@ -73,12 +78,16 @@ __host__ __device__ constexpr int waitcnt_vm(int n)
 }
 
 // 16-byte direct HBM -> LDS copy: lane i's piece lands at lds_dst + 16 i.
-// The builtin only exists for the device pass (in the host pass it makes
-// clang drop the kernel's launch stub), hence the guard.
-__device__ __forceinline__ void lds_copy16(const void* src, u32x4* lds_dst)
+// The nontemporal hint (the latent rows are read once per step) raises the
+// copy stream's rate on the random 1152-byte rows (measured: 3.1 -> 3.6
+// TB/s for the copies alone). The builtin only exists for the device pass
+// (in the host pass it makes clang drop the kernel's launch stub), hence
+// the guard.
+__device__ __forceinline__ void lds_copy16(const void* src, __attribute__((address_space(3))) void* lds_dst)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+    constexpr int kNontemporal = 2;  // cache-policy bits: nt
+    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, kNontemporal);
 #else
     (void)src;
     (void)lds_dst;
@@ -147,24 +156,22 @@ __device__ __forceinline__ float half_sum(float x)
     return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
-// Largest divisor of `ins` that is at most `nw` (waves issuing the copies).
-__host__ __device__ constexpr int loader_waves(int ins, int nw)
-{
-    int best = 1;
-    for (int d = 1; d <= nw; ++d)
-        if (ins % d == 0) best = d;
-    return best;
-}
-
-// LDS column offset of the pieces of ring row t (XORed into the piece index
-// within each group of 8 pieces): bit 2 = t2 ^ t1, bit 1 = t1, bit 0 = t3.
-// Rows t and t + 2 share LDS banks (a row is 1152 B, 32 mod 64 dwords); bit
-// 2 puts their 64-byte value groups on different banks, so the transposed
-// P.V reads (rows t0 .. t0 + 3 in one instruction) are conflict-free. With
-// t2 alone there, they took two extra cycles each (measured). Over the 8
-// rows of one parity the offsets are a permutation, so the 16-row QK reads
-// stay conflict-free.
-__host__ __device__ constexpr int mla_swz(int t) { return ((((t >> 2) ^ (t >> 1)) & 1) << 2) | (t & 2) | ((t >> 3) & 1); }
+// Ring layout of one chunk (32 latent rows): the first 64 16-byte pieces of
+// every row (the 512 value columns, also the first 512 key columns) as a
+// 1 KB row, then the last 8 pieces (the remaining key columns) of all 32
+// rows as 128-byte rows. Piece pc of main row t sits at position pc ^
+// mla_fmain(t), piece q of tail row t at q ^ mla_ftail(t) (XOR within groups
+// of 16 and 8 pieces). LDS serves 256 B per clock, 16 lanes of a b128 access:
+//  - QK reads (16 lanes: rows 0..15 or 16..31 at one piece) land on 16
+//    distinct 16-byte bank groups since mla_fmain is a bijection on t & 15
+//    and (t & 1, mla_ftail) one on t & 15;
+//  - transposed P.V reads (32 lanes: rows 4u .. 4u+3, four consecutive
+//    pieces each) since bits 2-3 of the XOR are t & 3 and bits 0-1
+//    the same for the four rows.
+// A main row is one copy instruction (64 lanes x 16 B) from one page: its
+// page id is uniform, the lane's source piece is lane ^ mla_fmain(t).
+__host__ __device__ constexpr int mla_fmain(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__host__ __device__ constexpr int mla_ftail(int t) { return (t >> 1) & 7; }
 
 #ifndef PA_MLA_BUF
 #define PA_MLA_BUF 4
@@ -172,15 +179,14 @@ __host__ __device__ constexpr int mla_swz(int t) { return ((((t >> 2) ^ (t >> 1)
 #ifndef PA_MLA_KAHEAD
 #define PA_MLA_KAHEAD 8
 #endif
-#ifndef PA_MLA_VAHEAD
-#define PA_MLA_VAHEAD 6
-#endif
 constexpr int kMlaChunk = 32;             // tokens per chunk
 constexpr int kMlaBuf = PA_MLA_BUF;       // chunk slots in the LDS ring
-constexpr int kMlaPageWin = 1024;         // page ids staged in LDS at a time
 constexpr int kMlaKAhead = PA_MLA_KAHEAD; // QK operand reads in flight ahead of their MFMAs
-constexpr int kMlaVAhead = PA_MLA_VAHEAD; // PV MFMAs whose operand reads are in flight ahead
 constexpr int kMlaHeadsPerWave = 32;
+// Balanced splits: virtual tokens charged for each piece a worker starts
+// (measured: a piece costs about 20 us beyond its chunks on the MLA batch,
+// the time of ~250 tokens).
+constexpr int kMlaPieceCharge = 256;
 
 // Wave-wide int64 inclusive prefix sum and max of an int.
 __device__ __forceinline__ int64_t wave_incl_sum_i64(int64_t v, int lane)
@@ -199,6 +205,112 @@ __device__ __forceinline__ int wave_max_i32(int v)
     return v;
 }
 
+// s_waitcnt lgkmcnt(N), with the value operand of the next MFMAs (and, for
+// the first value operand of a k-step, its probability operands) threaded
+// through it, so that nothing using them is scheduled above the wait.
+template <int N, class B>
+__device__ __forceinline__ void lds_wait_v(B& b0, B& b1)
+{
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is a 4-bit field");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(b0), "+v"(b1) : "n"(N));
+}
+template <int N, class A, class B>
+__device__ __forceinline__ void lds_wait_pv(A (&a)[4], B& b0, B& b1)
+{
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is a 4-bit field");
+    asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b0), "+v"(b1)
+                 : "n"(N));
+}
+template <int N, class A, class B>
+__device__ __forceinline__ void lds_wait_pv(A (&a)[2], B& b0, B& b1)
+{
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is a 4-bit field");
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(b0), "+v"(b1) : "n"(N));
+}
+// Workgroup barrier that orders LDS accesses only: this wave's LDS
+// operations are complete, then s_barrier. __syncthreads() also fences
+// global memory, i.e. waits for every outstanding store and copy; under a
+// saturated memory system that is a full round trip (several microseconds)
+// each time, for ordering nothing here needs.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// max of three scores (they are never NaN: no quieting needed)
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ void lds_write_b128(uint32_t lds_addr, u32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(lds_addr), "v"(v), "n"(OFF) : "memory");
+}
+
+// Two probabilities rounded to the cache type, packed, and their sum.
+template <class E> struct MlaPack;
+template <> struct MlaPack<BF16> {
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ uint32_t pack(float a, float b, float& sum)
+    {
+        const v2 x = {(__bf16)a, (__bf16)b};
+        const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(x, one, sum, false);
+        return __builtin_bit_cast(uint32_t, x);
+    }
+};
+template <> struct MlaPack<F16> {
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ uint32_t pack(float a, float b, float& sum)
+    {
+        const v2 x = {(_Float16)a, (_Float16)b};
+        const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        sum = __builtin_amdgcn_fdot2(x, one, sum, false);
+        return __builtin_bit_cast(uint32_t, x);
+    }
+};
+
+// P.V operand schedule of one chunk (per wave): 2 k-steps of 16 tokens, each
+// with HT probability operands (one b128 read of the P buffer each) and DT
+// value operands (two transposed reads each), read in that order; MFMA m =
+// (kk, dt, ht), ht fastest, needs value operand (kk, dt) and everything
+// read before it. Reads are issued as far ahead as 15 outstanding LDS
+// operations (the lgkmcnt limit) allow.
+template <int HT, int DT> struct PvSchedule {
+    static constexpr int kReads = 2 * (HT + DT);   // operand reads (P: 1 op, V: 2 ops)
+    static constexpr int kMfma = 2 * DT * HT;
+    // LDS operations up to and including read r
+    static constexpr int ops_through(int r)
+    {
+        int n = 0;
+        for (int i = 0; i <= r; ++i) n += (i % (HT + DT)) < HT ? 1 : 2;
+        return n;
+    }
+    // read index that MFMA m needs last: value operand (kk, dt)
+    static constexpr int need(int m)
+    {
+        const int kk = m / (DT * HT), dt = (m / HT) % DT;
+        return kk * (HT + DT) + HT + dt;
+    }
+    // last read issued before MFMA m: all that fit in 15 outstanding operations
+    // once the reads MFMA m-1 needed have landed
+    static constexpr int issued(int m)
+    {
+        const int done = m == 0 ? -1 : need(m - 1);
+        const int base = done < 0 ? 0 : ops_through(done);
+        int r = done;
+        while (r + 1 < kReads && ops_through(r + 1) - base <= 15) ++r;
+        return r;
+    }
+    static constexpr int wait(int m) { return ops_through(issued(m)) - ops_through(need(m)); }
+};
+
 // ALIBI: scores carry the slopes' bias (a separate instance, so the plain
 // kernel keeps its registers).
 // BAL = false: one workgroup per (seq, kv head, split) of the fixed or
@@ -214,36 +326,39 @@ void k_decode_mla(DecodeParams p)
     constexpr int D = 576, DV = 512;
     constexpr int CT = kMlaChunk;
     constexpr int PR = D * (int)sizeof(T) / 16;  // 16-byte pieces per latent row (72)
-    constexpr int RB = PR * 16;                   // bytes per latent row
-    constexpr int INS = CT * PR / 64;             // copy instructions per chunk
-    constexpr int LW = loader_waves(INS, NW);     // waves that issue copies
-    constexpr int IPW = INS / LW;                 // copies per loader wave per chunk
+    constexpr int MP = 64;                        // pieces of a main row (1 KB)
+    constexpr int TP = PR - MP;                   // pieces of a tail row (8)
+    constexpr int TAIL = CT * MP * 16;            // byte offset of the tail rows in a slot
+    constexpr int TPW = CT / NW;                  // rows each wave copies
+    constexpr int IPW = TPW + TPW * TP / 64;      // copy instructions per wave per chunk
     constexpr int KS = D / 16;                    // QK k-steps
-    constexpr int MT = DV / 32;                   // PV value-column tiles
     constexpr int NB = kMlaBuf;
     constexpr int HPW = kMlaHeadsPerWave;
-    static_assert(CT * PR % 64 == 0, "chunk must be a whole number of copy instructions");
-    static_assert(PR % 8 == 0, "row pieces must be a multiple of 8 for the swizzle");
-    static_assert(KS % 4 == 0 && MT % 2 == 0, "tiling");
+    constexpr int G = HPW * NW;                   // heads of the workgroup
+    constexpr int HT = NW;                        // P.V head tiles: all G heads
+    constexpr int DT = DV / 32 / NW;              // P.V value-column tiles of one wave
+    using Sched = PvSchedule<HT, DT>;
+    static_assert(PR == MP + 8 && TPW % 8 == 0, "ring layout: 64 + 8 pieces a row, tail rows 8 to a copy");
+    static_assert(KS % 4 == 0 && DT % 2 == 0, "tiling");
     static_assert(IPW * (NB - 2) <= 63, "vmcnt is a 6-bit field");
 
     __shared__ u32x4 ring[NB][CT * PR];
-    __shared__ int32_t page_lds[kMlaPageWin];
+    __shared__ u32x4 pbuf[G * 4];  // probabilities of a chunk: [head][32 tokens] of T, 64 B a head
     __shared__ int rerun_flag;
 
-    const int ngroups = p.group / (HPW * NW);
+    const int ngroups = p.group / G;
     const int hg = blockIdx.y % ngroups, kq = blockIdx.y / ngroups;
     // query token qg of every sequence (rows s * num_group + qg)
     const int qg = kq % p.num_group, kvh = kq / p.num_group;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63, c32 = lane & 31, hl = lane >> 5;
-    const int h0 = kvh * p.group + hg * HPW * NW;  // first head of the workgroup
+    const int h0 = kvh * p.group + hg * G;  // first head of the workgroup
     const int h = h0 + wave * HPW + c32;
 
     // One split (or balanced piece): tokens [start, end) of sequence s, its
     // statistics and normalised output stored in split slot `part`.
     auto piece = [&](const int s, const int part, const int start, const int end) {
-    __syncthreads();  // the previous piece's LDS reads are done
+    lds_barrier();  // the previous piece's LDS reads are done
     // With balanced splits the pieces run in a loop. The lane and head
     // indices are then re-derived through an opaque zero, so the compiler
     // cannot hoist what depends on them out of that loop: kept live across
@@ -252,58 +367,83 @@ void k_decode_mla(DecodeParams p)
     int opaque = 0;
     if constexpr (BAL) asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
     const int lane = (int)(threadIdx.x & 63) + opaque, c32 = lane & 31, hl = lane >> 5;
-    const int wave = (int)(threadIdx.x >> 6) + opaque;
-    const int h = h0 + opaque + wave * HPW + c32;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) + opaque;  // scalar
+    const int h = h0 + opaque + wave * HPW + c32;  // this lane's head in QK and the softmax
     const int nc = (end - start + CT - 1) / CT;
 
-    // B operand of QK: lane (hl, c32) holds q[h][16*ks + 8*hl .. +8]
+    // B operand of QK: lane (hl, c32) holds q[h][16*ks + 8*hl .. +8]. With a
+    // negative scale the query is negated (exact) and |scale| used, so the
+    // largest raw score is the largest logit.
+    const float scale = fabsf(p.scale_log2);
+    const uint32_t qflip = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
     vec8 qv[KS];
     {
         const T* q = reinterpret_cast<const T*>(p.q) + (int64_t)(s * p.num_group + qg) * p.q_ss + (int64_t)h * p.q_sh + 8 * hl;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(vec8, load16(q + ks * 16));
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 w = load16(q + ks * 16);
+            w ^= qflip;
+            qv[ks] = __builtin_bit_cast(vec8, w);
+        }
     }
 
-    const int32_t* row = page_row(p.pl, s);
+    // the sequence's page list, read through the scalar data cache: every
+    // page id a wave needs is uniform across it
+    typedef __attribute__((address_space(4))) const int32_t* cptr;
     const int64_t sb = p.pl.stride_b;
+    const int64_t roff = p.pl.indptr ? (int64_t)((cptr)(uintptr_t)p.pl.indptr)[s] * sb : (int64_t)s * p.pl.stride_s;
+    const cptr rowc = (cptr)(uintptr_t)(p.pl.pages + roff);
     const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)kvh * p.k_sh;
-    // ALiBi: head c32's slope in base-2 units (0 without slopes). Scores then
-    // grow toward the end of the sequence, so a split usually passes the
-    // first chunk's reference by more than the headroom and runs twice.
+    // ALiBi: head h's slope in base-2 units. Scores then grow toward the end
+    // of the sequence, so a split usually passes the first chunk's reference
+    // by more than the headroom and runs twice.
     const int L = ALIBI ? p.seq_lens[s] : 0;
     const float slope = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
 
-    // page ids of tokens [wbase, wbase + kMlaPageWin) of this split
-    int wbase = start;
-    auto stage_pages = [&](int base) {
-        const int n = min(kMlaPageWin, end - base);
-        for (int i = threadIdx.x; i < n; i += 64 * NW) page_lds[i] = row[(int64_t)(base + i) * sb];
-    };
-    stage_pages(wbase);
-    __syncthreads();
-
-    // copy chunk `c` (tokens start + CT*c ...) into ring slot c % NB
-    auto issue = [&](int c) {
-        if (wave >= LW) return;
-        const int c0 = start + CT * c;
-        u32x4* dst = &ring[c % NB][0];
-        int32_t pg[IPW];  // all page ids first: one LDS round trip per chunk
+    // page ids of the rows this wave copies for chunk c (rows past the split
+    // end take the last valid row's page: real data, masked later)
+    auto load_pages = [&](int c, int32_t (&pg)[TPW]) {
+        const int r0 = start + CT * c + TPW * wave;
+        if (sb == 1 && r0 + TPW <= end) {  // consecutive ids, all before the split end: wide loads
+            const cptr b = rowc + r0;
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) {
-            const int t = ((wave * IPW + j) * 64 + lane) / PR;
-            pg[j] = page_lds[min(c0 + t, end - 1) - wbase];
-        }
+            for (int j = 0; j < TPW; ++j) pg[j] = b[j];
+        } else {
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) {
-            const int ins = wave * IPW + j;
-            const int piece = ins * 64 + lane;
-            const int t = piece / PR, pc = piece % PR;
-            const T* src = kc + (int64_t)pg[j] * p.k_sb + (int64_t)((pc ^ mla_swz(t)) * 8);
-            lds_copy16(src, dst + ins * 64);
+            for (int j = 0; j < TPW; ++j) pg[j] = rowc[(int64_t)min(r0 + j, end - 1) * sb];
         }
     };
 
-    // Fixed reference: probabilities are taken against mref, head c32's max
+    // copy chunk `c` (tokens start + CT*c ...) into ring slot c % NB: wave w
+    // copies rows TPW*w .. TPW*w + TPW-1, one instruction per main row (a
+    // scalar base address) and one per 8 tail rows.
+    auto issue = [&](int c, const int32_t (&pg)[TPW]) {
+        // an opaque zero: the lane offsets below are recomputed per chunk (one
+        // XOR a copy) rather than hoisted out of the chunk loop, where they
+        // would take 20 registers and be spilled
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const uint32_t lane16 = (uint32_t)(lane * 16 + z);
+        const uint32_t slot = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = TPW * wave + j;
+            const char* rowp = reinterpret_cast<const char*>(kc + (int64_t)pg[j] * p.k_sb);
+            lds_copy16(rowp + (lane16 ^ (uint32_t)(16 * mla_fmain(t))),
+                       (__attribute__((address_space(3))) void*)(uintptr_t)(slot + t * MP * 16));
+        }
+#pragma unroll
+        for (int k = 0; k < TPW / 8; ++k) {
+            const int t0 = TPW * wave + 8 * k, r = (lane + z) >> 3, t = t0 + r, q = (lane + z) & 7;
+            int pgl = pg[8 * k];  // the page of this lane's row
+#pragma unroll
+            for (int i = 1; i < 8; ++i) pgl = r == i ? pg[8 * k + i] : pgl;
+            const T* src = kc + (int64_t)pgl * p.k_sb + 8 * (MP + (q ^ mla_ftail(t)));
+            lds_copy16(src, (__attribute__((address_space(3))) void*)(uintptr_t)(slot + TAIL + t0 * TP * 16));
+        }
+    };
+
+    // Fixed reference: probabilities are taken against mref, head h's max
     // over the split's first chunk, and never rescaled, so the 256
     // accumulators are only ever touched by MFMAs. While no later score
     // passes mref by more than kHeadroom (base 2), p <= 2^kHeadroom and the
@@ -316,55 +456,73 @@ void k_decode_mla(DecodeParams p)
     // so the headroom must keep 2^kHeadroom finite there: bf16 reaches 2^127,
     // f16 only 65504 < 2^16 (2^16 would round to +inf).
     constexpr float kHeadroom = std::is_same<E, F16>::value ? 15.0f : 64.0f;
-    float mref = -INFINITY;  // reference max of head c32 (base 2)
-    float mtrue = -INFINITY; // true running max of head c32 (base 2)
-    float l = 0.0f;          // this lane's share of sum_t exp2(z_t - mref)
-    bool over = false;       // a score of head c32 passed mref + kHeadroom
-    f32x16 acc[MT];
+    float mref = -INFINITY;  // reference max of head h (base 2)
+    float mtrue = -INFINITY; // true running max of head h (base 2)
+    float l = 0.0f;          // this lane's share of sum_t exp2(z_t - mref), rounded p
+    bool over = false;       // a score of head h passed mref + kHeadroom
+    f32x16 acc[DT][HT];      // O^T[value column][head] of this wave's columns, all G heads
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[dt][ht][i] = 0.0f;
 
-    // QK operand addresses: A-row c32 reads ring row perm(c32); piece
-    // 2*ks + hl of it sits at column 8*(ks>>2) + ((2*(ks&3) + hl) ^ swz), i.e.
-    // four base addresses (ks mod 4) plus 128*(ks/4) as the immediate.
+    // QK operand addresses: A-row c32 reads ring row perm(c32), piece
+    // 2*ks + hl. For ks < 32 that is main-row position 16*(ks>>3) + ((2*(ks&7)
+    // + hl) ^ fmain): eight base addresses (ks mod 8) plus 256*(ks/8) as the
+    // immediate; for ks >= 32 tail position (2*(ks-32) + hl) ^ ftail: four
+    // bases.
     const int trow = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
-    const int ksw = mla_swz(trow);
-    uint32_t kb_lane[4];
+    uint32_t kb_main[8], kb_tail[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) kb_lane[q4] = trow * RB + 16 * ((2 * q4 + hl) ^ ksw);
-    // PV operand addresses: read (kk, rd) of value tile mt covers rows
-    // t = 16kk + 8hl + 4rd + a/4 (a = lane & 15) and value columns
-    // 32mt + 16*g16 + 4*(a&3) .. +3 (g16 = (lane >> 4) & 1): piece
-    // 4mt + 2*g16 + ((a&3) >> 1) at column 4*(mt ^ rd ^ t1) + low, with
-    // t1 = (a >> 3) & 1 (bit 1 of the row) and low = 2*(g16 ^ (a >> 3)) +
-    // (((a & 3) >> 1) ^ hl), 8 bytes in when a is odd. As the immediate
-    // kk*16*RB + rd*4*RB + 64*(mt ^ rd); the lane's t1 then moves the
-    // address by +64 when mt ^ rd is even and -64 when it is odd, so there
-    // are two lane bases (vb_lane for even, vb_lane_odd for odd).
-    uint32_t vb_lane, vb_lane_odd;
+    for (int k8 = 0; k8 < 8; ++k8) kb_main[k8] = trow * MP * 16 + 16 * ((2 * k8 + hl) ^ mla_fmain(trow));
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) kb_tail[k4] = TAIL + trow * TP * 16 + 16 * ((2 * k4 + hl) ^ mla_ftail(trow));
+    // P.V value operands (A = V^T[32 value columns][16 tokens]) of column
+    // tile mt = NW*dt + wave (the wave's tiles interleave with the others'):
+    // transposed read (kk, rd) covers rows t = 16kk + 8hl + 4rd + a/4 (a =
+    // lane & 15) and value columns 32mt + 16*g16 + 4*(a&3) .. +3 (g16 = (lane
+    // >> 4) & 1), i.e. piece pc = 4mt + 2*g16 + ((a&3) >> 1), 8 bytes in when
+    // a is odd. With fmain(t) = 4*(a/4) + 2hl + rd, position pc ^ fmain(t) has
+    // bits 0-1 (2*g16 + ((a&3) >> 1)) ^ 2hl ^ rd, bits 2-3 (mt & 3) ^ a/4 and
+    // bits 4-5 mt >> 2: lane bases for rd = 0, 1 and (NW*dt) & 3 (0, or 0 and
+    // 2 when NW = 2), plus kk*16 KB + rd*4 KB + 256*(mt >> 2) as the immediate.
+    uint32_t vb_lane[2][2];
     {
-        const int a = lane & 15, g16 = (lane >> 4) & 1, t1 = (a >> 3) & 1;
-        const int low = 2 * (g16 ^ (a >> 3)) + (((a & 3) >> 1) ^ hl);
-        const uint32_t vb = (8 * hl + (a >> 2)) * RB + 16 * low + 8 * (a & 1);
-        vb_lane = vb + 64 * t1;
-        vb_lane_odd = vb - 64 * t1;  // t1 = 1 only for rows >= 2: no wrap
+        const int a = lane & 15, g16 = (lane >> 4) & 1;
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                vb_lane[rd][x] = (8 * hl + (a >> 2)) * MP * 16 + 64 * (((2 * x) | wave) ^ (a >> 2)) +
+                                 16 * ((2 * g16 + ((a & 3) >> 1)) ^ (2 * hl) ^ rd) + 8 * (a & 1);
     }
+    // P buffer: head j's 32 probabilities are one 64-byte row, tokens 8i ..
+    // 8i+7 in 16-byte piece i ^ ((j >> 2) & 3), so the 16 lanes of one b128
+    // access (16 heads, one piece) cover distinct banks. Lane (hl, c32)
+    // writes head 32*wave + c32's pieces hl and 2 + hl (its tokens) and, for
+    // P.V head tile ht, reads head 32*ht + c32's piece 2kk + hl (B operand:
+    // tokens 16kk + 8hl .. +7).
+    const uint32_t pbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&pbuf[0]);
+    const int psw = (c32 >> 2) & 3;
+    const uint32_t pa0 = pbase + c32 * 64 + 16 * (hl ^ psw);        // piece hl
+    const uint32_t pa1 = pbase + c32 * 64 + 16 * ((hl ^ psw) ^ 2);  // piece 2 + hl
+    const uint32_t pw0 = pa0 + 2048 * wave, pw1 = pa1 + 2048 * wave;
 
-    // scores of chunk c for this lane's 16 tokens (base 2, masked past the
-    // split end) and their max over both lane halves (head c32). One
-    // accumulator: a second does not fit beside q and the 256 output
-    // accumulators without spilling.
-    auto scores = [&](int c, float (&sc)[16]) -> float {
-        const int c0 = start + CT * c;
+    // raw scores S^T[t][h] of chunk c: lane (hl, c32) gets head h's scores of
+    // tokens 16*(r>>3) + 8*hl + (r&7), r = 0..15
+    auto qk = [&](int c) -> f32x16 {
         const uint32_t bufa =
             (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
         constexpr int RA = kMlaKAhead < KS ? kMlaKAhead : KS;
         u32x4 kr[KS];
         auto kread = [&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
-            kr[ks] = lds_read_b128<128 * (ks >> 2)>(bufa + kb_lane[ks & 3]);
+            if constexpr (ks < 32)
+                kr[ks] = lds_read_b128<256 * (ks >> 3)>(bufa + kb_main[ks & 7]);
+            else
+                kr[ks] = lds_read_b128<0>(bufa + kb_tail[ks - 32]);
         };
         static_for<RA>(kread);
         f32x16 sacc;
@@ -378,58 +536,98 @@ void k_decode_mla(DecodeParams p)
             if constexpr (i + RA < KS) kread(std::integral_constant<int, i + RA>{});
             __builtin_amdgcn_sched_barrier(0);  // keep wait -> MFMA -> next read in order
         });
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = c0 + 16 * (r >> 3) + 8 * hl + (r & 7);
-            float z = sacc[r] * p.scale_log2;
-            if constexpr (ALIBI) z += slope * (float)(t - (L - 1));
-            sc[r] = t < end ? z : -INFINITY;
-            mloc = fmaxf(mloc, sc[r]);
-        }
-        return half_max(mloc);
+        return sacc;
     };
 
-    // probabilities of chunk c against mref, and their weighted value rows
-    auto weigh = [&](int c, const float (&sc)[16]) {
-        const uint32_t slot =
-            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
-        const uint32_t vbase = slot + vb_lane, vbase_odd = slot + vb_lane_odd;
-        // MFMA j (0 .. 2*MT-1) is (kk = j / MT, mt = j % MT): all tiles of the
-        // first 16 tokens, then of the second, so consecutive MFMAs update
-        // different accumulators
-        constexpr int NJ = 2 * MT;
-        constexpr int RA = kMlaVAhead < NJ ? kMlaVAhead : NJ;
-        s16x4 vr[NJ][2];
-        auto vread = [&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            constexpr int kk = j / MT, mt = j % MT;
-            vr[j][0] = lds_read_tr16<kk * 16 * RB + 64 * mt>((mt & 1) ? vbase_odd : vbase);
-            vr[j][1] = lds_read_tr16<kk * 16 * RB + 4 * RB + 64 * (mt ^ 1)>(((mt ^ 1) & 1) ? vbase_odd : vbase);
-        };
-        static_for<RA>(vread);
-        __builtin_amdgcn_sched_barrier(0);
-
-        vec8 pv[2];
-        float psum = 0.0f;
+    // probabilities of chunk c against mref, rounded to the cache type and
+    // written to the P buffer; TAILC: the chunk at the split end, whose
+    // tokens from nvalid on are masked (every other chunk is full)
+    auto softmax = [&](int c, const f32x16& sacc, auto tailc) {
+        constexpr bool TAILC = decltype(tailc)::value;
+        const int c0 = start + CT * c;
+        const int nvalid = end - c0;  // >= 1
+        float z[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const T e = (T)fast_exp2(sc[r] - mref);
-            pv[r >> 3][r & 7] = e;
-            psum += (float)e;
+            const int t = 16 * (r >> 3) + 8 * hl + (r & 7);
+            if constexpr (ALIBI)
+                z[r] = sacc[r] * scale + slope * (float)(c0 + t - (L - 1));
+            else
+                z[r] = sacc[r];
+            if constexpr (TAILC) z[r] = t < nvalid ? z[r] : -INFINITY;
         }
-        l += psum;
-        static_for<NJ>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            constexpr int issued = (j + RA < NJ) ? j + RA : NJ;
-            lds_wait<2 * (issued - j - 1)>(vr[j][0], vr[j][1]);
-            const u32x4 a = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][0], vr[j][0], 0, 1)),
-                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][0], vr[j][0], 2, 3)),
-                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][1], vr[j][1], 0, 1)),
-                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[j][1], vr[j][1], 2, 3))};
-            acc[j % MT] = Ops::mma(__builtin_bit_cast(vec8, a), pv[j / MT], acc[j % MT]);
-            if constexpr (j + RA < NJ) vread(std::integral_constant<int, j + RA>{});
+        float mx = max3f(z[0], z[1], z[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) mx = max3f(mx, z[r], z[r + 1]);
+        mx = fmaxf(mx, z[15]);
+        float mloc = half_max(mx);  // token 0 is valid, so lane half 0 has a finite score
+        if constexpr (!ALIBI) mloc *= scale;
+        mref = mref == -INFINITY ? mloc : mref;
+        over |= mloc > mref + kHeadroom;
+        mtrue = fmaxf(mtrue, mloc);
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            e[r] = fast_exp2(ALIBI ? z[r] - mref : fmaf(z[r], scale, -mref));
+            if constexpr (TAILC) e[r] = 16 * (r >> 3) + 8 * hl + (r & 7) < nvalid ? e[r] : 0.0f;
+        }
+        u32x4 w0, w1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w0[i] = MlaPack<E>::pack(e[2 * i], e[2 * i + 1], l);
+            w1[i] = MlaPack<E>::pack(e[8 + 2 * i], e[8 + 2 * i + 1], l);
+        }
+        lds_write_b128<0>(pw0, w0);
+        lds_write_b128<0>(pw1, w1);
+    };
+
+    // O^T[this wave's value columns][all G heads] += V^T P over chunk c
+    auto pv = [&](int c, auto after_reads) {
+        const uint32_t slot =
+            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+        u32x4 pr[2][HT];
+        s16x4 vr[2][DT][2];
+        // read r of the schedule: (kk, P operand ht) or (kk, value operand dt)
+        auto read = [&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            constexpr int kk = r / (HT + DT), i = r % (HT + DT);
+            if constexpr (i < HT) {
+                pr[kk][i] = lds_read_b128<2048 * i>(kk ? pa1 : pa0);
+            } else {
+                constexpr int dt = i - HT;
+                constexpr int x = ((NW * dt) & 3) >> 1;  // (NW*dt) & 3 is 0 or 2
+                constexpr int imm = kk * 16 * MP * 16 + 256 * ((NW * dt) >> 2);
+                vr[kk][dt][0] = lds_read_tr16<imm>(slot + vb_lane[0][x]);
+                vr[kk][dt][1] = lds_read_tr16<imm + 4 * MP * 16>(slot + vb_lane[1][x]);
+            }
+        };
+        static_for<Sched::kMfma>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int kk = m / (DT * HT), dt = (m / HT) % DT, ht = m % HT;
+            constexpr int from = m == 0 ? 0 : Sched::issued(m - 1) + 1;
+            static_for<Sched::issued(m) + 1 - from>([&](auto jc) {
+                read(std::integral_constant<int, from + decltype(jc)::value>{});
+            });
+            // a wait before the first MFMA of each value operand (the
+            // probability operands of the k-step were read before it)
+            if constexpr (ht == 0) {
+                if constexpr (dt == 0)
+                    lds_wait_pv<Sched::wait(m)>(pr[kk], vr[kk][dt][0], vr[kk][dt][1]);
+                else
+                    lds_wait_v<Sched::wait(m)>(vr[kk][dt][0], vr[kk][dt][1]);
+            }
+            const u32x4 a = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[kk][dt][0], vr[kk][dt][0], 0, 1)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[kk][dt][0], vr[kk][dt][0], 2, 3)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[kk][dt][1], vr[kk][dt][1], 0, 1)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(vr[kk][dt][1], vr[kk][dt][1], 2, 3))};
+            acc[dt][ht] = Ops::mma(__builtin_bit_cast(vec8, a), __builtin_bit_cast(vec8, pr[kk][ht]), acc[dt][ht]);
             __builtin_amdgcn_sched_barrier(0);
+            // every read of the chunk has landed: scalar loads issued here
+            // cannot hold up a counted LDS wait
+            if constexpr (m == Sched::kMfma - HT) {
+                after_reads();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         });
     };
 
@@ -437,84 +635,92 @@ void k_decode_mla(DecodeParams p)
     // used. Copies complete in issue order, so before chunk c a loader wave
     // waits until at most IPW copies per later chunk remain outstanding
     // (all of them in the last NB-2 chunks); the barrier then makes every
-    // wave's copies visible and frees the slot chunk c-1 used, which the
-    // copy of chunk c+NB-1 reuses.
-    // chunk c's copies are visible to every wave; chunk c+NB-1 is issued
+    // wave's copies visible, and, since every wave has finished chunk c-1,
+    // frees its ring slot (reused by the copy of chunk c+NB-1) and the P
+    // buffer.
+    int32_t pg_next[TPW];  // page ids of the next chunk to copy
     auto advance = [&](int c) {
         if (c + NB - 2 < nc)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(IPW * (NB - 2)));
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        // A plain s_barrier: __syncthreads() would add a workgroup fence that
-        // waits for every outstanding copy. The copies this barrier publishes
-        // are covered by the explicit wait above; the compiler fences keep
-        // LDS accesses on their side of the barrier.
+        // A plain s_barrier (see lds_barrier): the copies this barrier
+        // publishes are covered by the explicit wait above; the compiler
+        // fences keep LDS accesses on their side of the barrier.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const int cn = c + NB - 1;
-        if (cn < nc) {
-            const int tlast = min(start + CT * cn + CT, end) - 1;
-            if (tlast >= wbase + kMlaPageWin) {  // next page window (all waves here)
-                wbase = start + CT * cn;
-                stage_pages(wbase);
-                __syncthreads();
-            }
-            issue(cn);
-        }
+        if (c + NB - 1 < nc) issue(c + NB - 1, pg_next);
     };
+    // every wave's probabilities of the chunk are in the P buffer
+    auto p_ready = [&]() { lds_barrier(); };
     // one pass over the split
     auto run = [&]() {
-        // q (first pass) or the previous pass's copies are complete, so no
-        // wait inside the loop has to cover them
+        for (int c = 0; c < NB - 1 && c < nc; ++c) {
+            int32_t pg[TPW];
+            load_pages(c, pg);
+            issue(c, pg);
+        }
+        if (NB - 1 < nc) load_pages(NB - 1, pg_next);
+        // One memory round trip for the query, the first chunks and the
+        // previous piece's stores; no wait inside the loop covers them.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        for (int c = 0; c < NB - 1 && c < nc; ++c) issue(c);
         for (int c = 0; c < nc; ++c) {
-            float sc[16];
             advance(c);
-            const float mloc = scores(c, sc);
-            mtrue = fmaxf(mtrue, mloc);
-            mref = mref == -INFINITY ? mloc : mref;
-            over |= mloc > mref + kHeadroom;
-            weigh(c, sc);
+            const f32x16 sacc = qk(c);
+            if (end - start - CT * c < CT)
+                softmax(c, sacc, std::true_type{});
+            else
+                softmax(c, sacc, std::false_type{});
+            p_ready();
+            pv(c, [&]() {
+                if (c + NB < nc) load_pages(c + NB, pg_next);
+            });
         }
     };
 
     if (threadIdx.x == 0) rerun_flag = 0;
     run();
     if (over) rerun_flag = 1;  // benign race: every writer stores 1
-    __syncthreads();
+    lds_barrier();
     if (rerun_flag) {  // uniform across the workgroup
         mref = mtrue;
         l = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
-        if (wbase != start) {
-            wbase = start;
-            stage_pages(wbase);
-        }
-        __syncthreads();  // every wave is done with the ring and the page window
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[dt][ht][i] = 0.0f;
+        lds_barrier();  // every wave is done with the ring
         run();
     }
+    lds_barrier();  // every wave is done with the P buffer
 
+    // statistics of head h; every wave needs the sums of all G heads
     l = half_sum(l);
+    float* lsum = reinterpret_cast<float*>(&pbuf[0]);
     const int64_t mloff = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)h * p.ml_sh + part;
     if (hl == 0) {
+        lsum[wave * HPW + c32] = l;
         p.max_logits[mloff] = mtrue * kLn2;
         p.exp_sums[mloff] = l * fast_exp2(mref - mtrue);
     }
-    // lane (hl, c32), register 4i + j of tile mt holds value column
-    // 32mt + 8i + 4hl + j of head c32
-    const float inv = 1.0f / l;
-    float* out = p.tmp + (int64_t)(s * p.num_group + qg) * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp + 4 * hl;
+    lds_barrier();
+    // lane (hl, c32), register 4i + j of tile (dt, ht) holds value column
+    // 32*(NW*dt + wave) + 8i + 4hl + j of head 32ht + c32
+    float* out = p.tmp + (int64_t)(s * p.num_group + qg) * p.tmp_ss + (int64_t)(h0 + c32) * p.tmp_sh +
+                 (int64_t)part * p.tmp_sp + 32 * wave + 4 * hl;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int ht = 0; ht < HT; ++ht) {
+        const float inv = 1.0f / lsum[32 * ht + c32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<f32x4*>(out + 32 * mt + 8 * i) =
-                f32x4{acc[mt][4 * i], acc[mt][4 * i + 1], acc[mt][4 * i + 2], acc[mt][4 * i + 3]} * inv;
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(out + (int64_t)(32 * ht) * p.tmp_sh + 32 * NW * dt + 8 * i) =
+                    f32x4{acc[dt][ht][4 * i], acc[dt][ht][4 * i + 1], acc[dt][ht][4 * i + 2], acc[dt][ht][4 * i + 3]} * inv;
+    }
     };
 
     if constexpr (!BAL) {
@@ -534,9 +740,14 @@ void k_decode_mla(DecodeParams p)
         return;
     }
 
-    // ---- balanced splits: worker w = blockIdx.x takes tokens [w*U, (w+1)*U)
-    // of all sequences concatenated (lengths <= 0 count as 0)
+    // ---- balanced splits: the sequences' tokens in sequence order, each
+    // non-empty sequence preceded by kMlaPieceCharge virtual tokens (the cost
+    // of starting a piece: loading its query and the first chunks, storing
+    // its partial output), total T'; worker w = blockIdx.x takes virtual
+    // positions [w*U, (w+1)*U), so a worker that starts a sequence inside its
+    // range gets that many fewer real tokens.
     constexpr int BT = 64 * NW;
+    constexpr int C = kMlaPieceCharge;
     constexpr int GH = HPW * NW;  // heads of this workgroup
     __shared__ int64_t bal_w64[NW];
     __shared__ int bal_w32[NW];
@@ -555,11 +766,16 @@ void k_decode_mla(DecodeParams p)
         }
     };
 
+    // With at most BT sequences every thread loads its length once and keeps
+    // it for the scan below (one memory round trip for the whole schedule).
+    const bool one_round = p.num_seqs <= BT;
+    int Lmine = 0;
     int64_t tsum = 0;
     int tmax = 0;
     for (int i = tid; i < p.num_seqs; i += BT) {
         const int Li = max(p.seq_lens[i], 0);
-        tsum += Li;
+        if (i == tid) Lmine = Li;
+        tsum += Li > 0 ? Li + C : 0;
         tmax = max(tmax, Li);
         if (w == 0 && Li == 0) {  // worker 0 covers the empty sequences, one thread each
             for (int e = 0; e < GH * p.max_num_parts; ++e) {
@@ -575,37 +791,38 @@ void k_decode_mla(DecodeParams p)
         bal_w64[wave] = tsum;
         bal_w32[wave] = tmax;
     }
-    __syncthreads();
-    int64_t total_tokens = 0;
+    lds_barrier();
+    int64_t total_virtual = 0;
     int maxL = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        total_tokens += bal_w64[i];
+        total_virtual += bal_w64[i];
         maxL = max(maxL, bal_w32[i]);
     }
-    total_tokens = uniform_i64(total_tokens);
+    total_virtual = uniform_i64(total_virtual);
     maxL = __builtin_amdgcn_readfirstlane(maxL);
-    __syncthreads();  // bal_w64 is reused by the scan below
+    lds_barrier();  // bal_w64 is reused by the scan below
     const int64_t W = p.num_workers;
-    int64_t U = max((total_tokens + W - 1) / W, ((int64_t)maxL + p.max_num_parts - 2) / (p.max_num_parts - 1));
+    int64_t U = max((total_virtual + W - 1) / W, ((int64_t)maxL + p.max_num_parts - 2) / (p.max_num_parts - 1));
     U = max((U + 31) & ~int64_t(31), int64_t(32));
-    if (total_tokens == 0 || (int64_t)w * U >= total_tokens) return;
-    const int64_t r0 = (int64_t)w * U, r1 = min(r0 + U, total_tokens);
+    if (total_virtual == 0 || (int64_t)w * U >= total_virtual) return;
+    const int64_t r0 = (int64_t)w * U, r1 = min(r0 + U, total_virtual);
 
-    // sequences in batches of BT: block scan of the lengths gives their
-    // offsets; the ones meeting [r0, r1) form a contiguous run
+    // sequences in batches of BT: a block scan of the virtual lengths gives
+    // their virtual offsets; the ones meeting [r0, r1) form a contiguous run
     int64_t base = 0;
     for (int b0 = 0; b0 < p.num_seqs && base < r1; b0 += BT) {
         const int i = b0 + tid;
-        const int Li = i < p.num_seqs ? max(p.seq_lens[i], 0) : 0;
-        const int64_t inc = wave_incl_sum_i64(Li, lane);
+        const int Li = one_round ? Lmine : (i < p.num_seqs ? max(p.seq_lens[i], 0) : 0);
+        const int Vi = Li > 0 ? Li + C : 0;
+        const int64_t inc = wave_incl_sum_i64(Vi, lane);
         if (lane == kWave - 1) bal_w64[wave] = inc;
         if (tid == 0) {
             bal_first = BT;
             bal_last = -1;
         }
-        __syncthreads();
-        int64_t off = base + inc - Li, total = 0;
+        lds_barrier();
+        int64_t off = base + inc - Vi + C, total = 0;  // virtual position of the sequence's first token
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             if (j < wave) off += bal_w64[j];
@@ -617,7 +834,7 @@ void k_decode_mla(DecodeParams p)
             atomicMin(&bal_first, tid);
             atomicMax(&bal_last, tid);
         }
-        __syncthreads();
+        lds_barrier();
         const int first = __builtin_amdgcn_readfirstlane(bal_first);
         const int last = __builtin_amdgcn_readfirstlane(bal_last);
         total = uniform_i64(total);
@@ -630,7 +847,7 @@ void k_decode_mla(DecodeParams p)
             if ((so + Ls - 1) / U == w) mark_empty(b0 + j, k + 1);  // this worker has the last piece
         }
         base += total;
-        __syncthreads();  // bal_* are rewritten by the next batch
+        lds_barrier();  // bal_* are rewritten by the next batch
     }
 }
 

@@ -466,22 +466,27 @@ def test_full_config(orc, cfg):
 # ---------------------------------------------------------------------------
 # balanced splits (partition_size 0): equal token ranges over the batch
 # ---------------------------------------------------------------------------
+PIECE_CHARGE = 256  # virtual tokens before each non-empty sequence (pagedattn.h)
+
+
 def balanced_pieces(lens, workers, max_parts):
     """Per sequence, the (slot, start, end) pieces of the balanced split rule
     stated in pagedattn.h."""
     L = [max(0, int(x)) for x in lens]
-    T, maxL = sum(L), max(L + [0])
+    T = sum(Ls + PIECE_CHARGE for Ls in L if Ls > 0)
+    maxL = max(L + [0])
     U = max(-(-T // workers), -(-maxL // (max_parts - 1)))
     U = max(-(-U // 32) * 32, 32)
-    out, off = [], 0
+    out, v = [], 0
     for Ls in L:
         pieces = []
         if Ls > 0:
+            off = v + PIECE_CHARGE  # position of the sequence's first token
             w0, w1 = off // U, (off + Ls - 1) // U
             for w in range(w0, w1 + 1):
                 pieces.append((w - w0, max(w * U, off) - off, min((w + 1) * U, off + Ls) - off))
+            v += Ls + PIECE_CHARGE
         out.append(pieces)
-        off += Ls
     return out
 
 
