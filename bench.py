@@ -11,8 +11,9 @@ tokens, 64 query heads over 8 kv heads, head_dim 128, block size 16, 20000
 physical blocks in random order, 512-token partitions (64 per sequence).
 
 Prints one JSON line: KV read GB/s (value), microseconds per step, the
-roofline of the dominant kernel (phase 1) and the CPU oracle timed on a
-bounded sample of the same workload.
+roofline of the dominant kernel (phase 1), the same GPU's plain read rate on
+the workload's gather pattern and on contiguous memory (read_stream), and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -171,6 +172,62 @@ def cpu_baseline(w: workloads.Workload, out: torch.Tensor, sample_seqs: int, min
              "sample": f"{n} of {w.num_seqs} sequences (all heads), {kv} KV bytes, "
                        f"{runs} runs in {total:.1f} s", "seconds": dt},
             {"sample_seqs": n, "max_abs_err": err})
+
+
+def read_stream(w: workloads.Workload, step: "Step", reps: int):
+    """The same GPU's plain read rate (pa_read_probe, no arithmetic), on 1 GiB
+    of contiguous memory and on the workload's own gather: every live block
+    of every sequence through its page list, one run per kv head for keys
+    (and values), or every latent row for the MLA layout."""
+    from paged_attention_decode_tables_amd import api
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * cus * 1024, dtype=torch.int32, device="cuda")
+
+    def timed(*args, **kw):
+        for _ in range(2):
+            api.read_probe(sink, *args, **kw)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            api.read_probe(sink, *args, **kw)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / reps * 1e-3  # seconds per launch
+
+    n = 1 << 30
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    pages = torch.arange(n // 4096, dtype=torch.int32, device="cuda")
+    t_contig = timed(buf, pages, 1, 4096, 0, 4096)
+    del buf, pages
+    g = step.g
+    if w.latent is not None:
+        esz = w.latent.element_size()
+        step.pre()  # the flat page list of the step
+        pages = step.flat if step.indptr is not None else g.block_tables.reshape(-1)
+        row = w.head_size * esz
+        t_gather = timed(g.latent, pages, 1, row, 0, row)
+        nbytes = pages.numel() * row
+        pattern = f"{pages.numel()} latent rows of {row} B at random pages"
+    else:
+        esz = w.kv_elem_size
+        live = [w.block_tables[s, :(max(int(L), 0) + w.block_size - 1) // w.block_size]
+                for s, L in enumerate(w.seq_lens)]
+        pages = torch.cat(live).to(torch.int32).to("cuda")
+        kc, vc = g.key_cache, g.value_cache
+        run = w.head_size * w.block_size * esz
+        t_gather = timed(kc, pages, w.num_kv_heads, kc.stride(0) * esz, kc.stride(1) * esz, run, base1=vc)
+        nbytes = pages.numel() * w.num_kv_heads * run * 2
+        pattern = (f"{pages.numel()} blocks x {w.num_kv_heads} kv heads, keys and values, "
+                   f"runs of {run} B at random blocks")
+    gc = n / t_contig / 1e9
+    gg = nbytes / t_gather / 1e9
+    return {"kernel": "pa_read_probe", "contiguous_gbs": round(gc, 1),
+            "contiguous_frac": round(gc / HBM_PEAK_GBS, 4), "paged_gather_gbs": round(gg, 1),
+            "paged_gather_frac": round(gg / HBM_PEAK_GBS, 4), "gather_pattern": pattern,
+            "gather_bytes": int(nbytes), "gather_us": round(t_gather * 1e6, 2),
+            "contiguous_us": round(t_contig * 1e6, 2)}
 
 
 # Decode-metadata workloads: the batches of configs 4 and 5 as a serving
@@ -341,6 +398,8 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="size of the buffer read before each step of the cold-cache pass "
                          "(0: no cold-cache pass)")
+    ap.add_argument("--no-read-stream", action="store_true",
+                    help="skip the plain read-stream legs (pa_read_probe)")
     ap.add_argument("--fixed-splits", action="store_true",
                     help="run the MLA workload with its fixed 512-token partitions instead of "
                          "balanced splits")
@@ -504,6 +563,13 @@ def main():
     }
     if cold is not None:
         res["cold_cache"] = cold
+    if not args.no_read_stream:
+        log("bench: read-stream legs")
+        rs = read_stream(w, step, reps=20)
+        res["read_stream"] = rs
+        # phase 1 and the whole step against the same gather with no math
+        res["pct_of_read_stream"] = round(100.0 * achieved / rs["paged_gather_gbs"], 1)
+        res["step_pct_of_read_stream"] = round(100.0 * value / rs["paged_gather_gbs"], 1)
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         cb, parity = cpu_baseline(w, step.out, args.cpu_sample_seqs, args.cpu_seconds)

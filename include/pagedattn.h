@@ -252,8 +252,10 @@ int num_kv_splits(int32_t* out, const int32_t* seq_lens, int32_t num_seq, int32_
                   int32_t device_core_count, void* stream);
 
 /*
- * Test hook for the address arithmetic shared by the decode kernels
- * ([T2522] block-table example): for t < seq_lens[s],
+ * Test hook for the token -> (block, slot) map ([T2522] block-table
+ * example). It runs the device functions every decode kernel uses to look
+ * up a token's block and (block sizes above 1) its slot, page_of and
+ * slot_of in csrc/common.h: for t < seq_lens[s],
  *     out[s*out_stride_s + t] = pages[t / block_size] * block_stride
  *                              + (t % block_size) * slot_stride
  * with the page list as in pa_decode_args (kv_indptr may be NULL). Entries

@@ -114,6 +114,7 @@ def load_library() -> ctypes.CDLL:
     lib.normal_decode_set_metadata.argtypes = [ctypes.POINTER(MetadataArgs), _vp]
     lib.prepare_swa_spec_page_table.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                                 _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+    lib.pa_read_probe.argtypes = [_vp, _vp, _vp, _i64, _i32, _i64, _i64, _i32, _vp, _i32, _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     _lib = lib
@@ -477,3 +478,22 @@ def paged_token_offsets(out: torch.Tensor, block_tables: torch.Tensor, seq_lens:
     _check(lib.paged_token_offsets(_ptr(out), out.stride(0), _ptr(block_tables), bs_s, bs_b,
                                    _ptr(kv_indptr), _ptr(seq_lens), S, max_len, block_size,
                                    block_stride, slot_stride, _stream(stream)))
+
+
+def read_probe(sink: torch.Tensor, base0: torch.Tensor, pages: torch.Tensor, runs_per_page: int,
+               page_stride: int, run_stride: int, run_bytes: int,
+               base1: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Plain read stream (measurement only, include/pagedattn_probe.h): reads
+    run_bytes at base + pages[i] * page_stride + r * run_stride (bytes) for
+    every page id, run r < runs_per_page and base in (base0, base1), folding
+    the data into sink (uint32 [workgroups * 256 * 4]; workgroups = its
+    length / 1024)."""
+    lib = load_library()
+    _need(pages, "pages", torch.int32, ndim=1, contiguous=True)
+    _need(sink, "sink", (torch.int32, torch.uint32), ndim=1, contiguous=True)
+    if sink.numel() % 1024:
+        raise ValueError("sink must hold workgroups * 1024 uint32 entries")
+    _same_gpu(stream, sink=sink, base0=base0, base1=base1, pages=pages)
+    _check(lib.pa_read_probe(_ptr(base0), _ptr(base1), _ptr(pages), pages.numel(), runs_per_page,
+                             page_stride, run_stride, run_bytes, _ptr(sink), sink.numel() // 1024,
+                             _stream(stream)))

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "pagedattn_probe.h"
 
 #define PA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -369,4 +370,30 @@ PA_EXPORT int paged_token_offsets(int64_t* out, int64_t out_stride_s, const int3
                                              log2i(block_size), block_stride, slot_stride,
                                              reinterpret_cast<hipStream_t>(stream)),
                     "paged_token_offsets");
+}
+
+PA_EXPORT int pa_read_probe(const void* base0, const void* base1, const int32_t* pages, int64_t num_pages,
+                            int32_t runs_per_page, int64_t page_stride, int64_t run_stride, int32_t run_bytes,
+                            uint32_t* sink, int32_t workgroups, void* stream)
+{
+    if (num_pages < 0 || runs_per_page < 1 || workgroups < 1)
+        return fail(PA_EINVAL, "pa_read_probe: num_pages >= 0, runs_per_page >= 1 and workgroups >= 1 required");
+    if (run_bytes < 16 || run_bytes > 8192 || run_bytes % 16 || page_stride % 16 || run_stride % 16)
+        return fail(PA_EINVAL, "pa_read_probe: run_bytes must be a multiple of 16 in [16, 8192] and the strides "
+                               "multiples of 16");
+    if (!sink || (num_pages > 0 && (!base0 || !pages)))
+        return fail(PA_EINVAL, "pa_read_probe: a required pointer is NULL");
+    if (!aligned16(base0) || !aligned16(base1) || !aligned16(sink))
+        return fail(PA_EINVAL, "pa_read_probe: base0, base1 and sink must be 16-byte aligned");
+    pa::ProbeParams p{};
+    p.base0 = static_cast<const char*>(base0);
+    p.base1 = static_cast<const char*>(base1);
+    p.pages = pages;
+    p.num_pages = num_pages;
+    p.page_stride = page_stride;
+    p.run_stride = run_stride;
+    p.runs_per_page = runs_per_page;
+    p.pieces = run_bytes / 16;
+    p.sink = sink;
+    return launched(pa::launch_read_probe(p, workgroups, reinterpret_cast<hipStream_t>(stream)), "pa_read_probe");
 }

@@ -147,20 +147,29 @@ __device__ __forceinline__ const int32_t* page_row(const PageList& pl, int s)
     return pl.pages + off;
 }
 
-// Physical block holding token t (block_size = 1 << bs_shift).
-__device__ __forceinline__ int64_t token_block(const int32_t* row, int64_t stride_b, int64_t t,
-                                               int bs_shift)
+// The two gather steps for token t (block_size = 1 << bs_shift): its page
+// (physical block) pages[(t >> bs_shift) * stride_b], then its slot inside
+// the block, t & (block_size - 1). Every decode kernel reads its block ids
+// through page_of and takes slots with slot_of; the test hook
+// paged_token_offsets() computes its offsets with the same two functions.
+// P is int32_t* or the scalar-cache (constant address space) view of the
+// same list.
+template <class P>
+__device__ __forceinline__ int32_t page_of(P row, int64_t stride_b, int64_t t, int bs_shift)
 {
-    return (int64_t)row[(t >> bs_shift) * stride_b];
+    return row[(t >> bs_shift) * stride_b];
+}
+__device__ __forceinline__ int64_t slot_of(int64_t t, int bs_shift)
+{
+    return t & ((int64_t(1) << bs_shift) - 1);
 }
 
-// Offset of token t: block * block_stride + slot * slot_stride.
+// Offset of token t: page * block_stride + slot * slot_stride.
 __device__ __forceinline__ int64_t token_offset(const int32_t* row, int64_t stride_b, int64_t t,
                                                 int bs_shift, int64_t block_stride,
                                                 int64_t slot_stride)
 {
-    int64_t slot = t & ((int64_t(1) << bs_shift) - 1);
-    return token_block(row, stride_b, t, bs_shift) * block_stride + slot * slot_stride;
+    return (int64_t)page_of(row, stride_b, t, bs_shift) * block_stride + slot_of(t, bs_shift) * slot_stride;
 }
 
 // Split rule shared by phase 1 and phase 2: fixed partition size, or the

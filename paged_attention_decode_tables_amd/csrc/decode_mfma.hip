@@ -210,7 +210,7 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     const int nblk = ca < cb ? ((wend - 1) >> bs_shift) - blk0 + 1 : 0;
     auto fetch_window = [&](int base) -> int32_t {
         const int b = base + lane;
-        return b < nblk ? row[(int64_t)(blk0 + b) * sb] : 0;
+        return b < nblk ? page_of(row, sb, (int64_t)(blk0 + b) << bs_shift, bs_shift) : 0;
     };
     int wb = 0;
     int32_t win = fetch_window(0);
@@ -244,7 +244,7 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
         for (int u = 0; u < NSUB; ++u) {
             const int tk = min(c0 + 32 * u + 8 * (r >> 2), last_group);
             // piece (4*kp + g) of the token's D/KX pieces
-            const KT* kp = kc + block_of(tk) * p.k_sb + (((tk & (bs - 1)) + (r & 3)) * KX + g * bs * KX);
+            const KT* kp = kc + block_of(tk) * p.k_sb + ((slot_of(tk, bs_shift) + (r & 3)) * KX + g * bs * KX);
 #pragma unroll
             for (int kp_ = 0; kp_ < KP; ++kp_) {
                 t.k[u][2 * kp_] = load16_stream(kp + kp_ * 4 * bs * KX);
@@ -256,7 +256,7 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
 #pragma unroll
         for (int u = 0; u < NSUB; ++u) {
             const int tv = min(c0 + 32 * u + 8 * g, last_group);
-            const KT* vp = vc + block_of(tv) * p.v_sb + (r * bs + (tv & (bs - 1)));
+            const KT* vp = vc + block_of(tv) * p.v_sb + (r * bs + slot_of(tv, bs_shift));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if constexpr (F8) t.v[u][mt] = load8_stream(vp + mt * 16 * bs);

@@ -405,12 +405,11 @@ void k_decode_mla(DecodeParams p)
     auto load_pages = [&](int c, int32_t (&pg)[TPW]) {
         const int r0 = start + CT * c + TPW * wave;
         if (sb == 1 && r0 + TPW <= end) {  // consecutive ids, all before the split end: wide loads
-            const cptr b = rowc + r0;
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) pg[j] = b[j];
+            for (int j = 0; j < TPW; ++j) pg[j] = page_of(rowc, 1, r0 + j, 0);
         } else {
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) pg[j] = rowc[(int64_t)min(r0 + j, end - 1) * sb];
+            for (int j = 0; j < TPW; ++j) pg[j] = page_of(rowc, sb, min(r0 + j, end - 1), 0);
         }
     };
 

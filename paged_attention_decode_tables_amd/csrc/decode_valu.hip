@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
         const int n = (int)((wend - c0) < kWave ? (wend - c0) : kWave);
         // ---- scores: lane <-> token (clamped to a valid token for the load)
         const int64_t t = c0 + (lane < n ? lane : n - 1);
-        const KT* kp = kc + token_block(row, sb, t, bs_shift) * p.k_sb + (t & (bs - 1)) * X;
+        const KT* kp = kc + page_of(row, sb, t, bs_shift) * p.k_sb + slot_of(t, bs_shift) * X;
         float dot = 0.0f;
 #pragma unroll 8
         for (int c = 0; c < D / X; ++c) {
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
                 for (int v = 0; v < nv; v += 2) {
                     const bool two = v + 1 < nv;
                     const int64_t tv0 = c0 + v * VT, tv1 = two ? tv0 + VT : tv0;
-                    const KT* vp0 = vc + token_block(row, sb, tv0, bs_shift) * p.v_sb + (tv0 & (bs - 1));
-                    const KT* vp1 = vc + token_block(row, sb, tv1, bs_shift) * p.v_sb + (tv1 & (bs - 1));
+                    const KT* vp0 = vc + page_of(row, sb, tv0, bs_shift) * p.v_sb + slot_of(tv0, bs_shift);
+                    const KT* vp1 = vc + page_of(row, sb, tv1, bs_shift) * p.v_sb + slot_of(tv1, bs_shift);
                     u32x4 va[DVR], vb[DVR];
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
                 // small blocks: one token at a time, one element per row
                 for (int j = 0; j < n; ++j) {
                     const int64_t tj = c0 + j;
-                    const KT* vp = vc + token_block(row, sb, tj, bs_shift) * p.v_sb + (tj & (bs - 1));
+                    const KT* vp = vc + page_of(row, sb, tj, bs_shift) * p.v_sb + slot_of(tj, bs_shift);
                     const float pj = p_lds[j];
 #pragma unroll
                     for (int r = 0; r < DVR; ++r) acc[r] += pj * to_f32(vp[(int64_t)(lane + kWave * r) * bs]);
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
             // page size 1: lane <-> values [lane*DVR, lane*DVR + DVR) of each row
             for (int j = 0; j < n; ++j) {
                 const int64_t tj = c0 + j;
-                const KT* vp = vc + token_block(row, sb, tj, 0) * p.v_sb + lane * DVR;
+                const KT* vp = vc + (int64_t)page_of(row, sb, tj, 0) * p.v_sb + lane * DVR;
                 const float pj = p_lds[j];
                 if constexpr (DVR * KE::size == 16) {
                     const u32x4 vv = STREAM ? load16_stream(vp) : load16(vp);

@@ -159,7 +159,8 @@ hipError_t launch_num_kv_splits(int32_t* out, const int32_t* seq_lens, int num_s
 }
 
 // ---------------------------------------------------------------------------
-// Token offsets through the same address helper the decode kernels use.
+// Token offsets through page_of / slot_of, the functions every decode
+// kernel uses to find a token's block and slot.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_token_offsets(int64_t* __restrict__ out, int64_t out_ss,
                                                        PageList pl,

@@ -89,6 +89,19 @@ struct SpecTableParams {
     int bs, len_a, len_b, draft_tokens, col_blocks;
 };
 
+// Read-stream probe parameters (validated copy of pa_read_probe's).
+struct ProbeParams {
+    const char* base0;
+    const char* base1;  // optional
+    const int32_t* pages;
+    int64_t num_pages;
+    int64_t page_stride, run_stride;  // bytes
+    int runs_per_page;
+    int pieces;  // 16-byte pieces per run
+    uint32_t* sink;
+};
+hipError_t launch_read_probe(const ProbeParams& p, int workgroups, hipStream_t st);
+
 // Message returned by pa_last_error() on this thread.
 void set_last_error(const char* msg);
 

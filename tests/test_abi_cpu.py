@@ -2,6 +2,7 @@
 include/pagedattn.h declares, its argument blocks have the header's layout,
 and invalid arguments are rejected on the host before any launch."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -16,10 +17,12 @@ HEADER = os.path.join(ROOT, "include", "pagedattn.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
-    return sorted(set(names))
+    """Functions declared in every public header (include/*.h)."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -414,3 +417,18 @@ def test_static_scratch_entry_rejects_on_the_host(lib):
     a.num_seqs = 0
     assert lib.paged_attn_decode_static(ctypes.byref(a), None, 0, 0, api.PA_F32, None) == api.PA_OK
     assert lib.paged_attn_decode_static(None, None, 0, 0, api.PA_F32, None) == api.PA_EINVAL
+
+
+def test_read_probe_rejects_on_the_host(lib):
+    f = lib.pa_read_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p]
+    assert f(FAKE, None, FAKE, 10, 1, 4096, 0, 4008, FAKE, 4, None) == api.PA_EINVAL  # run not 16k
+    assert f(FAKE, None, FAKE, 10, 1, 4096, 0, 16384, FAKE, 4, None) == api.PA_EINVAL  # run > 8 KB
+    assert f(FAKE, None, FAKE, 10, 0, 4096, 0, 4096, FAKE, 4, None) == api.PA_EINVAL  # no runs
+    assert f(FAKE, None, FAKE, 10, 1, 4100, 0, 4096, FAKE, 4, None) == api.PA_EINVAL  # stride
+    assert f(FAKE + 8, None, FAKE, 10, 1, 4096, 0, 4096, FAKE, 4, None) == api.PA_EINVAL  # alignment
+    assert f(None, None, FAKE, 10, 1, 4096, 0, 4096, FAKE, 4, None) == api.PA_EINVAL  # no base
+    assert f(FAKE, None, FAKE, 10, 1, 4096, 0, 4096, FAKE, 0, None) == api.PA_EINVAL  # no workgroups
+    assert b"pa_read_probe" in lib.pa_last_error()
