@@ -69,7 +69,8 @@ def kernel_source_hash(kind: str) -> str:
 class Step:
     """Device buffers and the launches of one decode step."""
 
-    def __init__(self, w: workloads.Workload, out_dtype=torch.bfloat16, balanced_workers=0):
+    def __init__(self, w: workloads.Workload, out_dtype=torch.bfloat16, balanced_workers=0,
+                 tmp_dtype=torch.float32):
         self.w = w
         self.g = g = w.to("cuda")
         self.ns = None
@@ -86,7 +87,7 @@ class Step:
             self.indptr = w.cu_num_blocks.to("cuda")
             self.flat = torch.empty(int(w.cu_num_blocks[-1]), dtype=torch.int32, device="cuda")
         S, H, Dv = w.num_seqs * w.num_group, w.num_heads, w.v_head_size  # query rows
-        self.tmp = torch.empty((S, H, self.max_parts, Dv), dtype=torch.float32, device="cuda")
+        self.tmp = torch.empty((S, H, self.max_parts, Dv), dtype=tmp_dtype, device="cuda")
         self.ml = torch.empty((S, H, self.max_parts), dtype=torch.float32, device="cuda")
         self.es = torch.empty((S, H, self.max_parts), dtype=torch.float32, device="cuda")
         self.out = torch.empty((S, H, Dv), dtype=out_dtype, device="cuda")
@@ -411,6 +412,9 @@ def main():
     ap.add_argument("--kv-cache", choices=("same", "fp8"), default="same",
                     help="fp8: the same workload with FP8 E4M3 caches (configs 2-4)")
     ap.add_argument("--alibi", action="store_true", help="the same workload with ALiBi slopes")
+    ap.add_argument("--tmp-dtype", choices=("query", "f32"), default="query",
+                    help="element type of the split-output workspace: the query's type (phase 1 "
+                         "stores each split's output converted to it) or fp32")
     ap.add_argument("--num-group", type=int, default=1,
                     help="query tokens per sequence (configs 2-5): each attends over the whole "
                          "sequence; the grouped-head kernel reads the cache once for all of them")
@@ -450,7 +454,8 @@ def main():
     # with balanced splits, one token range per compute unit.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     workers = cus if (kind == "mla" and not args.fixed_splits) else 0
-    step = Step(w, balanced_workers=workers)
+    tmp_dtype = w.dtype if args.tmp_dtype == "query" else torch.float32
+    step = Step(w, balanced_workers=workers, tmp_dtype=tmp_dtype)
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup}")
@@ -553,6 +558,8 @@ def main():
                    "kv_cache": (f"fp8 e4m3, k_scale = v_scale = {w.k_scale}" if w.kv_dtype is not None
                                 else "query dtype"),
                    "alibi": w.alibi_slopes is not None, "num_group": w.num_group,
+                   "split_workspace": {torch.bfloat16: "bf16", torch.float16: "f16",
+                                       torch.float32: "f32"}[tmp_dtype],
                    "query_tokens_per_s": round(w.num_seqs * w.num_group / (ms_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

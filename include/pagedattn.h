@@ -112,8 +112,8 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
  *     (and every output) keeps dtype.
  */
 typedef struct pa_decode_args {
-    /* outputs: fp32 workspaces */
-    float* tmp_output;           /* [num_seqs, num_heads, max_num_parts, v_head_size] */
+    /* outputs: workspaces (tmp_output of tmp_dtype, the statistics fp32) */
+    void* tmp_output;            /* [num_seqs, num_heads, max_num_parts, v_head_size] */
     int64_t tmp_stride_s, tmp_stride_h, tmp_stride_p, tmp_stride_d; /* stride_d must be 1 */
     float* exp_sums;             /* [num_seqs, num_heads, max_num_parts] */
     float* max_logits;           /* same shape and strides as exp_sums */
@@ -169,6 +169,11 @@ typedef struct pa_decode_args {
     float k_scale, v_scale;      /* fp8 caches only; must be finite and nonzero */
     int32_t num_group;           /* query tokens per sequence (0 or 1: one); see
                                     "Query groups" */
+    int32_t tmp_dtype;           /* element type of tmp_output: PA_F32 (0, the default),
+                                    PA_F16 or PA_BF16. [PAv2] phase 1 stores the split
+                                    output converted to the workspace's element type;
+                                    16-bit types are rounded to nearest even, which
+                                    halves the workspace traffic of both phases. */
 } pa_decode_args;
 
 #define PA_KERNEL_AUTO 0
@@ -202,7 +207,7 @@ typedef struct pa_reduce_args {
     void* output;                /* [num_seqs, num_heads, v_head_size] of out_dtype */
     int64_t out_stride_s, out_stride_h, out_stride_d;               /* stride_d must be 1 */
     int32_t out_dtype;           /* pa_dtype */
-    const float* tmp_output;
+    const void* tmp_output;      /* of tmp_dtype, as written by paged_attn_decode */
     int64_t tmp_stride_s, tmp_stride_h, tmp_stride_p, tmp_stride_d; /* stride_d must be 1 */
     const float* exp_sums;
     const float* max_logits;
@@ -216,6 +221,8 @@ typedef struct pa_reduce_args {
     int32_t max_num_parts;
     int32_t num_group;           /* as given to paged_attn_decode: output, tmp_output,
                                     max_logits and exp_sums have num_seqs * num_group rows */
+    int32_t tmp_dtype;           /* as given to paged_attn_decode (0: PA_F32); the merge
+                                    itself runs in fp32 */
 } pa_reduce_args;
 
 int paged_attn_reduce(const pa_reduce_args* args, void* stream);
@@ -353,8 +360,9 @@ int prepare_swa_spec_page_table(int32_t* dst, int64_t dst_stride0, int64_t dst_s
  * args is as for paged_attn_decode() except that tmp_output, exp_sums and
  * max_logits must be NULL (their strides are ignored); max_num_parts sizes
  * the partials, which need num_seqs * max(num_group, 1) * num_heads *
- * max_num_parts * (v_head_size + 2) * 4 bytes. More than
- * PA_STATIC_SCRATCH_BYTES returns PA_EINVAL before any work is queued.
+ * max_num_parts * (v_head_size * e + 8) bytes, e = 4 for tmp_dtype PA_F32
+ * and 2 for PA_F16 / PA_BF16. More than PA_STATIC_SCRATCH_BYTES returns
+ * PA_EINVAL before any work is queued.
  * output [num_seqs * max(num_group, 1), num_heads, v_head_size] of out_dtype
  * (f32, f16 or bf16), row strides out_stride_s, out_stride_h, innermost
  * stride 1, receives the merged result of paged_attn_reduce().

@@ -54,7 +54,7 @@ class DecodeArgs(ctypes.Structure):
         ("partition_size", _i32), ("max_num_parts", _i32), ("max_seq_len", _i32),
         ("dtype", _i32), ("kernel_hint", _i32), ("num_workers", _i32),
         ("alibi_slopes", _vp), ("kv_dtype", _i32), ("k_scale", ctypes.c_float),
-        ("v_scale", ctypes.c_float), ("num_group", _i32),
+        ("v_scale", ctypes.c_float), ("num_group", _i32), ("tmp_dtype", _i32),
     ]
 
 
@@ -69,6 +69,7 @@ class ReduceArgs(ctypes.Structure):
         ("seq_lens", _vp), ("num_splits", _vp),
         ("num_seqs", _i32), ("num_heads", _i32), ("v_head_size", _i32),
         ("partition_size", _i32), ("max_num_parts", _i32), ("num_group", _i32),
+        ("tmp_dtype", _i32),
     ]
 
 
@@ -212,7 +213,7 @@ def _decode_args(tmp_output, exp_sums, max_logits, query, key_cache, value_cache
     NB, Hkv, Dx, bs, x = key_cache.shape
     Dv = value_cache.shape[2]
     if max_num_parts is None:
-        _need(tmp_output, "tmp_output", torch.float32, ndim=4)
+        _need(tmp_output, "tmp_output", tuple(_DTYPE), ndim=4)
         P = tmp_output.shape[2]
         _need(tmp_output, "tmp_output", shape=(R, H, P, Dv))
         _need(exp_sums, "exp_sums", torch.float32, shape=(R, H, P))
@@ -232,6 +233,7 @@ def _decode_args(tmp_output, exp_sums, max_logits, query, key_cache, value_cache
     if tmp_output is not None:
         a.tmp_output = _ptr(tmp_output)
         a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
+        a.tmp_dtype = _dtype(tmp_output)
         a.exp_sums = _ptr(exp_sums)
         a.max_logits = _ptr(max_logits)
         if exp_sums.stride() != max_logits.stride():
@@ -275,7 +277,8 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
                       stream=None) -> None:
     """Phase 1: per-split max logits, exp sums and normalised outputs.
 
-    Shapes: tmp_output [S, H, P, Dv] fp32; exp_sums / max_logits [S, H, P]
+    Shapes: tmp_output [S, H, P, Dv] fp32, f16 or bf16 (the split outputs
+    are stored converted to its type); exp_sums / max_logits [S, H, P]
     fp32; query [S, H, D]; key_cache [NB, Hkv, D/x, bs, x]; value_cache
     [NB, Hkv, Dv, bs]; block_tables [S, max_blocks] int32 (or the flat page
     list when kv_indptr is given); seq_lens [S] int32. partition_size=0 with
@@ -301,16 +304,20 @@ def paged_attn_decode_static(output: torch.Tensor, query: torch.Tensor, key_cach
                              kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
                              num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
                              k_scale: float = 1.0, v_scale: float = 1.0, num_group: int = 1,
-                             stream=None) -> None:
+                             tmp_dtype: torch.dtype = torch.float32, stream=None) -> None:
     """Phase 1 and phase 2 in one call with the split partials in the
     library's own device buffer (PA_STATIC_SCRATCH_BYTES per GPU), for
     callers that cannot allocate: output [S * num_group, H, Dv] receives the
     merged result. Arguments as for paged_attn_decode; max_num_parts sizes
-    the partials. Overlapping calls on one GPU race on that buffer."""
+    the partials, tmp_dtype is their element type. Overlapping calls on one
+    GPU race on that buffer."""
     lib = load_library()
     a = _decode_args(None, None, None, query, key_cache, value_cache, block_tables, seq_lens, scale,
                      max_seq_len, partition_size, num_splits, kv_indptr, kernel, num_workers,
                      alibi_slopes, k_scale, v_scale, num_group, stream, max_num_parts=max_num_parts)
+    if tmp_dtype not in _DTYPE:
+        raise TypeError(f"tmp_dtype must be one of {tuple(_DTYPE)}, got {tmp_dtype}")
+    a.tmp_dtype = _DTYPE[tmp_dtype]
     R, H, Dv = query.shape[0], query.shape[1], value_cache.shape[2]
     _need(output, "output", tuple(_DTYPE), shape=(R, H, Dv))
     if Dv > 1 and output.stride(2) != 1:
@@ -326,7 +333,7 @@ def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: 
                       num_group: int = 1, stream=None) -> None:
     """Phase 2: log-sum-exp merge of the splits into output [S * num_group, H, Dv]."""
     lib = load_library()
-    _need(tmp_output, "tmp_output", torch.float32, ndim=4)
+    _need(tmp_output, "tmp_output", tuple(_DTYPE), ndim=4)
     _need(seq_lens, "seq_lens", torch.int32, ndim=1, contiguous=True)
     R, H, P, Dv = tmp_output.shape
     S = seq_lens.shape[0]
@@ -344,6 +351,7 @@ def paged_attn_reduce(output: torch.Tensor, tmp_output: torch.Tensor, exp_sums: 
     a.out_dtype = _dtype(output)
     a.tmp_output = _ptr(tmp_output)
     a.tmp_stride_s, a.tmp_stride_h, a.tmp_stride_p, a.tmp_stride_d = tmp_output.stride()
+    a.tmp_dtype = _dtype(tmp_output)
     a.exp_sums = _ptr(exp_sums)
     a.max_logits = _ptr(max_logits)
     if exp_sums.stride() != max_logits.stride():

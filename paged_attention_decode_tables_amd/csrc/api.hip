@@ -107,6 +107,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     } else {
         parts = a->max_num_parts;
     }
+    if (a->tmp_dtype != PA_F32 && a->tmp_dtype != PA_F16 && a->tmp_dtype != PA_BF16)
+        return fail(PA_EINVAL, "paged_attn_decode: tmp_dtype %d is not PA_F32, PA_F16 or PA_BF16", a->tmp_dtype);
     if (a->num_seqs == 0 || parts == 0) return PA_OK;
     if (!a->tmp_output || !a->exp_sums || !a->max_logits || !a->query || !a->key_cache ||
         !a->value_cache || !a->block_tables || !a->seq_lens)
@@ -136,6 +138,7 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
 
     pa::DecodeParams p{};
     p.tmp = a->tmp_output;
+    p.tmp_dtype = a->tmp_dtype;
     p.tmp_ss = a->tmp_stride_s;
     p.tmp_sh = a->tmp_stride_h;
     p.tmp_sp = a->tmp_stride_p;
@@ -203,6 +206,8 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
     if (!a->num_splits && a->partition_size != 0 && (a->partition_size < 64 || a->partition_size % 64))
         return fail(PA_EINVAL, "paged_attn_reduce: partition_size %d is neither 0 nor a positive multiple of 64",
                     a->partition_size);
+    if (a->tmp_dtype != PA_F32 && a->tmp_dtype != PA_F16 && a->tmp_dtype != PA_BF16)
+        return fail(PA_EINVAL, "paged_attn_reduce: tmp_dtype %d is not PA_F32, PA_F16 or PA_BF16", a->tmp_dtype);
     if (a->num_seqs == 0) return PA_OK;
     if (!a->output || !a->tmp_output || !a->exp_sums || !a->max_logits || !a->seq_lens)
         return fail(PA_EINVAL, "paged_attn_reduce: a required pointer is NULL");
@@ -220,6 +225,7 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
     p.out_ss = a->out_stride_s;
     p.out_sh = a->out_stride_h;
     p.tmp = a->tmp_output;
+    p.tmp_dtype = a->tmp_dtype;
     p.tmp_ss = a->tmp_stride_s;
     p.tmp_sh = a->tmp_stride_h;
     p.tmp_sp = a->tmp_stride_p;

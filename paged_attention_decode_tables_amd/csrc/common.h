@@ -67,6 +67,63 @@ __device__ __forceinline__ float to_f32(__bf16 v)
     return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, v) << 16);
 }
 
+// ---------------------------------------------------------------------------
+// Split partials (tmp_output). Phase 1 stores each split's normalised output
+// converted to the workspace's element type (fp32, or f16 / bf16 rounded to
+// nearest even); the type is uniform across a launch, so the branch on it is
+// a scalar one. Phase 2 reads them back widened to fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 x = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, x);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 x = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, x);
+}
+// four consecutive values at element offset off; NT: nontemporal hint
+template <bool NT = false>
+__device__ __forceinline__ void store_tmp4(void* tmp, int dtype, int64_t off, f32x4 v)
+{
+    if (dtype == PA_F32) {
+        f32x4* at = reinterpret_cast<f32x4*>(tmp) + (off >> 2);
+        if constexpr (NT) __builtin_nontemporal_store(v, at);
+        else *at = v;
+    } else {
+        const u32x2 w = dtype == PA_BF16 ? u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}
+                                         : u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+        u32x2* at = reinterpret_cast<u32x2*>(tmp) + (off >> 2);
+        if constexpr (NT) __builtin_nontemporal_store(w, at);
+        else *at = w;
+    }
+}
+__device__ __forceinline__ void store_tmp1(void* tmp, int dtype, int64_t off, float v)
+{
+    if (dtype == PA_F32)
+        reinterpret_cast<float*>(tmp)[off] = v;
+    else if (dtype == PA_BF16)
+        reinterpret_cast<__bf16*>(tmp)[off] = (__bf16)v;
+    else
+        reinterpret_cast<_Float16*>(tmp)[off] = (_Float16)v;
+}
+// four consecutive partial values of element type E at p (4-element aligned)
+template <class E>
+__device__ __forceinline__ f32x4 load_tmp4(const typename E::storage* p)
+{
+    if constexpr (E::size == 4) {
+        return *reinterpret_cast<const f32x4*>(p);
+    } else {
+        using S = typename E::storage;
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+        auto half = [&](int i) { return to_f32(__builtin_bit_cast(S, (uint16_t)(w[i >> 1] >> (16 * (i & 1))))); };
+        return f32x4{half(0), half(1), half(2), half(3)};
+    }
+}
+
 // Low / high 16-bit halves of a packed dword, widened.
 template <class E> __device__ __forceinline__ float lo16(uint32_t w);
 template <class E> __device__ __forceinline__ float hi16(uint32_t w);

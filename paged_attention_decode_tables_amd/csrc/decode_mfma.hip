@@ -108,16 +108,11 @@ constexpr int kMfmaMaxRun = 4;
 #define PA_MFMA_PERSIST_OCCUPANCY 2
 #endif
 
-// Rows of the split outputs (tmp_output). PA_PARTIAL_NT: with the
+// Rows of the split outputs (tmp_output). PA_PARTIAL_NT: stored with the
 // nontemporal hint.
 #ifndef PA_PARTIAL_NT
 #define PA_PARTIAL_NT 1
 #endif
-__device__ __forceinline__ void store_partial(float* at, f32x4 v)
-{
-    if constexpr (PA_PARTIAL_NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(at));
-    else *reinterpret_cast<f32x4*>(at) = v;
-}
 
 // One run of nrun consecutive splits [part0, part0 + nrun) of sequence s for
 // kv head kvh (the kernel body). L is the sequence length and len64 its split
@@ -450,9 +445,9 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
             const int c = e / NCH, k = e - c * NCH;  // column, piece (dv 4k .. 4k+3)
             const f32x4 v = park[(slot * MT + (k >> 2)) * kWave + 16 * (k & 3) + c];
             const int cq = c / G, ch = c - cq * G;
-            float* o = p.tmp + (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
-                       (int64_t)split * p.tmp_sp + 4 * k;
-            store_partial(o, v);
+            const int64_t o = (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
+                              (int64_t)split * p.tmp_sp + 4 * k;
+            store_tmp4<PA_PARTIAL_NT>(p.tmp, p.tmp_dtype, o, v);
         }
     };
     wave_lds_sync();  // other lanes' parked rows

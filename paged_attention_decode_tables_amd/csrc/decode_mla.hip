@@ -708,8 +708,8 @@ void k_decode_mla(DecodeParams p)
     lds_barrier();
     // lane (hl, c32), register 4i + j of tile (dt, ht) holds value column
     // 32*(NW*dt + wave) + 8i + 4hl + j of head 32ht + c32
-    float* out = p.tmp + (int64_t)(s * p.num_group + qg) * p.tmp_ss + (int64_t)(h0 + c32) * p.tmp_sh +
-                 (int64_t)part * p.tmp_sp + 32 * wave + 4 * hl;
+    const int64_t out = (int64_t)(s * p.num_group + qg) * p.tmp_ss + (int64_t)(h0 + c32) * p.tmp_sh +
+                        (int64_t)part * p.tmp_sp + 32 * wave + 4 * hl;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const float inv = 1.0f / lsum[32 * ht + c32];
@@ -717,8 +717,9 @@ void k_decode_mla(DecodeParams p)
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<f32x4*>(out + (int64_t)(32 * ht) * p.tmp_sh + 32 * NW * dt + 8 * i) =
-                    f32x4{acc[dt][ht][4 * i], acc[dt][ht][4 * i + 1], acc[dt][ht][4 * i + 2], acc[dt][ht][4 * i + 3]} * inv;
+                store_tmp4(p.tmp, p.tmp_dtype, out + (int64_t)(32 * ht) * p.tmp_sh + 32 * NW * dt + 8 * i,
+                           f32x4{acc[dt][ht][4 * i], acc[dt][ht][4 * i + 1], acc[dt][ht][4 * i + 2],
+                                 acc[dt][ht][4 * i + 3]} * inv);
     }
     };
 

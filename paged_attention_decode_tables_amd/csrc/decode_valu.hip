@@ -227,11 +227,11 @@ __global__ __launch_bounds__(64 * NW) void k_decode_valu(DecodeParams p)
         *esp = lsum;
     }
     const float inv = p.v_scale / lsum;
-    float* out = p.tmp + (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp;
+    const int64_t out = (int64_t)s * p.tmp_ss + (int64_t)h * p.tmp_sh + (int64_t)part * p.tmp_sp;
 #pragma unroll
     for (int r = 0; r < DVR; ++r) {
         const int dv = ROWV ? lane * DVR + r : lane + kWave * r;
-        out[dv] = acc[r] * inv;
+        store_tmp1(p.tmp, p.tmp_dtype, out + dv, acc[r] * inv);
     }
 }
 

@@ -12,7 +12,8 @@ namespace pa {
 
 // Phase-1 parameters (validated copy of pa_decode_args).
 struct DecodeParams {
-    float* tmp;
+    void* tmp;         // split outputs, element type tmp_dtype (strides in elements)
+    int tmp_dtype;     // PA_F32, PA_F16 or PA_BF16
     int64_t tmp_ss, tmp_sh, tmp_sp;
     float* exp_sums;
     float* max_logits;
@@ -43,7 +44,8 @@ struct DecodeParams {
 struct ReduceParams {
     void* out;
     int64_t out_ss, out_sh;
-    const float* tmp;
+    const void* tmp;   // element type tmp_dtype
+    int tmp_dtype;
     int64_t tmp_ss, tmp_sh, tmp_sp;
     const float* exp_sums;
     const float* max_logits;

@@ -65,15 +65,18 @@ PA_EXPORT int paged_attn_decode_static(const pa_decode_args* a, void* output, in
     if (a->num_seqs < 0 || a->num_heads < 1 || a->v_head_size < 1 || a->max_num_parts < 1 || a->num_group < 0)
         return fail_static(PA_EINVAL, "num_seqs, num_group >= 0 and num_heads, v_head_size, max_num_parts >= 1 "
                                       "required");
+    if (a->tmp_dtype != PA_F32 && a->tmp_dtype != PA_F16 && a->tmp_dtype != PA_BF16)
+        return fail_static(PA_EINVAL, "tmp_dtype is not PA_F32, PA_F16 or PA_BF16");
+    const int64_t esz = a->tmp_dtype == PA_F32 ? 4 : 2;  // bytes per partial value
     const int64_t rows = (int64_t)a->num_seqs * (a->num_group < 1 ? 1 : a->num_group);
     const int64_t slots = rows * a->num_heads * a->max_num_parts;  // (row, head, split) triples
-    const int64_t bytes = slots * ((int64_t)a->v_head_size + 2) * 4;
+    const int64_t bytes = slots * ((int64_t)a->v_head_size * esz + 8);
     if (bytes > (int64_t)PA_STATIC_SCRATCH_BYTES) {
         char buf[256];
         snprintf(buf, sizeof buf,
-                 "the partials need %lld bytes (rows %lld x heads %d x splits %d x (v_head_size %d + 2) x 4), "
+                 "the partials need %lld bytes (rows %lld x heads %d x splits %d x (v_head_size %d x %d + 8)), "
                  "more than the %lld-byte scratch buffer",
-                 (long long)bytes, (long long)rows, a->num_heads, a->max_num_parts, a->v_head_size,
+                 (long long)bytes, (long long)rows, a->num_heads, a->max_num_parts, a->v_head_size, (int)esz,
                  (long long)PA_STATIC_SCRATCH_BYTES);
         return fail_static(PA_EINVAL, buf);
     }
@@ -91,9 +94,11 @@ PA_EXPORT int paged_attn_decode_static(const pa_decode_args* a, void* output, in
     const int rc = scratch_on(dev, &base);
     if (rc != PA_OK) return fail_static(rc, "cannot look up the scratch buffer on the stream's device");
 
-    // partials, contiguous: tmp [rows, H, P, Dv], then max_logits and exp_sums [rows, H, P]
-    float* tmp = static_cast<float*>(base);
-    float* ml = tmp + slots * a->v_head_size;
+    // partials, contiguous: tmp [rows, H, P, Dv] of tmp_dtype, then max_logits
+    // and exp_sums [rows, H, P] (every supported v_head_size is a multiple
+    // of 64, so both start 128-byte aligned; others are rejected by phase 1)
+    char* tmp = static_cast<char*>(base);
+    float* ml = reinterpret_cast<float*>(tmp + slots * a->v_head_size * esz);
     float* es = ml + slots;
     pa_decode_args d = *a;
     d.tmp_output = tmp;
@@ -132,6 +137,7 @@ PA_EXPORT int paged_attn_decode_static(const pa_decode_args* a, void* output, in
     q.partition_size = a->partition_size;
     q.max_num_parts = a->max_num_parts;
     q.num_group = a->num_group;
+    q.tmp_dtype = a->tmp_dtype;
     r = paged_attn_reduce(&q, stream);
     return r == PA_OK ? r : fail_static(r, pa_last_error());
 }

@@ -36,7 +36,7 @@ constexpr int kRedBatch = 8;  // splits per thread per round of loads (at most)
 // workgroups (split counts: 8192 one-wave workgroups on the skewed batch).
 template <int DV, int NG> constexpr int red_heads() { return kRedMaxThreads / (DV / 4 * NG) > 0 ? kRedMaxThreads / (DV / 4 * NG) : 1; }
 
-template <class OutE, int DV, int NG, int RB>
+template <class OutE, class TmpE, int DV, int NG, int RB>
 __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C * NG * HPW = 256
 {
     constexpr int C = DV / 4;             // threads per row (float4 columns)
@@ -58,7 +58,8 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
 
     const float* ml = p.max_logits + (int64_t)row * p.ml_ss + (int64_t)h * p.ml_sh;
     const float* es = p.exp_sums + (int64_t)row * p.ml_ss + (int64_t)h * p.ml_sh;
-    const float* tmp = p.tmp + (int64_t)row * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
+    using TT = typename TmpE::storage;
+    const TT* tmp = reinterpret_cast<const TT*>(p.tmp) + (int64_t)row * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
 
     const int L = p.seq_lens[s];
     // balanced splits (partition_size 0): every slot, empty ones skipped below
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
         for (int r = 0; r < RB; ++r) {
             const int64_t q = q0 + (int64_t)r * NG;
             if (q < p.max_num_parts) {
-                rows[r] = *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp);
+                rows[r] = load_tmp4<TmpE>(tmp + q * p.tmp_sp);
                 mv[r] = ml[q];
                 lv[r] = es[q];
             } else {
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
             for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 if (q < n) {
-                    rows[r] = *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp);
+                    rows[r] = load_tmp4<TmpE>(tmp + q * p.tmp_sp);
                     mv[r] = ml[q];
                     lv[r] = es[q];
                 } else {
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
-                rows[r] = mv[r] != -INFINITY ? *reinterpret_cast<const f32x4*>(tmp + q * p.tmp_sp)
+                rows[r] = mv[r] != -INFINITY ? load_tmp4<TmpE>(tmp + q * p.tmp_sp)
                                              : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -217,18 +218,18 @@ static int reduce_groups(int Dv, int max_parts)
     return ng;
 }
 
-template <class OutE, int DV, int NG>
+template <class OutE, class TmpE, int DV, int NG>
 static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
 {
     constexpr int HPW = red_heads<DV, NG>();
     const int64_t hblocks = (p.num_heads + HPW - 1) / HPW;
     const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * hblocks)), block(DV / 4 * NG * HPW);
     const bool few = p.num_splits || p.partition_size == 0 || (p.max_num_parts + NG - 1) / NG <= 4;
-    if (few) hipLaunchKernelGGL((k_reduce<OutE, DV, NG, 4>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_reduce<OutE, DV, NG, kRedBatch>), grid, block, 0, st, p);
+    if (few) hipLaunchKernelGGL((k_reduce<OutE, TmpE, DV, NG, 4>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((k_reduce<OutE, TmpE, DV, NG, kRedBatch>), grid, block, 0, st, p);
 }
 
-template <class OutE, int DV>
+template <class OutE, class TmpE, int DV>
 static void launch_reduce_dv(const ReduceParams& p, hipStream_t st)
 {
     constexpr int C = DV / 4, LO = C >= 64 ? 1 : 64 / C, HI = kRedMaxThreads / C;
@@ -236,30 +237,41 @@ static void launch_reduce_dv(const ReduceParams& p, hipStream_t st)
     // sequences have a few splits; smaller workgroups keep every one resident)
     const bool few = p.num_splits || p.partition_size == 0;
     const int ng = few ? LO : reduce_groups(DV, p.max_num_parts);
-    if (ng <= LO) launch_reduce_ng<OutE, DV, LO>(p, st);
-    else if (ng <= 2 * LO || 2 * LO > HI) launch_reduce_ng<OutE, DV, (2 * LO <= HI ? 2 * LO : HI)>(p, st);
-    else launch_reduce_ng<OutE, DV, HI>(p, st);
+    if (ng <= LO) launch_reduce_ng<OutE, TmpE, DV, LO>(p, st);
+    else if (ng <= 2 * LO || 2 * LO > HI) launch_reduce_ng<OutE, TmpE, DV, (2 * LO <= HI ? 2 * LO : HI)>(p, st);
+    else launch_reduce_ng<OutE, TmpE, DV, HI>(p, st);
 }
 
-template <class OutE>
+template <class OutE, class TmpE>
 static hipError_t launch_reduce_t(const ReduceParams& p, int Dv, hipStream_t st)
 {
     switch (Dv) {
-    case 64: launch_reduce_dv<OutE, 64>(p, st); break;
-    case 128: launch_reduce_dv<OutE, 128>(p, st); break;
-    case 256: launch_reduce_dv<OutE, 256>(p, st); break;
-    case 512: launch_reduce_dv<OutE, 512>(p, st); break;
+    case 64: launch_reduce_dv<OutE, TmpE, 64>(p, st); break;
+    case 128: launch_reduce_dv<OutE, TmpE, 128>(p, st); break;
+    case 256: launch_reduce_dv<OutE, TmpE, 256>(p, st); break;
+    case 512: launch_reduce_dv<OutE, TmpE, 512>(p, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <class OutE>
+static hipError_t launch_reduce_o(const ReduceParams& p, int Dv, hipStream_t st)
+{
+    switch (p.tmp_dtype) {
+    case PA_F32: return launch_reduce_t<OutE, F32>(p, Dv, st);
+    case PA_F16: return launch_reduce_t<OutE, F16>(p, Dv, st);
+    case PA_BF16: return launch_reduce_t<OutE, BF16>(p, Dv, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_reduce(const ReduceParams& p, int out_dtype, int Dv, hipStream_t st)
 {
     switch (out_dtype) {
-    case PA_F32: return launch_reduce_t<F32>(p, Dv, st);
-    case PA_F16: return launch_reduce_t<F16>(p, Dv, st);
-    case PA_BF16: return launch_reduce_t<BF16>(p, Dv, st);
+    case PA_F32: return launch_reduce_o<F32>(p, Dv, st);
+    case PA_F16: return launch_reduce_o<F16>(p, Dv, st);
+    case PA_BF16: return launch_reduce_o<BF16>(p, Dv, st);
     default: return hipErrorInvalidValue;
     }
 }

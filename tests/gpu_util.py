@@ -58,10 +58,17 @@ def tolerances(w: workloads.Workload, kernel: str = "auto"):
     return ATOL[w.dtype], LTOL[w.dtype]
 
 
-def workspace(w: workloads.Workload, max_parts: int, device=DEV):
+# Split outputs stored in a 16-bit workspace are rounded to nearest even:
+# relative error at most half an ulp (2^-9 bf16, 2^-11 f16). Phase 2 forms a
+# convex combination of the stored rows, so the merged output moves by at
+# most that much of the largest stored value.
+TMP_HALF_ULP = {torch.float32: 0.0, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -9}
+
+
+def workspace(w: workloads.Workload, max_parts: int, device=DEV, tmp_dtype=torch.float32):
     S, H, Dv = w.num_seqs * w.num_group, w.num_heads, w.v_head_size
     nan = float("nan")
-    tmp = torch.full((S, H, max_parts, Dv), nan, dtype=torch.float32, device=device)
+    tmp = torch.full((S, H, max_parts, Dv), nan, dtype=tmp_dtype, device=device)
     ml = torch.full((S, H, max_parts), nan, dtype=torch.float32, device=device)
     es = torch.full((S, H, max_parts), nan, dtype=torch.float32, device=device)
     return tmp, ml, es
@@ -72,12 +79,13 @@ def max_parts_for(w: workloads.Workload, partition_size: int) -> int:
 
 
 def run_gpu(w: workloads.Workload, *, partition_size=512, num_splits=None, max_parts=None,
-            kernel="auto", out_dtype=torch.float32, csr=False, block_tables=None):
+            kernel="auto", out_dtype=torch.float32, csr=False, block_tables=None,
+            tmp_dtype=torch.float32):
     """Phase 1 + phase 2 on the GPU. Returns (out, tmp, ml, es) on the CPU."""
     g = w.to(DEV)
     if max_parts is None:
         max_parts = max_parts_for(w, partition_size) if num_splits is None else 32
-    tmp, ml, es = workspace(w, max_parts)
+    tmp, ml, es = workspace(w, max_parts, tmp_dtype=tmp_dtype)
     ns = None if num_splits is None else torch.as_tensor(num_splits, dtype=torch.int32, device=DEV)
     R = w.num_seqs * w.num_group  # query rows
     bt = g.block_tables if block_tables is None else block_tables.to(DEV)
@@ -145,7 +153,7 @@ def check_partials(w, orc, tmp, ml, es, *, partition_size=512, num_splits=None, 
         el = np.abs(ge[:, :n] / oes[i, :, :n] - 1.0)
         bound = ltol + 2.0 * 2.0 ** -23 * np.abs(oml[i, :, :n])
         assert (el <= bound).all(), (s, el.max(), float((el - bound).max()))
-        et = np.abs(gt[:, :n] - otmp[i, :, :n])
+        et = np.abs(gt[:, :n] - otmp[i, :, :n]) - TMP_HALF_ULP[tmp.dtype] * np.abs(otmp[i, :, :n])
         assert et.max() <= atol, (s, et.max())
 
 
@@ -153,19 +161,25 @@ def subset(w: workloads.Workload, seqs) -> workloads.Workload:
     return w.subset(seqs)
 
 
-def check_output(w, orc, out, seqs=None, kernel="auto"):
-    """Compare final outputs (any dtype) with the oracle's attention."""
+def check_output(w, orc, out, seqs=None, kernel="auto", tmp=None):
+    """Compare final outputs (any dtype) with the oracle's attention. tmp:
+    the 16-bit workspace the output was merged from (its rounding bound is
+    added: half an ulp of the largest stored value of each (row, head))."""
     idx = list(range(w.num_seqs)) if seqs is None else list(seqs)
     sub = w if seqs is None else subset(w, idx)
     ref = orc.attention(*oracle_args(sub), **oracle_kw(sub))
     got = out[idx].double().numpy()
     tol = tolerances(w, kernel)[0]
+    if tmp is not None and TMP_HALF_ULP[tmp.dtype] > 0:
+        rows = [r for s in idx for r in range(s * w.num_group, (s + 1) * w.num_group)]
+        t = tmp[rows].double().abs().nan_to_num(0.0).amax(dim=(2, 3)).numpy()  # [rows, H]
+        tol = tol + TMP_HALF_ULP[tmp.dtype] * t.reshape(got.shape[0], got.shape[1], 1)
     if out.dtype == torch.float32:
         err = np.abs(got - ref)
-        assert err.max() <= tol, err.max()
+        assert np.all(err <= tol), float(np.max(err - tol))
     else:
         # output rounded to a 16-bit type: allow its half ulp on top
         half_ulp = 2.0 ** (-8 if out.dtype == torch.bfloat16 else -10)
         err = np.abs(got - ref) - half_ulp * np.abs(ref)
-        assert err.max() <= tol, err.max()
+        assert np.all(err <= tol), float(np.max(err - tol))
     return float(np.abs(got - ref).max())

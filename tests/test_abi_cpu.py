@@ -132,6 +132,8 @@ DECODE_BAD = [
     ("neg_seqs", dict(num_seqs=-1), api.PA_EINVAL),
     ("neg_num_group", dict(num_group=-1), api.PA_EINVAL),
     ("grid_rows", dict(num_group=1 << 27), api.PA_ENOTSUP),
+    ("tmp_dtype_fp8", dict(tmp_dtype=api.PA_FP8_E4M3), api.PA_EINVAL),
+    ("tmp_dtype_neg", dict(tmp_dtype=-1), api.PA_EINVAL),
 ]
 
 
@@ -236,6 +238,7 @@ REDUCE_BAD = [
     ("inner", dict(out_stride_d=2), api.PA_ENOTSUP),
     ("tmp_align", dict(tmp_stride_p=130), api.PA_ENOTSUP),
     ("neg_num_group", dict(num_group=-1), api.PA_EINVAL),
+    ("tmp_dtype", dict(tmp_dtype=9), api.PA_EINVAL),
 ]
 
 
@@ -336,7 +339,7 @@ def _bad_decode(**change):
 @pytest.mark.parametrize("name,change,exc", [
     ("seq_lens_int64", dict(seq_lens=torch.ones(3, dtype=torch.int64)), TypeError),
     ("seq_lens_sliced", dict(seq_lens=torch.ones(6, dtype=torch.int32)[::2]), ValueError),
-    ("workspace_bf16", dict(tmp_output=torch.zeros(3, 8, 2, 128, dtype=torch.bfloat16)), TypeError),
+    ("workspace_int32", dict(tmp_output=torch.zeros(3, 8, 2, 128, dtype=torch.int32)), TypeError),
     ("workspace_short", dict(tmp_output=torch.zeros(3, 8, 2, 64)), ValueError),
     ("exp_sums_shape", dict(exp_sums=torch.zeros(3, 8, 1)), ValueError),
     ("max_logits_f16", dict(max_logits=torch.zeros(3, 8, 2, dtype=torch.float16)), TypeError),
@@ -371,7 +374,7 @@ def test_binding_rejects_reduce():
                         (dict(output=torch.zeros(3, 8, 128, dtype=torch.int32)), TypeError),
                         (dict(exp_sums=torch.zeros(3, 8, 2, dtype=torch.float64)), TypeError),
                         (dict(seq_lens=torch.ones(3, dtype=torch.int64)), TypeError),
-                        (dict(tmp_output=torch.zeros(3, 8, 2, 128, dtype=torch.bfloat16)), TypeError),
+                        (dict(tmp_output=torch.zeros(3, 8, 2, 128, dtype=torch.int16)), TypeError),
                         ({}, ValueError)):
         with pytest.raises(exc):
             api.paged_attn_reduce(**{**ok, **change})
@@ -417,6 +420,15 @@ def test_static_scratch_entry_rejects_on_the_host(lib):
     a.num_seqs = 0
     assert lib.paged_attn_decode_static(ctypes.byref(a), None, 0, 0, api.PA_F32, None) == api.PA_OK
     assert lib.paged_attn_decode_static(None, None, 0, 0, api.PA_F32, None) == api.PA_EINVAL
+    # 16-bit partials: sized at 2 bytes a value (+ 8 for the statistics)
+    a = good_decode()
+    a.tmp_output = a.exp_sums = a.max_logits = None
+    a.max_num_parts, a.tmp_dtype = 1 << 20, api.PA_BF16
+    assert lib.paged_attn_decode_static(ctypes.byref(a), FAKE, 1024, 128, api.PA_F32, None) == api.PA_EINVAL
+    msg = lib.pa_last_error().decode()
+    assert "x 2 + 8" in msg and str(a.num_seqs * a.num_heads * (1 << 20) * (128 * 2 + 8)) in msg, msg
+    a.tmp_dtype = 7
+    assert lib.paged_attn_decode_static(ctypes.byref(a), FAKE, 1024, 128, api.PA_F32, None) == api.PA_EINVAL
 
 
 def test_read_probe_rejects_on_the_host(lib):

@@ -36,7 +36,7 @@ def _csr(w):
 
 
 def _both(w, *, max_parts, partition_size=512, num_splits=None, csr=False, workers=0,
-          out_dtype=torch.float32):
+          out_dtype=torch.float32, tmp_dtype=torch.float32):
     """(static-scratch output, workspace-path output) on the same inputs."""
     g = w.to(DEV)
     bt, indptr = _csr(w) if csr else (g.block_tables, None)
@@ -47,8 +47,8 @@ def _both(w, *, max_parts, partition_size=512, num_splits=None, csr=False, worke
               num_group=w.num_group)
     out_s = torch.full((R, w.num_heads, w.v_head_size), float("nan"), dtype=out_dtype, device=DEV)
     pad.paged_attn_decode_static(out_s, g.query, g.key_cache, g.value_cache, bt, g.seq_lens, w.scale,
-                                 w.max_seq_len, max_num_parts=max_parts, **kw)
-    tmp, ml, es = workspace(w, max_parts)
+                                 w.max_seq_len, max_num_parts=max_parts, tmp_dtype=tmp_dtype, **kw)
+    tmp, ml, es = workspace(w, max_parts, tmp_dtype=tmp_dtype)
     pad.paged_attn_decode(tmp, es, ml, g.query, g.key_cache, g.value_cache, bt, g.seq_lens, w.scale,
                           w.max_seq_len, **kw)
     out_w = torch.full_like(out_s, float("nan"))
@@ -58,10 +58,10 @@ def _both(w, *, max_parts, partition_size=512, num_splits=None, csr=False, worke
     return out_s.cpu(), out_w.cpu()
 
 
-def _check_pair(w, orc, out_s, out_w):
+def _check_pair(w, orc, out_s, out_w, tmp=None):
     assert torch.isfinite(out_s).all()
     assert torch.equal(out_s, out_w)
-    check_output(w.expanded() if w.num_group > 1 else w, orc, out_s)
+    check_output(w.expanded() if w.num_group > 1 else w, orc, out_s, tmp=tmp)
 
 
 def test_static_fixed_splits_grouped_heads(orc):
@@ -110,6 +110,23 @@ def test_static_latent_rows_balanced(orc):
     out_s, out_w = _both(w2, max_parts=1, csr=True, out_dtype=torch.bfloat16)
     assert torch.equal(out_s, out_w)
     check_output(w2, orc, out_s)
+
+
+def test_static_16bit_partials(orc):
+    """Split outputs in bf16 (then f16, on a smaller batch) in the library's
+    buffer: bit-identical to the workspace path with the same element type."""
+    for w, tdt, kw in (
+            (workloads.mla_custom(seed=708, seq_lens=[2500, 3, 900], num_heads=128, poison=True),
+             torch.bfloat16, dict(max_parts=8, partition_size=0, csr=True, workers=12)),
+            (workloads.custom(seed=709, seq_lens=[1500, 7], num_heads=16, num_kv_heads=2, head_size=128,
+                              block_size=16, dtype="f16", poison=True),
+             torch.float16, dict(max_parts=3))):
+        say(f"static scratch: {tdt} partials, {w.num_seqs} seqs")
+        out_s, out_w = _both(w, tmp_dtype=tdt, **kw)
+        assert torch.isfinite(out_s).all() and torch.equal(out_s, out_w)
+        # bound: the 16-bit rounding of every stored value (at most |v| <= max|V|)
+        bound = np.abs(w.value_cache.float().numpy()).max()
+        check_output(w, orc, out_s, tmp=torch.full((w.num_seqs, w.num_heads, 1, 1), float(bound), dtype=tdt))
 
 
 def test_static_rejects_oversized_partials():
