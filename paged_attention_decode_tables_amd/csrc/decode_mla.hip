@@ -311,6 +311,123 @@ template <int HT, int DT> struct PvSchedule {
     static constexpr int wait(int m) { return ops_through(issued(m)) - ops_through(need(m)); }
 };
 
+// ---- balanced splits: the sequences' tokens in sequence order, each
+// non-empty sequence preceded by kMlaPieceCharge virtual tokens (the cost of
+// starting a piece: loading its query and the first chunks, storing its
+// partial output), total T'; worker w = blockIdx.x takes virtual positions
+// [w*U, (w+1)*U), so a worker that starts a sequence inside its range gets
+// that many fewer real tokens. piece(s, slot, start, end) runs one piece of
+// sequence s for the workgroup's GH heads h0 .. h0+GH-1 (query token qg).
+template <int NW, class Piece>
+__device__ __forceinline__ void mla_balanced(const DecodeParams& p, const int qg, const int h0, const int GH,
+                                             Piece&& piece)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    constexpr int BT = 64 * NW;
+    constexpr int C = kMlaPieceCharge;
+    __shared__ int64_t bal_w64[NW];
+    __shared__ int bal_w32[NW];
+    __shared__ int64_t bal_off[BT];
+    __shared__ int bal_len[BT];
+    __shared__ int bal_first, bal_last;
+    const int tid = threadIdx.x;
+    const int w = blockIdx.x;
+    // m = -inf, l = 0 in slots [k0, max_num_parts) of sequence s, all heads
+    // here (all threads of the workgroup together)
+    auto mark_empty = [&](int s, int k0) {
+        for (int e = tid; e < GH * (p.max_num_parts - k0); e += BT) {
+            const int64_t off = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + k0 + e / GH;
+            p.max_logits[off] = -INFINITY;
+            p.exp_sums[off] = 0.0f;
+        }
+    };
+
+    // With at most BT sequences every thread loads its length once and keeps
+    // it for the scan below (one memory round trip for the whole schedule).
+    const bool one_round = p.num_seqs <= BT;
+    int Lmine = 0;
+    int64_t tsum = 0;
+    int tmax = 0;
+    for (int i = tid; i < p.num_seqs; i += BT) {
+        const int Li = max(p.seq_lens[i], 0);
+        if (i == tid) Lmine = Li;
+        tsum += Li > 0 ? Li + C : 0;
+        tmax = max(tmax, Li);
+        if (w == 0 && Li == 0) {  // worker 0 covers the empty sequences, one thread each
+            for (int e = 0; e < GH * p.max_num_parts; ++e) {
+                const int64_t off = (int64_t)(i * p.num_group + qg) * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + e / GH;
+                p.max_logits[off] = -INFINITY;
+                p.exp_sums[off] = 0.0f;
+            }
+        }
+    }
+    tsum = __shfl(wave_incl_sum_i64(tsum, lane), kWave - 1, kWave);
+    tmax = wave_max_i32(tmax);
+    if (lane == 0) {
+        bal_w64[wave] = tsum;
+        bal_w32[wave] = tmax;
+    }
+    lds_barrier();
+    int64_t total_virtual = 0;
+    int maxL = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        total_virtual += bal_w64[i];
+        maxL = max(maxL, bal_w32[i]);
+    }
+    total_virtual = uniform_i64(total_virtual);
+    maxL = __builtin_amdgcn_readfirstlane(maxL);
+    lds_barrier();  // bal_w64 is reused by the scan below
+    const int64_t W = p.num_workers;
+    int64_t U = max((total_virtual + W - 1) / W, ((int64_t)maxL + p.max_num_parts - 2) / (p.max_num_parts - 1));
+    U = max((U + 31) & ~int64_t(31), int64_t(32));
+    if (total_virtual == 0 || (int64_t)w * U >= total_virtual) return;
+    const int64_t r0 = (int64_t)w * U, r1 = min(r0 + U, total_virtual);
+
+    // sequences in batches of BT: a block scan of the virtual lengths gives
+    // their virtual offsets; the ones meeting [r0, r1) form a contiguous run
+    int64_t base = 0;
+    for (int b0 = 0; b0 < p.num_seqs && base < r1; b0 += BT) {
+        const int i = b0 + tid;
+        const int Li = one_round ? Lmine : (i < p.num_seqs ? max(p.seq_lens[i], 0) : 0);
+        const int Vi = Li > 0 ? Li + C : 0;
+        const int64_t inc = wave_incl_sum_i64(Vi, lane);
+        if (lane == kWave - 1) bal_w64[wave] = inc;
+        if (tid == 0) {
+            bal_first = BT;
+            bal_last = -1;
+        }
+        lds_barrier();
+        int64_t off = base + inc - Vi + C, total = 0;  // virtual position of the sequence's first token
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if (j < wave) off += bal_w64[j];
+            total += bal_w64[j];
+        }
+        bal_off[tid] = off;
+        bal_len[tid] = Li;
+        if (Li > 0 && off < r1 && off + Li > r0) {
+            atomicMin(&bal_first, tid);
+            atomicMax(&bal_last, tid);
+        }
+        lds_barrier();
+        const int first = __builtin_amdgcn_readfirstlane(bal_first);
+        const int last = __builtin_amdgcn_readfirstlane(bal_last);
+        total = uniform_i64(total);
+        for (int j = first; j <= last; ++j) {
+            const int64_t so = uniform_i64(bal_off[j]);
+            const int Ls = __builtin_amdgcn_readfirstlane(bal_len[j]);
+            if (Ls <= 0) continue;
+            const int k = (int)(w - so / U);
+            piece(b0 + j, k, (int)(max(r0, so) - so), (int)(min(r1, so + Ls) - so));
+            if ((so + Ls - 1) / U == w) mark_empty(b0 + j, k + 1);  // this worker has the last piece
+        }
+        base += total;
+        lds_barrier();  // bal_* are rewritten by the next batch
+    }
+}
+
 // ALIBI: scores carry the slopes' bias (a separate instance, so the plain
 // kernel keeps its registers).
 // BAL = false: one workgroup per (seq, kv head, split) of the fixed or
@@ -454,7 +571,19 @@ void k_decode_mla(DecodeParams p)
     // of exp(z - max). p is rounded to the cache type before the P.V product,
     // so the headroom must keep 2^kHeadroom finite there: bf16 reaches 2^127,
     // f16 only 65504 < 2^16 (2^16 would round to +inf).
+    //
+    // ALiBi (bf16): the bias slope * position grows along the split, by at
+    // most shift = slope * (end - 1 - start) (base 2) past any first-chunk
+    // token, so the reference starts at the first chunk's max + shift and a
+    // split reruns only when its scores grow by more than that plus the
+    // headroom. If the true max ends more than kUnder below the reference,
+    // the split also reruns (against the true max): otherwise a token flushed
+    // to zero (below mref - 126) would be one within 126 - kUnder of the true
+    // max. With kUnder = 64 every flushed token weighs < 2^-62 of the largest.
     constexpr float kHeadroom = std::is_same<E, F16>::value ? 15.0f : 64.0f;
+    constexpr bool kShift = ALIBI && std::is_same<E, BF16>::value;
+    constexpr float kUnder = 64.0f;
+    const float shift = kShift && slope > 0.0f ? slope * (float)(end - 1 - start) : 0.0f;
     float mref = -INFINITY;  // reference max of head h (base 2)
     float mtrue = -INFINITY; // true running max of head h (base 2)
     float l = 0.0f;          // this lane's share of sum_t exp2(z_t - mref), rounded p
@@ -561,7 +690,7 @@ void k_decode_mla(DecodeParams p)
         mx = fmaxf(mx, z[15]);
         float mloc = half_max(mx);  // token 0 is valid, so lane half 0 has a finite score
         if constexpr (!ALIBI) mloc *= scale;
-        mref = mref == -INFINITY ? mloc : mref;
+        mref = mref == -INFINITY ? mloc + shift : mref;
         over |= mloc > mref + kHeadroom;
         mtrue = fmaxf(mtrue, mloc);
         float e[16];
@@ -680,7 +809,7 @@ void k_decode_mla(DecodeParams p)
 
     if (threadIdx.x == 0) rerun_flag = 0;
     run();
-    if (over) rerun_flag = 1;  // benign race: every writer stores 1
+    if (over || (kShift && mtrue < mref - kUnder)) rerun_flag = 1;  // benign race: every writer stores 1
     lds_barrier();
     if (rerun_flag) {  // uniform across the workgroup
         mref = mtrue;
@@ -740,115 +869,7 @@ void k_decode_mla(DecodeParams p)
         return;
     }
 
-    // ---- balanced splits: the sequences' tokens in sequence order, each
-    // non-empty sequence preceded by kMlaPieceCharge virtual tokens (the cost
-    // of starting a piece: loading its query and the first chunks, storing
-    // its partial output), total T'; worker w = blockIdx.x takes virtual
-    // positions [w*U, (w+1)*U), so a worker that starts a sequence inside its
-    // range gets that many fewer real tokens.
-    constexpr int BT = 64 * NW;
-    constexpr int C = kMlaPieceCharge;
-    constexpr int GH = HPW * NW;  // heads of this workgroup
-    __shared__ int64_t bal_w64[NW];
-    __shared__ int bal_w32[NW];
-    __shared__ int64_t bal_off[BT];
-    __shared__ int bal_len[BT];
-    __shared__ int bal_first, bal_last;
-    const int tid = threadIdx.x;
-    const int w = blockIdx.x;
-    // m = -inf, l = 0 in slots [k0, max_num_parts) of sequence s, all heads
-    // here (all threads of the workgroup together)
-    auto mark_empty = [&](int s, int k0) {
-        for (int e = tid; e < GH * (p.max_num_parts - k0); e += BT) {
-            const int64_t off = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + k0 + e / GH;
-            p.max_logits[off] = -INFINITY;
-            p.exp_sums[off] = 0.0f;
-        }
-    };
-
-    // With at most BT sequences every thread loads its length once and keeps
-    // it for the scan below (one memory round trip for the whole schedule).
-    const bool one_round = p.num_seqs <= BT;
-    int Lmine = 0;
-    int64_t tsum = 0;
-    int tmax = 0;
-    for (int i = tid; i < p.num_seqs; i += BT) {
-        const int Li = max(p.seq_lens[i], 0);
-        if (i == tid) Lmine = Li;
-        tsum += Li > 0 ? Li + C : 0;
-        tmax = max(tmax, Li);
-        if (w == 0 && Li == 0) {  // worker 0 covers the empty sequences, one thread each
-            for (int e = 0; e < GH * p.max_num_parts; ++e) {
-                const int64_t off = (int64_t)(i * p.num_group + qg) * p.ml_ss + (int64_t)(h0 + e % GH) * p.ml_sh + e / GH;
-                p.max_logits[off] = -INFINITY;
-                p.exp_sums[off] = 0.0f;
-            }
-        }
-    }
-    tsum = __shfl(wave_incl_sum_i64(tsum, lane), kWave - 1, kWave);
-    tmax = wave_max_i32(tmax);
-    if (lane == 0) {
-        bal_w64[wave] = tsum;
-        bal_w32[wave] = tmax;
-    }
-    lds_barrier();
-    int64_t total_virtual = 0;
-    int maxL = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        total_virtual += bal_w64[i];
-        maxL = max(maxL, bal_w32[i]);
-    }
-    total_virtual = uniform_i64(total_virtual);
-    maxL = __builtin_amdgcn_readfirstlane(maxL);
-    lds_barrier();  // bal_w64 is reused by the scan below
-    const int64_t W = p.num_workers;
-    int64_t U = max((total_virtual + W - 1) / W, ((int64_t)maxL + p.max_num_parts - 2) / (p.max_num_parts - 1));
-    U = max((U + 31) & ~int64_t(31), int64_t(32));
-    if (total_virtual == 0 || (int64_t)w * U >= total_virtual) return;
-    const int64_t r0 = (int64_t)w * U, r1 = min(r0 + U, total_virtual);
-
-    // sequences in batches of BT: a block scan of the virtual lengths gives
-    // their virtual offsets; the ones meeting [r0, r1) form a contiguous run
-    int64_t base = 0;
-    for (int b0 = 0; b0 < p.num_seqs && base < r1; b0 += BT) {
-        const int i = b0 + tid;
-        const int Li = one_round ? Lmine : (i < p.num_seqs ? max(p.seq_lens[i], 0) : 0);
-        const int Vi = Li > 0 ? Li + C : 0;
-        const int64_t inc = wave_incl_sum_i64(Vi, lane);
-        if (lane == kWave - 1) bal_w64[wave] = inc;
-        if (tid == 0) {
-            bal_first = BT;
-            bal_last = -1;
-        }
-        lds_barrier();
-        int64_t off = base + inc - Vi + C, total = 0;  // virtual position of the sequence's first token
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            if (j < wave) off += bal_w64[j];
-            total += bal_w64[j];
-        }
-        bal_off[tid] = off;
-        bal_len[tid] = Li;
-        if (Li > 0 && off < r1 && off + Li > r0) {
-            atomicMin(&bal_first, tid);
-            atomicMax(&bal_last, tid);
-        }
-        lds_barrier();
-        const int first = __builtin_amdgcn_readfirstlane(bal_first);
-        const int last = __builtin_amdgcn_readfirstlane(bal_last);
-        total = uniform_i64(total);
-        for (int j = first; j <= last; ++j) {
-            const int64_t so = uniform_i64(bal_off[j]);
-            const int Ls = __builtin_amdgcn_readfirstlane(bal_len[j]);
-            if (Ls <= 0) continue;
-            const int k = (int)(w - so / U);
-            piece(b0 + j, k, (int)(max(r0, so) - so), (int)(min(r1, so + Ls) - so));
-            if ((so + Ls - 1) / U == w) mark_empty(b0 + j, k + 1);  // this worker has the last piece
-        }
-        base += total;
-        lds_barrier();  // bal_* are rewritten by the next batch
-    }
+    mla_balanced<NW>(p, qg, h0, HPW * NW, piece);
 }
 
 bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size)

@@ -168,9 +168,10 @@ def test_alibi_moves_the_output(orc):
 @pytest.mark.parametrize("kernel", ["auto", "valu"])
 def test_alibi_latent_rows(orc, kernel):
     """Latent rows (V aliasing K, page size 1) with ALiBi, 64 and 128 heads on
-    the latent-row kernel (auto) and on the vector kernel. Slopes make later
-    scores pass the latent-row kernel's first-chunk reference, so its
-    splits take the second, exact-reference pass."""
+    the latent-row kernel (auto) and on the vector kernel. On the latent-row
+    kernel the bf16 splits start from a reference raised by the bias growth
+    over the split; the f16 ones (and any split whose scores outgrow it)
+    take the second, exact-reference pass."""
     for H, lens in ((64, [300, 1, 1000, 2049]), (128, [700, 33])):
         say(f"alibi latent rows H={H} kernel={kernel}")
         w = workloads.mla_custom(seed=122 + H, seq_lens=lens, num_heads=H, poison=True)
@@ -178,6 +179,33 @@ def test_alibi_latent_rows(orc, kernel):
         out, tmp, ml, es = run_gpu(w, kernel=kernel)
         check_partials(w, orc, tmp, ml, es)
         check_output(w, orc, out)
+
+
+def test_alibi_latent_rows_reference_guards(orc):
+    """The latent-row kernel's raised ALiBi reference and its two reruns.
+    One 2048-token split per sequence, slopes 0.07 (the bias grows by ~202
+    in base 2 over a split: more than an fp32 exponent below the reference
+    can hold). Sequence 0, head 0: the first eight keys are aligned with the
+    head's query, so its scores peak in the first chunk, ~202 below the
+    raised reference (the kernel must rerun it against the true max; kept,
+    its sums would underflow). Sequence 1, head 1: the last eight keys are
+    aligned with its query, so its scores outgrow the raised reference by
+    more than the headroom (rerun as before). Other heads keep one pass."""
+    say("alibi latent rows: raised reference, both reruns")
+    w = workloads.mla_custom(seed=131, seq_lens=[2000, 1900], num_heads=128, poison=True)
+    w.alibi_slopes = torch.full((128,), 0.07, dtype=torch.float32)
+    q = w.query.float()
+    scale_nat = w.scale
+    # alpha * |q|^2 * scale ~ 160 nats (head 0), 120 nats (head 1)
+    for seq, head, toks, nats in ((0, 0, range(0, 8), 160.0), (1, 1, range(1892, 1900), 120.0)):
+        qh = q[seq, head]
+        alpha = nats / (float(qh.dot(qh)) * scale_nat)
+        pages = w.block_tables[seq, list(toks)].long()
+        w.latent[pages] = (alpha * qh).to(w.latent.dtype)
+    out, tmp, ml, es = run_gpu(w, partition_size=2048)
+    assert torch.isfinite(out).all() and torch.isfinite(es).all()
+    check_partials(w, orc, tmp, ml, es, partition_size=2048)
+    check_output(w, orc, out)
 
 
 def test_fp8_scales_scale_linearly(orc):
