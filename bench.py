@@ -50,7 +50,7 @@ def kernel_kind(w) -> str:
     group = w.num_heads // w.num_kv_heads
     low = w.dtype in (torch.float16, torch.bfloat16)
     if low and w.head_size == 576 and w.v_head_size == 512 and w.block_size == 1 \
-            and group in (64, 128) and w.latent is not None and w.kv_dtype is None:
+            and group in (64, 128) and w.latent is not None:
         return "mla"
     cols = group * w.num_group  # (query token, head) pairs of a kv head
     if low and 1 <= cols <= 16 and w.block_size >= 8 and w.head_size in (64, 128):

@@ -174,17 +174,17 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // latent rows: the value cache is the leading v_head_size columns of the key rows
-    // The matrix-core kernels take ALiBi; fp8 caches the grouped-head one only.
+    // (query-dtype or fp8 codes). The matrix-core kernels take ALiBi and fp8 caches.
     const bool mla_ok = pa::decode_mla_supported(a->dtype, D, Dv, group, a->block_size) &&
                         a->value_cache == a->key_cache && a->v_stride_b == a->k_stride_b &&
-                        a->v_stride_h == a->k_stride_h && !fp8;
+                        a->v_stride_h == a->k_stride_h;
     // its 16 columns hold the (query token, head) pairs of a kv head
     const bool mfma_ok = pa::decode_mfma_supported(a->dtype, D, Dv, group * ng, a->block_size);
     if (a->kernel_hint == PA_KERNEL_MFMA && !mfma_ok && !mla_ok)
         return fail(PA_ENOTSUP, "paged_attn_decode: no matrix-core kernel serves this problem");
     if (balanced && (!mla_ok || a->kernel_hint == PA_KERNEL_VALU))
         return fail(PA_ENOTSUP, "paged_attn_decode: balanced splits are built for the MLA matrix-core kernel only "
-                                "(query-dtype caches)");
+                                "(latent rows: V the leading columns of K, page size 1)");
     if (a->kernel_hint != PA_KERNEL_VALU && mla_ok)
         return launched(pa::launch_decode_mla(p, a->dtype, a->num_seqs, (int)parts, st),
                         "paged_attn_decode (mla)");

@@ -57,6 +57,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <class E> struct MlaOps;
 template <> struct MlaOps<BF16> {
     typedef bf16x8 vec8;
+    // two E4M3 codes (bytes 0-1 or, high, 2-3 of w) as two bf16 values
+    static __device__ __forceinline__ uint32_t widen2(uint32_t w, bool high)
+    {
+        return high ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+                    : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    }
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,6 +70,11 @@ template <> struct MlaOps<BF16> {
 };
 template <> struct MlaOps<F16> {
     typedef f16x8 vec8;
+    static __device__ __forceinline__ uint32_t widen2(uint32_t w, bool high)
+    {
+        return high ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+                    : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    }
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -113,6 +124,20 @@ __device__ __forceinline__ s16x4 lds_read_tr16(uint32_t lds_addr)
     s16x4 v;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "n"(OFF));
     return v;
+}
+
+// r == I ? a : b for a per-lane r and a uniform a, as a compare and a
+// select: written as plain code, a chain of these over an array of page ids
+// becomes a table in scratch memory indexed per lane.
+template <int I>
+__device__ __forceinline__ int select_eq(int r, int a, int b)
+{
+    int t;
+    asm volatile("v_mov_b32 %1, %4\n\tv_cmp_eq_u32_e32 vcc, %2, %3\n\tv_cndmask_b32_e32 %0, %0, %1, vcc"
+                 : "+v"(b), "=&v"(t)
+                 : "n"(I), "v"(r), "s"(a)
+                 : "vcc");
+    return b;
 }
 
 // Waits until at most N LDS operations of this wave are outstanding. LDS
@@ -181,6 +206,10 @@ __host__ __device__ constexpr int mla_ftail(int t) { return (t >> 1) & 7; }
 #endif
 constexpr int kMlaChunk = 32;             // tokens per chunk
 constexpr int kMlaBuf = PA_MLA_BUF;       // chunk slots in the LDS ring
+#ifndef PA_MLA_BUF8
+#define PA_MLA_BUF8 6
+#endif
+constexpr int kMlaBuf8 = PA_MLA_BUF8;     // fp8 caches: chunk slots of fp8 rows in the copy ring
 constexpr int kMlaKAhead = PA_MLA_KAHEAD; // QK operand reads in flight ahead of their MFMAs
 constexpr int kMlaHeadsPerWave = 32;
 // Balanced splits: virtual tokens charged for each piece a worker starts
@@ -433,7 +462,7 @@ __device__ __forceinline__ void mla_balanced(const DecodeParams& p, const int qg
 // BAL = false: one workgroup per (seq, kv head, split) of the fixed or
 // per-sequence split rule. BAL = true: balanced splits, one workgroup per
 // (token range, kv head).
-template <class E, int NW, bool BAL, bool ALIBI>
+template <class E, int NW, bool BAL, bool ALIBI, bool KV8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_decode_mla(DecodeParams p)
 {
@@ -449,7 +478,10 @@ void k_decode_mla(DecodeParams p)
     constexpr int TPW = CT / NW;                  // rows each wave copies
     constexpr int IPW = TPW + TPW * TP / 64;      // copy instructions per wave per chunk
     constexpr int KS = D / 16;                    // QK k-steps
-    constexpr int NB = kMlaBuf;
+    constexpr int P8 = D / 16;                    // 16-byte pieces of an fp8 latent row (36)
+    constexpr int IP8 = (TPW * P8 + 63) / 64;     // fp8 copy instructions per wave per chunk
+    constexpr int NB = KV8 ? kMlaBuf8 : kMlaBuf;  // chunk slots of the copy ring
+    constexpr int IPC = KV8 ? IP8 : IPW;          // copy instructions per wave per chunk
     constexpr int HPW = kMlaHeadsPerWave;
     constexpr int G = HPW * NW;                   // heads of the workgroup
     constexpr int HT = NW;                        // P.V head tiles: all G heads
@@ -457,9 +489,23 @@ void k_decode_mla(DecodeParams p)
     using Sched = PvSchedule<HT, DT>;
     static_assert(PR == MP + 8 && TPW % 8 == 0, "ring layout: 64 + 8 pieces a row, tail rows 8 to a copy");
     static_assert(KS % 4 == 0 && DT % 2 == 0, "tiling");
-    static_assert(IPW * (NB - 2) <= 63, "vmcnt is a 6-bit field");
+    static_assert(IPC * (NB - 2) <= 63, "vmcnt is a 6-bit field");
 
-    __shared__ u32x4 ring[NB][CT * PR];
+    // The copy ring: NB slots of CT rows. Caches of the query's type are
+    // copied straight into the layout QK and P.V read (see mla_fmain); fp8
+    // rows land as copied (576-byte rows) and each wave widens its rows of
+    // the current chunk into one more slot in that layout.
+    constexpr int SLOT = CT * PR, SLOT8 = CT * P8;  // u32x4 words of a slot
+    __shared__ __attribute__((aligned(256))) u32x4 ring[KV8 ? SLOT + NB * SLOT8 : NB * SLOT];
+    // LDS byte addresses: the slot QK and P.V read for chunk c, the slot its
+    // copies land in
+    auto use_slot = [](int c) -> uint32_t {
+        return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[KV8 ? 0 : (c % NB) * SLOT]);
+    };
+    auto copy_slot = [](int c) -> uint32_t {
+        return (uint32_t)(uintptr_t)((
+            __attribute__((address_space(3))) const char*)&ring[KV8 ? SLOT + (c % NB) * SLOT8 : (c % NB) * SLOT]);
+    };
     __shared__ u32x4 pbuf[G * 4];  // probabilities of a chunk: [head][32 tokens] of T, 64 B a head
     __shared__ int rerun_flag;
 
@@ -532,15 +578,34 @@ void k_decode_mla(DecodeParams p)
 
     // copy chunk `c` (tokens start + CT*c ...) into ring slot c % NB: wave w
     // copies rows TPW*w .. TPW*w + TPW-1, one instruction per main row (a
-    // scalar base address) and one per 8 tail rows.
+    // scalar base address) and one per 8 tail rows; fp8 rows as 16-byte
+    // pieces, 64 consecutive pieces of the wave's rows an instruction (a
+    // lane's row is one of the 3 an instruction can touch).
     auto issue = [&](int c, const int32_t (&pg)[TPW]) {
         // an opaque zero: the lane offsets below are recomputed per chunk (one
         // XOR a copy) rather than hoisted out of the chunk loop, where they
         // would take 20 registers and be spilled
         int z;
         asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        if constexpr (KV8) {
+            const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(p.kc) + (int64_t)kvh * p.k_sh;
+            const uint32_t base = copy_slot(c) + 16 * TPW * P8 * wave;
+            static_for<IP8>([&](auto kc_) {
+                constexpr int k = decltype(kc_)::value;
+                constexpr int r0 = 64 * k / P8;  // first row an instruction touches
+                const int i = 64 * k + lane + z;  // piece of the wave's rows
+                const int rl = i / P8, q = i - rl * P8;
+                int pgl = pg[r0];
+                if constexpr (r0 + 1 < TPW) pgl = select_eq<r0 + 1>(rl, pg[r0 + 1], pgl);
+                if constexpr (r0 + 2 < TPW) pgl = select_eq<r0 + 2>(rl, pg[r0 + 2], pgl);
+                const uint8_t* src = kc8 + (int64_t)pgl * p.k_sb + 16 * q;
+                if (64 * k + 64 <= TPW * P8 || i < TPW * P8)
+                    lds_copy16(src, (__attribute__((address_space(3))) void*)(uintptr_t)(base + 1024 * k));
+            });
+            return;
+        }
         const uint32_t lane16 = (uint32_t)(lane * 16 + z);
-        const uint32_t slot = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+        const uint32_t slot = copy_slot(c);
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = TPW * wave + j;
@@ -641,8 +706,7 @@ void k_decode_mla(DecodeParams p)
     // raw scores S^T[t][h] of chunk c: lane (hl, c32) gets head h's scores of
     // tokens 16*(r>>3) + 8*hl + (r&7), r = 0..15
     auto qk = [&](int c) -> f32x16 {
-        const uint32_t bufa =
-            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+        const uint32_t bufa = use_slot(c);
         constexpr int RA = kMlaKAhead < KS ? kMlaKAhead : KS;
         u32x4 kr[KS];
         auto kread = [&](auto ksc) {
@@ -711,8 +775,7 @@ void k_decode_mla(DecodeParams p)
 
     // O^T[this wave's value columns][all G heads] += V^T P over chunk c
     auto pv = [&](int c, auto after_reads) {
-        const uint32_t slot =
-            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[c % NB][0]);
+        const uint32_t slot = use_slot(c);
         u32x4 pr[2][HT];
         s16x4 vr[2][DT][2];
         // read r of the schedule: (kk, P operand ht) or (kk, value operand dt)
@@ -767,9 +830,54 @@ void k_decode_mla(DecodeParams p)
     // frees its ring slot (reused by the copy of chunk c+NB-1) and the P
     // buffer.
     int32_t pg_next[TPW];  // page ids of the next chunk to copy
+    // fp8: widen this wave's rows of chunk c (its own copies, landed) into
+    // the use slot, bit-exact (E4M3 values are bf16 and f16 values)
+    auto widen = [&](int c) {
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const int ln = lane + z;
+        const uint32_t src = copy_slot(c) + 16 * TPW * P8 * wave + 16 * ln;
+        const uint32_t dst = use_slot(c);
+        u32x4 w[IP8];
+        static_for<IP8>([&](auto kc_) {
+            constexpr int k = decltype(kc_)::value;
+            w[k] = lds_read_b128<1024 * k>(src);
+        });
+        lds_wait<0>(w[0]);
+        static_for<IP8>([&](auto kc_) {
+            constexpr int k = decltype(kc_)::value;
+            const int i = 64 * k + ln;
+            if (64 * k + 64 <= TPW * P8 || i < TPW * P8) {
+                const int rl = i / P8, q = i - rl * P8, t = TPW * wave + rl;
+                u32x4 lo, hi;  // values 0-7 and 8-15 of the piece's 16 codes
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t a = MlaOps<E>::widen2(w[k][d], false), b = MlaOps<E>::widen2(w[k][d], true);
+                    if (d < 2) {
+                        lo[2 * d] = a;
+                        lo[2 * d + 1] = b;
+                    } else {
+                        hi[2 * d - 4] = a;
+                        hi[2 * d - 3] = b;
+                    }
+                }
+                uint32_t a0, a1;  // byte addresses of the two widened pieces
+                if (q < MP / 2) {
+                    a0 = dst + t * MP * 16 + 16 * ((2 * q) ^ mla_fmain(t));
+                    a1 = dst + t * MP * 16 + 16 * ((2 * q + 1) ^ mla_fmain(t));
+                } else {
+                    const int tq = 2 * (q - MP / 2);
+                    a0 = dst + TAIL + t * TP * 16 + 16 * (tq ^ mla_ftail(t));
+                    a1 = dst + TAIL + t * TP * 16 + 16 * ((tq + 1) ^ mla_ftail(t));
+                }
+                lds_write_b128<0>(a0, lo);
+                lds_write_b128<0>(a1, hi);
+            }
+        });
+    };
     auto advance = [&](int c) {
         if (c + NB - 2 < nc)
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(IPW * (NB - 2)));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(IPC * (NB - 2)));
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         // A plain s_barrier (see lds_barrier): the copies this barrier
@@ -779,6 +887,11 @@ void k_decode_mla(DecodeParams p)
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (c + NB - 1 < nc) issue(c + NB - 1, pg_next);
+        if constexpr (KV8) {
+            // the barrier above: every wave is done with chunk c-1 in the use slot
+            widen(c);
+            lds_barrier();  // every wave's rows of chunk c are widened
+        }
     };
     // every wave's probabilities of the chunk are in the P buffer
     auto p_ready = [&]() { lds_barrier(); };
@@ -841,7 +954,7 @@ void k_decode_mla(DecodeParams p)
                         (int64_t)part * p.tmp_sp + 32 * wave + 4 * hl;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        const float inv = 1.0f / lsum[32 * ht + c32];
+        const float inv = p.v_scale / lsum[32 * ht + c32];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -878,15 +991,22 @@ bool decode_mla_supported(int dtype, int D, int Dv, int group, int block_size)
            (group == 64 || group == 128);
 }
 
+template <class E, int NW, bool ALIBI, bool KV8>
+static void launch_mla_k(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
+{
+    if (p.num_workers > 0)
+        hipLaunchKernelGGL((k_decode_mla<E, NW, true, ALIBI, KV8>),
+                           dim3(p.num_workers, p.num_kv_heads * p.num_group, 1), dim3(64 * NW), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_decode_mla<E, NW, false, ALIBI, KV8>),
+                           dim3(num_seqs, p.num_kv_heads * p.num_group, parts), dim3(64 * NW), 0, st, p);
+}
+
 template <class E, int NW, bool ALIBI>
 static void launch_mla_a(const DecodeParams& p, int num_seqs, int parts, hipStream_t st)
 {
-    if (p.num_workers > 0)
-        hipLaunchKernelGGL((k_decode_mla<E, NW, true, ALIBI>), dim3(p.num_workers, p.num_kv_heads * p.num_group, 1),
-                           dim3(64 * NW), 0, st, p);
-    else
-        hipLaunchKernelGGL((k_decode_mla<E, NW, false, ALIBI>), dim3(num_seqs, p.num_kv_heads * p.num_group, parts),
-                           dim3(64 * NW), 0, st, p);
+    if (p.kv_fp8) launch_mla_k<E, NW, ALIBI, true>(p, num_seqs, parts, st);
+    else launch_mla_k<E, NW, ALIBI, false>(p, num_seqs, parts, st);
 }
 
 template <class E, int NW>

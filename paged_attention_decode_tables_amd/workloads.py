@@ -299,8 +299,8 @@ def config(cfg: int, *, poison: bool = False, kv_cache: str = "same",
     name suffix "_kvfp8"), with ALiBi slopes (suffix "_alibi") and with
     num_group query tokens per sequence (configs 2-5, suffix "_qg<n>"; the
     query draw has num_group rows per sequence)."""
-    if kv_cache != "same" and cfg not in (2, 3, 4):
-        raise ValueError("fp8 caches are drawn for configs 2-4")
+    if kv_cache != "same" and cfg not in (2, 3, 4, 5):
+        raise ValueError("fp8 caches are drawn for configs 2-5")
     if num_group != 1 and cfg not in (2, 3, 4, 5):
         raise ValueError("query groups are drawn for configs 2-5")
     w = _config(cfg, poison=poison, kv_cache=kv_cache, num_group=num_group)
@@ -353,7 +353,7 @@ def _config(cfg: int, *, poison: bool, kv_cache: str, num_group: int = 1) -> Wor
         w.device_core_count = 256
         return w
     if cfg == 5:
-        return _mla(gen, poison=poison, num_group=num_group)
+        return _mla(gen, poison=poison, num_group=num_group, kv_cache=kv_cache)
     raise ValueError(f"unknown config {cfg}")
 
 
@@ -389,7 +389,23 @@ def _standard(gen, name, desc, lens, *, H, Hkv, D, bs, dt, nb, poison, kv_cache=
     return w
 
 
-def _mla(gen, *, poison, num_group=1):
+def _latent_rows(gen, nb, D, dt, kv_cache):
+    """[nb, D] latent rows: N(0, 1) draws of the query's type, or (kv_cache
+    "fp8") uint8 E4M3 codes of N(0, 1) / FP8_WORKLOAD_SCALE."""
+    if kv_cache == "same":
+        return _randn(gen, (nb, D), dt)
+    return _fp8_cache(gen, (nb, D), kv_cache, FP8_WORKLOAD_SCALE)
+
+
+def _poison_rows(latent, rows):
+    """NaN in unused latent rows: the float NaN, or the E4M3 NaN code."""
+    if latent.dtype == torch.uint8:
+        latent[rows] = FP8_NAN_CODE
+    else:
+        latent[rows] = float("nan")
+
+
+def _mla(gen, *, poison, num_group=1, kv_cache="same"):
     S, H, D, Dv = 64, 128, 576, 512
     lens = _draw_lengths(5, gen)
     total = int(lens.sum())
@@ -397,27 +413,33 @@ def _mla(gen, *, poison, num_group=1):
     perm = torch.randperm(nb, generator=gen)
     dt = torch.bfloat16
     q = _randn(gen, (S * num_group, H, D), dt)
-    latent = _randn(gen, (nb, D), dt)
+    latent = _latent_rows(gen, nb, D, dt, kv_cache)
     poison_block = int(perm[total]) if poison else None
     bt = _assign_blocks(perm, lens.tolist(), 8192, poison_block if poison else 0)
     cu = torch.zeros(S + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
     if poison:
-        latent[poison_block] = float("nan")
+        _poison_rows(latent, poison_block)
         used = torch.zeros(nb, dtype=torch.bool)
         used[perm[:total]] = True
-        latent[~used] = float("nan")
+        _poison_rows(latent, ~used)
     k, v = _mla_views(latent, Dv)
-    return Workload(name=CONFIG_NAMES[5], description="MLA-style decode bf16", dtype=dt,
-                    seq_lens=lens, block_tables=bt, query=q, key_cache=k, value_cache=v,
+    fp8 = kv_cache != "same"
+    sc = FP8_WORKLOAD_SCALE if fp8 else 1.0
+    return Workload(name=CONFIG_NAMES[5] + ("_kvfp8" if fp8 else ""), description="MLA-style decode bf16",
+                    dtype=dt, seq_lens=lens, block_tables=bt, query=q, key_cache=k, value_cache=v,
                     scale=1.0 / math.sqrt(192.0), num_heads=H, num_kv_heads=1, head_size=D,
-                    v_head_size=Dv, block_size=1, x=8, num_blocks=nb, cu_num_blocks=cu,
-                    latent=latent, poison_block=poison_block, num_group=num_group)
+                    v_head_size=Dv, block_size=1, x=16 if fp8 else 8, num_blocks=nb, cu_num_blocks=cu,
+                    latent=latent, poison_block=poison_block, num_group=num_group,
+                    kv_dtype=torch.uint8 if fp8 else None, k_scale=sc, v_scale=sc)
 
 
 def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512, max_blocks=None,
-               poison=False, num_group=1, dtype="bf16") -> Workload:
-    """Smaller MLA-style workload (page size 1, V aliasing the first Dv values of K)."""
+               poison=False, num_group=1, dtype="bf16", kv_cache="same", k_scale=None,
+               v_scale=None) -> Workload:
+    """Smaller MLA-style workload (page size 1, V aliasing the first Dv values
+    of K). kv_cache "fp8": the latent rows are E4M3 codes (k_scale and
+    v_scale default to FP8_WORKLOAD_SCALE)."""
     gen = torch.Generator().manual_seed(seed)
     lens = torch.as_tensor(seq_lens, dtype=torch.int32).clone()
     S = lens.shape[0]
@@ -426,21 +448,25 @@ def mla_custom(*, seed, seq_lens, num_heads=128, head_size=576, v_head_size=512,
     perm = torch.randperm(nb, generator=gen)
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     q = _randn(gen, (S * num_group, num_heads, head_size), dt)
-    latent = _randn(gen, (nb, head_size), dt)
+    latent = _latent_rows(gen, nb, head_size, dt, kv_cache)
     poison_block = int(perm[total]) if poison else None
     mb = max_blocks or max(1, int(lens.max()))
     bt = _assign_blocks(perm, [max(0, int(L)) for L in lens], mb, poison_block if poison else 0)
     cu = torch.zeros(S + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(lens.clamp(min=0), 0).to(torch.int32)
     if poison:
-        latent[poison_block] = float("nan")
+        _poison_rows(latent, poison_block)
     k, v = _mla_views(latent, v_head_size)
+    fp8 = kv_cache != "same"
+    ks = (FP8_WORKLOAD_SCALE if k_scale is None else k_scale) if fp8 else 1.0
+    vs = (FP8_WORKLOAD_SCALE if v_scale is None else v_scale) if fp8 else 1.0
     return Workload(name="mla_custom", description="MLA-style custom", dtype=dt, seq_lens=lens,
                     block_tables=bt, query=q, key_cache=k, value_cache=v,
                     scale=1.0 / math.sqrt(192.0), num_heads=num_heads, num_kv_heads=1,
-                    head_size=head_size, v_head_size=v_head_size, block_size=1, x=8,
-                    num_blocks=nb, cu_num_blocks=cu, latent=latent, poison_block=poison_block,
-                    num_group=num_group)
+                    head_size=head_size, v_head_size=v_head_size, block_size=1,
+                    x=16 if fp8 else 16 // latent.element_size(), num_blocks=nb, cu_num_blocks=cu,
+                    latent=latent, poison_block=poison_block, num_group=num_group,
+                    kv_dtype=torch.uint8 if fp8 else None, k_scale=ks, v_scale=vs)
 
 
 # ---------------------------------------------------------------------------

@@ -196,14 +196,19 @@ def test_decode_kv_dtype_must_be_query_dtype_or_fp8(lib):
 
 
 def test_decode_balanced_splits_need_the_mla_kernel(lib):
-    """Balanced splits are built into the latent-row kernel only, which does
-    not read fp8 caches."""
+    """Balanced splits are built into the latent-row kernel only: 64 or 128
+    heads over one latent row whose leading columns are the values. 16 heads
+    over latent rows, and 128 heads whose values are a separate cache, are
+    not that shape (fp8 codes or not)."""
     a = good_fp8(D=576, Dv=512, H=16, Hkv=1, bs=1)
     a.value_cache = a.key_cache
     a.v_stride_b, a.v_stride_h, a.v_stride_d = a.k_stride_b, a.k_stride_h, 1
     a.partition_size, a.num_workers, a.max_num_parts = 0, 256, 256
     assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_ENOTSUP
     assert "balanced" in lib.pa_last_error().decode()
+    b = good_fp8(D=576, Dv=512, H=128, Hkv=1, bs=1)  # value cache not the key rows
+    b.partition_size, b.num_workers, b.max_num_parts = 0, 256, 256
+    assert lib.paged_attn_decode(ctypes.byref(b), None) == api.PA_ENOTSUP
 
 
 def test_decode_empty_batch_is_a_noop(lib):
