@@ -53,7 +53,8 @@ def kernel_kind(w) -> str:
             and group in (64, 128) and w.latent is not None:
         return "mla"
     cols = group * w.num_group  # (query token, head) pairs of a kv head
-    if low and 1 <= cols <= 16 and w.block_size >= 8 and w.head_size in (64, 128):
+    if low and (cols >= 2 or w.kv_dtype is not None) and cols <= 16 and w.block_size >= 8 \
+            and w.head_size in (64, 128):
         return "mfma"
     return "valu"
 
@@ -70,8 +71,9 @@ class Step:
     """Device buffers and the launches of one decode step."""
 
     def __init__(self, w: workloads.Workload, out_dtype=torch.bfloat16, balanced_workers=0,
-                 tmp_dtype=torch.float32):
+                 tmp_dtype=torch.float32, kernel="auto"):
         self.w = w
+        self.kernel = kernel
         self.g = g = w.to("cuda")
         self.ns = None
         self.indptr = None
@@ -107,7 +109,7 @@ class Step:
                               g.seq_lens, w.scale, w.max_seq_len, partition_size=self.partition,
                               num_splits=self.ns, kv_indptr=self.indptr, num_workers=self.workers,
                               alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale,
-                              num_group=w.num_group)
+                              num_group=w.num_group, kernel=self.kernel)
 
     def reduce(self):
         w, g = self.w, self.g
@@ -412,6 +414,8 @@ def main():
     ap.add_argument("--kv-cache", choices=("same", "fp8"), default="same",
                     help="fp8: the same workload with FP8 E4M3 caches (configs 2-4)")
     ap.add_argument("--alibi", action="store_true", help="the same workload with ALiBi slopes")
+    ap.add_argument("--kernel", choices=("auto", "valu"), default="auto",
+                    help="phase-1 kernel hint (valu: the vector-ALU kernel, for comparison)")
     ap.add_argument("--tmp-dtype", choices=("query", "f32"), default="query",
                     help="element type of the split-output workspace: the query's type (phase 1 "
                          "stores each split's output converted to it) or fp32")
@@ -449,13 +453,13 @@ def main():
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config, kv_cache=args.kv_cache, alibi=args.alibi,
                          num_group=args.num_group)
-    kind = kernel_kind(w)
+    kind = kernel_kind(w) if args.kernel == "auto" else args.kernel
     # The MLA workload's split policy is not fixed by its definition: it runs
     # with balanced splits, one token range per compute unit.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     workers = cus if (kind == "mla" and not args.fixed_splits) else 0
     tmp_dtype = w.dtype if args.tmp_dtype == "query" else torch.float32
-    step = Step(w, balanced_workers=workers, tmp_dtype=tmp_dtype)
+    step = Step(w, balanced_workers=workers, tmp_dtype=tmp_dtype, kernel=args.kernel)
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup}")
@@ -560,6 +564,7 @@ def main():
                    "alibi": w.alibi_slopes is not None, "num_group": w.num_group,
                    "split_workspace": {torch.bfloat16: "bf16", torch.float16: "f16",
                                        torch.float32: "f32"}[tmp_dtype],
+                   "kernel_hint": args.kernel,
                    "query_tokens_per_s": round(w.num_seqs * w.num_group / (ms_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

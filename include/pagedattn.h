@@ -184,13 +184,16 @@ typedef struct pa_decode_args {
  * Supported combinations (others return PA_ENOTSUP):
  *   dtype f32, f16, bf16 with x = 16 / element size;
  *   (head_size, v_head_size) in {(64,64), (128,128), (256,256), (576,512)};
- *   any group size num_heads / num_kv_heads (f16/bf16 queries with D = Dv in
- *   {64, 128} run on MFMA when block_size >= 8 and num_group * group is
- *   1..16).
- * ALiBi slopes run on every kernel. fp8 caches (x = 16) run on the
- * grouped-head matrix-core kernel (f16/bf16 queries, the conditions above)
- * and on the vector kernel; latent rows over fp8 caches go to the vector
- * kernel, and balanced splits over fp8 caches return PA_ENOTSUP.
+ *   any group size num_heads / num_kv_heads.
+ * Kernel choice (PA_KERNEL_AUTO): latent rows (D = 576, Dv = 512, page size
+ * 1, value_cache = key_cache, 64 or 128 heads a kv head, f16/bf16 queries)
+ * on the latent-row matrix-core kernel, with query-dtype or fp8 caches and
+ * fixed or balanced splits; f16/bf16 queries with D = Dv in {64, 128},
+ * block_size >= 8 and num_group * group in 2..16 (or 1 with fp8 caches) on
+ * the grouped-head matrix-core kernel; everything else on the vector
+ * kernel. PA_KERNEL_MFMA also takes one column with query-dtype caches.
+ * ALiBi slopes and fp8 caches (x = 16) run on every kernel. Balanced splits
+ * need the latent-row kernel (PA_ENOTSUP otherwise).
  */
 int paged_attn_decode(const pa_decode_args* args, void* stream);
 

@@ -191,6 +191,8 @@ def test_decode_small(orc, case):
     w = workloads.custom(seed=zlib.crc32(name.encode()) % 10007, seq_lens=lens, num_heads=H, num_kv_heads=Hkv,
                          head_size=D, block_size=bs, dtype=dt, partition_size=P, poison=True)
     kernels = ["auto", "valu"]
+    if dt != "f32" and D in (64, 128) and bs >= 8 and H // Hkv <= 16:
+        kernels.append("mfma")  # the grouped-head kernel (also one column: MHA)
     for kernel in kernels:
         out, tmp, ml, es = run_gpu(w, partition_size=P, kernel=kernel)
         check_partials(w, orc, tmp, ml, es, partition_size=P)
