@@ -305,8 +305,7 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
         float mloc = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[j]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+        mloc = across32(across16(mloc, MaxOp{}), MaxOp{});
         const float mn = fmaxf(m, mloc);
         alpha = fast_exp2(m - mn);
         m = mn;
@@ -370,8 +369,7 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     int parked = 0;
     int64_t next_boundary = start64 + len64;
     auto flush = [&](float* m_out, float* l_out, f32x4* rows) {
-        float lt = l + __shfl_xor(l, 16, kWave);
-        lt += __shfl_xor(lt, 32, kWave);
+        const float lt = across32(across16(l, SumOp{}), SumOp{});
         const float inv = p.v_scale / lt;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) rows[mt * kWave] = acc[mt] * inv;
@@ -436,8 +434,7 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     // store instruction covers whole 128-byte lines (from registers a store
     // covers 64 bytes of each of its 16 rows). The parked splits go first;
     // the last split then takes slot 0.
-    float lt = l + __shfl_xor(l, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    const float lt = across32(across16(l, SumOp{}), SumOp{});
     const int cols = G * p.num_group;  // live columns
     constexpr int NCH = DV / 4;        // 16-byte pieces per row
     auto rows_out = [&](int slot, int split) {

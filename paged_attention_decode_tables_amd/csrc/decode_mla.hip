@@ -169,18 +169,6 @@ __device__ __forceinline__ void static_for(F&& f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// max and sum of x over lanes l and l ^ 32
-__device__ __forceinline__ float half_max(float x)
-{
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-}
-__device__ __forceinline__ float half_sum(float x)
-{
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
-}
-
 // Ring layout of one chunk (32 latent rows): the first 64 16-byte pieces of
 // every row (the 512 value columns, also the first 512 key columns) as a
 // 1 KB row, then the last 8 pieces (the remaining key columns) of all 32
@@ -752,7 +740,7 @@ void k_decode_mla(DecodeParams p)
 #pragma unroll
         for (int r = 3; r < 15; r += 2) mx = max3f(mx, z[r], z[r + 1]);
         mx = fmaxf(mx, z[15]);
-        float mloc = half_max(mx);  // token 0 is valid, so lane half 0 has a finite score
+        float mloc = across32(mx, MaxOp{});  // token 0 is valid, so lane half 0 has a finite score
         if constexpr (!ALIBI) mloc *= scale;
         mref = mref == -INFINITY ? mloc + shift : mref;
         over |= mloc > mref + kHeadroom;
@@ -939,7 +927,7 @@ void k_decode_mla(DecodeParams p)
     lds_barrier();  // every wave is done with the P buffer
 
     // statistics of head h; every wave needs the sums of all G heads
-    l = half_sum(l);
+    l = across32(l, SumOp{});
     float* lsum = reinterpret_cast<float*>(&pbuf[0]);
     const int64_t mloff = (int64_t)(s * p.num_group + qg) * p.ml_ss + (int64_t)h * p.ml_sh + part;
     if (hl == 0) {
