@@ -127,7 +127,8 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if ((a->q_stride_s * esz) % 16 || (a->q_stride_h * esz) % 16 || (a->k_stride_b * kv_esz) % 16 ||
         (a->k_stride_h * kv_esz) % 16 || (a->v_stride_b * kv_esz) % 16 || (a->v_stride_h * kv_esz) % 16 ||
         a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
-        return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
+        return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep query and cache rows 16-byte aligned and "
+                    "tmp_output rows 4-element aligned");
     if (parts > kMaxGridYZ || (int64_t)a->num_heads * ng > kMaxGridYZ)
         return fail(PA_ENOTSUP, "paged_attn_decode: partitions and num_heads * num_group must be <= %d", kMaxGridYZ);
     if ((int64_t)a->num_seqs * ng * a->num_heads > 0x7fffffff)

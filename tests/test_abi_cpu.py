@@ -134,6 +134,7 @@ DECODE_BAD = [
     ("grid_rows", dict(num_group=1 << 27), api.PA_ENOTSUP),
     ("tmp_dtype_fp8", dict(tmp_dtype=api.PA_FP8_E4M3), api.PA_EINVAL),
     ("tmp_dtype_neg", dict(tmp_dtype=-1), api.PA_EINVAL),
+    ("tmp_row_misaligned", dict(tmp_stride_p=130), api.PA_ENOTSUP),
 ]
 
 
