@@ -24,7 +24,9 @@
  *     and completes asynchronously.
  *   - Strides are in ELEMENTS. Index tensors honour every stride ([PR35765]
  *     review); for the caches and activations the innermost dimensions must
- *     be packed as stated, anything else returns PA_ENOTSUP.
+ *     be packed as stated, anything else returns PA_ENOTSUP. Their base
+ *     pointers and outer strides must keep every row 16-byte aligned
+ *     (PA_ENOTSUP otherwise).
  *   - Return value: PA_OK (0) or a negative code. Arguments are validated on
  *     the host before any launch; an error leaves every output untouched.
  *     Values stored in device memory (lengths, block ids) cannot be checked

@@ -124,11 +124,11 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if (!aligned16(a->query) || !aligned16(a->key_cache) || !aligned16(a->value_cache) ||
         !aligned16(a->tmp_output))
         return fail(PA_ENOTSUP, "paged_attn_decode: query, caches and tmp_output must be 16-byte aligned");
+    const int64_t tmp_esz = a->tmp_dtype == PA_F32 ? 4 : 2;
     if ((a->q_stride_s * esz) % 16 || (a->q_stride_h * esz) % 16 || (a->k_stride_b * kv_esz) % 16 ||
         (a->k_stride_h * kv_esz) % 16 || (a->v_stride_b * kv_esz) % 16 || (a->v_stride_h * kv_esz) % 16 ||
-        a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
-        return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep query and cache rows 16-byte aligned and "
-                    "tmp_output rows 4-element aligned");
+        (a->tmp_stride_s * tmp_esz) % 16 || (a->tmp_stride_h * tmp_esz) % 16 || (a->tmp_stride_p * tmp_esz) % 16)
+        return fail(PA_ENOTSUP, "paged_attn_decode: outer strides must keep rows 16-byte aligned");
     if (parts > kMaxGridYZ || (int64_t)a->num_heads * ng > kMaxGridYZ)
         return fail(PA_ENOTSUP, "paged_attn_decode: partitions and num_heads * num_group must be <= %d", kMaxGridYZ);
     if ((int64_t)a->num_seqs * ng * a->num_heads > 0x7fffffff)
@@ -223,7 +223,9 @@ PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)
         return fail(PA_ENOTSUP, "paged_attn_reduce: innermost strides must be 1");
     if (!pa::reduce_supported(a->v_head_size))
         return fail(PA_ENOTSUP, "paged_attn_reduce: v_head_size %d is not built", a->v_head_size);
-    if (!aligned16(a->tmp_output) || a->tmp_stride_s % 4 || a->tmp_stride_h % 4 || a->tmp_stride_p % 4)
+    const int64_t tmp_esz = a->tmp_dtype == PA_F32 ? 4 : 2;
+    if (!aligned16(a->tmp_output) || (a->tmp_stride_s * tmp_esz) % 16 || (a->tmp_stride_h * tmp_esz) % 16 ||
+        (a->tmp_stride_p * tmp_esz) % 16)
         return fail(PA_ENOTSUP, "paged_attn_reduce: tmp_output rows must be 16-byte aligned");
     const int64_t pairs = (int64_t)a->num_seqs * ng * a->num_heads;
     if (pairs > 0x7fffffff) return fail(PA_ENOTSUP, "paged_attn_reduce: too many (row, head) pairs");

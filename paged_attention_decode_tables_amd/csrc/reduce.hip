@@ -2,9 +2,10 @@
 // outputs (paged_attention_v2_triton.py, _paged_attn_v2_reduce_kernel:
 // global max, rescale by exp(m_p - M) * l_p, normalise, weighted sum).
 //
-// C = Dv/4 threads cover a Dv-wide row as float4 columns and NG thread
-// groups take every NG-th split of one (query row, head); a 256-thread
-// workgroup holds 256 / (C * NG) heads of one query row. With fixed
+// C = Dv/EPT threads cover a Dv-wide row, EPT consecutive columns each (4
+// for fp32 rows, 8 for 16-bit rows: one 16-byte load either way), and NG
+// thread groups take every NG-th split of one (query row, head); a
+// 256-thread workgroup holds 256 / (C * NG) heads of one query row. With fixed
 // partitions NG is the smallest power of two that lets every group read its
 // splits in one round; with split counts or balanced splits, whose
 // sequences mostly have a few splits, NG is the least that fills a wave.
@@ -15,9 +16,11 @@
 // partitions the first batch is requested together with the sequence's
 // length (slots past the split count are inside the workspaces; what they
 // hold is dropped by a select, never multiplied). Otherwise only splits
-// below the count are read. Skewed batch 13.3 -> 7.2 us and MLA batch
-// 25.0 -> 17.2 us against one workgroup per head, 8 splits per batch and
-// groups sized by max_num_parts.
+// below the count are read; with balanced splits the first batch is
+// requested with the length as well (every slot lies in the workspaces and
+// the balanced rule fills a prefix of them). Skewed batch 13.3 -> 7.2 us
+// and MLA batch 25.0 -> 17.2 us against one workgroup per head, 8 splits
+// per batch and groups sized by max_num_parts.
 #include "kernels.h"
 
 namespace pa {
@@ -34,14 +37,34 @@ constexpr int kRedBatch = 8;  // splits per thread per round of loads (at most)
 // threads), so the row's length and split count are loaded once for all of
 // them and small per-head thread counts do not turn into many tiny
 // workgroups (split counts: 8192 one-wave workgroups on the skewed batch).
-template <int DV, int NG> constexpr int red_heads() { return kRedMaxThreads / (DV / 4 * NG) > 0 ? kRedMaxThreads / (DV / 4 * NG) : 1; }
+template <int C, int NG> constexpr int red_heads() { return kRedMaxThreads / (C * NG) > 0 ? kRedMaxThreads / (C * NG) : 1; }
+
+// columns per thread for split rows of element type TmpE
+template <class TmpE> constexpr int red_ept() { return TmpE::size == 4 ? 4 : 8; }
+
+// EPT consecutive partial values at p (16-byte aligned), widened
+template <class TmpE, int EPT>
+__device__ __forceinline__ void load_cols(const typename TmpE::storage* p, float (&v)[EPT])
+{
+    if constexpr (EPT == 4) {
+        const f32x4 w = load_tmp4<TmpE>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = w[i];
+    } else {
+        using S = typename TmpE::storage;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = to_f32(__builtin_bit_cast(S, (uint16_t)(w[i >> 1] >> (16 * (i & 1)))));
+    }
+}
 
 template <class OutE, class TmpE, int DV, int NG, int RB>
 __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C * NG * HPW = 256
 {
-    constexpr int C = DV / 4;             // threads per row (float4 columns)
-    constexpr int HPW = red_heads<DV, NG>();
-    __shared__ f32x4 acc_lds[HPW][NG][C];
+    constexpr int EPT = red_ept<TmpE>();  // columns per thread
+    constexpr int C = DV / EPT;           // threads per row
+    constexpr int HPW = red_heads<C, NG>();
+    __shared__ float acc_lds[HPW][NG][EPT][C];
     __shared__ float m_lds[HPW][NG], w_lds[HPW][NG];
 
     const int hs = threadIdx.x / (C * NG), tid = threadIdx.x % (C * NG);
@@ -54,12 +77,12 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     const bool head_ok = hraw < p.num_heads;
     const int h = head_ok ? hraw : p.num_heads - 1;
     const int s = row / p.num_group;
-    const int64_t obase = (int64_t)row * p.out_ss + (int64_t)h * p.out_sh + 4 * col;
+    const int64_t obase = (int64_t)row * p.out_ss + (int64_t)h * p.out_sh + EPT * col;
 
     const float* ml = p.max_logits + (int64_t)row * p.ml_ss + (int64_t)h * p.ml_sh;
     const float* es = p.exp_sums + (int64_t)row * p.ml_ss + (int64_t)h * p.ml_sh;
     using TT = typename TmpE::storage;
-    const TT* tmp = reinterpret_cast<const TT*>(p.tmp) + (int64_t)row * p.tmp_ss + (int64_t)h * p.tmp_sh + 4 * col;
+    const TT* tmp = reinterpret_cast<const TT*>(p.tmp) + (int64_t)row * p.tmp_ss + (int64_t)h * p.tmp_sh + EPT * col;
 
     const int L = p.seq_lens[s];
     // balanced splits (partition_size 0): every slot, empty ones skipped below
@@ -68,9 +91,15 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     // this thread's splits grp, grp + NG, ...: local max M (base e), sum W
     // of exp(m_p - M) l_p, and acc = sum of exp(m_p - M) l_p tmp_p
     float M = -INFINITY, W = 0.0f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    f32x4 rows[RB];
+    float acc[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) acc[i] = 0.0f;
+    float rows[RB][EPT];
     float mv[RB], lv[RB];
+    auto zero_row = [&](int r) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) rows[r][i] = 0.0f;
+    };
     // Fold one batch: an empty split (m = -inf) adds nothing; its row may
     // never have been written, so it is dropped by a select, not a multiply.
     auto fold = [&]() {
@@ -79,13 +108,15 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
         for (int r = 0; r < RB; ++r) mb = fmaxf(mb, mv[r]);
         // mb = -inf: nothing live yet (acc, W are 0); avoids exp2(-inf + inf)
         const float f = mb == -INFINITY ? 1.0f : fast_exp2((M - mb) * kLog2e);
-        acc *= f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) acc[i] *= f;
         W *= f;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const bool live = mv[r] != -INFINITY;
             const float w = live ? fast_exp2((mv[r] - mb) * kLog2e) * lv[r] : 0.0f;
-            acc += live ? w * rows[r] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) acc[i] += live ? w * rows[r][i] : 0.0f;
             W += w;
         }
         M = mb;
@@ -98,17 +129,19 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     // or past the split count are dropped once it is known (their rows and
     // statistics are never used). With split counts most of such a batch
     // would be empty slots, read for nothing (skewed batch 8.6 -> 9.4 us).
-    const bool early = !balanced && !p.num_splits;
+    // Balanced splits fill a prefix of the slots, most sequences more than a
+    // batch of them: the first batch is requested the same way.
+    const bool early = !p.num_splits;
     if (early) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int64_t q = q0 + (int64_t)r * NG;
             if (q < p.max_num_parts) {
-                rows[r] = load_tmp4<TmpE>(tmp + q * p.tmp_sp);
+                load_cols<TmpE, EPT>(tmp + q * p.tmp_sp, rows[r]);
                 mv[r] = ml[q];
                 lv[r] = es[q];
             } else {
-                rows[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                zero_row(r);
                 mv[r] = -INFINITY;
                 lv[r] = 0.0f;
             }
@@ -129,7 +162,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     if (n == 0) {  // the same for the whole workgroup (one row)
         if (grp == 0 && head_ok)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, 0.0f);
+            for (int i = 0; i < EPT; ++i) store_out<OutE>(p.out, obase + i, 0.0f);
         return;
     }
     if (early) {
@@ -140,6 +173,13 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
                 lv[r] = 0.0f;
             }
         }
+        if (balanced) {
+            // once this group meets an empty slot, every later one is empty
+            bool ended = false;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) ended |= mv[r] == -INFINITY;
+            if (ended) n = q0 + 1;
+        }
         fold();
         q0 += (int64_t)NG * RB;
     }
@@ -149,11 +189,11 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
             for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 if (q < n) {
-                    rows[r] = load_tmp4<TmpE>(tmp + q * p.tmp_sp);
+                    load_cols<TmpE, EPT>(tmp + q * p.tmp_sp, rows[r]);
                     mv[r] = ml[q];
                     lv[r] = es[q];
                 } else {
-                    rows[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    zero_row(r);
                     mv[r] = -INFINITY;
                     lv[r] = 0.0f;
                 }
@@ -174,14 +214,17 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
-                rows[r] = mv[r] != -INFINITY ? load_tmp4<TmpE>(tmp + q * p.tmp_sp)
-                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+                if (mv[r] != -INFINITY)
+                    load_cols<TmpE, EPT>(tmp + q * p.tmp_sp, rows[r]);
+                else
+                    zero_row(r);
             }
         }
         fold();
     }
 
-    acc_lds[hs][grp][col] = acc;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) acc_lds[hs][grp][i][col] = acc[i];
     if (col == 0) {
         m_lds[hs][grp] = M;
         w_lds[hs][grp] = W;
@@ -191,26 +234,29 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     float Mt = m_lds[hs][0];
 #pragma unroll
     for (int g = 1; g < NG; ++g) Mt = fmaxf(Mt, m_lds[hs][g]);
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    float a[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) a[i] = 0.0f;
     float Wt = 0.0f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const float f = m_lds[hs][g] == -INFINITY ? 0.0f : fast_exp2((m_lds[hs][g] - Mt) * kLog2e);
-        a += f * acc_lds[hs][g][col];
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) a[i] += f * acc_lds[hs][g][i][col];
         Wt += f * w_lds[hs][g];
     }
     const float inv = Wt > 0.0f ? 1.0f / Wt : 0.0f;  // no live split: zero row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_out<OutE>(p.out, obase + i, a[i] * inv);
+    for (int i = 0; i < EPT; ++i) store_out<OutE>(p.out, obase + i, a[i] * inv);
 }
 
 bool reduce_supported(int Dv) { return Dv == 64 || Dv == 128 || Dv == 256 || Dv == 512; }
 
 // Split groups for up to max_parts splits: cdiv(max_parts, kRedBatch)
-// rounded up to a power of two, within [max(1, 64 / C), 256 / C].
-static int reduce_groups(int Dv, int max_parts)
+// rounded up to a power of two, within [max(1, 64 / C), 256 / C] (C threads
+// per row).
+static int reduce_groups(int C, int max_parts)
 {
-    const int C = Dv / 4;
     const int lo = C >= 64 ? 1 : 64 / C, hi = kRedMaxThreads / C;
     const int want = (max_parts + kRedBatch - 1) / kRedBatch;
     int ng = lo;
@@ -221,9 +267,10 @@ static int reduce_groups(int Dv, int max_parts)
 template <class OutE, class TmpE, int DV, int NG>
 static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
 {
-    constexpr int HPW = red_heads<DV, NG>();
+    constexpr int C = DV / red_ept<TmpE>();
+    constexpr int HPW = red_heads<C, NG>();
     const int64_t hblocks = (p.num_heads + HPW - 1) / HPW;
-    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * hblocks)), block(DV / 4 * NG * HPW);
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_group * hblocks)), block(C * NG * HPW);
     const bool few = p.num_splits || p.partition_size == 0 || (p.max_num_parts + NG - 1) / NG <= 4;
     if (few) hipLaunchKernelGGL((k_reduce<OutE, TmpE, DV, NG, 4>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_reduce<OutE, TmpE, DV, NG, kRedBatch>), grid, block, 0, st, p);
@@ -232,11 +279,11 @@ static void launch_reduce_ng(const ReduceParams& p, hipStream_t st)
 template <class OutE, class TmpE, int DV>
 static void launch_reduce_dv(const ReduceParams& p, hipStream_t st)
 {
-    constexpr int C = DV / 4, LO = C >= 64 ? 1 : 64 / C, HI = kRedMaxThreads / C;
+    constexpr int C = DV / red_ept<TmpE>(), LO = C >= 64 ? 1 : 64 / C, HI = kRedMaxThreads / C;
     // split counts and balanced splits: one wave's worth of groups (most
     // sequences have a few splits; smaller workgroups keep every one resident)
     const bool few = p.num_splits || p.partition_size == 0;
-    const int ng = few ? LO : reduce_groups(DV, p.max_num_parts);
+    const int ng = few ? LO : reduce_groups(C, p.max_num_parts);
     if (ng <= LO) launch_reduce_ng<OutE, TmpE, DV, LO>(p, st);
     else if (ng <= 2 * LO || 2 * LO > HI) launch_reduce_ng<OutE, TmpE, DV, (2 * LO <= HI ? 2 * LO : HI)>(p, st);
     else launch_reduce_ng<OutE, TmpE, DV, HI>(p, st);

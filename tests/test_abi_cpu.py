@@ -135,6 +135,8 @@ DECODE_BAD = [
     ("tmp_dtype_fp8", dict(tmp_dtype=api.PA_FP8_E4M3), api.PA_EINVAL),
     ("tmp_dtype_neg", dict(tmp_dtype=-1), api.PA_EINVAL),
     ("tmp_row_misaligned", dict(tmp_stride_p=130), api.PA_ENOTSUP),
+    # 16-bit rows: a stride of 4 elements keeps them 8-byte aligned only
+    ("tmp16_row_misaligned", dict(tmp_dtype=api.PA_BF16, tmp_stride_p=132), api.PA_ENOTSUP),
 ]
 
 
@@ -243,6 +245,7 @@ REDUCE_BAD = [
     ("dv", dict(v_head_size=96), api.PA_ENOTSUP),
     ("inner", dict(out_stride_d=2), api.PA_ENOTSUP),
     ("tmp_align", dict(tmp_stride_p=130), api.PA_ENOTSUP),
+    ("tmp16_align", dict(tmp_dtype=api.PA_BF16, tmp_stride_p=132), api.PA_ENOTSUP),
     ("neg_num_group", dict(num_group=-1), api.PA_EINVAL),
     ("tmp_dtype", dict(tmp_dtype=9), api.PA_EINVAL),
 ]
