@@ -12,8 +12,9 @@ physical blocks in random order, 512-token partitions (64 per sequence).
 
 Prints one JSON line: KV read GB/s (value), microseconds per step, the
 roofline of the dominant kernel (phase 1), the same GPU's plain read rate on
-the workload's gather pattern and on contiguous memory (read_stream), and
-the CPU oracle timed on a bounded sample of the same workload.
+the workload's gather pattern and on contiguous memory (read_stream), the
+same step captured into a HIP graph and replayed (graph_replay), and the
+CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -414,6 +415,8 @@ def main():
     ap.add_argument("--kv-cache", choices=("same", "fp8"), default="same",
                     help="fp8: the same workload with FP8 E4M3 caches (configs 2-4)")
     ap.add_argument("--alibi", action="store_true", help="the same workload with ALiBi slopes")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph_replay field (one step captured into a HIP graph, replayed K times)")
     ap.add_argument("--kernel", choices=("auto", "valu"), default="auto",
                     help="phase-1 kernel hint (valu: the vector-ALU kernel, for comparison)")
     ap.add_argument("--tmp-dtype", choices=("query", "f32"), default="query",
@@ -495,6 +498,36 @@ def main():
     torch.cuda.synchronize()
     dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     red_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    # Graph region: one step captured into a HIP graph (the library
+    # allocates nothing and never synchronises, so a captured step serves
+    # every replay), replayed K times back to back.
+    graph = None
+    if not args.no_graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step.run()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step.run()
+            for _ in range(2):
+                g.replay()
+            gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            gs.record()
+            for _ in range(K):
+                g.replay()
+            ge.record()
+            torch.cuda.synchronize()
+            g_ms = gs.elapsed_time(ge) / K
+            graph = {"us_per_step": round(g_ms * 1e3, 2), "kv_gbs": round(w.kv_bytes() / (g_ms * 1e-3) / 1e9, 1)}
+            del g
+        except Exception as e:  # reported, not fatal: the eager step is the measurement
+            graph = {"error": str(e)[:200]}
     kv = w.kv_bytes()
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (dec_ms * 1e-3) / 1e9
@@ -575,6 +608,8 @@ def main():
     }
     if cold is not None:
         res["cold_cache"] = cold
+    if graph is not None:
+        res["graph_replay"] = graph
     if not args.no_read_stream:
         log("bench: read-stream legs")
         rs = read_stream(w, step, reps=20)
