@@ -181,6 +181,36 @@ def test_alibi_latent_rows(orc, kernel):
         check_output(w, orc, out)
 
 
+@pytest.mark.parametrize("kv,dtype,H", [("same", "bf16", 128), ("same", "bf16", 64), ("fp8", "bf16", 128),
+                                         ("same", "f16", 128), ("fp8", "f16", 64)])
+def test_alibi_latent_rows_balanced(orc, kv, dtype, H):
+    """ALiBi on the latent-row kernel with balanced splits (the form the MLA
+    benchmark runs): every piece's statistics and row against the oracle on
+    its token range (max logits moved by the bias offset of the range), and
+    the merged output; fp8 rows and f16 queries included."""
+    import test_gpu_parity as tp
+    say(f"alibi latent rows, balanced: kv={kv} dtype={dtype} H={H}")
+    lens = [1, 300, 2049, 0, 1000, 4100]
+    w = workloads.mla_custom(seed=140 + H, seq_lens=lens, num_heads=H, poison=True, dtype=dtype, kv_cache=kv)
+    w.alibi_slopes = workloads.alibi_slopes(H)
+    workers, max_parts = 7, 12
+    out, tmp, ml, es = tp.run_balanced(w, workers, max_parts)
+    tp.check_balanced_pieces(w, orc, tmp, ml, es, workers, max_parts)
+    check_output(w, orc, out)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_alibi_latent_rows_fp8(orc, dtype):
+    """ALiBi with fp8 latent rows, fixed 512-token splits."""
+    say(f"alibi latent rows, fp8 rows, {dtype}")
+    w = workloads.mla_custom(seed=150, seq_lens=[700, 33, 1537, 1], num_heads=128, poison=True, dtype=dtype,
+                             kv_cache="fp8")
+    w.alibi_slopes = workloads.alibi_slopes(128)
+    out, tmp, ml, es = run_gpu(w)
+    check_partials(w, orc, tmp, ml, es)
+    check_output(w, orc, out)
+
+
 def test_alibi_latent_rows_reference_guards(orc):
     """The latent-row kernel's raised ALiBi reference and its two reruns.
     One 2048-token split per sequence, slopes 0.07 (the bias grows by ~202
