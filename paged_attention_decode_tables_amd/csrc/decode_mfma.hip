@@ -437,14 +437,37 @@ __device__ __forceinline__ void mfma_run(const DecodeParams& p, int kvh, int s, 
     const float lt = across32(across16(l, SumOp{}), SumOp{});
     const int cols = G * p.num_group;  // live columns
     constexpr int NCH = DV / 4;        // 16-byte pieces per row
+    // Piece k of column c (values 4k .. 4k+3) in the park layout.
+    auto parked_piece = [&](int slot, int c, int k) -> f32x4 {
+        return park[(slot * MT + (k >> 2)) * kWave + 16 * (k & 3) + c];
+    };
     auto rows_out = [&](int slot, int split) {
-        for (int e = lane; e < cols * NCH; e += kWave) {
-            const int c = e / NCH, k = e - c * NCH;  // column, piece (dv 4k .. 4k+3)
-            const f32x4 v = park[(slot * MT + (k >> 2)) * kWave + 16 * (k & 3) + c];
+        auto row_at = [&](int c) -> int64_t {  // element offset of column c's row
             const int cq = c / G, ch = c - cq * G;
-            const int64_t o = (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
-                              (int64_t)split * p.tmp_sp + 4 * k;
-            store_tmp4<PA_PARTIAL_NT>(p.tmp, p.tmp_dtype, o, v);
+            return (int64_t)(s * p.num_group + cq) * p.tmp_ss + (int64_t)(kvh * G + ch) * p.tmp_sh +
+                   (int64_t)split * p.tmp_sp;
+        };
+        if (p.tmp_dtype == PA_F32) {
+            for (int e = lane; e < cols * NCH; e += kWave) {
+                const int c = e / NCH, k = e - c * NCH;  // column, piece
+                store_tmp4<PA_PARTIAL_NT>(p.tmp, PA_F32, row_at(c) + 4 * k, parked_piece(slot, c, k));
+            }
+        } else {
+            // 16-bit rows: 8 values a lane, 16-byte stores like the fp32 rows
+            // (measured: phase 2 reads rows written in 8-byte pieces slower)
+            constexpr int NC8 = DV / 8;
+            const bool bf = p.tmp_dtype == PA_BF16;
+            for (int e = lane; e < cols * NC8; e += kWave) {
+                const int c = e / NC8, k2 = e - c * NC8;
+                const f32x4 a = parked_piece(slot, c, 2 * k2), b = parked_piece(slot, c, 2 * k2 + 1);
+                const u32x4 w = bf ? u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                           pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])}
+                                   : u32x4{pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]),
+                                           pack_f16x2(b[0], b[1]), pack_f16x2(b[2], b[3])};
+                u32x4* at = reinterpret_cast<u32x4*>(p.tmp) + ((row_at(c) + 8 * k2) >> 3);
+                if constexpr (PA_PARTIAL_NT) __builtin_nontemporal_store(w, at);
+                else *at = w;
+            }
         }
     };
     wave_lds_sync();  // other lanes' parked rows
