@@ -46,8 +46,10 @@ def log(msg):
 
 
 def kernel_kind(w) -> str:
-    """Which phase-1 kernel the library dispatches for workload `w` (the
-    selection rule of paged_attn_decode with the automatic kernel hint)."""
+    """Which phase-1 kernel the library dispatches for workload `w` with the
+    automatic kernel hint, from its shapes alone (the rule include/pagedattn.h
+    states; the library's own answer, paged_attn_decode_kernel, needs device
+    buffers and is what the measured step reports)."""
     group = w.num_heads // w.num_kv_heads
     low = w.dtype in (torch.float16, torch.bfloat16)
     if low and w.head_size == 576 and w.v_head_size == 512 and w.block_size == 1 \
@@ -103,14 +105,23 @@ class Step:
         if self.indptr is not None:
             pad.build_page_indices(self.flat, g.block_tables, self.indptr)
 
-    def decode(self):
+    def _decode_args(self):
         w, g = self.w, self.g
         bt = self.flat if self.indptr is not None else g.block_tables
-        pad.paged_attn_decode(self.tmp, self.es, self.ml, g.query, g.key_cache, g.value_cache, bt,
-                              g.seq_lens, w.scale, w.max_seq_len, partition_size=self.partition,
-                              num_splits=self.ns, kv_indptr=self.indptr, num_workers=self.workers,
-                              alibi_slopes=g.alibi_slopes, k_scale=w.k_scale, v_scale=w.v_scale,
-                              num_group=w.num_group, kernel=self.kernel)
+        return ((self.tmp, self.es, self.ml, g.query, g.key_cache, g.value_cache, bt, g.seq_lens, w.scale,
+                 w.max_seq_len),
+                dict(partition_size=self.partition, num_splits=self.ns, kv_indptr=self.indptr,
+                     num_workers=self.workers, alibi_slopes=g.alibi_slopes, k_scale=w.k_scale,
+                     v_scale=w.v_scale, num_group=w.num_group, kernel=self.kernel))
+
+    def decode(self):
+        args, kw = self._decode_args()
+        pad.paged_attn_decode(*args, **kw)
+
+    def kernel_kind(self) -> str:
+        """The phase-1 kernel the library launches for this step."""
+        args, kw = self._decode_args()
+        return pad.paged_attn_decode_kernel(*args, **kw)
 
     def reduce(self):
         w, g = self.w, self.g
@@ -385,7 +396,7 @@ def bench_spec_table(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
+def build_parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -413,7 +424,7 @@ def main():
                          "SWA page-table concat on the MLA batch")
     ap.add_argument("--md-workload", choices=sorted(MD_WORKLOADS), default="metadata_skewed_ps32_swa")
     ap.add_argument("--kv-cache", choices=("same", "fp8"), default="same",
-                    help="fp8: the same workload with FP8 E4M3 caches (configs 2-4)")
+                    help="fp8: the same workload with FP8 E4M3 caches (configs 2-5)")
     ap.add_argument("--alibi", action="store_true", help="the same workload with ALiBi slopes")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph_replay field (one step captured into a HIP graph, replayed K times)")
@@ -425,7 +436,11 @@ def main():
     ap.add_argument("--num-group", type=int, default=1,
                     help="query tokens per sequence (configs 2-5): each attends over the whole "
                          "sequence; the grouped-head kernel reads the cache once for all of them")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = build_parser().parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only: the decode path has no "
@@ -456,13 +471,13 @@ def main():
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config, kv_cache=args.kv_cache, alibi=args.alibi,
                          num_group=args.num_group)
-    kind = kernel_kind(w) if args.kernel == "auto" else args.kernel
     # The MLA workload's split policy is not fixed by its definition: it runs
     # with balanced splits, one token range per compute unit.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    workers = cus if (kind == "mla" and not args.fixed_splits) else 0
+    workers = cus if (kernel_kind(w) == "mla" and args.kernel == "auto" and not args.fixed_splits) else 0
     tmp_dtype = w.dtype if args.tmp_dtype == "query" else torch.float32
     step = Step(w, balanced_workers=workers, tmp_dtype=tmp_dtype, kernel=args.kernel)
+    kind = step.kernel_kind()  # the library's own choice
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup}")

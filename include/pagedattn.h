@@ -160,8 +160,9 @@ typedef struct pa_decode_args {
     int32_t dtype;               /* pa_dtype of query, key_cache and value_cache */
     int32_t kernel_hint;         /* PA_KERNEL_AUTO (0): pick the kernel; PA_KERNEL_VALU: the
                                     vector-ALU kernel; PA_KERNEL_MFMA: the matrix-core kernel
-                                    (PA_ENOTSUP where it does not apply). Results agree
-                                    within the documented tolerance either way. */
+                                    (PA_ENOTSUP where it does not apply); any other value
+                                    is PA_EINVAL. Results agree within the documented
+                                    tolerance either way. */
     int32_t num_workers;         /* balanced splits only (partition_size == 0): number of
                                     token ranges, typically the compute-unit count;
                                     ignored otherwise */
@@ -181,6 +182,7 @@ typedef struct pa_decode_args {
 #define PA_KERNEL_AUTO 0
 #define PA_KERNEL_VALU 1
 #define PA_KERNEL_MFMA 2
+#define PA_KERNEL_MLA 3  /* returned by paged_attn_decode_kernel only; not a hint */
 
 /*
  * Supported combinations (others return PA_ENOTSUP):
@@ -198,6 +200,16 @@ typedef struct pa_decode_args {
  * need the latent-row kernel (PA_ENOTSUP otherwise).
  */
 int paged_attn_decode(const pa_decode_args* args, void* stream);
+
+/*
+ * The phase-1 kernel paged_attn_decode would launch for `args`
+ * (PA_KERNEL_VALU: the vector kernel, PA_KERNEL_MFMA: the grouped-head
+ * matrix-core kernel, PA_KERNEL_MLA: the latent-row kernel), after the same
+ * validation and with the same error codes, or a negative error. Host only:
+ * nothing is launched or read through the pointers, which must still pass
+ * the checks (non-null, aligned). An empty batch reports the kernel too.
+ */
+int paged_attn_decode_kernel(const pa_decode_args* args);
 
 /*
  * Phase 2 ([PAv2] _paged_attn_v2_reduce_kernel): for each (s, h), over the n

@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     normal_decode_set_metadata,
     num_kv_splits,
     paged_attn_decode,
+    paged_attn_decode_kernel,
     paged_attn_decode_static,
     paged_attn_reduce,
     paged_token_offsets,

@@ -20,6 +20,7 @@ LIB_NAME = "libpagedattn.so"
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_ELAUNCH = 0, -1, -2, -3
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_KERNEL = {"auto": 0, "valu": 1, "mfma": 2}
+KERNEL_NAMES = {1: "valu", 2: "mfma", 3: "mla"}  # paged_attn_decode_kernel results
 _DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 _FP8_CACHE = (torch.uint8, torch.float8_e4m3fn)  # cache tensors holding E4M3 codes
 _CODE_NAMES = {PA_EINVAL: "PA_EINVAL", PA_ENOTSUP: "PA_ENOTSUP", PA_ELAUNCH: "PA_ELAUNCH"}
@@ -106,6 +107,7 @@ def load_library() -> ctypes.CDLL:
             f"{path} is missing: build it with `python -m paged_attention_decode_tables_amd.build`")
     lib = ctypes.CDLL(path)
     lib.paged_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+    lib.paged_attn_decode_kernel.argtypes = [ctypes.POINTER(DecodeArgs)]
     lib.paged_attn_reduce.argtypes = [ctypes.POINTER(ReduceArgs), _vp]
     lib.paged_attn_decode_static.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _i64, _i64, _i32, _vp]
     lib.build_page_indices.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp]
@@ -294,6 +296,26 @@ def paged_attn_decode(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logi
                      seq_lens, scale, max_seq_len, partition_size, num_splits, kv_indptr, kernel,
                      num_workers, alibi_slopes, k_scale, v_scale, num_group, stream)
     _check(lib.paged_attn_decode(ctypes.byref(a), _stream(stream)))
+
+
+def paged_attn_decode_kernel(tmp_output: torch.Tensor, exp_sums: torch.Tensor, max_logits: torch.Tensor,
+                             query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                             block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                             max_seq_len: int, *, partition_size: int = 512,
+                             num_splits: Optional[torch.Tensor] = None,
+                             kv_indptr: Optional[torch.Tensor] = None, kernel: str = "auto",
+                             num_workers: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
+                             k_scale: float = 1.0, v_scale: float = 1.0, num_group: int = 1,
+                             stream=None) -> str:
+    """The phase-1 kernel paged_attn_decode would launch with these
+    arguments ("valu", "mfma" or "mla"); nothing is launched."""
+    lib = load_library()
+    a = _decode_args(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                     seq_lens, scale, max_seq_len, partition_size, num_splits, kv_indptr, kernel,
+                     num_workers, alibi_slopes, k_scale, v_scale, num_group, stream)
+    rc = lib.paged_attn_decode_kernel(ctypes.byref(a))
+    _check(min(rc, 0))
+    return KERNEL_NAMES[rc]
 
 
 def paged_attn_decode_static(output: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

@@ -63,9 +63,14 @@ namespace pa {
 void set_last_error(const char* msg) { g_last_error = msg; }
 }  // namespace pa
 
-PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
+// The whole host side of paged_attn_decode: validation, parameters and the
+// kernel choice. With `kind` non-null nothing is launched and the chosen
+// kernel (PA_KERNEL_VALU / _MFMA / _MLA) is stored there instead.
+static int decode_impl(const pa_decode_args* a, void* stream, int* kind)
 {
     if (!a) return fail(PA_EINVAL, "paged_attn_decode: args is NULL");
+    if (a->kernel_hint != PA_KERNEL_AUTO && a->kernel_hint != PA_KERNEL_VALU && a->kernel_hint != PA_KERNEL_MFMA)
+        return fail(PA_EINVAL, "paged_attn_decode: kernel_hint %d is not PA_KERNEL_AUTO, _VALU or _MFMA", a->kernel_hint);
     const int esz = elem_size(a->dtype);
     if (!esz) return fail(PA_EINVAL, "paged_attn_decode: unknown dtype %d", a->dtype);
     const bool fp8 = a->kv_dtype == PA_FP8_E4M3;
@@ -109,7 +114,7 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     }
     if (a->tmp_dtype != PA_F32 && a->tmp_dtype != PA_F16 && a->tmp_dtype != PA_BF16)
         return fail(PA_EINVAL, "paged_attn_decode: tmp_dtype %d is not PA_F32, PA_F16 or PA_BF16", a->tmp_dtype);
-    if (a->num_seqs == 0 || parts == 0) return PA_OK;
+    if ((a->num_seqs == 0 || parts == 0) && !kind) return PA_OK;
     if (!a->tmp_output || !a->exp_sums || !a->max_logits || !a->query || !a->key_cache ||
         !a->value_cache || !a->block_tables || !a->seq_lens)
         return fail(PA_EINVAL, "paged_attn_decode: a required pointer is NULL");
@@ -186,9 +191,11 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     if (balanced && (!mla_ok || a->kernel_hint == PA_KERNEL_VALU))
         return fail(PA_ENOTSUP, "paged_attn_decode: balanced splits are built for the MLA matrix-core kernel only "
                                 "(latent rows: V the leading columns of K, page size 1)");
-    if (a->kernel_hint != PA_KERNEL_VALU && mla_ok)
+    if (a->kernel_hint != PA_KERNEL_VALU && mla_ok) {
+        if (kind) return *kind = PA_KERNEL_MLA, PA_OK;
         return launched(pa::launch_decode_mla(p, a->dtype, a->num_seqs, (int)parts, st),
                         "paged_attn_decode (mla)");
+    }
     // Automatic choice: the matrix cores where several (query token, head)
     // columns share a kv head's rows (a real contraction), and for fp8 caches
     // also with one column. With query-dtype caches one column runs on the
@@ -196,11 +203,23 @@ PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream)
     // the single-column tile buys nothing there; with fp8 caches the matrix
     // kernel's register-tile staging is 7% faster (46.3 vs 49.8 us).
     const bool mfma_auto = mfma_ok && (group * ng > 1 || fp8);
-    if (a->kernel_hint == PA_KERNEL_MFMA ? mfma_ok : (a->kernel_hint != PA_KERNEL_VALU && mfma_auto))
+    if (a->kernel_hint == PA_KERNEL_MFMA ? mfma_ok : (a->kernel_hint != PA_KERNEL_VALU && mfma_auto)) {
+        if (kind) return *kind = PA_KERNEL_MFMA, PA_OK;
         return launched(pa::launch_decode_mfma(p, a->dtype, D, Dv, a->num_seqs, (int)parts, st),
                         "paged_attn_decode (mfma)");
+    }
+    if (kind) return *kind = PA_KERNEL_VALU, PA_OK;
     return launched(pa::launch_decode_valu(p, a->dtype, D, Dv, a->num_seqs, (int)parts, st),
                     "paged_attn_decode (valu)");
+}
+
+PA_EXPORT int paged_attn_decode(const pa_decode_args* a, void* stream) { return decode_impl(a, stream, nullptr); }
+
+PA_EXPORT int paged_attn_decode_kernel(const pa_decode_args* a)
+{
+    int kind = 0;
+    const int rc = decode_impl(a, nullptr, &kind);
+    return rc < 0 ? rc : kind;
 }
 
 PA_EXPORT int paged_attn_reduce(const pa_reduce_args* a, void* stream)

@@ -453,3 +453,55 @@ def test_read_probe_rejects_on_the_host(lib):
     assert f(None, None, FAKE, 10, 1, 4096, 0, 4096, FAKE, 4, None) == api.PA_EINVAL  # no base
     assert f(FAKE, None, FAKE, 10, 1, 4096, 0, 4096, FAKE, 0, None) == api.PA_EINVAL  # no workgroups
     assert b"pa_read_probe" in lib.pa_last_error()
+
+
+# ---------------------------------------------------------------------------
+# paged_attn_decode_kernel: the kernel choice, host only (no GPU)
+# ---------------------------------------------------------------------------
+def _latent_args(H=128, dtype=api.PA_BF16, fp8=False):
+    """Latent rows: D 576, Dv 512, page size 1, V the leading columns of K."""
+    a = good_decode(dtype=dtype, D=576, Dv=512, H=H, Hkv=1, bs=1)
+    if fp8:
+        a.x, a.kv_dtype, a.k_scale, a.v_scale = 16, api.PA_FP8_E4M3, 0.05, 0.05
+        a.k_stride_dx, a.k_stride_bs = 16, 16
+    a.value_cache = a.key_cache
+    a.v_stride_b, a.v_stride_h, a.v_stride_d, a.v_stride_bs = a.k_stride_b, a.k_stride_h, 1, 1
+    return a
+
+
+KERNEL_CHOICE = [
+    ("mha_one_column", lambda: good_decode(H=8, Hkv=8), "valu"),
+    ("mha_one_column_fp8", lambda: good_fp8(H=8, Hkv=8), "mfma"),
+    ("mha_one_column_mfma_hint", lambda: _mut(good_decode(H=8, Hkv=8), kernel_hint=api.PA_KERNEL["mfma"]), "mfma"),
+    ("gqa_8", lambda: good_decode(H=8, Hkv=1), "mfma"),
+    ("gqa_8_valu_hint", lambda: _mut(good_decode(H=8, Hkv=1), kernel_hint=api.PA_KERNEL["valu"]), "valu"),
+    ("gqa_32_columns", lambda: good_decode(H=32, Hkv=1), "valu"),
+    ("mha_two_tokens", lambda: _mut(good_decode(H=8, Hkv=8), num_group=2), "mfma"),
+    ("fp32", lambda: good_decode(dtype=api.PA_F32, D=64, Dv=64, H=8, Hkv=1), "valu"),
+    ("head_256", lambda: good_decode(D=256, Dv=256, H=8, Hkv=1), "valu"),
+    ("small_blocks", lambda: good_decode(H=8, Hkv=1, bs=4), "valu"),
+    ("latent_rows", lambda: _latent_args(), "mla"),
+    ("latent_rows_64", lambda: _latent_args(H=64), "mla"),
+    ("latent_rows_f16", lambda: _latent_args(dtype=api.PA_F16), "mla"),
+    ("latent_rows_fp8", lambda: _latent_args(fp8=True), "mla"),
+    ("latent_rows_valu_hint", lambda: _mut(_latent_args(), kernel_hint=api.PA_KERNEL["valu"]), "valu"),
+    ("latent_rows_32_heads", lambda: _latent_args(H=32), "valu"),
+    ("latent_rows_not_aliased", lambda: _mut(_latent_args(), value_cache=FAKE + 4096), "valu"),
+    ("empty_batch", lambda: _mut(good_decode(H=8, Hkv=1), num_seqs=0), "mfma"),
+]
+
+
+@pytest.mark.parametrize("name,make,kind", KERNEL_CHOICE, ids=[c[0] for c in KERNEL_CHOICE])
+def test_decode_kernel_choice(lib, name, make, kind):
+    rc = lib.paged_attn_decode_kernel(ctypes.byref(make()))
+    assert rc > 0, lib.pa_last_error()
+    assert api.KERNEL_NAMES[rc] == kind
+
+
+def test_decode_kernel_choice_rejects_like_decode(lib):
+    for name, change, code in DECODE_BAD:
+        a = _mut(good_decode(), **change)
+        assert lib.paged_attn_decode_kernel(ctypes.byref(a)) == code, name
+    a = _mut(good_decode(), kernel_hint=7)
+    assert lib.paged_attn_decode_kernel(ctypes.byref(a)) == api.PA_EINVAL
+    assert lib.paged_attn_decode(ctypes.byref(a), None) == api.PA_EINVAL

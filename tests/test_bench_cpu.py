@@ -1,0 +1,55 @@
+"""bench.py on the CPU: the one-GPU contract and the kernel the benchmark
+expects the library to pick (the selection rule of paged_attn_decode with
+the automatic kernel hint, as include/pagedattn.h states it)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from paged_attention_decode_tables_amd import workloads  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == n and "one GPU" in line["error"]
+
+
+def _custom(**kw):
+    base = dict(seed=1, seq_lens=[40, 3], num_heads=8, num_kv_heads=8, head_size=128, block_size=16,
+                dtype="bf16")
+    base.update(kw)
+    return workloads.custom(**base)
+
+
+@pytest.mark.parametrize("name,w,kind", [
+    ("mha_one_column", lambda: _custom(), "valu"),
+    ("mha_one_column_fp8", lambda: _custom(kv_cache="fp8"), "mfma"),
+    ("gqa_8", lambda: _custom(num_kv_heads=1), "mfma"),
+    ("gqa_32_columns", lambda: _custom(num_heads=32, num_kv_heads=1), "valu"),
+    ("mha_two_tokens", lambda: _custom(num_group=2), "mfma"),
+    ("fp32", lambda: _custom(dtype="f32", num_kv_heads=1), "valu"),
+    ("head_256", lambda: _custom(head_size=256, num_kv_heads=1), "valu"),
+    ("small_blocks", lambda: _custom(block_size=4, num_kv_heads=1), "valu"),
+    ("latent_rows", lambda: workloads.mla_custom(seed=2, seq_lens=[50, 7], num_heads=128), "mla"),
+    ("latent_rows_64", lambda: workloads.mla_custom(seed=3, seq_lens=[50], num_heads=64), "mla"),
+    ("latent_rows_fp8", lambda: workloads.mla_custom(seed=4, seq_lens=[50], num_heads=128, kv_cache="fp8"), "mla"),
+], ids=lambda x: x if isinstance(x, str) else "")
+def test_kernel_kind(name, w, kind):
+    assert bench.kernel_kind(w()) == kind
+
+
+def test_headline_workload_is_the_default():
+    """No flags: the long-context GQA batch (8 x 32768 tokens, 64/8 heads,
+    head_dim 128, block size 16, 512-token partitions)."""
+    args = bench.build_parser().parse_args([])
+    assert args.config == 3 and args.gpus == 1 and args.op == "decode" and args.kv_cache == "same"
