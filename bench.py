@@ -511,8 +511,22 @@ def main():
         step.reduce()
         ev[k][2].record()
     torch.cuda.synchronize()
-    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ev_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     red_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    # Phase-1 region: K phase-1 launches back to back (after one step's
+    # split counts and page list), bracketed by two events: the kernel's
+    # average duration plus the launch gaps, without an event packet next to
+    # every launch (those add a few microseconds each).
+    step.pre()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record()
+    for _ in range(K):
+        step.decode()
+    d1.record()
+    torch.cuda.synchronize()
+    dec_ms = d0.elapsed_time(d1) / K
 
     # Graph region: one step captured into a HIP graph (the library
     # allocates nothing and never synchronises, so a captured step serves
@@ -617,7 +631,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": f"paged_attn_decode ({kind})",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(dec_ms * 1e3, 2)},
+                     "avg_launch_us": round(dec_ms * 1e3, 2),
+                     "avg_launch_us_evented": round(dec_ev_ms * 1e3, 2)},
         "phase2_us": round(red_ms * 1e3, 2),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }
