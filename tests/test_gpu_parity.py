@@ -199,6 +199,24 @@ def test_decode_small(orc, case):
         check_output(w, orc, out)
 
 
+@pytest.mark.parametrize("bs", [256, 1024])
+@pytest.mark.parametrize("kv", ["same", "fp8"])
+def test_decode_largest_blocks(orc, bs, kv):
+    """Block sizes up to the ABI's largest (1024): a split lies inside one or
+    two blocks, a sequence may end anywhere in its last block; every
+    phase-1 kernel that takes the shape (auto = the grouped-head one, and
+    the vector one), query-dtype and fp8 caches."""
+    say(f"decode block size {bs} kv={kv}")
+    w = workloads.custom(seed=60 + bs, seq_lens=[3000, 1, bs, bs + 1, 0, 700, 2 * bs - 1], num_heads=16,
+                         num_kv_heads=2, head_size=128, block_size=bs, dtype="bf16", kv_cache=kv,
+                         k_scale=0.05 if kv == "fp8" else 1.0, v_scale=0.05 if kv == "fp8" else 1.0,
+                         poison=True)
+    for kernel in ("auto", "valu"):
+        out, tmp, ml, es = run_gpu(w, kernel=kernel)
+        check_partials(w, orc, tmp, ml, es)
+        check_output(w, orc, out)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
 def test_decode_output_dtypes(orc, out_dtype):
     say(f"decode output dtype {out_dtype}")
