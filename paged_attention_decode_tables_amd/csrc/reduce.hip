@@ -133,6 +133,12 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     // Balanced splits fill a prefix of the slots, most sequences more than a
     // batch of them: the first batch is requested the same way.
     const bool early = !p.num_splits;
+    // Balanced splits: the statistics of the second batch and of the slot
+    // after it come with the first batch, so a group with at most 2*RB
+    // splits needs two dependent round trips (statistics and first rows,
+    // then the second rows) instead of four, and knows where its splits end
+    // without reading a batch of empty slots.
+    float mv2[RB], lv2[RB], mnext = -INFINITY;
     if (early) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
@@ -146,6 +152,16 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
                 mv[r] = -INFINITY;
                 lv[r] = 0.0f;
             }
+        }
+        if (balanced) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int64_t q = q0 + (int64_t)(RB + r) * NG;
+                mv2[r] = q < p.max_num_parts ? ml[q] : -INFINITY;
+                lv2[r] = q < p.max_num_parts ? es[q] : 0.0f;
+            }
+            const int64_t q = q0 + (int64_t)2 * RB * NG;
+            mnext = q < p.max_num_parts ? ml[q] : -INFINITY;
         }
     }
     // the split count is read alongside the length (not behind a test of
@@ -183,6 +199,26 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
         }
         fold();
         q0 += (int64_t)NG * RB;
+        if (balanced && q0 < n) {  // the second batch, its statistics in hand
+            bool ended = false;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                mv[r] = mv2[r];
+                lv[r] = lv2[r];
+                ended |= mv[r] == -INFINITY;
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                if (mv[r] != -INFINITY)
+                    load_cols<TmpE, EPT>(tmp + (q0 + (int64_t)r * NG) * p.tmp_sp, rows[r]);
+                else
+                    zero_row(r);
+            }
+            fold();
+            // an empty slot in this batch or right after it ends the group
+            n = ended || mnext == -INFINITY ? q0 : n;
+            q0 += (int64_t)NG * RB;
+        }
     }
     for (; q0 < n; q0 += (int64_t)NG * RB) {
         if (!balanced) {  // every split below n is live: all loads at once

@@ -609,6 +609,43 @@ def test_decode_mla_balanced_all_empty():
     assert torch.all(ml == -math.inf) and torch.all(es == 0)
 
 
+BAL_REDUCE_CASES = [
+    # name, Dv, split-row dtype, max_parts, live slots per row (0: empty sequence)
+    ("dv512_bf16", 512, torch.bfloat16, 16, [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 0]),
+    ("dv128_f32", 128, torch.float32, 40, [1, 4, 15, 16, 17, 31, 32, 33, 39, 40, 0, 8]),
+]
+
+
+@pytest.mark.parametrize("case", BAL_REDUCE_CASES, ids=[c[0] for c in BAL_REDUCE_CASES])
+def test_reduce_balanced_slot_counts(orc, case):
+    """Phase 2 on balanced-split partials alone: each row's live slots are a
+    prefix of its slots (m = -inf, l = 0 and NaN rows after it), of every
+    length from one slot to all of them, around the merge's batch
+    boundaries. Against the oracle's merge over that many splits (a split
+    count k with lengths 6400 k gives exactly k splits of 6400 tokens)."""
+    name, Dv, tdt, P, counts = case
+    say(f"reduce balanced slot counts {name}")
+    gen = torch.Generator().manual_seed(zlib.crc32(name.encode()))
+    S, H = len(counts), 4
+    ml = torch.randn((S, H, P), generator=gen) * 3.0
+    es = torch.rand((S, H, P), generator=gen) * 50.0 + 0.5
+    tmp = torch.randn((S, H, P, Dv), generator=gen).to(tdt)
+    for s, k in enumerate(counts):
+        ml[s, :, k:] = -math.inf
+        es[s, :, k:] = 0.0
+        tmp[s, :, k:] = float("nan")
+    lens = torch.tensor([6400 * k for k in counts], dtype=torch.int32)
+    out = torch.full((S, H, Dv), float("nan"), device=DEV)
+    pad.paged_attn_reduce(out, tmp.to(DEV), es.to(DEV), ml.to(DEV), lens.to(DEV), partition_size=0)
+    torch.cuda.synchronize()
+    want = orc.reduce(np64(tmp), np64(ml), np64(es), lens.numpy(), partition_size=64,
+                      num_splits=np.array([max(k, 1) for k in counts], dtype=np.int32))
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    err = np.abs(got - want)
+    assert (err <= 2e-6 + 2e-6 * np.abs(want)).all(), err.max()
+
+
 def test_decode_mla_balanced_config5(orc):
     """The MLA workload as the benchmark runs it (one token range per compute
     unit): every sequence's output and every piece's statistics."""
