@@ -195,7 +195,7 @@ __host__ __device__ constexpr int mla_ftail(int t) { return (t >> 1) & 7; }
 constexpr int kMlaChunk = 32;             // tokens per chunk
 constexpr int kMlaBuf = PA_MLA_BUF;       // chunk slots in the LDS ring
 #ifndef PA_MLA_BUF8
-#define PA_MLA_BUF8 6
+#define PA_MLA_BUF8 4
 #endif
 constexpr int kMlaBuf8 = PA_MLA_BUF8;     // fp8 caches: chunk slots of fp8 rows in the copy ring
 constexpr int kMlaKAhead = PA_MLA_KAHEAD; // QK operand reads in flight ahead of their MFMAs
@@ -484,21 +484,22 @@ void k_decode_mla(DecodeParams p)
     static_assert(PR == MP + 8 && TPW % 8 == 0, "ring layout: 64 + 8 pieces a row, tail rows 8 to a copy");
     static_assert(KS % 4 == 0 && DT % 2 == 0, "tiling");
     static_assert(IPC * (NB - 2) <= 63, "vmcnt is a 6-bit field");
+    static_assert(!KV8 || NB >= 3, "fp8: chunk c+1 is widened while chunk c is in use");
 
     // The copy ring: NB slots of CT rows. Caches of the query's type are
     // copied straight into the layout QK and P.V read (see mla_fmain); fp8
     // rows land as copied (576-byte rows) and each wave widens its rows of
-    // the current chunk into one more slot in that layout.
+    // chunk c+1, during chunk c, into the other of two slots in that layout.
     constexpr int SLOT = CT * PR, SLOT8 = CT * P8;  // u32x4 words of a slot
-    __shared__ __attribute__((aligned(256))) u32x4 ring[KV8 ? SLOT + NB * SLOT8 : NB * SLOT];
+    __shared__ __attribute__((aligned(256))) u32x4 ring[KV8 ? 2 * SLOT + NB * SLOT8 : NB * SLOT];
     // LDS byte addresses: the slot QK and P.V read for chunk c, the slot its
     // copies land in
     auto use_slot = [](int c) -> uint32_t {
-        return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[KV8 ? 0 : (c % NB) * SLOT]);
+        return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[KV8 ? (c & 1) * SLOT : (c % NB) * SLOT]);
     };
     auto copy_slot = [](int c) -> uint32_t {
         return (uint32_t)(uintptr_t)((
-            __attribute__((address_space(3))) const char*)&ring[KV8 ? SLOT + (c % NB) * SLOT8 : (c % NB) * SLOT]);
+            __attribute__((address_space(3))) const char*)&ring[KV8 ? 2 * SLOT + (c % NB) * SLOT8 : (c % NB) * SLOT]);
     };
     __shared__ u32x4 pbuf[G * 4];  // probabilities of a chunk: [head][32 tokens] of T, 64 B a head
     __shared__ int rerun_flag;
@@ -884,15 +885,27 @@ void k_decode_mla(DecodeParams p)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if constexpr (KV8) {
-            // the barrier above: every wave is done with chunk c-1 in the use slot
-            widen(c);
-            lds_barrier();  // every wave's rows of chunk c are widened
-        }
+    };
+    // fp8: widen this wave's rows of chunk c+1 into the other use slot (every
+    // wave finished chunk c-1, its last reader, before chunk c's first
+    // barrier), once its copies have landed: at most the copies of the
+    // chunks after it, up to c+NB-2, are still outstanding. The next
+    // barrier publishes the rows; it is one fewer barrier a chunk than
+    // widening chunk c at its start, and early waves do it while they would
+    // wait at the probability barrier anyway.
+    auto widen_next = [&](int c) {
+        if (c + 1 >= nc) return;
+        if (c + NB - 2 < nc)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(IPC * (NB - 3)));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        widen(c + 1);
     };
     // refill the slot freed at chunk c's first barrier; then every wave's
-    // probabilities of the chunk are in the P buffer
+    // probabilities of the chunk (and, fp8, its widened rows of chunk c+1)
+    // are in LDS
     auto p_ready = [&](int c) {
+        if constexpr (KV8) widen_next(c);
         if (c + NB - 1 < nc) issue(c + NB - 1, pg_next);
         lds_barrier();
     };
@@ -907,6 +920,7 @@ void k_decode_mla(DecodeParams p)
         // One memory round trip for the query, the first chunks and the
         // previous piece's stores; no wait inside the loop covers them.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        if constexpr (KV8) widen(0);  // published by chunk 0's first barrier
         for (int c = 0; c < nc; ++c) {
             advance(c);
             const f32x16 sacc = qk(c);
