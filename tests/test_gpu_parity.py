@@ -902,3 +902,68 @@ def test_decode_mla_fp8_balanced_config5(orc):
     check_balanced_pieces(w, orc, tmp, ml, es, cus, max_parts)
     err = check_output(w, orc, out)
     say(f"decode mla fp8 balanced config5: max abs err {err:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Cache offsets past 2^31 elements: every decode kernel forms a cache address
+# as a 64-bit page id times a 64-bit page stride. The same step on a cache
+# whose used blocks sit past element 2^31 (the rest NaN) must give the same
+# bits as on the compact cache, and match the oracle.
+
+BIG_OFFSET_CASES = [
+    ("grouped_heads_bf16", lambda: workloads.custom(seed=41, seq_lens=[700, 33, 1100], num_heads=16, num_kv_heads=2,
+                                                    head_size=128, block_size=16, dtype="bf16")),
+    ("one_column_f16", lambda: workloads.custom(seed=42, seq_lens=[900, 5, 1300], num_heads=4, num_kv_heads=4,
+                                                head_size=128, block_size=16, dtype="f16")),
+    ("latent_rows_bf16", lambda: workloads.mla_custom(seed=43, seq_lens=[600, 70], num_heads=128)),
+    ("latent_rows_fp8", lambda: workloads.mla_custom(seed=44, seq_lens=[600, 70], num_heads=128, kv_cache="fp8")),
+]
+
+
+def _page_elems(t: torch.Tensor) -> int:
+    return t[0].numel()
+
+
+@pytest.mark.parametrize("case", BIG_OFFSET_CASES, ids=[c[0] for c in BIG_OFFSET_CASES])
+def test_cache_offsets_past_2_31_elements(orc, case):
+    name, make = case
+    w = make()
+    say(f"cache offsets past 2^31 elements: {name}")
+    want = run_gpu(w)
+    g = w.to(DEV)
+    fp8 = g.key_cache.dtype == torch.uint8
+    poison = dict(fill_value=workloads.FP8_NAN_CODE) if fp8 else dict(fill_value=float("nan"))
+    nb = g.key_cache.shape[0]
+    if w.latent is not None:
+        off = 2 ** 31 // _page_elems(g.latent) + 1000
+        big = torch.full((off + nb, *g.latent.shape[1:]), dtype=g.latent.dtype, device=DEV, **poison)
+        big[off:] = g.latent
+        kc, vc = workloads._mla_views(big, w.v_head_size)
+    else:
+        off = 2 ** 31 // _page_elems(g.key_cache) + 1000
+        kc = torch.full((off + nb, *g.key_cache.shape[1:]), dtype=g.key_cache.dtype, device=DEV, **poison)
+        vc = torch.full((off + nb, *g.value_cache.shape[1:]), dtype=g.value_cache.dtype, device=DEV, **poison)
+        kc[off:] = g.key_cache
+        vc[off:] = g.value_cache
+    assert off * kc.stride(0) > 2 ** 31 and off * vc.stride(0) > 2 ** 31
+    bt = g.block_tables + off
+    assert int(bt.max()) < kc.shape[0]
+    R = w.num_seqs * w.num_group
+    max_parts = max_parts_for(w, 512)
+    tmp = torch.full((R, w.num_heads, max_parts, w.v_head_size), float("nan"), device=DEV)
+    ml = torch.full((R, w.num_heads, max_parts), float("nan"), device=DEV)
+    es = torch.full((R, w.num_heads, max_parts), float("nan"), device=DEV)
+    pad.paged_attn_decode(tmp, es, ml, g.query, kc, vc, bt, g.seq_lens, w.scale, w.max_seq_len,
+                          partition_size=512, alibi_slopes=g.alibi_slopes, k_scale=w.k_scale,
+                          v_scale=w.v_scale, num_group=w.num_group)
+    out = torch.full((R, w.num_heads, w.v_head_size), float("nan"), device=DEV)
+    pad.paged_attn_reduce(out, tmp, es, ml, g.seq_lens, partition_size=512, num_group=w.num_group)
+    torch.cuda.synchronize()
+    got = (out.cpu(), tmp.cpu(), ml.cpu(), es.cpu())
+    del kc, vc, tmp, ml, es, out
+    if w.latent is not None:
+        del big
+    torch.cuda.empty_cache()
+    for a, b, what in zip(got, want, ("output", "tmp_output", "max_logits", "exp_sums")):
+        torch.testing.assert_close(a, b, rtol=0, atol=0, equal_nan=True, msg=f"{name}: {what}")
+    check_output(w, orc, got[0])
