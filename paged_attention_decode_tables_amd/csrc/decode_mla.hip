@@ -13,8 +13,9 @@
 //
 //   staging  the chunk's 32 latent rows are copied HBM -> LDS by direct
 //            global-to-LDS loads (no registers hold data in flight, the
-//            nontemporal hint on) into a ring of kMlaBuf chunk slots,
-//            up to kMlaBuf-1 chunks ahead. A slot holds the rows' first 64 16-byte
+//            nontemporal hint on) into a ring of kMlaBuf chunk slots
+//            (kMlaBuf64 at G = 64, so that two workgroups share a compute
+//            unit), up to one fewer chunks ahead. A slot holds the rows' first 64 16-byte
 //            pieces as 1 KB rows and their last 8 pieces as 128-byte rows
 //            (see mla_fmain / mla_ftail for the bank swizzle), so each copy
 //            instruction is one row from one page: wave w copies rows
@@ -198,6 +199,12 @@ constexpr int kMlaBuf = PA_MLA_BUF;       // chunk slots in the LDS ring
 #define PA_MLA_BUF8 4
 #endif
 constexpr int kMlaBuf8 = PA_MLA_BUF8;     // fp8 caches: chunk slots of fp8 rows in the copy ring
+// G = 64 (two waves): two chunk slots, so that two workgroups fit in a
+// compute unit's LDS and all four SIMDs work (one chunk in flight each)
+#ifndef PA_MLA_BUF64
+#define PA_MLA_BUF64 2
+#endif
+constexpr int kMlaBuf64 = PA_MLA_BUF64;
 constexpr int kMlaKAhead = PA_MLA_KAHEAD; // QK operand reads in flight ahead of their MFMAs
 constexpr int kMlaHeadsPerWave = 32;
 // Balanced splits: virtual tokens charged for each piece a worker starts
@@ -474,7 +481,7 @@ void k_decode_mla(DecodeParams p)
     constexpr int KS = D / 16;                    // QK k-steps
     constexpr int P8 = D / 16;                    // 16-byte pieces of an fp8 latent row (36)
     constexpr int IP8 = (TPW * P8 + 63) / 64;     // fp8 copy instructions per wave per chunk
-    constexpr int NB = KV8 ? kMlaBuf8 : kMlaBuf;  // chunk slots of the copy ring
+    constexpr int NB = KV8 ? kMlaBuf8 : NW == 2 ? kMlaBuf64 : kMlaBuf;  // chunk slots of the copy ring
     constexpr int IPC = KV8 ? IP8 : IPW;          // copy instructions per wave per chunk
     constexpr int HPW = kMlaHeadsPerWave;
     constexpr int G = HPW * NW;                   // heads of the workgroup
