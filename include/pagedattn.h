@@ -166,9 +166,9 @@ typedef struct pa_decode_args {
     int32_t num_workers;         /* balanced splits only (partition_size == 0): number of
                                     token ranges. One range per workgroup: one
                                     workgroup fills a compute unit at 128 heads per
-                                    kv head, two share one at 64 heads (caches of the
-                                    query's type), so the compute-unit count or twice
-                                    it. Ignored otherwise */
+                                    kv head, two share one at 64 heads, so the
+                                    compute-unit count or twice it. Ignored
+                                    otherwise */
     const float* alibi_slopes;   /* optional, [num_heads] fp32 (see "Variants") */
     int32_t kv_dtype;            /* 0 (or equal to dtype): caches hold dtype;
                                     PA_FP8_E4M3: fp8 caches with the scales below */

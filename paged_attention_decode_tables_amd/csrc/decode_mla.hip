@@ -205,6 +205,9 @@ constexpr int kMlaBuf8 = PA_MLA_BUF8;     // fp8 caches: chunk slots of fp8 rows
 #define PA_MLA_BUF64 2
 #endif
 constexpr int kMlaBuf64 = PA_MLA_BUF64;
+// G = 64 over fp8 caches: two fp8 slots and one widened slot (widened at the
+// start of each chunk), for the same two workgroups a compute unit
+constexpr int kMlaBuf8x64 = 2;
 constexpr int kMlaKAhead = PA_MLA_KAHEAD; // QK operand reads in flight ahead of their MFMAs
 constexpr int kMlaHeadsPerWave = 32;
 // Balanced splits: virtual tokens charged for each piece a worker starts
@@ -481,7 +484,8 @@ void k_decode_mla(DecodeParams p)
     constexpr int KS = D / 16;                    // QK k-steps
     constexpr int P8 = D / 16;                    // 16-byte pieces of an fp8 latent row (36)
     constexpr int IP8 = (TPW * P8 + 63) / 64;     // fp8 copy instructions per wave per chunk
-    constexpr int NB = KV8 ? kMlaBuf8 : NW == 2 ? kMlaBuf64 : kMlaBuf;  // chunk slots of the copy ring
+    constexpr int NB = KV8 ? (NW == 2 ? kMlaBuf8x64 : kMlaBuf8) : NW == 2 ? kMlaBuf64 : kMlaBuf;  // chunk slots of the copy ring
+    constexpr int NUSE = KV8 ? (NW == 2 ? 1 : 2) : 0;  // fp8: slots of widened rows
     constexpr int IPC = KV8 ? IP8 : IPW;          // copy instructions per wave per chunk
     constexpr int HPW = kMlaHeadsPerWave;
     constexpr int G = HPW * NW;                   // heads of the workgroup
@@ -491,22 +495,23 @@ void k_decode_mla(DecodeParams p)
     static_assert(PR == MP + 8 && TPW % 8 == 0, "ring layout: 64 + 8 pieces a row, tail rows 8 to a copy");
     static_assert(KS % 4 == 0 && DT % 2 == 0, "tiling");
     static_assert(IPC * (NB - 2) <= 63, "vmcnt is a 6-bit field");
-    static_assert(!KV8 || NB >= 3, "fp8: chunk c+1 is widened while chunk c is in use");
+    static_assert(!KV8 || NUSE == 1 || NB >= 3, "fp8: chunk c+1 is widened while chunk c is in use");
 
     // The copy ring: NB slots of CT rows. Caches of the query's type are
     // copied straight into the layout QK and P.V read (see mla_fmain); fp8
     // rows land as copied (576-byte rows) and each wave widens its rows of
-    // chunk c+1, during chunk c, into the other of two slots in that layout.
+    // chunk c+1, during chunk c, into the other of two slots in that layout
+    // (G = 64: its rows of chunk c into the one slot, at the chunk's start).
     constexpr int SLOT = CT * PR, SLOT8 = CT * P8;  // u32x4 words of a slot
-    __shared__ __attribute__((aligned(256))) u32x4 ring[KV8 ? 2 * SLOT + NB * SLOT8 : NB * SLOT];
+    __shared__ __attribute__((aligned(256))) u32x4 ring[KV8 ? NUSE * SLOT + NB * SLOT8 : NB * SLOT];
     // LDS byte addresses: the slot QK and P.V read for chunk c, the slot its
     // copies land in
     auto use_slot = [](int c) -> uint32_t {
-        return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[KV8 ? (c & 1) * SLOT : (c % NB) * SLOT]);
+        return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)&ring[KV8 ? (NUSE == 2 ? (c & 1) * SLOT : 0) : (c % NB) * SLOT]);
     };
     auto copy_slot = [](int c) -> uint32_t {
         return (uint32_t)(uintptr_t)((
-            __attribute__((address_space(3))) const char*)&ring[KV8 ? 2 * SLOT + (c % NB) * SLOT8 : (c % NB) * SLOT]);
+            __attribute__((address_space(3))) const char*)&ring[KV8 ? NUSE * SLOT + (c % NB) * SLOT8 : (c % NB) * SLOT]);
     };
     __shared__ u32x4 pbuf[G * 4];  // probabilities of a chunk: [head][32 tokens] of T, 64 B a head
     __shared__ int rerun_flag;
@@ -892,6 +897,11 @@ void k_decode_mla(DecodeParams p)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (KV8 && NUSE == 1) {
+            // the barrier above: every wave is done with chunk c-1 in the slot
+            widen(c);
+            lds_barrier();  // every wave's rows of chunk c are widened
+        }
     };
     // fp8: widen this wave's rows of chunk c+1 into the other use slot (every
     // wave finished chunk c-1, its last reader, before chunk c's first
@@ -912,7 +922,7 @@ void k_decode_mla(DecodeParams p)
     // probabilities of the chunk (and, fp8, its widened rows of chunk c+1)
     // are in LDS
     auto p_ready = [&](int c) {
-        if constexpr (KV8) widen_next(c);
+        if constexpr (KV8 && NUSE == 2) widen_next(c);
         if (c + NB - 1 < nc) issue(c + NB - 1, pg_next);
         lds_barrier();
     };
@@ -927,7 +937,7 @@ void k_decode_mla(DecodeParams p)
         // One memory round trip for the query, the first chunks and the
         // previous piece's stores; no wait inside the loop covers them.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        if constexpr (KV8) widen(0);  // published by chunk 0's first barrier
+        if constexpr (KV8 && NUSE == 2) widen(0);  // published by chunk 0's first barrier
         for (int c = 0; c < nc; ++c) {
             advance(c);
             const f32x16 sacc = qk(c);

@@ -890,6 +890,17 @@ def test_decode_mla_fp8_balanced(orc):
     check_output(w, orc, out)
 
 
+def test_decode_mla_fp8_balanced_g64(orc):
+    """64 heads over fp8 latent rows (one widened slot, two workgroups a
+    compute unit), balanced splits over 16 token ranges."""
+    say("decode mla fp8 balanced, 64 heads")
+    w = workloads.mla_custom(seed=512, seq_lens=[1, 15, 16, 17, 100, 513, 1030, 0, 700, 33, 2200], num_heads=64,
+                             kv_cache="fp8", k_scale=0.04, v_scale=0.05, poison=True)
+    out, tmp, ml, es = run_balanced(w, 16, 12)
+    check_balanced_pieces(w, orc, tmp, ml, es, 16, 12)
+    check_output(w, orc, out)
+
+
 def test_decode_mla_fp8_balanced_config5(orc):
     """The MLA workload with fp8 latent rows as the benchmark runs it
     (balanced splits, one token range per compute unit): every sequence's
