@@ -62,6 +62,13 @@ def kernel_kind(w) -> str:
     return "valu"
 
 
+def balanced_workers(w: workloads.Workload, cus: int) -> int:
+    """Token ranges for the latent-row kernel's balanced splits: one
+    workgroup a compute unit at 128 heads per kv head, two at 64 (the
+    library's rule for num_workers)."""
+    return cus * (2 if w.num_heads // w.num_kv_heads == 64 else 1)
+
+
 def kernel_source_hash(kind: str) -> str:
     path = os.path.join(ROOT, "paged_attention_decode_tables_amd", "csrc", KERNEL_SOURCES[kind])
     h = hashlib.sha256()
@@ -448,6 +455,9 @@ def build_parser() -> argparse.ArgumentParser:
     ap.add_argument("--num-group", type=int, default=1,
                     help="query tokens per sequence (configs 2-5): each attends over the whole "
                          "sequence; the grouped-head kernel reads the cache once for all of them")
+    ap.add_argument("--mla-heads", type=int, choices=(128, 64), default=128,
+                    help="query heads over config 5's latent head (64: the same lengths, a "
+                         "64-head query)")
     return ap
 
 
@@ -482,11 +492,12 @@ def main():
 
     log(f"bench: generating workload {args.config}")
     w = workloads.config(args.config, kv_cache=args.kv_cache, alibi=args.alibi,
-                         num_group=args.num_group)
+                         num_group=args.num_group, mla_heads=args.mla_heads)
     # The MLA workload's split policy is not fixed by its definition: it runs
-    # with balanced splits, one token range per compute unit.
+    # with balanced splits, as many token ranges as workgroups fit at once.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    workers = cus if (kernel_kind(w) == "mla" and args.kernel == "auto" and not args.fixed_splits) else 0
+    mla = kernel_kind(w) == "mla" and args.kernel == "auto" and not args.fixed_splits
+    workers = balanced_workers(w, cus) if mla else 0
     tmp_dtype = w.dtype if args.tmp_dtype == "query" else torch.float32
     step = Step(w, balanced_workers=workers, tmp_dtype=tmp_dtype, kernel=args.kernel)
     kind = step.kernel_kind()  # the library's own choice

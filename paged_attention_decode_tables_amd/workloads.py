@@ -293,17 +293,21 @@ FP8_WORKLOAD_SCALE = 1.0 / 32
 
 
 def config(cfg: int, *, poison: bool = False, kv_cache: str = "same",
-           alibi: bool = False, num_group: int = 1) -> Workload:
+           alibi: bool = False, num_group: int = 1, mla_heads: int = 128) -> Workload:
     """The five reference workloads (seed = config number). Configs 2-4 also
     come with fp8 caches (kv_cache "fp8", both scales FP8_WORKLOAD_SCALE,
     name suffix "_kvfp8"), with ALiBi slopes (suffix "_alibi") and with
     num_group query tokens per sequence (configs 2-5, suffix "_qg<n>"; the
-    query draw has num_group rows per sequence)."""
+    query draw has num_group rows per sequence). Config 5 also comes with 64
+    query heads over its latent head (mla_heads=64, suffix "_h64": the same
+    lengths and draw order, a query of 64 heads)."""
     if kv_cache != "same" and cfg not in (2, 3, 4, 5):
         raise ValueError("fp8 caches are drawn for configs 2-5")
     if num_group != 1 and cfg not in (2, 3, 4, 5):
         raise ValueError("query groups are drawn for configs 2-5")
-    w = _config(cfg, poison=poison, kv_cache=kv_cache, num_group=num_group)
+    if mla_heads != 128 and (cfg != 5 or mla_heads != 64):
+        raise ValueError("config 5 alone comes with 64 heads")
+    w = _config(cfg, poison=poison, kv_cache=kv_cache, num_group=num_group, mla_heads=mla_heads)
     if num_group != 1:
         w.name += f"_qg{num_group}"
     if alibi:
@@ -312,7 +316,7 @@ def config(cfg: int, *, poison: bool = False, kv_cache: str = "same",
     return w
 
 
-def _config(cfg: int, *, poison: bool, kv_cache: str, num_group: int = 1) -> Workload:
+def _config(cfg: int, *, poison: bool, kv_cache: str, num_group: int = 1, mla_heads: int = 128) -> Workload:
     gen = torch.Generator().manual_seed(cfg)
     kv = dict(kv_cache=kv_cache, num_group=num_group)
     if cfg == 1:
@@ -353,7 +357,7 @@ def _config(cfg: int, *, poison: bool, kv_cache: str, num_group: int = 1) -> Wor
         w.device_core_count = 256
         return w
     if cfg == 5:
-        return _mla(gen, poison=poison, num_group=num_group, kv_cache=kv_cache)
+        return _mla(gen, poison=poison, num_group=num_group, kv_cache=kv_cache, H=mla_heads)
     raise ValueError(f"unknown config {cfg}")
 
 
@@ -405,8 +409,8 @@ def _poison_rows(latent, rows):
         latent[rows] = float("nan")
 
 
-def _mla(gen, *, poison, num_group=1, kv_cache="same"):
-    S, H, D, Dv = 64, 128, 576, 512
+def _mla(gen, *, poison, num_group=1, kv_cache="same", H=128):
+    S, D, Dv = 64, 576, 512
     lens = _draw_lengths(5, gen)
     total = int(lens.sum())
     nb = total + (1 if poison else 0)
@@ -426,7 +430,8 @@ def _mla(gen, *, poison, num_group=1, kv_cache="same"):
     k, v = _mla_views(latent, Dv)
     fp8 = kv_cache != "same"
     sc = FP8_WORKLOAD_SCALE if fp8 else 1.0
-    return Workload(name=CONFIG_NAMES[5] + ("_kvfp8" if fp8 else ""), description="MLA-style decode bf16",
+    name = CONFIG_NAMES[5] + ("_h64" if H == 64 else "") + ("_kvfp8" if fp8 else "")
+    return Workload(name=name, description="MLA-style decode bf16",
                     dtype=dt, seq_lens=lens, block_tables=bt, query=q, key_cache=k, value_cache=v,
                     scale=1.0 / math.sqrt(192.0), num_heads=H, num_kv_heads=1, head_size=D,
                     v_head_size=Dv, block_size=1, x=16 if fp8 else 8, num_blocks=nb, cu_num_blocks=cu,

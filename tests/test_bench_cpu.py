@@ -7,6 +7,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -53,3 +54,17 @@ def test_headline_workload_is_the_default():
     head_dim 128, block size 16, 512-token partitions)."""
     args = bench.build_parser().parse_args([])
     assert args.config == 3 and args.gpus == 1 and args.op == "decode" and args.kv_cache == "same"
+
+
+def test_latent_rows_at_64_heads():
+    """Config 5 at 64 heads: the same lengths, the latent-row kernel, and two
+    token ranges a compute unit (two workgroups fit one)."""
+    w64 = workloads.config(5, mla_heads=64)
+    w = workloads.config(5)
+    assert w64.num_heads == 64 and w64.name.endswith("_h64")
+    assert torch.equal(w64.seq_lens, w.seq_lens)
+    assert bench.kernel_kind(w64) == "mla"
+    assert bench.balanced_workers(w64, 256) == 512 and bench.balanced_workers(w, 256) == 256
+    assert bench.build_parser().parse_args(["--config", "5", "--mla-heads", "64"]).mla_heads == 64
+    with pytest.raises(ValueError):
+        workloads.config(3, mla_heads=64)
