@@ -11,7 +11,9 @@
 // still one round); with split counts or balanced splits, whose
 // sequences mostly have a few splits, NG is the least that fills a wave.
 // Each thread folds its splits into a local (max, sum, row) state, RB
-// splits at a time with all their loads in flight, and the groups' states
+// splits at a time with all their loads in flight (16-bit rows: each
+// split's 16 bytes kept packed until the fold, 4 registers and not 8
+// widened values, which lets 7 instead of 6 waves share a SIMD), and the groups' states
 // are merged once through LDS with the same rule (M = max m_g, weights
 // exp(m_g - M)): one memory round trip and one barrier. With fixed
 // partitions the first batch is requested together with the sequence's
@@ -22,6 +24,8 @@
 // the balanced rule fills a prefix of them). Skewed batch 13.3 -> 7.2 us
 // and MLA batch 25.0 -> 17.2 us against one workgroup per head, 8 splits
 // per batch and groups sized by max_num_parts.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace pa {
@@ -43,19 +47,25 @@ template <int C, int NG> constexpr int red_heads() { return kRedMaxThreads / (C 
 // columns per thread for split rows of element type TmpE
 template <class TmpE> constexpr int red_ept() { return TmpE::size == 4 ? 4 : 8; }
 
-// EPT consecutive partial values at p (16-byte aligned), widened
+// The 16 bytes of EPT consecutive partial values at p (16-byte aligned):
+// four fp32 values, or eight 16-bit values kept packed as loaded (a batch
+// of rows then takes 4 registers a split, not 8) and widened at the fold.
+template <int EPT> using RowPiece = typename std::conditional<EPT == 4, f32x4, u32x4>::type;
 template <class TmpE, int EPT>
-__device__ __forceinline__ void load_cols(const typename TmpE::storage* p, float (&v)[EPT])
+__device__ __forceinline__ RowPiece<EPT> load_cols(const typename TmpE::storage* p)
+{
+    if constexpr (EPT == 4) return load_tmp4<TmpE>(p);
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+// value i of such a piece, widened
+template <class TmpE, int EPT>
+__device__ __forceinline__ float col_of(const RowPiece<EPT>& w, int i)
 {
     if constexpr (EPT == 4) {
-        const f32x4 w = load_tmp4<TmpE>(p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = w[i];
+        return w[i];
     } else {
         using S = typename TmpE::storage;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = to_f32(__builtin_bit_cast(S, (uint16_t)(w[i >> 1] >> (16 * (i & 1)))));
+        return to_f32(__builtin_bit_cast(S, (uint16_t)(w[i >> 1] >> (16 * (i & 1)))));
     }
 }
 
@@ -95,12 +105,9 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
     float acc[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) acc[i] = 0.0f;
-    float rows[RB][EPT];
+    RowPiece<EPT> rows[RB];  // 16-byte pieces as loaded
     float mv[RB], lv[RB];
-    auto zero_row = [&](int r) {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) rows[r][i] = 0.0f;
-    };
+    auto zero_row = [&](int r) { rows[r] = RowPiece<EPT>{}; };
     // Fold one batch: an empty split (m = -inf) adds nothing; its row may
     // never have been written, so it is dropped by a select, not a multiply.
     auto fold = [&]() {
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
             const bool live = mv[r] != -INFINITY;
             const float w = live ? fast_exp2((mv[r] - mb) * kLog2e) * lv[r] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) acc[i] += live ? w * rows[r][i] : 0.0f;
+            for (int i = 0; i < EPT; ++i) acc[i] += live ? w * col_of<TmpE, EPT>(rows[r], i) : 0.0f;
             W += w;
         }
         M = mb;
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
         for (int r = 0; r < RB; ++r) {
             const int64_t q = q0 + (int64_t)r * NG;
             if (q < p.max_num_parts) {
-                load_cols<TmpE, EPT>(tmp + q * p.tmp_sp, rows[r]);
+                rows[r] = load_cols<TmpE, EPT>(tmp + q * p.tmp_sp);
                 mv[r] = ml[q];
                 lv[r] = es[q];
             } else {
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 if (mv[r] != -INFINITY)
-                    load_cols<TmpE, EPT>(tmp + (q0 + (int64_t)r * NG) * p.tmp_sp, rows[r]);
+                    rows[r] = load_cols<TmpE, EPT>(tmp + (q0 + (int64_t)r * NG) * p.tmp_sp);
                 else
                     zero_row(r);
             }
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
             for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 if (q < n) {
-                    load_cols<TmpE, EPT>(tmp + q * p.tmp_sp, rows[r]);
+                    rows[r] = load_cols<TmpE, EPT>(tmp + q * p.tmp_sp);
                     mv[r] = ml[q];
                     lv[r] = es[q];
                 } else {
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(kRedMaxThreads) void k_reduce(ReduceParams p)  // C
             for (int r = 0; r < RB; ++r) {
                 const int64_t q = q0 + (int64_t)r * NG;
                 if (mv[r] != -INFINITY)
-                    load_cols<TmpE, EPT>(tmp + q * p.tmp_sp, rows[r]);
+                    rows[r] = load_cols<TmpE, EPT>(tmp + q * p.tmp_sp);
                 else
                     zero_row(r);
             }
